@@ -1,0 +1,154 @@
+"""Oracle: the DiT stack forward with every weight resident, in float64.
+
+The weight-streaming method must reproduce exactly what a fully resident model
+computes: the pages verify it by byte-identical outputs across execution
+strategies ([Aug] "NVIDIA B300 GPU Results", correctness paragraph).  So the
+oracle is the plain resident forward.  It reads the same bf16 weights, widened
+exactly to float64, and computes every activation in float64 with no rounding
+to bf16 anywhere.
+
+The pages never spell out the block (the model code is used unchanged, [Jul]
+"Module Architecture").  The block below is the plainest adaLN-Zero DiT block
+that matches the stated workloads (adaLN 6-way modulation from a conditioning
+vector, LayerNorm, fused QKV, attention, output projection, 4d GELU MLP,
+residual).  Readings, all listed in the design doc:
+
+* mod = SiLU(c[:d]) @ W_ada^T + b_ada, split into six d-wide chunks in the
+  order shift1, scale1, gate1, shift2, scale2, gate2;
+* modulation h = LN(x) * (1 + scale) + shift; LN uses the biased variance over
+  the d features and the block's own eps buffer;
+* fused QKV weight [3d, d] holds q, k, v row blocks; head j owns the
+  contiguous columns [j*dh, (j+1)*dh) of each;
+* attention is non-causal, unmasked, scaled by 1/sqrt(dh), softmax over all
+  tokens (max-subtracted);
+* GELU is the exact erf form;
+* residual updates are gated: x += gate * branch;
+* a block of width d reads and updates x[:, :d] (residual width D >= d) and
+  uses c[:d];
+* passes chain: x <- stack(x).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def param_dict(params):
+    """[(name, dtype, array)] -> {name: float64 array} (bf16 widened)."""
+    out = {}
+    for name, dt, arr in params:
+        out[name] = widen_bf16(arr) if dt == "bf16" else np.asarray(arr, dtype=np.float64)
+    return out
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def layer_norm(v, gamma, beta, eps):
+    mean = v.mean(axis=-1, keepdims=True)
+    dev = v - mean
+    var = (dev * dev).mean(axis=-1, keepdims=True)
+    return dev / np.sqrt(var + eps) * gamma + beta
+
+
+def gelu_erf(z):
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def linear(a, w, b):
+    """a @ w^T + b with w stored [out, in]."""
+    return a @ w.T + b
+
+
+def attention(q, k, v, n_heads, chunk=1024):
+    """Per head: softmax(q_j k_j^T / sqrt(dh)) v_j over all keys; heads concatenated.
+
+    q: [Tq, d], k and v: [Tk, d]; computed in query chunks of at most ``chunk``
+    rows (a memory bound only: each query row is independent).
+    """
+    tq, d = q.shape
+    dh = d // n_heads
+    scale = 1.0 / math.sqrt(dh)
+    out = np.empty((tq, d), dtype=np.float64)
+    for j in range(n_heads):
+        cols = slice(j * dh, (j + 1) * dh)
+        kj, vj = k[:, cols], v[:, cols]
+        for r0 in range(0, tq, chunk):
+            s = (q[r0:r0 + chunk, cols] @ kj.T) * scale
+            s -= s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[r0:r0 + chunk, cols] = p @ vj
+    return out
+
+
+def modulation(c, P, d):
+    mod = linear(silu(np.asarray(c[:d], dtype=np.float64))[None, :], P["adaln.weight"],
+                 P["adaln.bias"])[0]
+    return [mod[i * d:(i + 1) * d] for i in range(6)]
+
+
+def dit_block(x, c, P, n_heads):
+    """One block on residual x [T, D] (float64, updated copy returned)."""
+    d = P["norm1.weight"].shape[0]
+    x = np.array(x, dtype=np.float64, copy=True)
+    shift1, scale1, gate1, shift2, scale2, gate2 = modulation(c, P, d)
+    xb = x[:, :d]
+    h = layer_norm(xb, P["norm1.weight"], P["norm1.bias"], P["norm1.eps"][0]) * (1.0 + scale1) + shift1
+    qkv = linear(h, P["attn.qkv.weight"], P["attn.qkv.bias"])
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    a = attention(q, k, v, n_heads)
+    xb += gate1 * linear(a, P["attn.out.weight"], P["attn.out.bias"])
+    h2 = layer_norm(xb, P["norm2.weight"], P["norm2.bias"], P["norm2.eps"][0]) * (1.0 + scale2) + shift2
+    u = gelu_erf(linear(h2, P["mlp.fc1.weight"], P["mlp.fc1.bias"]))
+    xb += gate2 * linear(u, P["mlp.fc2.weight"], P["mlp.fc2.bias"])
+    return x
+
+
+def dit_block_rows(x, c, P, n_heads, rows):
+    """Output rows ``rows`` of one block, computed one query row at a time.
+
+    Keys and values need every token, so LN1 and the k/v projections run over
+    all T rows; everything else runs only for the requested rows.  Used to
+    check sampled outputs at sizes where the full block is too slow on a CPU.
+    """
+    d = P["norm1.weight"].shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float64)
+    shift1, scale1, gate1, shift2, scale2, gate2 = modulation(c, P, d)
+    xb = x[:, :d]
+    h = layer_norm(xb, P["norm1.weight"], P["norm1.bias"], P["norm1.eps"][0]) * (1.0 + scale1) + shift1
+    W, bqkv = P["attn.qkv.weight"], P["attn.qkv.bias"]
+    k = linear(h, W[d:2 * d], bqkv[d:2 * d])
+    v = linear(h, W[2 * d:], bqkv[2 * d:])
+    q = linear(h[rows], W[:d], bqkv[:d])
+    a = attention(q, k, v, n_heads)
+    y = np.array(x[rows], dtype=np.float64, copy=True)
+    yb = y[:, :d]
+    yb += gate1 * linear(a, P["attn.out.weight"], P["attn.out.bias"])
+    h2 = layer_norm(yb, P["norm2.weight"], P["norm2.bias"], P["norm2.eps"][0]) * (1.0 + scale2) + shift2
+    u = gelu_erf(linear(h2, P["mlp.fc1.weight"], P["mlp.fc1.bias"]))
+    yb += gate2 * linear(u, P["mlp.fc2.weight"], P["mlp.fc2.bias"])
+    return y
+
+
+def forward_stack(x, c, blocks, heads, passes):
+    """``passes`` chained passes over the blocks.
+
+    blocks: list of [(name, dtype, array)] per block; heads: heads per block.
+    """
+    Ps = [param_dict(b) for b in blocks]
+    y = np.asarray(x, dtype=np.float64)
+    for _ in range(passes):
+        for P, H in zip(Ps, heads):
+            y = dit_block(y, c, P, H)
+    return y
