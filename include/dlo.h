@@ -1,0 +1,350 @@
+/*
+ * dlo.h -- C ABI of libdlo: double-buffered, layerwise weight streaming of a
+ * DiT block stack on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title):
+ *   [Jul] "Distributed Layerwise Offload", vLLM-Omni project blog, 2026-07-30.
+ *   [Aug] "Distributed Layerwise Offload: Scaling Toward 200B+ DiT Models
+ *         Efficiently in vLLM-Omni", vLLM blog, 2026-08-17.
+ *   [Doc] "Distributed Layerwise Offload", vLLM-Omni design documentation.
+ *
+ * What the library does, end to end:
+ *   1. dlo_plan_blocks      -- per block, flatten parameters by dtype, split each
+ *                              flat buffer into k equal zero-padded shards, and lay
+ *                              the block out in a slot at the offsets an all-gather
+ *                              of those shards would produce ([Aug] s.2).
+ *   2. dlo_pack_host_shards -- copy parameters into the shards, held in pinned host
+ *                              memory ([Jul] "Weight Sharding + AllGather").
+ *   3. dlo_forward_stack    -- stream the blocks through exactly two device slots:
+ *                              a copy stream places block N+1's k shards into the
+ *                              free slot while the compute stream runs block N from
+ *                              the other, parameters re-pointed into the slot with
+ *                              no copy, compute waiting on the copy event
+ *                              ([Jul] "How It Works", [Aug] s.3, [Doc] "AllGather
+ *                              path").  One GPU: the shards are assembled locally,
+ *                              no collective is issued.
+ *   4. dlo_slot_trace       -- the per-step slot record of a run (which block read
+ *                              which slot, what was prefetched where), with
+ *                              optional slot digests and timestamps ([Jul] "Slot
+ *                              Tracking: i%2 + Dynamic Correction").
+ *
+ * Conventions for every entry point:
+ *   - Status codes: DLO_OK (0) or a negative dlo_status.  On any error nothing is
+ *     enqueued on any stream, output handles are set to NULL, and
+ *     dlo_last_error() returns a message (fail closed, [Jul] "Fail-Closed
+ *     Design").  The one exception is DLO_E_HIP during dlo_forward_stack: a HIP
+ *     call failed after work was enqueued; the caller must synchronise both
+ *     streams and treat x as undefined.
+ *   - "device pointer" = memory from hipMalloc (e.g. a PyTorch tensor on the GPU);
+ *     "host pointer" = ordinary or pinned CPU memory.  Streams are hipStream_t
+ *     values passed as void*.
+ *   - Caller-owned memory (slots, x, cond, workspace, streams, parameter sources)
+ *     is never freed or retained by the library beyond the documented lifetime.
+ *   - A plan and its stores may be used from one host thread at a time.
+ */
+#ifndef DLO_H
+#define DLO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DLO_OK = 0,
+  DLO_E_ARG = -1,           /* invalid argument (null pointer, bad size, bad index) */
+  DLO_E_HOSTMEM = -2,       /* ordinary host allocation failed */
+  DLO_E_PIN = -3,           /* pinned host allocation failed */
+  DLO_E_SLOT_SMALL = -4,    /* a slot buffer is smaller than the plan's slot size */
+  DLO_E_PLAN_MISMATCH = -5, /* store / parameter list does not belong to this plan */
+  DLO_E_HIP = -6,           /* a HIP runtime call failed */
+  DLO_E_STATE = -7,         /* object in the wrong state (e.g. store not packed) */
+  DLO_E_UNSUPPORTED = -8,   /* valid but unsupported (block schema, head dim, width) */
+  DLO_E_WORKSPACE = -9      /* workspace smaller than dlo_plan_workspace_bytes */
+} dlo_status;
+
+/* element types of parameter groups */
+enum { DLO_BF16 = 0, DLO_F32 = 1 };
+
+#define DLO_MAX_GROUPS 2   /* one group per element type */
+#define DLO_ALIGN 256      /* byte alignment of regions and extents inside a slot */
+
+/* One parameter, in the block's registration order.  `src` is a host pointer to
+ * numel elements of `dtype` (read by dlo_pack_host_shards only; may be NULL for
+ * dlo_plan_blocks).  `name` is copied by the plan. */
+typedef struct {
+  const char *name;
+  int32_t dtype;
+  int64_t numel;
+  const void *src;
+} dlo_param;
+
+/* One block: its width d_model (the residual columns it reads and updates), its
+ * attention heads, and its parameters in registration order. */
+typedef struct {
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_params;
+  const dlo_param *params;
+} dlo_block;
+
+typedef struct dlo_plan dlo_plan;
+typedef struct dlo_host_store dlo_host_store;
+typedef struct dlo_run dlo_run;
+
+/* ---------------------------------------------------------------------------
+ * Plan ([Aug] s.2 "Weight Sharding with AllGather Reconstruction"; [Jul]
+ * "Double-Buffer Memory Bound")
+ *
+ * For block b and dtype group g (groups in order of first appearance):
+ *   N_g = total elements, S_g = ceil(N_g / k) (equal shards, zero padded),
+ *   region_g = byte offset of the group in a slot: region_0 = 0,
+ *   region_{g+1} = align256(region_g + k * S_g * elt_g);
+ *   extent = align256(end of the last region);
+ *   parameter p lives at region_{g(p)} + (elements before p in its group) * elt.
+ * slot_bytes = max extent over the blocks: the two device slots are each this
+ * large whatever the block count.
+ * ------------------------------------------------------------------------- */
+
+/* Plans n_blocks blocks for k shards.  k >= 1, n_blocks >= 1, every dtype known,
+ * numel >= 0.  The plan copies names and sizes and never keeps `src`.  *out is
+ * set to a new plan (free with dlo_plan_destroy) or NULL on error. */
+int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_plan **out);
+void dlo_plan_destroy(dlo_plan *plan);   /* waits for runs started without a handle */
+
+int32_t dlo_plan_n_blocks(const dlo_plan *plan);
+int32_t dlo_plan_k(const dlo_plan *plan);
+int64_t dlo_plan_slot_bytes(const dlo_plan *plan);   /* -1 if plan is NULL */
+
+typedef struct {
+  int32_t d_model, n_heads, n_params, n_groups;
+  int32_t dtype[DLO_MAX_GROUPS];
+  int64_t numel[DLO_MAX_GROUPS];   /* N_g */
+  int64_t shard[DLO_MAX_GROUPS];   /* S_g, elements per shard */
+  int64_t region[DLO_MAX_GROUPS];  /* byte offset of the group in the slot */
+  int64_t extent;                  /* bytes of the slot the block occupies */
+  int64_t copy_bytes;              /* sum_g k * S_g * elt_g: bytes moved per placement */
+  int32_t is_dit;                  /* 1 if the parameter list is the DiT block schema */
+} dlo_block_info;
+
+int dlo_plan_block_info(const dlo_plan *plan, int32_t b, dlo_block_info *out);
+
+/* Byte offset of parameter p of block b inside a slot (the zero-copy re-point). */
+int dlo_plan_param_offset(const dlo_plan *plan, int32_t b, int32_t p, int64_t *byte_offset);
+
+/* Device workspace needed by dlo_forward_stack for `tokens` rows (batch 1):
+ * activations of one block at the widest d; -1 on error. */
+int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens);
+
+/* ---------------------------------------------------------------------------
+ * Host store ([Aug] s.2: each shard is a pinned DMA buffer)
+ * ------------------------------------------------------------------------- */
+
+#define DLO_STORE_PINNED 0u     /* hipHostMalloc'd shards (DMA-capable; the default) */
+#define DLO_STORE_PAGEABLE 1u   /* ordinary aligned host memory (no GPU needed) */
+
+/* Allocates every shard of every block of the plan (zero-filled).  Shards start
+ * on 4096-byte boundaries.  Fails with DLO_E_PIN / DLO_E_HOSTMEM after freeing
+ * whatever it had allocated. */
+int dlo_host_store_create(const dlo_plan *plan, uint32_t flags, dlo_host_store **out);
+
+/* Destroys the store.  Copies that read it must have completed: the caller
+ * synchronises the copy stream of every run that used it first. */
+void dlo_host_store_destroy(dlo_host_store *store);
+
+/* Packs blocks [b_begin, b_end): blocks[i] describes block b_begin + i and must
+ * list the same parameters (name, dtype, numel, order) as the plan
+ * (DLO_E_PLAN_MISMATCH otherwise), with non-NULL host `src` pointers.  Shard r of
+ * group g receives flat_g[r*S_g, (r+1)*S_g), zero beyond N_g ([Aug] s.2).
+ * Host-only; the sources may be freed afterwards. */
+int dlo_pack_host_shards(dlo_host_store *store, int32_t b_begin, int32_t b_end,
+                         const dlo_block *blocks);
+
+/* Host pointer to shard r of group g of block b, and its size in bytes
+ * (S_g * elt_g).  The memory belongs to the store. */
+int dlo_host_store_shard(const dlo_host_store *store, int32_t b, int32_t g, int32_t r,
+                         const void **ptr, int64_t *bytes);
+
+/* 1 if every block has been packed, else 0. */
+int32_t dlo_host_store_complete(const dlo_host_store *store);
+
+/* ---------------------------------------------------------------------------
+ * Schedule (host-only view of what dlo_forward_stack enqueues)
+ *
+ * Hook rule ([Jul] "Slot Tracking"): hook i starts at slot i % 2; when the
+ * previous hook (block i-1 mod n) has a prefetched slot, hook i uses it; hook i
+ * prefetches block (i+1) mod n into the other slot.  Block 0 is placed in slot 0
+ * before step 0; the last step prefetches nothing.
+ *
+ * Program per run: RECORD(compute, START), WAIT(copy, START),
+ * COPY(block 0 -> slot 0), RECORD(copy, COPIED[0]); then for step t (pass p,
+ * block i, read slot s):
+ *   if t is not the last step:  [t >= 1: WAIT(copy, COMPUTED[s'])]
+ *                               COPY(next block -> s'), RECORD(copy, COPIED[s'])
+ *   WAIT(compute, COPIED[s]), COMPUTE(block i, slot s), RECORD(compute, COMPUTED[s])
+ * where s' = 1 - s.  COPY issues 2k hipMemcpyAsync calls (k shards per dtype
+ * group) to slot + region_g + r * S_g * elt_g.
+ * ------------------------------------------------------------------------- */
+
+enum { DLO_OP_COPY = 0, DLO_OP_COMPUTE = 1, DLO_OP_RECORD = 2, DLO_OP_WAIT = 3 };
+enum { DLO_STREAM_COMPUTE = 0, DLO_STREAM_COPY = 1 };
+enum { DLO_EV_COPIED0 = 0, DLO_EV_COPIED1 = 1, DLO_EV_COMPUTED0 = 2, DLO_EV_COMPUTED1 = 3,
+       DLO_EV_START = 4 };
+
+typedef struct {
+  int32_t kind;     /* DLO_OP_* */
+  int32_t stream;   /* DLO_STREAM_* */
+  int32_t block;    /* COPY / COMPUTE: block index; else -1 */
+  int32_t slot;     /* COPY / COMPUTE: slot; else -1 */
+  int32_t event;    /* RECORD / WAIT: DLO_EV_*; else -1 */
+  int32_t pad;
+  int64_t step;     /* COMPUTE: step t; COPY: the step that will read it; else -1 */
+} dlo_sched_op;
+
+/* Writes the program for `passes` passes (passes >= 1).  If ops is NULL or cap is
+ * too small, only *n_ops is set (and DLO_OK is returned when ops is NULL). */
+int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, int64_t cap,
+                      int64_t *n_ops);
+
+/* ---------------------------------------------------------------------------
+ * Forward ([Jul] "How It Works"; [Aug] s.3 "Double-Buffered Prefetch")
+ *
+ * Block forward (every block must carry the DiT schema of dlo_block_schema;
+ * width d % 256 == 0, d <= 8192, head dim d / n_heads in {64, 128}):
+ *   mod = SiLU(cond[:d]) W_ada^T + b_ada -> shift1, scale1, gate1, shift2, scale2, gate2
+ *   h   = LN1(x[:, :d]) * (1 + scale1) + shift1                      (bf16)
+ *   qkv = h W_qkv^T + b_qkv                                           (bf16)
+ *   a   = per head softmax(q k^T / sqrt(dh)) v                        (bf16)
+ *   x[:, :d] += gate1 * (a W_out^T + b_out)                           (fp32)
+ *   h2  = LN2(x[:, :d]) * (1 + scale2) + shift2                       (bf16)
+ *   u   = GELU_erf(h2 W_1^T + b_1)                                    (bf16)
+ *   x[:, :d] += gate2 * (u W_2^T + b_2)                               (fp32)
+ * bf16 MFMA products accumulate in fp32; LayerNorm statistics and softmax in fp32.
+ * ------------------------------------------------------------------------- */
+
+#define DLO_TRACE_DIGEST 1u  /* digest the slot's regions before and after each block */
+#define DLO_TRACE_TIMING 2u  /* timestamp copies, block computes and every kernel */
+#define DLO_RESIDENT 4u      /* no streaming: block b is read from resident_blocks[b] */
+
+typedef struct {
+  void *slot[2];            /* device, slot_bytes each, distinct (unused if DLO_RESIDENT) */
+  int64_t slot_bytes;       /* capacity of each slot */
+  float *x;                 /* device fp32 [tokens, x_row_stride], updated in place */
+  int64_t x_row_stride;     /* elements; >= the widest block's d */
+  const float *cond;        /* device fp32 [>= widest d]: conditioning vector */
+  void *workspace;          /* device, >= dlo_plan_workspace_bytes(plan, tokens) */
+  int64_t workspace_bytes;
+  void *compute_stream;     /* hipStream_t */
+  void *copy_stream;        /* hipStream_t, distinct from compute_stream */
+  int32_t tokens;           /* rows of x (batch 1), >= 1 */
+  int32_t passes;           /* chained passes over the stack, >= 1 */
+  uint32_t flags;           /* DLO_TRACE_* | DLO_RESIDENT */
+  int32_t pad;
+  const void *const *resident_blocks; /* DLO_RESIDENT: device pointer per block, holding the
+                                         block's slot image (see dlo_place_block) */
+} dlo_forward_args;
+
+/* Enqueues `passes` passes of the stack and returns without waiting.  x is
+ * updated on the compute stream; everything the caller enqueued on the compute
+ * stream before the call happens before the run, and the copy stream waits for
+ * it too.  Each call starts afresh at block 0 in slot 0.  Caller memory must stay
+ * valid until the compute stream has drained.  If run_out is non-NULL it receives
+ * a handle for dlo_slot_trace (free with dlo_run_destroy); otherwise the library
+ * releases the run's resources once it has completed. */
+int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
+                      const dlo_forward_args *args, dlo_run **run_out);
+
+/* Places block b (its k shards per group, at the all-gather offsets) into the
+ * device buffer dst (>= the block's extent) on `stream`: the same copies a
+ * prefetch performs.  Used to build resident images. */
+int dlo_place_block(const dlo_plan *plan, const dlo_host_store *store, int32_t b, void *dst,
+                    int64_t dst_bytes, void *stream);
+
+typedef struct {
+  int64_t step;
+  int32_t pass, block;
+  int32_t read_slot;        /* -1 for a resident run */
+  int32_t prefetch_block;   /* -1 on the last step and for a resident run */
+  int32_t prefetch_slot;    /* -1 likewise */
+  int32_t pad;
+  int64_t prefetch_bytes;   /* bytes copied by this step's prefetch (0 if none) */
+  uint64_t digest_pre;      /* DLO_TRACE_DIGEST: slot regions before the block ran */
+  uint64_t digest_post;     /* ... and after (0 without the flag) */
+  /* DLO_TRACE_TIMING, milliseconds since the run's start event, else -1: */
+  float t_copy_begin, t_copy_end;       /* the copy placing this step's block */
+  float t_compute_begin, t_compute_end; /* this step's block forward */
+} dlo_slot_event;
+
+/* Waits for the run to complete, then copies up to cap records (one per step, in
+ * step order) to out and sets *n_out to the number of steps.  The digest of a
+ * slot is the wrap-around sum, over its regions' 8-byte little-endian words w at
+ * slot byte offset o (a region's last partial word zero-extended), of
+ * splitmix64_finalizer(w + (o / 8) * 0x9E3779B97F4A7C15). */
+int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_out);
+
+/* DLO_TRACE_TIMING: per step, the duration in ms of each of the block's kernels in
+ * launch order (DLO_KERNELS_PER_BLOCK per step), after the run completed. */
+#define DLO_KERNELS_PER_BLOCK 8
+int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
+/* name of kernel j (0 <= j < DLO_KERNELS_PER_BLOCK) of a block forward */
+const char *dlo_kernel_name(int32_t j);
+
+void dlo_run_destroy(dlo_run *run);   /* waits for the run first */
+
+/* Message for the last failure on this thread (valid until the next call). */
+const char *dlo_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * The DiT block schema and its single kernels
+ * ------------------------------------------------------------------------- */
+
+/* Parameter i (0 <= i < 16) of the DiT block schema for width d: name, dtype and
+ * numel, in registration order (adaln.weight [6d,d] bf16, adaln.bias, norm1.weight,
+ * norm1.bias, norm1.eps [1], attn.qkv.weight [3d,d] bf16, attn.qkv.bias,
+ * attn.out.weight [d,d] bf16, attn.out.bias, norm2.weight, norm2.bias, norm2.eps,
+ * mlp.fc1.weight [4d,d] bf16, mlp.fc1.bias, mlp.fc2.weight [d,4d] bf16,
+ * mlp.fc2.bias; all others fp32).  Returns DLO_E_ARG for i out of range. */
+#define DLO_DIT_N_PARAMS 16
+int dlo_block_schema(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel);
+
+/* The kernels the block forward is made of, callable one at a time (device
+ * pointers, row-major, enqueued on `stream`, asynchronous).  Each validates its
+ * shapes and returns DLO_E_UNSUPPORTED for shapes its kernel does not take. */
+
+/* out[r] = sum_j W[r, j] * silu(c[j]) + b[r], r < rows; W bf16 [rows, d]. */
+int dlo_op_adaln(const uint16_t *W, const float *b, const float *cond, int32_t rows, int32_t d,
+                 float *out, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* out[t, :] = bf16( LN(x[t, :d]; gamma, beta, *eps) * (1 + scale) + shift ), t < T;
+ * x fp32 with row stride ldx; out bf16 [T, d]. */
+int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const float *gamma,
+                       const float *beta, const float *eps, const float *shift,
+                       const float *scale, uint16_t *out, void *stream);
+
+/* C = A B^T + bias with A bf16 [M, K] (row stride lda), B bf16 [N, K] (ldb):
+ *   epilogue 0: C bf16 [M, N] (ldc)
+ *   epilogue 1: C bf16 = GELU_erf(A B^T + bias)
+ *   epilogue 2: X fp32 (ldc) += gate[n] * (A B^T + bias)  (C points at X)
+ * N % 256 == 0, K % 64 == 0, M >= 1. */
+enum { DLO_EPI_BIAS = 0, DLO_EPI_BIAS_GELU = 1, DLO_EPI_GATED_RESIDUAL = 2 };
+int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int32_t M,
+                int32_t N, int32_t K, const float *bias, const float *gate, void *C, int64_t ldc,
+                int32_t epilogue, void *stream);
+
+/* Per head j < H: out[:, j*dh:(j+1)*dh] = softmax(q_j k_j^T / sqrt(dh)) v_j, with
+ * q, k, v read from qkv bf16 [T, 3*H*dh] (row stride ldqkv) at column offsets 0,
+ * H*dh, 2*H*dh; out bf16 [T, H*dh] (row stride ldo).  dh in {64, 128}. */
+int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t H, int32_t dh,
+                     uint16_t *out, int64_t ldo, void *stream);
+
+/* Slot digest (see dlo_slot_trace) of up to DLO_MAX_GROUPS regions of `base`,
+ * written to *out (device uint64). */
+int dlo_op_digest(const void *base, const int64_t *offsets, const int64_t *lengths,
+                  int32_t n_regions, uint64_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLO_H */

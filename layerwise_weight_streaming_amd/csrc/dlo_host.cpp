@@ -1,0 +1,987 @@
+// libdlo host side: plan, host store, two-slot schedule, executor, C ABI.
+//
+// Pages cited (by title):
+//   [Jul] "Distributed Layerwise Offload", vLLM-Omni project blog, 2026-07-30.
+//   [Aug] "Distributed Layerwise Offload: Scaling Toward 200B+ DiT Models
+//         Efficiently in vLLM-Omni", vLLM blog, 2026-08-17.
+//   [Doc] "Distributed Layerwise Offload", vLLM-Omni design documentation.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/dlo.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return DLO_OK;
+}
+
+int64_t elt_bytes(int dtype) { return dtype == DLO_BF16 ? 2 : 4; }
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// DiT block schema (registration order)
+// ---------------------------------------------------------------------------
+
+struct SchemaEntry {
+  const char *name;
+  int dtype;
+  int64_t rows_per_d;  // numel = rows_per_d * d * cols_per_d * d, or fixed
+  int64_t cols_per_d;
+  int64_t fixed;       // > 0: numel is this constant
+};
+
+// numel(d) = fixed if fixed > 0, else rows_per_d * d * (cols_per_d ? cols_per_d * d : 1)
+const SchemaEntry kDit[DLO_DIT_N_PARAMS] = {
+    {"adaln.weight", DLO_BF16, 6, 1, 0},    {"adaln.bias", DLO_F32, 6, 0, 0},
+    {"norm1.weight", DLO_F32, 1, 0, 0},     {"norm1.bias", DLO_F32, 1, 0, 0},
+    {"norm1.eps", DLO_F32, 0, 0, 1},        {"attn.qkv.weight", DLO_BF16, 3, 1, 0},
+    {"attn.qkv.bias", DLO_F32, 3, 0, 0},    {"attn.out.weight", DLO_BF16, 1, 1, 0},
+    {"attn.out.bias", DLO_F32, 1, 0, 0},    {"norm2.weight", DLO_F32, 1, 0, 0},
+    {"norm2.bias", DLO_F32, 1, 0, 0},       {"norm2.eps", DLO_F32, 0, 0, 1},
+    {"mlp.fc1.weight", DLO_BF16, 4, 1, 0},  {"mlp.fc1.bias", DLO_F32, 4, 0, 0},
+    {"mlp.fc2.weight", DLO_BF16, 1, 4, 0},  {"mlp.fc2.bias", DLO_F32, 1, 0, 0},
+};
+enum {
+  P_ADA_W, P_ADA_B, P_N1_W, P_N1_B, P_N1_EPS, P_QKV_W, P_QKV_B, P_OUT_W, P_OUT_B, P_N2_W, P_N2_B,
+  P_N2_EPS, P_FC1_W, P_FC1_B, P_FC2_W, P_FC2_B
+};
+
+int64_t schema_numel(const SchemaEntry &e, int64_t d) {
+  if (e.fixed > 0) return e.fixed;
+  return e.rows_per_d * d * (e.cols_per_d ? e.cols_per_d * d : 1);
+}
+
+const char *kKernelNames[DLO_KERNELS_PER_BLOCK] = {
+    "adaln_gemv", "ln1_modulate", "gemm_qkv", "attention",
+    "gemm_out_residual", "ln2_modulate", "gemm_fc1_gelu", "gemm_fc2_residual"};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// objects
+// ---------------------------------------------------------------------------
+
+struct BlockPlan {
+  int32_t d = 0, heads = 0;
+  std::vector<std::string> names;
+  std::vector<int32_t> dtypes;
+  std::vector<int64_t> numels;
+  std::vector<int32_t> pgroup;   // param -> group
+  std::vector<int64_t> poff;     // param -> element offset in its group
+  int32_t n_groups = 0;
+  int32_t gdtype[DLO_MAX_GROUPS] = {0, 0};
+  int64_t gnumel[DLO_MAX_GROUPS] = {0, 0};
+  int64_t gshard[DLO_MAX_GROUPS] = {0, 0};
+  int64_t gregion[DLO_MAX_GROUPS] = {0, 0};
+  int64_t extent = 0, copy_bytes = 0;
+  bool is_dit = false;
+
+  int64_t param_byte(int p) const {
+    const int g = pgroup[p];
+    return gregion[g] + poff[p] * elt_bytes(gdtype[g]);
+  }
+};
+
+struct dlo_run;
+
+struct dlo_plan {
+  int32_t k = 1;
+  std::vector<BlockPlan> blocks;
+  int64_t slot_bytes = 0;
+  int32_t max_d = 0;
+  uint64_t id = 0;
+  mutable std::mutex mu;
+  mutable std::vector<dlo_run *> detached;   // runs started without a handle
+  mutable hipEvent_t last_done = nullptr;    // end of the previous run (any stream)
+};
+
+struct dlo_host_store {
+  const dlo_plan *plan = nullptr;
+  uint64_t plan_id = 0;
+  bool pinned = true;
+  std::vector<char *> mem;                     // per block
+  std::vector<std::vector<int64_t>> shard_at;  // per block: byte offset of (g * k + r)
+  std::vector<int64_t> shard_bytes_g;          // scratch
+  std::vector<uint8_t> packed;                 // per block flag
+  const void *shard(int b, int g, int r) const {
+    return mem[b] + shard_at[b][g * plan->k + r];
+  }
+};
+
+struct dlo_run {
+  int device = 0;
+  hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  hipEvent_t final_ev = nullptr;
+  bool timing = false, digest = false;
+  std::vector<dlo_slot_event> recs;
+  // timing events, per step: copy begin, copy end, compute begin, kernel ends [8]
+  std::vector<hipEvent_t> tev;
+  uint64_t *d_digest = nullptr;
+  bool finished = false;
+  std::vector<float> kernel_ms;
+};
+
+namespace {
+
+std::atomic<uint64_t> g_plan_ids{1};
+
+int check_hip(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(DLO_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DLO_OK;
+}
+
+void run_free(dlo_run *r) {
+  if (!r) return;
+  if (r->final_ev) (void)hipEventSynchronize(r->final_ev);
+  for (auto &e : r->ev)
+    if (e) (void)hipEventDestroy(e);
+  if (r->final_ev) (void)hipEventDestroy(r->final_ev);
+  for (auto e : r->tev)
+    if (e) (void)hipEventDestroy(e);
+  if (r->d_digest) (void)hipFree(r->d_digest);
+  delete r;
+}
+
+void reap_detached(const dlo_plan *p, bool wait) {
+  std::vector<dlo_run *> keep;
+  for (dlo_run *r : p->detached) {
+    if (wait || hipEventQuery(r->final_ev) == hipSuccess)
+      run_free(r);
+    else
+      keep.push_back(r);
+  }
+  p->detached.swap(keep);
+}
+
+// ---------------------------------------------------------------------------
+// the schedule: hook rule -> program of stream operations
+// ---------------------------------------------------------------------------
+
+struct Step {
+  int64_t t;
+  int32_t pass, block, slot, next_block, next_slot;
+};
+
+// [Jul] "Slot Tracking: i%2 + Dynamic Correction": each hook starts at i % 2 and
+// takes the slot its predecessor (circularly) prefetched into, once there is one.
+std::vector<Step> hook_steps(int n, int passes) {
+  std::vector<int> cur(n), pref(n, -1);
+  for (int i = 0; i < n; ++i) cur[i] = i % 2;
+  const int64_t total = (int64_t)n * passes;
+  std::vector<Step> out;
+  out.reserve((size_t)total);
+  for (int64_t t = 0; t < total; ++t) {
+    const int i = (int)(t % n), p = (int)(t / n);
+    const int prev = (i + n - 1) % n;
+    if (pref[prev] >= 0) cur[i] = pref[prev];
+    Step s{t, p, i, cur[i], -1, -1};
+    if (t + 1 < total) {
+      s.next_block = (i + 1) % n;
+      s.next_slot = 1 - cur[i];
+      pref[i] = s.next_slot;
+    }
+    out.push_back(s);
+  }
+  return out;
+}
+
+std::vector<dlo_sched_op> build_program(const std::vector<Step> &steps, bool resident) {
+  std::vector<dlo_sched_op> prog;
+  auto op = [&](int kind, int stream, int block, int slot, int event, int64_t step) {
+    dlo_sched_op o;
+    o.kind = kind; o.stream = stream; o.block = block; o.slot = slot; o.event = event;
+    o.pad = 0; o.step = step;
+    prog.push_back(o);
+  };
+  if (resident) {
+    for (const Step &s : steps) op(DLO_OP_COMPUTE, DLO_STREAM_COMPUTE, s.block, -1, -1, s.t);
+    return prog;
+  }
+  op(DLO_OP_RECORD, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_START, -1);
+  op(DLO_OP_WAIT, DLO_STREAM_COPY, -1, -1, DLO_EV_START, -1);
+  // initial prefetch: block 0 into slot 0 ([Doc] "Pre-service transaction boundary")
+  op(DLO_OP_COPY, DLO_STREAM_COPY, steps[0].block, steps[0].slot, -1, 0);
+  op(DLO_OP_RECORD, DLO_STREAM_COPY, -1, -1, DLO_EV_COPIED0 + steps[0].slot, -1);
+  for (const Step &s : steps) {
+    if (s.next_block >= 0) {
+      // the slot being refilled was last read by step t-1: wait for that compute
+      if (s.t >= 1) op(DLO_OP_WAIT, DLO_STREAM_COPY, -1, -1, DLO_EV_COMPUTED0 + s.next_slot, -1);
+      op(DLO_OP_COPY, DLO_STREAM_COPY, s.next_block, s.next_slot, -1, s.t + 1);
+      op(DLO_OP_RECORD, DLO_STREAM_COPY, -1, -1, DLO_EV_COPIED0 + s.next_slot, -1);
+    }
+    op(DLO_OP_WAIT, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_COPIED0 + s.slot, -1);
+    op(DLO_OP_COMPUTE, DLO_STREAM_COMPUTE, s.block, s.slot, -1, s.t);
+    op(DLO_OP_RECORD, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_COMPUTED0 + s.slot, -1);
+  }
+  return prog;
+}
+
+// ---------------------------------------------------------------------------
+// host copies for packing: split into chunks over a few threads
+// ---------------------------------------------------------------------------
+
+struct CopyTask {
+  char *dst;
+  const char *src;   // nullptr: zero-fill
+  int64_t bytes;
+};
+
+void run_copies(std::vector<CopyTask> &tasks) {
+  constexpr int64_t CHUNK = 16 << 20;
+  std::vector<CopyTask> pieces;
+  int64_t total = 0;
+  for (const CopyTask &t : tasks) {
+    for (int64_t o = 0; o < t.bytes; o += CHUNK) {
+      const int64_t n = std::min(CHUNK, t.bytes - o);
+      pieces.push_back({t.dst + o, t.src ? t.src + o : nullptr, n});
+    }
+    total += t.bytes;
+  }
+  unsigned hw = std::thread::hardware_concurrency();
+  int nth = (int)std::min<int64_t>(std::max(1u, std::min(hw, 16u)), (int64_t)pieces.size());
+  if (total < (64 << 20)) nth = 1;
+  std::atomic<size_t> next{0};
+  auto worker = [&]() {
+    for (size_t i = next++; i < pieces.size(); i = next++) {
+      const CopyTask &p = pieces[i];
+      if (p.src)
+        std::memcpy(p.dst, p.src, (size_t)p.bytes);
+      else
+        std::memset(p.dst, 0, (size_t)p.bytes);
+    }
+  };
+  if (nth <= 1) {
+    worker();
+    return;
+  }
+  std::vector<std::thread> th;
+  for (int i = 0; i < nth; ++i) th.emplace_back(worker);
+  for (auto &t : th) t.join();
+}
+
+int64_t workspace_bytes_for(int32_t max_d, int64_t T) {
+  const int64_t d = max_d;
+  return align_up(4 * d, DLO_ALIGN) + align_up(24 * d, DLO_ALIGN) + align_up(2 * T * d, DLO_ALIGN) +
+         align_up(8 * T * d, DLO_ALIGN);
+}
+
+int validate_block_against(const BlockPlan &bp, const dlo_block &blk, int b, bool need_src) {
+  if (blk.n_params != (int32_t)bp.names.size())
+    return fail(DLO_E_PLAN_MISMATCH, "block %d: %d parameters, plan has %zu", b, blk.n_params,
+                bp.names.size());
+  if (blk.n_params > 0 && !blk.params) return fail(DLO_E_ARG, "block %d: params is NULL", b);
+  for (int p = 0; p < blk.n_params; ++p) {
+    const dlo_param &pr = blk.params[p];
+    if (!pr.name || bp.names[p] != pr.name || pr.dtype != bp.dtypes[p] || pr.numel != bp.numels[p])
+      return fail(DLO_E_PLAN_MISMATCH, "block %d parameter %d (%s) does not match the plan", b, p,
+                  pr.name ? pr.name : "(null)");
+    if (need_src && pr.numel > 0 && !pr.src)
+      return fail(DLO_E_ARG, "block %d parameter %d (%s) has no source", b, p, pr.name);
+  }
+  return DLO_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+extern "C" {
+
+const char *dlo_last_error(void) { return g_err.c_str(); }
+
+int dlo_block_schema(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel) {
+  if (i < 0 || i >= DLO_DIT_N_PARAMS || d < 1) return fail(DLO_E_ARG, "schema index out of range");
+  if (name) *name = kDit[i].name;
+  if (dtype) *dtype = kDit[i].dtype;
+  if (numel) *numel = schema_numel(kDit[i], d);
+  return ok();
+}
+
+const char *dlo_kernel_name(int32_t j) {
+  return (j >= 0 && j < DLO_KERNELS_PER_BLOCK) ? kKernelNames[j] : nullptr;
+}
+
+// --------------------------------------------------------------------------- plan
+
+int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_plan **out) {
+  if (!out) return fail(DLO_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!blocks) return fail(DLO_E_ARG, "blocks is NULL");
+  if (n_blocks < 1) return fail(DLO_E_ARG, "n_blocks must be >= 1 (got %d)", n_blocks);
+  if (k < 1) return fail(DLO_E_ARG, "k must be >= 1 (got %d)", k);
+  dlo_plan *pl = new (std::nothrow) dlo_plan;
+  if (!pl) return fail(DLO_E_HOSTMEM, "out of host memory");
+  pl->k = k;
+  pl->blocks.resize(n_blocks);
+  for (int b = 0; b < n_blocks; ++b) {
+    const dlo_block &blk = blocks[b];
+    BlockPlan &bp = pl->blocks[b];
+    if (blk.n_params < 0 || (blk.n_params > 0 && !blk.params)) {
+      delete pl;
+      return fail(DLO_E_ARG, "block %d: bad parameter list", b);
+    }
+    bp.d = blk.d_model;
+    bp.heads = blk.n_heads;
+    // dtype groups in order of first appearance ([Aug] s.2: flattened by dtype)
+    for (int p = 0; p < blk.n_params; ++p) {
+      const dlo_param &pr = blk.params[p];
+      if (!pr.name) {
+        delete pl;
+        return fail(DLO_E_ARG, "block %d parameter %d has no name", b, p);
+      }
+      if (pr.dtype != DLO_BF16 && pr.dtype != DLO_F32) {
+        delete pl;
+        return fail(DLO_E_ARG, "block %d parameter %s: unknown dtype %d", b, pr.name, pr.dtype);
+      }
+      if (pr.numel < 0) {
+        delete pl;
+        return fail(DLO_E_ARG, "block %d parameter %s: negative numel", b, pr.name);
+      }
+      int g = -1;
+      for (int q = 0; q < bp.n_groups; ++q)
+        if (bp.gdtype[q] == pr.dtype) g = q;
+      if (g < 0) {
+        g = bp.n_groups++;
+        bp.gdtype[g] = pr.dtype;
+      }
+      bp.names.emplace_back(pr.name);
+      bp.dtypes.push_back(pr.dtype);
+      bp.numels.push_back(pr.numel);
+      bp.pgroup.push_back(g);
+      bp.poff.push_back(bp.gnumel[g]);
+      bp.gnumel[g] += pr.numel;
+    }
+    // ceil-div equal shards; regions at the all-gather offsets, 256-B aligned
+    int64_t cursor = 0;
+    for (int g = 0; g < bp.n_groups; ++g) {
+      bp.gshard[g] = ceil_div(bp.gnumel[g], k);
+      bp.gregion[g] = cursor;
+      const int64_t bytes = (int64_t)k * bp.gshard[g] * elt_bytes(bp.gdtype[g]);
+      bp.copy_bytes += bytes;
+      cursor = align_up(cursor + bytes, DLO_ALIGN);
+    }
+    bp.extent = cursor;
+    pl->slot_bytes = std::max(pl->slot_bytes, bp.extent);
+    // DiT schema?
+    bool dit = blk.n_params == DLO_DIT_N_PARAMS && bp.d > 0;
+    for (int p = 0; dit && p < DLO_DIT_N_PARAMS; ++p)
+      dit = bp.names[p] == kDit[p].name && bp.dtypes[p] == kDit[p].dtype &&
+            bp.numels[p] == schema_numel(kDit[p], bp.d);
+    bp.is_dit = dit;
+    pl->max_d = std::max(pl->max_d, bp.d);
+  }
+  pl->id = g_plan_ids++;
+  *out = pl;
+  return ok();
+}
+
+void dlo_plan_destroy(dlo_plan *plan) {
+  if (!plan) return;
+  {
+    std::lock_guard<std::mutex> lk(plan->mu);
+    reap_detached(plan, true);
+    if (plan->last_done) (void)hipEventDestroy(plan->last_done);
+  }
+  delete plan;
+}
+
+int32_t dlo_plan_n_blocks(const dlo_plan *plan) { return plan ? (int32_t)plan->blocks.size() : -1; }
+int32_t dlo_plan_k(const dlo_plan *plan) { return plan ? plan->k : -1; }
+int64_t dlo_plan_slot_bytes(const dlo_plan *plan) { return plan ? plan->slot_bytes : -1; }
+
+int dlo_plan_block_info(const dlo_plan *plan, int32_t b, dlo_block_info *out) {
+  if (!plan || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (b < 0 || b >= (int32_t)plan->blocks.size()) return fail(DLO_E_ARG, "block %d out of range", b);
+  const BlockPlan &bp = plan->blocks[b];
+  std::memset(out, 0, sizeof *out);
+  out->d_model = bp.d;
+  out->n_heads = bp.heads;
+  out->n_params = (int32_t)bp.names.size();
+  out->n_groups = bp.n_groups;
+  for (int g = 0; g < bp.n_groups; ++g) {
+    out->dtype[g] = bp.gdtype[g];
+    out->numel[g] = bp.gnumel[g];
+    out->shard[g] = bp.gshard[g];
+    out->region[g] = bp.gregion[g];
+  }
+  out->extent = bp.extent;
+  out->copy_bytes = bp.copy_bytes;
+  out->is_dit = bp.is_dit ? 1 : 0;
+  return ok();
+}
+
+int dlo_plan_param_offset(const dlo_plan *plan, int32_t b, int32_t p, int64_t *byte_offset) {
+  if (!plan || !byte_offset) return fail(DLO_E_ARG, "NULL argument");
+  if (b < 0 || b >= (int32_t)plan->blocks.size()) return fail(DLO_E_ARG, "block %d out of range", b);
+  const BlockPlan &bp = plan->blocks[b];
+  if (p < 0 || p >= (int32_t)bp.names.size()) return fail(DLO_E_ARG, "param %d out of range", p);
+  *byte_offset = bp.param_byte(p);
+  return ok();
+}
+
+int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens) {
+  if (!plan || tokens < 1) {
+    fail(DLO_E_ARG, "bad plan or tokens");
+    return -1;
+  }
+  g_err.clear();
+  return workspace_bytes_for(plan->max_d, tokens);
+}
+
+int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, int64_t cap,
+                      int64_t *n_ops) {
+  if (!plan || !n_ops) return fail(DLO_E_ARG, "NULL argument");
+  if (passes < 1) return fail(DLO_E_ARG, "passes must be >= 1");
+  const std::vector<Step> steps = hook_steps((int)plan->blocks.size(), passes);
+  const std::vector<dlo_sched_op> prog = build_program(steps, false);
+  *n_ops = (int64_t)prog.size();
+  if (!ops) return ok();
+  if (cap < (int64_t)prog.size()) return fail(DLO_E_ARG, "cap %lld < %zu ops", (long long)cap, prog.size());
+  std::memcpy(ops, prog.data(), prog.size() * sizeof(dlo_sched_op));
+  return ok();
+}
+
+// --------------------------------------------------------------------------- store
+
+void dlo_host_store_destroy(dlo_host_store *store) {
+  if (!store) return;
+  for (char *m : store->mem) {
+    if (!m) continue;
+    if (store->pinned)
+      (void)hipHostFree(m);
+    else
+      std::free(m);
+  }
+  delete store;
+}
+
+int dlo_host_store_create(const dlo_plan *plan, uint32_t flags, dlo_host_store **out) {
+  if (!out) return fail(DLO_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!plan) return fail(DLO_E_ARG, "plan is NULL");
+  if (flags & ~DLO_STORE_PAGEABLE) return fail(DLO_E_ARG, "unknown store flags 0x%x", flags);
+  dlo_host_store *st = new (std::nothrow) dlo_host_store;
+  if (!st) return fail(DLO_E_HOSTMEM, "out of host memory");
+  st->plan = plan;
+  st->plan_id = plan->id;
+  st->pinned = !(flags & DLO_STORE_PAGEABLE);
+  const int nb = (int)plan->blocks.size(), k = plan->k;
+  st->mem.assign(nb, nullptr);
+  st->shard_at.resize(nb);
+  st->packed.assign(nb, 0);
+  for (int b = 0; b < nb; ++b) {
+    const BlockPlan &bp = plan->blocks[b];
+    int64_t cursor = 0;
+    st->shard_at[b].resize((size_t)bp.n_groups * k);
+    for (int g = 0; g < bp.n_groups; ++g)
+      for (int r = 0; r < k; ++r) {
+        st->shard_at[b][g * k + r] = cursor;
+        cursor = align_up(cursor + bp.gshard[g] * elt_bytes(bp.gdtype[g]), 4096);
+      }
+    const size_t bytes = (size_t)std::max<int64_t>(cursor, 4096);
+    void *m = nullptr;
+    if (st->pinned) {
+      // [Aug] s.2: the shard is a pinned DMA buffer for fast H2D
+      hipError_t e = hipHostMalloc(&m, bytes, hipHostMallocDefault);
+      if (e != hipSuccess) {
+        m = nullptr;
+        dlo_host_store_destroy(st);
+        return fail(DLO_E_PIN, "hipHostMalloc(%zu) for block %d failed: %s", bytes, b,
+                    hipGetErrorString(e));
+      }
+    } else {
+      m = std::aligned_alloc(4096, align_up((int64_t)bytes, 4096));
+      if (!m) {
+        dlo_host_store_destroy(st);
+        return fail(DLO_E_HOSTMEM, "host allocation of %zu bytes for block %d failed", bytes, b);
+      }
+    }
+    st->mem[b] = static_cast<char *>(m);
+  }
+  *out = st;
+  return ok();
+}
+
+int dlo_pack_host_shards(dlo_host_store *store, int32_t b_begin, int32_t b_end,
+                         const dlo_block *blocks) {
+  if (!store || !blocks) return fail(DLO_E_ARG, "NULL argument");
+  const dlo_plan *plan = store->plan;
+  const int nb = (int)plan->blocks.size(), k = plan->k;
+  if (b_begin < 0 || b_end > nb || b_begin >= b_end)
+    return fail(DLO_E_ARG, "block range [%d, %d) invalid for %d blocks", b_begin, b_end, nb);
+  for (int b = b_begin; b < b_end; ++b) {
+    int rc = validate_block_against(plan->blocks[b], blocks[b - b_begin], b, true);
+    if (rc) return rc;
+  }
+  std::vector<CopyTask> tasks;
+  for (int b = b_begin; b < b_end; ++b) {
+    const BlockPlan &bp = plan->blocks[b];
+    const dlo_block &blk = blocks[b - b_begin];
+    for (int g = 0; g < bp.n_groups; ++g) {
+      const int64_t S = bp.gshard[g], elt = elt_bytes(bp.gdtype[g]);
+      if (S == 0) continue;
+      auto shard_ptr = [&](int r) { return const_cast<char *>(static_cast<const char *>(store->shard(b, g, r))); };
+      // [Aug] s.2: shard r holds flat[r*S, (r+1)*S) of the group's flat buffer
+      for (int p = 0; p < (int)bp.names.size(); ++p) {
+        if (bp.pgroup[p] != g || bp.numels[p] == 0) continue;
+        const char *src = static_cast<const char *>(blk.params[p].src);
+        int64_t e = bp.poff[p];
+        const int64_t end = e + bp.numels[p];
+        while (e < end) {
+          const int64_t r = e / S, pos = e % S, len = std::min(S - pos, end - e);
+          tasks.push_back({shard_ptr((int)r) + pos * elt, src + (e - bp.poff[p]) * elt, len * elt});
+          e += len;
+        }
+      }
+      // zero padding beyond N_g, so that every shard has S_g elements
+      int64_t e = bp.gnumel[g];
+      const int64_t end = (int64_t)k * S;
+      while (e < end) {
+        const int64_t r = e / S, pos = e % S, len = std::min(S - pos, end - e);
+        tasks.push_back({shard_ptr((int)r) + pos * elt, nullptr, len * elt});
+        e += len;
+      }
+    }
+  }
+  run_copies(tasks);
+  for (int b = b_begin; b < b_end; ++b) store->packed[b] = 1;
+  return ok();
+}
+
+int dlo_host_store_shard(const dlo_host_store *store, int32_t b, int32_t g, int32_t r,
+                         const void **ptr, int64_t *bytes) {
+  if (!store || !ptr || !bytes) return fail(DLO_E_ARG, "NULL argument");
+  const dlo_plan *plan = store->plan;
+  if (b < 0 || b >= (int32_t)plan->blocks.size()) return fail(DLO_E_ARG, "block out of range");
+  const BlockPlan &bp = plan->blocks[b];
+  if (g < 0 || g >= bp.n_groups || r < 0 || r >= plan->k) return fail(DLO_E_ARG, "shard out of range");
+  *ptr = store->shard(b, g, r);
+  *bytes = bp.gshard[g] * elt_bytes(bp.gdtype[g]);
+  return ok();
+}
+
+int32_t dlo_host_store_complete(const dlo_host_store *store) {
+  if (!store) return 0;
+  for (uint8_t f : store->packed)
+    if (!f) return 0;
+  return 1;
+}
+
+// --------------------------------------------------------------------------- placement
+
+namespace {
+// the k shards of every group at region_g + r * S_g * elt_g ([Jul] "Weight
+// Sharding + AllGather": the all-gather output is the rank-ordered concatenation)
+hipError_t place(const dlo_plan *plan, const dlo_host_store *st, int b, char *dst, hipStream_t s) {
+  const BlockPlan &bp = plan->blocks[b];
+  for (int g = 0; g < bp.n_groups; ++g) {
+    const int64_t sb = bp.gshard[g] * elt_bytes(bp.gdtype[g]);
+    if (sb == 0) continue;
+    for (int r = 0; r < plan->k; ++r) {
+      hipError_t e = hipMemcpyAsync(dst + bp.gregion[g] + r * sb, st->shard(b, g, r), (size_t)sb,
+                                    hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+int dlo_place_block(const dlo_plan *plan, const dlo_host_store *store, int32_t b, void *dst,
+                    int64_t dst_bytes, void *stream) {
+  if (!plan || !store || !dst) return fail(DLO_E_ARG, "NULL argument");
+  if (store->plan_id != plan->id) return fail(DLO_E_PLAN_MISMATCH, "store was made by another plan");
+  if (b < 0 || b >= (int32_t)plan->blocks.size()) return fail(DLO_E_ARG, "block out of range");
+  if (!store->packed[b]) return fail(DLO_E_STATE, "block %d has not been packed", b);
+  if (dst_bytes < plan->blocks[b].extent)
+    return fail(DLO_E_SLOT_SMALL, "destination %lld < extent %lld", (long long)dst_bytes,
+                (long long)plan->blocks[b].extent);
+  int rc = check_hip(place(plan, store, b, static_cast<char *>(dst), (hipStream_t)stream), "hipMemcpyAsync");
+  return rc ? rc : ok();
+}
+
+// --------------------------------------------------------------------------- forward
+
+namespace {
+
+struct Workspace {
+  float *silu_c, *mod;
+  uint16_t *h, *big;
+};
+
+Workspace carve(void *ws, int32_t max_d, int64_t T) {
+  char *p = static_cast<char *>(ws);
+  Workspace w;
+  w.silu_c = reinterpret_cast<float *>(p);
+  p += align_up(4 * (int64_t)max_d, DLO_ALIGN);
+  w.mod = reinterpret_cast<float *>(p);
+  p += align_up(24 * (int64_t)max_d, DLO_ALIGN);
+  w.h = reinterpret_cast<uint16_t *>(p);
+  p += align_up(2 * T * max_d, DLO_ALIGN);
+  w.big = reinterpret_cast<uint16_t *>(p);  // qkv [T,3d] then a [T,d]; later u [T,4d]
+  return w;
+}
+
+// One block forward on the compute stream, parameters re-pointed into `base`
+// (a slot or a resident image) with no copy ([Jul] "How It Works", step 3).
+hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forward_args *a,
+                         const Workspace &w, hipStream_t s, hipEvent_t *kernel_end) {
+  const int d = bp.d, H = bp.heads, dh = d / H, T = a->tokens;
+  auto P = [&](int p) { return base + bp.param_byte(p); };
+  auto W = [&](int p) { return reinterpret_cast<const uint16_t *>(P(p)); };
+  auto F = [&](int p) { return reinterpret_cast<const float *>(P(p)); };
+  float *x = a->x;
+  const int64_t ldx = a->x_row_stride;
+  const float *mod = w.mod;
+  uint16_t *qkv = w.big;
+  uint16_t *attn = w.big + (int64_t)T * 3 * d;
+  uint16_t *u = w.big;
+  hipError_t e;
+#define DLO_STEP(call, j)                                                   \
+  if ((e = (call)) != hipSuccess) return e;                                 \
+  if (kernel_end && (e = hipEventRecord(kernel_end[j], s)) != hipSuccess) return e;
+  DLO_STEP(dlo::launch_adaln_gemv(W(P_ADA_W), w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 0)
+  DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N1_W), F(P_N1_B), F(P_N1_EPS), mod + 0 * d,
+                                   mod + 1 * d, w.h, s), 1)
+  DLO_STEP(dlo::launch_gemm(w.h, d, W(P_QKV_W), d, T, 3 * d, d, F(P_QKV_B), nullptr, qkv, 3 * d,
+                            dlo::EPI_BIAS, s), 2)
+  DLO_STEP(dlo::launch_attention(qkv, 3 * d, T, H, dh, attn, d, s), 3)
+  DLO_STEP(dlo::launch_gemm(attn, d, W(P_OUT_W), d, T, d, d, F(P_OUT_B), mod + 2 * d, x, ldx,
+                            dlo::EPI_GATED_RESIDUAL, s), 4)
+  DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N2_W), F(P_N2_B), F(P_N2_EPS), mod + 3 * d,
+                                   mod + 4 * d, w.h, s), 5)
+  DLO_STEP(dlo::launch_gemm(w.h, d, W(P_FC1_W), d, T, 4 * d, d, F(P_FC1_B), nullptr, u, 4 * d,
+                            dlo::EPI_BIAS_GELU, s), 6)
+  DLO_STEP(dlo::launch_gemm(u, 4 * d, W(P_FC2_W), 4 * d, T, d, 4 * d, F(P_FC2_B), mod + 5 * d, x,
+                            ldx, dlo::EPI_GATED_RESIDUAL, s), 7)
+#undef DLO_STEP
+  return hipSuccess;
+}
+
+int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dlo_forward_args *a) {
+  if (!plan || !a) return fail(DLO_E_ARG, "NULL plan or args");
+  const bool resident = a->flags & DLO_RESIDENT;
+  if (a->flags & ~(DLO_TRACE_DIGEST | DLO_TRACE_TIMING | DLO_RESIDENT))
+    return fail(DLO_E_ARG, "unknown flags 0x%x", a->flags);
+  if (!resident) {
+    if (!store) return fail(DLO_E_ARG, "store is NULL");
+    if (store->plan_id != plan->id)
+      return fail(DLO_E_PLAN_MISMATCH, "the host store was built for another plan");
+    if (!dlo_host_store_complete(store)) return fail(DLO_E_STATE, "the host store is not fully packed");
+  }
+  if (a->tokens < 1) return fail(DLO_E_ARG, "tokens must be >= 1");
+  if (a->passes < 1) return fail(DLO_E_ARG, "passes must be >= 1");
+  if (!a->x || !a->cond || !a->workspace) return fail(DLO_E_ARG, "x, cond and workspace are required");
+  if (!a->compute_stream) return fail(DLO_E_ARG, "compute_stream is NULL");
+  if (!resident && (!a->copy_stream || a->copy_stream == a->compute_stream))
+    return fail(DLO_E_ARG, "copy_stream must be non-NULL and distinct from compute_stream");
+  for (size_t b = 0; b < plan->blocks.size(); ++b) {
+    const BlockPlan &bp = plan->blocks[b];
+    if (!bp.is_dit) return fail(DLO_E_UNSUPPORTED, "block %zu does not carry the DiT block schema", b);
+    if (bp.d % 256 || bp.d > 8192)
+      return fail(DLO_E_UNSUPPORTED, "block %zu: d = %d (need a multiple of 256, at most 8192)", b, bp.d);
+    if (bp.heads < 1 || bp.d % bp.heads)
+      return fail(DLO_E_UNSUPPORTED, "block %zu: %d heads do not divide d = %d", b, bp.heads, bp.d);
+    const int dh = bp.d / bp.heads;
+    if (dh != 64 && dh != 128) return fail(DLO_E_UNSUPPORTED, "block %zu: head dim %d (need 64 or 128)", b, dh);
+  }
+  if (a->x_row_stride < plan->max_d)
+    return fail(DLO_E_ARG, "x_row_stride %lld < widest block %d", (long long)a->x_row_stride, plan->max_d);
+  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens);
+  if (a->workspace_bytes < need)
+    return fail(DLO_E_WORKSPACE, "workspace %lld < %lld bytes", (long long)a->workspace_bytes, (long long)need);
+  if (!resident) {
+    if (!a->slot[0] || !a->slot[1]) return fail(DLO_E_ARG, "both slots are required");
+    if (a->slot_bytes < plan->slot_bytes)
+      return fail(DLO_E_SLOT_SMALL, "slot %lld < plan slot %lld bytes", (long long)a->slot_bytes,
+                  (long long)plan->slot_bytes);
+    const char *s0 = static_cast<const char *>(a->slot[0]), *s1 = static_cast<const char *>(a->slot[1]);
+    const int64_t gap = s0 < s1 ? s1 - s0 : s0 - s1;
+    if (gap < plan->slot_bytes) return fail(DLO_E_ARG, "the two slots overlap");
+  } else {
+    if (!a->resident_blocks) return fail(DLO_E_ARG, "DLO_RESIDENT needs resident_blocks");
+    for (size_t b = 0; b < plan->blocks.size(); ++b)
+      if (!a->resident_blocks[b]) return fail(DLO_E_ARG, "resident block %zu is NULL", b);
+  }
+  return DLO_OK;
+}
+
+}  // namespace
+
+int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
+                      const dlo_forward_args *a, dlo_run **run_out) {
+  if (run_out) *run_out = nullptr;
+  int rc = validate_forward(plan, store, a);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(plan->mu);
+  reap_detached(plan, false);
+
+  const bool resident = a->flags & DLO_RESIDENT;
+  const int n = (int)plan->blocks.size();
+  const std::vector<Step> steps = hook_steps(n, a->passes);
+  const std::vector<dlo_sched_op> prog = build_program(steps, resident);
+  hipStream_t cs = (hipStream_t)a->compute_stream, ps = (hipStream_t)a->copy_stream;
+
+  dlo_run *run = new (std::nothrow) dlo_run;
+  if (!run) return fail(DLO_E_HOSTMEM, "out of host memory");
+  run->timing = a->flags & DLO_TRACE_TIMING;
+  run->digest = a->flags & DLO_TRACE_DIGEST;
+  const int64_t total = (int64_t)steps.size();
+  constexpr int TEV = 3 + DLO_KERNELS_PER_BLOCK;  // copy begin, copy end, compute begin, kernels
+
+  // --- resources (events, digest buffer): failures here have enqueued nothing
+  (void)hipGetDevice(&run->device);
+  rc = DLO_OK;
+  for (auto &e : run->ev)
+    if (!rc) rc = check_hip(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
+  if (!rc) rc = check_hip(hipEventCreateWithFlags(&run->final_ev, hipEventDisableTiming), "hipEventCreate");
+  if (!rc && !plan->last_done)
+    rc = check_hip(hipEventCreateWithFlags(&plan->last_done, hipEventDisableTiming), "hipEventCreate");
+  if (!rc && run->timing) {
+    run->tev.assign((size_t)(total * TEV + 1), nullptr);
+    for (auto &e : run->tev)
+      if (!rc) rc = check_hip(hipEventCreate(&e), "hipEventCreate");
+  }
+  if (!rc && run->digest)
+    rc = check_hip(hipMalloc(&run->d_digest, (size_t)(2 * total) * sizeof(uint64_t)), "hipMalloc");
+  if (rc) {
+    run_free(run);
+    return rc;
+  }
+
+  run->recs.resize((size_t)total);
+  for (const Step &s : steps) {
+    dlo_slot_event &r = run->recs[(size_t)s.t];
+    std::memset(&r, 0, sizeof r);
+    r.step = s.t;
+    r.pass = s.pass;
+    r.block = s.block;
+    r.read_slot = resident ? -1 : s.slot;
+    r.prefetch_block = resident ? -1 : s.next_block;
+    r.prefetch_slot = resident ? -1 : s.next_slot;
+    r.prefetch_bytes = (resident || s.next_block < 0) ? 0 : plan->blocks[s.next_block].copy_bytes;
+    r.t_copy_begin = r.t_copy_end = r.t_compute_begin = r.t_compute_end = -1.f;
+  }
+
+  const Workspace w = carve(a->workspace, plan->max_d, a->tokens);
+  hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
+  auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
+  hipError_t e = hipSuccess;
+  auto HIP = [&](hipError_t x) {
+    if (e == hipSuccess && x != hipSuccess) e = x;
+    return e == hipSuccess;
+  };
+
+  // order after the previous run (even one on other streams) and after the caller's
+  // work on the compute stream
+  HIP(hipStreamWaitEvent(cs, plan->last_done, 0));
+  if (!resident) HIP(hipStreamWaitEvent(ps, plan->last_done, 0));
+  if (t0) HIP(hipEventRecord(t0, cs));
+  HIP(dlo::launch_silu(a->cond, w.silu_c, plan->max_d, cs));
+
+  for (const dlo_sched_op &op : prog) {
+    if (e != hipSuccess) break;
+    hipStream_t s = op.stream == DLO_STREAM_COMPUTE ? cs : ps;
+    switch (op.kind) {
+      case DLO_OP_RECORD:
+        HIP(hipEventRecord(run->ev[op.event], s));
+        break;
+      case DLO_OP_WAIT:
+        HIP(hipStreamWaitEvent(s, run->ev[op.event], 0));
+        break;
+      case DLO_OP_COPY: {
+        if (run->timing) HIP(hipEventRecord(tev(op.step, 0), ps));
+        HIP(place(plan, store, op.block, static_cast<char *>(a->slot[op.slot]), ps));
+        if (run->timing) HIP(hipEventRecord(tev(op.step, 1), ps));
+        break;
+      }
+      case DLO_OP_COMPUTE: {
+        const BlockPlan &bp = plan->blocks[op.block];
+        const char *base = resident ? static_cast<const char *>(a->resident_blocks[op.block])
+                                    : static_cast<const char *>(a->slot[op.slot]);
+        int64_t offs[DLO_MAX_GROUPS], lens[DLO_MAX_GROUPS];
+        for (int g = 0; g < bp.n_groups; ++g) {
+          offs[g] = bp.gregion[g];
+          lens[g] = (int64_t)plan->k * bp.gshard[g] * elt_bytes(bp.gdtype[g]);
+        }
+        if (run->digest)
+          HIP(dlo::launch_digest(base, offs, lens, bp.n_groups, run->d_digest + 2 * op.step, cs));
+        if (run->timing) HIP(hipEventRecord(tev(op.step, 2), cs));
+        if (e == hipSuccess)
+          HIP(block_forward(bp, base, a, w, cs, run->timing ? &run->tev[(size_t)(op.step * TEV + 3)] : nullptr));
+        if (run->digest)
+          HIP(dlo::launch_digest(base, offs, lens, bp.n_groups, run->d_digest + 2 * op.step + 1, cs));
+        break;
+      }
+    }
+  }
+  HIP(hipEventRecord(run->final_ev, cs));
+  HIP(hipEventRecord(plan->last_done, cs));
+  if (e != hipSuccess) {
+    // work may already be enqueued: keep the run until it drains
+    plan->detached.push_back(run);
+    return fail(DLO_E_HIP, "enqueue failed: %s (synchronise both streams; x is undefined)",
+                hipGetErrorString(e));
+  }
+  if (run_out)
+    *run_out = run;
+  else
+    plan->detached.push_back(run);
+  return ok();
+}
+
+int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_out) {
+  if (!run || !n_out) return fail(DLO_E_ARG, "NULL argument");
+  const int64_t total = (int64_t)run->recs.size();
+  *n_out = total;
+  if (!run->finished) {
+    int rc = check_hip(hipEventSynchronize(run->final_ev), "hipEventSynchronize");
+    if (rc) return rc;
+    if (run->digest) {
+      std::vector<uint64_t> dg((size_t)(2 * total));
+      rc = check_hip(hipMemcpy(dg.data(), run->d_digest, dg.size() * sizeof(uint64_t),
+                               hipMemcpyDeviceToHost), "hipMemcpy");
+      if (rc) return rc;
+      for (int64_t t = 0; t < total; ++t) {
+        run->recs[(size_t)t].digest_pre = dg[(size_t)(2 * t)];
+        run->recs[(size_t)t].digest_post = dg[(size_t)(2 * t + 1)];
+      }
+    }
+    if (run->timing) {
+      constexpr int TEV = 3 + DLO_KERNELS_PER_BLOCK;
+      hipEvent_t t0 = run->tev.back();
+      auto since = [&](hipEvent_t ev) {
+        float ms = -1.f;
+        if (hipEventElapsedTime(&ms, t0, ev) != hipSuccess) ms = -1.f;
+        return ms;
+      };
+      run->kernel_ms.assign((size_t)(total * DLO_KERNELS_PER_BLOCK), -1.f);
+      const bool resident = total > 0 && run->recs[0].read_slot < 0;
+      for (int64_t t = 0; t < total; ++t) {
+        dlo_slot_event &r = run->recs[(size_t)t];
+        auto ev = [&](int j) { return run->tev[(size_t)(t * TEV + j)]; };
+        if (!resident) {
+          r.t_copy_begin = since(ev(0));
+          r.t_copy_end = since(ev(1));
+        }
+        r.t_compute_begin = since(ev(2));
+        r.t_compute_end = since(ev(3 + DLO_KERNELS_PER_BLOCK - 1));
+        float prev = r.t_compute_begin;
+        for (int j = 0; j < DLO_KERNELS_PER_BLOCK; ++j) {
+          const float tj = since(ev(3 + j));
+          run->kernel_ms[(size_t)(t * DLO_KERNELS_PER_BLOCK + j)] = tj - prev;
+          prev = tj;
+        }
+      }
+    }
+    run->finished = true;
+  }
+  if (out) std::memcpy(out, run->recs.data(), (size_t)std::min(cap, total) * sizeof(dlo_slot_event));
+  return ok();
+}
+
+int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out) {
+  if (!run || !n_out) return fail(DLO_E_ARG, "NULL argument");
+  if (!run->timing) return fail(DLO_E_STATE, "the run was not started with DLO_TRACE_TIMING");
+  int64_t n_steps = 0;
+  int rc = dlo_slot_trace(run, nullptr, 0, &n_steps);
+  if (rc) return rc;
+  *n_out = (int64_t)run->kernel_ms.size();
+  if (ms) std::memcpy(ms, run->kernel_ms.data(), (size_t)std::min(cap, *n_out) * sizeof(float));
+  return ok();
+}
+
+void dlo_run_destroy(dlo_run *run) { run_free(run); }
+
+// --------------------------------------------------------------------------- single ops
+
+int dlo_op_adaln(const uint16_t *W, const float *b, const float *cond, int32_t rows, int32_t d,
+                 float *out, void *workspace, int64_t workspace_bytes, void *stream) {
+  if (!W || !b || !cond || !out || !workspace) return fail(DLO_E_ARG, "NULL argument");
+  if (rows < 1 || d < 8 || d % 8) return fail(DLO_E_UNSUPPORTED, "adaln: rows >= 1, d % 8 == 0 required");
+  if (workspace_bytes < 4 * (int64_t)d) return fail(DLO_E_WORKSPACE, "adaln: workspace < 4 d bytes");
+  hipStream_t s = (hipStream_t)stream;
+  float *sc = static_cast<float *>(workspace);
+  int rc = check_hip(dlo::launch_silu(cond, sc, d, s), "silu");
+  if (!rc) rc = check_hip(dlo::launch_adaln_gemv(W, sc, b, out, rows, d, s), "adaln_gemv");
+  return rc ? rc : ok();
+}
+
+int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const float *gamma,
+                       const float *beta, const float *eps, const float *shift,
+                       const float *scale, uint16_t *out, void *stream) {
+  if (!x || !gamma || !beta || !eps || !shift || !scale || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (T < 1 || d < 256 || d % 256 || d > 8192 || ldx < d)
+    return fail(DLO_E_UNSUPPORTED, "ln_modulate: d %% 256 == 0, d <= 8192, ldx >= d required");
+  int rc = check_hip(dlo::launch_ln_modulate(x, ldx, T, d, gamma, beta, eps, shift, scale, out,
+                                             (hipStream_t)stream), "ln_modulate");
+  return rc ? rc : ok();
+}
+
+int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int32_t M,
+                int32_t N, int32_t K, const float *bias, const float *gate, void *C, int64_t ldc,
+                int32_t epilogue, void *stream) {
+  if (!A || !B || !bias || !C) return fail(DLO_E_ARG, "NULL argument");
+  if (epilogue < 0 || epilogue > 2) return fail(DLO_E_ARG, "unknown epilogue %d", epilogue);
+  if (epilogue == DLO_EPI_GATED_RESIDUAL && !gate) return fail(DLO_E_ARG, "gate is required");
+  if (M < 1 || N < 256 || N % 256 || K < 64 || K % 64 || lda < K || ldb < K || ldc < N ||
+      lda % 8 || ldb % 8)
+    return fail(DLO_E_UNSUPPORTED, "gemm: N %% 256 == 0, K %% 64 == 0, ld >= extent, ld %% 8 == 0");
+  if ((int64_t)256 * lda * 2 >= (int64_t)1 << 31 || (int64_t)256 * ldb * 2 >= (int64_t)1 << 31)
+    return fail(DLO_E_UNSUPPORTED, "gemm: leading dimension too large for 32-bit tile offsets");
+  int rc = check_hip(dlo::launch_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue,
+                                      (hipStream_t)stream), "gemm");
+  return rc ? rc : ok();
+}
+
+int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t H, int32_t dh,
+                     uint16_t *out, int64_t ldo, void *stream) {
+  if (!qkv || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (T < 1 || H < 1 || (dh != 64 && dh != 128) || ldqkv < 3LL * H * dh || ldo < (int64_t)H * dh ||
+      ldqkv % 8 || ldo % 4)
+    return fail(DLO_E_UNSUPPORTED, "attention: dh in {64,128}, ldqkv >= 3 H dh (multiple of 8)");
+  int rc = check_hip(dlo::launch_attention(qkv, ldqkv, T, H, dh, out, ldo, (hipStream_t)stream),
+                     "attention");
+  return rc ? rc : ok();
+}
+
+int dlo_op_digest(const void *base, const int64_t *offsets, const int64_t *lengths,
+                  int32_t n_regions, uint64_t *out, void *stream) {
+  if (!base || !offsets || !lengths || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (n_regions < 0 || n_regions > DLO_MAX_GROUPS) return fail(DLO_E_ARG, "n_regions out of range");
+  for (int i = 0; i < n_regions; ++i)
+    if (offsets[i] < 0 || offsets[i] % 8 || lengths[i] < 0) return fail(DLO_E_ARG, "bad region");
+  int rc = check_hip(dlo::launch_digest(base, offsets, lengths, n_regions, out, (hipStream_t)stream),
+                     "digest");
+  return rc ? rc : ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Internal launch interface of the gfx950 kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dlo {
+
+// out[i] = c[i] * sigmoid(c[i]), i < n
+hipError_t launch_silu(const float *c, float *out, int n, hipStream_t s);
+
+// out[r] = sum_j W[r, j] * sc[j] + b[r]   (W bf16 [rows, d], d % 8 == 0)
+hipError_t launch_adaln_gemv(const uint16_t *W, const float *sc, const float *b, float *out,
+                             int rows, int d, hipStream_t s);
+
+// out[t, :] = bf16(LN(x[t, :d]) * (1 + scale) + shift); d % 256 == 0, d <= 8192
+hipError_t launch_ln_modulate(const float *x, int64_t ldx, int T, int d, const float *gamma,
+                              const float *beta, const float *eps, const float *shift,
+                              const float *scale, uint16_t *out, hipStream_t s);
+
+enum GemmEpilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_GATED_RESIDUAL = 2 };
+
+// C = A B^T + bias (see dlo_op_gemm); N % 256 == 0, K % 64 == 0
+hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int M,
+                       int N, int K, const float *bias, const float *gate, void *C, int64_t ldc,
+                       int epilogue, hipStream_t s);
+
+// per-head softmax(q k^T / sqrt(dh)) v from a fused qkv buffer; dh in {64, 128}
+hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, int T, int H, int dh,
+                            uint16_t *out, int64_t ldo, hipStream_t s);
+
+// *out = digest of the regions (base + offsets[i], lengths[i]); offsets multiples of 8
+hipError_t launch_digest(const void *base, const int64_t *offsets, const int64_t *lengths,
+                         int n, uint64_t *out, hipStream_t s);
+
+}  // namespace dlo

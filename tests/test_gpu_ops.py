@@ -1,0 +1,185 @@
+"""Per-kernel parity on the GPU, through the C ABI, against the float64 oracle.
+
+Small shapes that span several tiles plus a ragged tail are compared element by
+element; the Super-shaped sizes are compared on sampled outputs that the oracle
+computes one at a time.  Inputs are seeded (synth); expected values come from
+oracle.forward only.
+"""
+import numpy as np
+import pytest
+
+import synth
+import layerwise_weight_streaming_amd as dlo
+from oracle import forward as of
+from oracle import plan as op
+from tests.gpu_util import bf16_to_f64, rel_err, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+# bf16 outputs carry a relative rounding error of at most 2^-9; fp32 accumulation
+# over K <= 20480 products of bf16 operands adds far less.  Element bound:
+# |gpu - ref| <= 2^-8 |ref| + 2^-9 max|ref|.
+def _close_bf16(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * np.max(np.abs(ref))
+    bad = np.abs(got - ref) > bound
+    return int(bad.sum()), float(np.max(np.abs(got - ref) / np.maximum(bound, 1e-30)))
+
+
+def _dev(torch, arr):
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def _bf16_rand(seed, shape, std=1.0):
+    return synth.normal_bf16(seed, 9, 0, 0, shape, 0.0, std)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 512, 128), (64, 768, 256), (1000, 256, 320), (1, 256, 64)])
+@pytest.mark.parametrize("epi", [dlo.EPI_BIAS, dlo.EPI_BIAS_GELU, dlo.EPI_GATED_RESIDUAL])
+def test_gemm_small(M, N, K, epi):
+    torch = require_gpu()
+    say("gemm", M, N, K, "epi", epi)
+    A = _bf16_rand(M * 7 + 1, (M, K))
+    B = _bf16_rand(N * 5 + 2, (N, K), 0.05)
+    bias = synth.normal_f32(3, 9, 1, 0, (N,), 0.0, 0.1)
+    gate = synth.normal_f32(4, 9, 2, 0, (N,), 0.0, 1.0)
+    X0 = synth.normal_f32(5, 9, 3, 0, (M, N))
+    ref = of.linear(bf16_to_f64(A), bf16_to_f64(B), bias.astype(np.float64))
+    dA, dB, db, dg = _dev(torch, A), _dev(torch, B), _dev(torch, bias), _dev(torch, gate)
+    s = torch.cuda.current_stream().cuda_stream
+    if epi == dlo.EPI_GATED_RESIDUAL:
+        dX = _dev(torch, X0)
+        dlo.op_gemm(dA.data_ptr(), K, dB.data_ptr(), K, M, N, K, db.data_ptr(), dg.data_ptr(),
+                    dX.data_ptr(), N, epi, s)
+        torch.cuda.synchronize()
+        got = dX.cpu().numpy().astype(np.float64)
+        want = X0.astype(np.float64) + gate.astype(np.float64) * ref
+        assert rel_err(got - X0, want - X0) < 1e-5
+    else:
+        dC = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+        dlo.op_gemm(dA.data_ptr(), K, dB.data_ptr(), K, M, N, K, db.data_ptr(), 0,
+                    dC.data_ptr(), N, epi, s)
+        torch.cuda.synchronize()
+        got = bf16_to_f64(dC.cpu().numpy().view(np.uint16))
+        want = of.gelu_erf(ref) if epi == dlo.EPI_BIAS_GELU else ref
+        nbad, worst = _close_bf16(got, want)
+        assert nbad == 0, (nbad, worst)
+
+
+def test_gemm_full_size_sampled():
+    """QKV-shaped product of the Super workload (M=28800, N=15360, K=5120), sampled."""
+    torch = require_gpu()
+    M, N, K = 28800, 15360, 5120
+    say("gemm full size", M, N, K)
+    A = _bf16_rand(11, (M, K))
+    B = _bf16_rand(12, (N, K), 0.02)
+    bias = synth.normal_f32(13, 9, 1, 0, (N,), 0.0, 0.02)
+    dA, dB, db = _dev(torch, A), _dev(torch, B), _dev(torch, bias)
+    dC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    dlo.op_gemm(dA.data_ptr(), K, dB.data_ptr(), K, M, N, K, db.data_ptr(), 0, dC.data_ptr(), N,
+                dlo.EPI_BIAS, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.concatenate([rng.integers(0, M, 48), [0, M - 1, 28671, 28672]])
+    cols = np.concatenate([rng.integers(0, N, 48), [0, N - 1, 255, 256]])
+    C = dC[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16)[:, cols]
+    ref = of.linear(bf16_to_f64(A[rows]), bf16_to_f64(B[cols]), bias[cols].astype(np.float64))
+    nbad, worst = _close_bf16(bf16_to_f64(C), ref)
+    assert nbad == 0, (nbad, worst)
+
+
+def _attention_case(torch, T, H, dh, seed):
+    d = H * dh
+    qkv = _bf16_rand(seed, (T, 3 * d), 1.0)
+    dq = _dev(torch, qkv)
+    dout = torch.zeros((T, d), dtype=torch.int16, device="cuda")
+    dlo.op_attention(dq.data_ptr(), 3 * d, T, H, dh, dout.data_ptr(), d,
+                     torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return qkv, bf16_to_f64(dout.cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("T,H,dh", [(1, 1, 64), (64, 4, 64), (300, 2, 128), (1000, 3, 64), (777, 2, 128)])
+def test_attention_small(T, H, dh):
+    torch = require_gpu()
+    say("attention", T, H, dh)
+    qkv, got = _attention_case(torch, T, H, dh, T + H + dh)
+    d = H * dh
+    q = bf16_to_f64(qkv[:, :d])
+    k = bf16_to_f64(qkv[:, d:2 * d])
+    v = bf16_to_f64(qkv[:, 2 * d:])
+    ref = of.attention(q, k, v, H)
+    # P is rounded to bf16 before P V and the output to bf16: 2^-7 of max|ref| is generous
+    assert rel_err(got, ref) < 2.0 ** -7, rel_err(got, ref)
+
+
+def test_attention_full_size_sampled():
+    """Super-shaped attention: T=28800, 40 heads of 128, sampled query rows and heads."""
+    torch = require_gpu()
+    T, H, dh = 28800, 40, 128
+    say("attention full size", T, H, dh)
+    qkv, got = _attention_case(torch, T, H, dh, 77)
+    d = H * dh
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([rng.integers(0, T, 12), [0, T - 1, 28672, 28671]])
+    for h in (0, 17, 39):
+        cols = slice(h * dh, (h + 1) * dh)
+        q = bf16_to_f64(qkv[rows, h * dh:(h + 1) * dh])
+        k = bf16_to_f64(qkv[:, d + h * dh:d + (h + 1) * dh])
+        v = bf16_to_f64(qkv[:, 2 * d + h * dh:2 * d + (h + 1) * dh])
+        ref = of.attention(q, k, v, 1)
+        assert rel_err(got[rows][:, cols], ref) < 2.0 ** -7
+
+
+@pytest.mark.parametrize("T,d,ldx", [(1, 256, 256), (33, 1024, 1024), (17, 5120, 5120), (9, 2048, 4096)])
+def test_ln_modulate(T, d, ldx):
+    torch = require_gpu()
+    say("ln_modulate", T, d, ldx)
+    x = synth.normal_f32(20, 9, 0, 0, (T, ldx), 0.5, 2.0)
+    gamma = synth.normal_f32(21, 9, 0, 0, (d,), 1.0, 0.1)
+    beta = synth.normal_f32(22, 9, 0, 0, (d,), 0.0, 0.1)
+    shift = synth.normal_f32(23, 9, 0, 0, (d,), 0.0, 0.1)
+    scale = synth.normal_f32(24, 9, 0, 0, (d,), 0.0, 0.1)
+    eps = np.array([1e-6], np.float32)
+    dx, dg, db, de, dsh, dsc = (_dev(torch, a) for a in (x, gamma, beta, eps, shift, scale))
+    dout = torch.zeros((T, d), dtype=torch.int16, device="cuda")
+    dlo.op_ln_modulate(dx.data_ptr(), ldx, T, d, dg.data_ptr(), db.data_ptr(), de.data_ptr(),
+                       dsh.data_ptr(), dsc.data_ptr(), dout.data_ptr(),
+                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(dout.cpu().numpy().view(np.uint16))
+    ref = of.layer_norm(x[:, :d].astype(np.float64), gamma, beta, 1e-6) * (1 + scale.astype(np.float64)) + shift
+    nbad, worst = _close_bf16(got, ref)
+    assert nbad == 0, (nbad, worst)
+
+
+@pytest.mark.parametrize("d", [256, 1024, 5120])
+def test_adaln(d):
+    torch = require_gpu()
+    say("adaln", d)
+    W = _bf16_rand(30 + d, (6 * d, d), 0.02)
+    b = synth.normal_f32(31, 9, 0, 0, (6 * d,), 0.0, 0.02)
+    c = synth.normal_f32(32, 9, 0, 0, (d,))
+    dW, db, dc = _dev(torch, W), _dev(torch, b), _dev(torch, c)
+    out = torch.zeros(6 * d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(4 * d, dtype=torch.uint8, device="cuda")
+    dlo.op_adaln(dW.data_ptr(), db.data_ptr(), dc.data_ptr(), 6 * d, d, out.data_ptr(),
+                 ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = of.linear(of.silu(c.astype(np.float64))[None, :], bf16_to_f64(W), b.astype(np.float64))[0]
+    assert rel_err(out.cpu().numpy(), ref) < 1e-5
+
+
+def test_digest_matches_oracle_definition():
+    torch = require_gpu()
+    say("digest")
+    rng = np.random.default_rng(5)
+    buf = rng.integers(0, 256, size=1 << 20, dtype=np.uint8)
+    dbuf = _dev(torch, buf)
+    out = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for offs, lens in [([0], [1 << 20]), ([256, 4096], [1001, 5000]), ([0, 1 << 19], [7, 3])]:
+        dlo.op_digest(dbuf.data_ptr(), offs, lens, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        got = int(out.cpu().numpy().view(np.uint64)[0])
+        want = op.digest_regions([(o, buf[o:o + n]) for o, n in zip(offs, lens)])
+        assert got == want

@@ -1,0 +1,190 @@
+"""End-to-end streamed stack on the GPU against the oracle.
+
+* activations: max|gpu - ref| / max|ref| <= 2e-2 on the final x, and the same on
+  the accumulated update x - x0 (a skipped block or a stale slot moves x by only
+  a few percent, so the update metric is the one that catches it);
+* slot trace: equal to the oracle's hook simulation, step by step;
+* slot contents: per-step digests equal the oracle digest of the expected block,
+  before and after the block ran (nothing overwrote a slot being read), and the
+  final slot bytes equal the oracle's reassembled shards;
+* streamed == resident and k-invariance: bit-exact (the method must not change
+  a single bit of what the resident model computes).
+"""
+import numpy as np
+import pytest
+
+import synth
+import layerwise_weight_streaming_amd as dlo
+from oracle import forward as of
+from oracle import plan as op
+from oracle import schedule as sc
+from tests.gpu_util import TOL, make_runner, rel_err, require_gpu, say, spec_blocks
+
+pytestmark = pytest.mark.gpu
+
+
+def _expected_regions(w, stack, k):
+    regs = []
+    for ps in stack.blocks:
+        bp = op.plan_block(op.specs_of(ps), k)
+        regs.append(op.slot_regions(bp, op.pack_block(ps, bp)))
+    return regs
+
+
+def _check_trace(tr, n, passes, regs=None):
+    ref = sc.simulate_hooks(n, passes)
+    assert len(tr) == len(ref)
+    for got, e in zip(tr, ref):
+        assert (got["step"], got["pass_"], got["block"], got["read_slot"], got["prefetch_block"],
+                got["prefetch_slot"]) == (e.step, e.pass_, e.block, e.read_slot, e.prefetch_block,
+                                          e.prefetch_slot)
+        if regs is not None:
+            want = op.digest_regions(regs[e.block])
+            assert got["digest_pre"] == want, f"step {e.step}: slot held other bytes before the block"
+            assert got["digest_post"] == want, f"step {e.step}: slot changed while the block ran"
+
+
+def _run_and_compare(name, n_blocks=None, passes=None, seed=0, tokens=None):
+    torch = require_gpu()
+    w = synth.WORKLOADS[name]
+    if tokens is not None:
+        w = w.with_(tokens=tokens)
+    n = w.n_blocks if n_blocks is None else n_blocks
+    P = w.passes if passes is None else passes
+    say(f"stack {name} n={n} passes={P} T={w.tokens} k={w.k}")
+    stack = synth.make_stack(w, seed, n)
+    r = make_runner(w, stack)
+    run = r.forward(P, flags=dlo.TRACE_DIGEST)
+    tr = run.trace()
+    x_gpu = r.x_host()
+    regs = _expected_regions(w, stack, w.k)
+    _check_trace(tr, n, P, regs)
+    # final slot bytes: the last two steps' blocks
+    total = n * P
+    for t in (total - 1, total - 2):
+        if t < 0:
+            continue
+        e = tr[t]
+        slot = r.slot_host(e["read_slot"])
+        for off, buf in regs[e["block"]]:
+            assert slot[off:off + buf.size].tobytes() == buf.tobytes()
+    say("oracle forward")
+    x_ref = of.forward_stack(stack.x, stack.c, stack.blocks, [w.heads(b) for b in range(n)], P)
+    e_abs = rel_err(x_gpu, x_ref)
+    e_upd = rel_err(x_gpu - stack.x, x_ref - stack.x)
+    say(f"rel err {e_abs:.3e}, update rel err {e_upd:.3e}")
+    assert e_abs <= TOL and e_upd <= TOL
+    r.close()
+    return e_abs, e_upd
+
+
+def test_tiny_stack_streamed():
+    _run_and_compare("tiny")
+
+
+def test_tiny_stack_three_passes_odd_tail():
+    _run_and_compare("tiny", passes=3, seed=5)
+
+
+def test_8blk_stack_streamed():
+    _run_and_compare("8blk")
+
+
+def test_irregular_prefix_small_tokens():
+    # mixed widths 2048/3072/4096 and an odd block count (tail -> head correction), 3 passes
+    _run_and_compare("irregular", n_blocks=3, tokens=256, seed=2)
+
+
+def test_nano_prefix_full_shape():
+    # full Nano width and tokens, two blocks, one pass
+    _run_and_compare("nano", n_blocks=2, passes=1, seed=4)
+
+
+def _streamed_vs_resident(name, n, passes, tokens=None, ks=None):
+    torch = require_gpu()
+    w = synth.WORKLOADS[name]
+    if tokens is not None:
+        w = w.with_(tokens=tokens)
+    say(f"streamed vs resident {name} n={n} passes={passes} T={w.tokens}")
+    stack = synth.make_stack(w, 0, n)
+    r = make_runner(w, stack)
+    r.forward(passes, want_run=False)
+    x_stream = r.x_host()
+    r.set_inputs(stack.x, stack.c)
+    r.forward(passes, resident=True, want_run=False)
+    x_res = r.x_host()
+    assert np.array_equal(x_stream.view(np.uint32), x_res.view(np.uint32))
+    r.close()
+    for k in ks or []:
+        say(f"k = {k}")
+        r2 = make_runner(w, stack, k=k)
+        r2.forward(passes, want_run=False)
+        assert np.array_equal(r2.x_host().view(np.uint32), x_stream.view(np.uint32)), k
+        r2.close()
+    return x_stream
+
+
+def test_streamed_equals_resident_and_k_invariant_small():
+    _streamed_vs_resident("tiny", 3, 3, ks=[1, 3, 4, 8])
+    _streamed_vs_resident("8blk", 8, 2, ks=[1, 4])
+
+
+def test_streamed_equals_resident_irregular_full_tokens():
+    _streamed_vs_resident("irregular", 5, 2)
+
+
+def test_streamed_equals_resident_super_prefix():
+    # Super width and tokens, three blocks (odd), two passes
+    _streamed_vs_resident("super", 3, 2)
+
+
+def test_super_block_sampled_rows():
+    """One Super-shaped block (T=28800, d=5120): sampled output rows vs the oracle."""
+    torch = require_gpu()
+    w = synth.WORKLOADS["super"]
+    say("super one block, sampled rows")
+    stack = synth.make_stack(w, 0, 1)
+    r = make_runner(w, stack)
+    r.forward(1, want_run=False)
+    x_gpu = r.x_host()
+    r.close()
+    rng = np.random.default_rng(3)
+    rows = np.concatenate([rng.integers(0, w.tokens, 6), [0, w.tokens - 1]])
+    say("oracle rows")
+    ref = of.dit_block_rows(stack.x, stack.c, of.param_dict(stack.blocks[0]), w.heads(0), rows)
+    x0 = stack.x[rows]
+    assert rel_err(x_gpu[rows], ref) <= TOL
+    assert rel_err(x_gpu[rows] - x0, ref - x0) <= TOL
+
+
+def test_repeated_calls_reuse_slots():
+    """Back-to-back runs on the same slots (no host sync between them) equal two passes."""
+    torch = require_gpu()
+    w = synth.WORKLOADS["tiny"]
+    stack = synth.make_stack(w, 9)
+    r = make_runner(w, stack)
+    r.forward(1, want_run=False)
+    r.forward(1, want_run=False)
+    x_two_calls = r.x_host()
+    r.set_inputs(stack.x, stack.c)
+    r.forward(2, want_run=False)
+    assert np.array_equal(x_two_calls.view(np.uint32), r.x_host().view(np.uint32))
+    r.close()
+
+
+def test_timing_trace_is_ordered():
+    torch = require_gpu()
+    w = synth.WORKLOADS["8blk"]
+    stack = synth.make_stack(w, 1)
+    r = make_runner(w, stack)
+    run = r.forward(2, flags=dlo.TRACE_TIMING)
+    tr = run.trace()
+    kt = run.kernel_times()
+    assert kt.shape == (16, dlo.KERNELS_PER_BLOCK) and np.all(kt >= 0)
+    for e in tr:
+        assert 0 <= e["t_copy_begin"] <= e["t_copy_end"] <= e["t_compute_end"]
+        assert e["t_copy_end"] <= e["t_compute_begin"] + 1e-3 <= e["t_compute_end"] + 1e-3
+    # a slot is refilled only after the compute that last read it has ended
+    for t in range(2, len(tr)):
+        assert tr[t]["t_copy_begin"] >= tr[t - 2]["t_compute_end"] - 1e-3
+    r.close()

@@ -1,0 +1,276 @@
+"""libdlo host logic on the CPU: exports, plan, pack, schedule and fail-closed errors.
+
+Everything here runs without a GPU: the plan, the pageable host store, the
+schedule program and every validation path return before any HIP call.  The
+plan, the packed bytes and the schedule are compared with the oracle's own,
+independently written, implementation.
+"""
+import ctypes
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import synth
+import layerwise_weight_streaming_amd as dlo
+from oracle import plan as op
+from oracle import schedule as sc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(dlo.LIB_PATH):
+        from layerwise_weight_streaming_amd import _build
+        _build.build()
+    dlo.lib()
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "dlo.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dlo_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported_and_bound():
+    names = _header_functions()
+    assert len(names) >= 25
+    L = ctypes.CDLL(dlo.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == dlo.EXPORTED
+
+
+def test_schema_matches_input_generator():
+    for d in (256, 1024, 5120):
+        assert dlo.block_schema(d) == [(n, dt, int(np.prod(s))) for n, dt, s in synth.block_schema(d)]
+
+
+def _dit_blocks(w, n=None):
+    n = w.n_blocks if n is None else n
+    return [(w.width(b), w.heads(b), [(nm, dt, int(np.prod(s))) for nm, dt, s in synth.block_schema(w.width(b))])
+            for b in range(n)]
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_plan_matches_oracle_on_workloads(name):
+    w = synth.WORKLOADS[name]
+    blocks = _dit_blocks(w, min(w.n_blocks, 7))
+    p = dlo.Plan(blocks, w.k)
+    plans, slot = op.plan_stack([b[2] for b in blocks], w.k)
+    assert p.slot_bytes == slot
+    for b, bp in enumerate(plans):
+        info = p.block_info(b)
+        assert info["is_dit"]
+        assert info["extent"] == bp.extent
+        assert info["dtype"] == [g.dtype for g in bp.groups]
+        assert info["numel"] == [g.numel for g in bp.groups]
+        assert info["shard"] == [g.shard for g in bp.groups]
+        assert info["region"] == [g.region for g in bp.groups]
+        assert info["copy_bytes"] == sum(bp.region_bytes(g) for g in range(len(bp.groups)))
+        for i in range(16):
+            assert p.param_offset(b, i) == bp.param_byte_offset(i)
+
+
+def _random_params(rng, n):
+    out = []
+    for i in range(n):
+        dt = rng.choice(["bf16", "f32"])
+        numel = rng.choice([0, 1, 3, 7, 64, 255, rng.randint(0, 3000)])
+        if dt == "bf16":
+            a = np.frombuffer(rng.randbytes(2 * numel), dtype=np.uint16).copy()
+        else:
+            a = np.array([rng.uniform(-3, 3) for _ in range(numel)], dtype=np.float32)
+        out.append((f"p{i}", dt, a))
+    return out
+
+
+def test_plan_and_pack_match_oracle_randomised():
+    rng = random.Random(7)
+    for trial in range(60):
+        nb = rng.randint(1, 4)
+        k = rng.randint(1, 8)
+        params = [_random_params(rng, rng.randint(1, 5)) for _ in range(nb)]
+        blocks = [(256, 4, ps) for ps in params]
+        p = dlo.Plan(blocks, k)
+        st = dlo.HostStore(p, pinned=False)
+        assert not st.complete
+        st.pack(0, blocks)
+        assert st.complete
+        for b, ps in enumerate(params):
+            bp = op.plan_block(op.specs_of(ps), k)
+            info = p.block_info(b)
+            assert info["extent"] == bp.extent and info["region"] == [g.region for g in bp.groups]
+            shards = op.pack_block(ps, bp)
+            for g in range(len(bp.groups)):
+                for r in range(k):
+                    assert st.shard(b, g, r).tobytes() == shards[g][r].tobytes(), (trial, b, g, r)
+
+
+def test_pack_tiny_workload_matches_oracle_bytes():
+    w = synth.WORKLOADS["tiny"]
+    stack = synth.make_stack(w, seed=3)
+    blocks = [(w.width(b), w.heads(b), ps) for b, ps in enumerate(stack.blocks)]
+    p = dlo.Plan(blocks, w.k)
+    st = dlo.HostStore(p, pinned=False)
+    st.pack(0, blocks[:1])
+    st.pack(1, blocks[1:])
+    for b, ps in enumerate(stack.blocks):
+        bp = op.plan_block(op.specs_of(ps), w.k)
+        sh = op.pack_block(ps, bp)
+        for g in range(2):
+            for r in range(w.k):
+                assert st.shard(b, g, r).tobytes() == sh[g][r].tobytes()
+        # reassembled region = the slot image a placement produces
+        for g, (off, buf) in enumerate(op.slot_regions(bp, sh)):
+            assert off == p.block_info(b)["region"][g]
+
+
+@pytest.mark.parametrize("passes", [1, 2, 3, 4])
+def test_schedule_program_is_race_free_and_follows_the_hook_rule(passes):
+    for n in list(range(1, 25)) + [72, 127, 128]:
+        blocks = [(256, 4, [("w", "bf16", 10)]) for _ in range(n)]
+        prog = dlo.Plan(blocks, 2).schedule(passes)
+        assert sc.program_hazards(prog) == [], (n, passes)
+        computes = [o for o in prog if o[0] == "compute"]
+        ref = sc.simulate_hooks(n, passes)
+        assert [(o[2], o[3], o[4]) for o in computes] == [(e.block, e.read_slot, e.step) for e in ref]
+        copies = [o for o in prog if o[0] == "copy"]
+        want = [(0, 0)] + [(e.prefetch_block, e.prefetch_slot) for e in ref if e.prefetch_block >= 0]
+        assert [(o[2], o[3]) for o in copies] == want
+        # two slots only
+        assert {o[3] for o in prog if o[0] in ("copy", "compute")} <= {0, 1}
+
+
+def test_schedule_negative_control_detected():
+    # dropping the copy stream's wait on the previous reader must be flagged by the checker
+    blocks = [(256, 4, [("w", "bf16", 10)]) for _ in range(3)]
+    prog = dlo.Plan(blocks, 2).schedule(2)
+    broken = [o for o in prog if not (o[0] == "wait" and o[1] == "copy" and o[2].startswith("computed"))]
+    assert sc.program_hazards(broken)
+
+
+# ---------------------------------------------------------------------------
+# fail-closed validation (no GPU needed: every check runs before any HIP call)
+# ---------------------------------------------------------------------------
+
+def _status(fn, *a, **k):
+    with pytest.raises(dlo.DLOError) as ei:
+        fn(*a, **k)
+    return ei.value.status
+
+
+def test_plan_errors():
+    good = [("w", "bf16", 4)]
+    assert _status(dlo.Plan, [(256, 4, good)], 0) == "DLO_E_ARG"
+    assert _status(dlo.Plan, [], 2) == "DLO_E_ARG"
+    assert _status(dlo.Plan, [(256, 4, [("w", 7, 4)])], 2) == "DLO_E_ARG"
+    assert _status(dlo.Plan, [(256, 4, [("w", "f32", -1)])], 2) == "DLO_E_ARG"
+    out = ctypes.c_void_p(123)
+    assert dlo.lib().dlo_plan_blocks(None, 1, 2, ctypes.byref(out)) == -1 and out.value is None
+    p = dlo.Plan([(256, 4, good)], 2)
+    assert _status(p.block_info, 5) == "DLO_E_ARG"
+    assert _status(p.param_offset, 0, 3) == "DLO_E_ARG"
+    assert _status(p.schedule, 0) == "DLO_E_ARG"
+    assert "passes" in dlo.last_error()
+
+
+def test_pack_errors():
+    a = np.arange(6, dtype=np.float32)
+    p = dlo.Plan([(256, 4, [("a", "f32", 6)]), (256, 4, [("b", "f32", 6)])], 4)
+    st = dlo.HostStore(p, pinned=False)
+    assert _status(st.pack, 0, [(256, 4, [("x", "f32", a)])]) == "DLO_E_PLAN_MISMATCH"  # name
+    assert _status(st.pack, 0, [(256, 4, [("a", "bf16", a.view(np.uint16)[:6])])]) == "DLO_E_PLAN_MISMATCH"
+    assert _status(st.pack, 0, [(256, 4, [("a", "f32", a[:5])])]) == "DLO_E_PLAN_MISMATCH"  # numel
+    assert _status(st.pack, 1, [(256, 4, [("a", "f32", a)])]) == "DLO_E_PLAN_MISMATCH"  # wrong block
+    assert _status(st.pack, 2, [(256, 4, [("b", "f32", a)])]) == "DLO_E_ARG"  # range
+    assert _status(st.pack, 0, [(256, 4, [("a", "f32", 6)])]) == "DLO_E_ARG"  # no source
+    assert not st.complete
+    st.pack(0, [(256, 4, [("a", "f32", a)])])
+    assert not st.complete
+
+
+def test_pinned_store_without_device_fails_closed():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present: pinned allocation would succeed")
+    except ImportError:
+        pass
+    p = dlo.Plan([(256, 4, [("a", "f32", 6)])], 2)
+    out = ctypes.c_void_p(77)
+    rc = dlo.lib().dlo_host_store_create(p.h, 0, ctypes.byref(out))
+    assert rc == -3 and out.value is None
+    assert "hipHostMalloc" in dlo.last_error()
+
+
+def _tiny_plan_and_store(n=3, d=256, heads=4, k=2):
+    blocks = [(d, heads, [(nm, dt, int(np.prod(s))) for nm, dt, s in synth.block_schema(d)])
+              for _ in range(n)]
+    p = dlo.Plan(blocks, k)
+    st = dlo.HostStore(p, pinned=False)
+    filled = [(d, heads, [(nm, dt, np.zeros(int(np.prod(s)), dtype=np.uint16 if dt == "bf16" else np.float32))
+                          for nm, dt, s in synth.block_schema(d)]) for _ in range(n)]
+    st.pack(0, filled)
+    return p, st
+
+
+def _args(p, **over):
+    kw = dict(x=0x1000, x_row_stride=256, cond=0x2000, workspace=0x3000,
+              workspace_bytes=p.workspace_bytes(64), compute_stream=0x10, copy_stream=0x20,
+              tokens=64, passes=2, slots=(0x100000, 0x100000 + p.slot_bytes), slot_bytes=p.slot_bytes)
+    kw.update(over)
+    return kw
+
+
+def test_forward_validation_errors():
+    p, st = _tiny_plan_and_store()
+    F = lambda **o: dlo.forward_stack(p, st, **_args(p, **o))
+    assert _status(F, tokens=0) == "DLO_E_ARG"
+    assert _status(F, passes=0) == "DLO_E_ARG"
+    assert _status(F, x=0) == "DLO_E_ARG"
+    assert _status(F, copy_stream=0x10) == "DLO_E_ARG"          # aliased streams
+    assert _status(F, copy_stream=0) == "DLO_E_ARG"
+    assert _status(F, x_row_stride=128) == "DLO_E_ARG"
+    assert _status(F, workspace_bytes=100) == "DLO_E_WORKSPACE"
+    assert _status(F, slot_bytes=p.slot_bytes - 1) == "DLO_E_SLOT_SMALL"
+    assert _status(F, slots=(0x100000, 0x100000 + 256)) == "DLO_E_ARG"   # overlapping slots
+    assert _status(F, slots=(0, 0x100000)) == "DLO_E_ARG"
+    assert _status(F, flags=64) == "DLO_E_ARG"
+    assert _status(F, flags=dlo.RESIDENT) == "DLO_E_ARG"        # no resident pointers
+    # a store made by another plan is the analogue of double sharding: rejected
+    p2, st2 = _tiny_plan_and_store()
+    assert _status(lambda: dlo.forward_stack(p, st2, **_args(p))) == "DLO_E_PLAN_MISMATCH"
+    # an incompletely packed store
+    st3 = dlo.HostStore(p, pinned=False)
+    assert _status(lambda: dlo.forward_stack(p, st3, **_args(p))) == "DLO_E_STATE"
+
+
+def test_forward_rejects_unsupported_blocks():
+    # head dim 32
+    p, st = _tiny_plan_and_store(heads=8)
+    assert _status(lambda: dlo.forward_stack(p, st, **_args(p))) == "DLO_E_UNSUPPORTED"
+    # width not a multiple of 256
+    blocks = [(320, 5, [(nm, dt, int(np.prod(s))) for nm, dt, s in synth.block_schema(320)])]
+    p = dlo.Plan(blocks, 2)
+    st = dlo.HostStore(p, pinned=False)
+    st.pack(0, [(320, 5, [(nm, dt, np.zeros(int(np.prod(s)), dtype=np.uint16 if dt == "bf16" else np.float32))
+                          for nm, dt, s in synth.block_schema(320)])])
+    assert _status(lambda: dlo.forward_stack(p, st, **_args(p, x_row_stride=320))) == "DLO_E_UNSUPPORTED"
+    # a block that is not the DiT schema
+    p = dlo.Plan([(256, 4, [("w", "bf16", 8)])], 2)
+    st = dlo.HostStore(p, pinned=False)
+    st.pack(0, [(256, 4, [("w", "bf16", np.zeros(8, np.uint16))])])
+    assert _status(lambda: dlo.forward_stack(p, st, **_args(p))) == "DLO_E_UNSUPPORTED"
+
+
+def test_op_validation_errors():
+    assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 100, 64, 1, 0, 1, 100, 0, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 256, 60, 1, 0, 1, 256, 0, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 256, 64, 1, 0, 1, 256, 2, 0) == "DLO_E_ARG"  # no gate
+    assert _status(dlo.op_attention, 1, 3 * 4 * 32, 10, 4, 32, 1, 128, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_ln_modulate, 1, 300, 4, 300, 1, 1, 1, 1, 1, 1, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_digest, 1, [3], [8], 1, 0) == "DLO_E_ARG"
