@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the double-buffered, layerwise weight-streamed DiT stack on one MI355X.
+
+One step = one call of dlo_forward_stack: every block of the stack, for the
+workload's number of chained passes, with block N+1's shards streaming into the
+free slot while block N computes.  Inputs are seeded synthetic data with the
+workload's shapes; the host store is packed before timing; x, cond and the slots
+live in HBM when the timed region starts.
+
+Printed: one JSON line (blocks/s as ``value``) with tokens/s, host-to-device
+GB/s against the PCIe 5.0 x16 link, bf16 MFMA utilisation against the dense
+peak, copy/compute overlap efficiency (all from HIP events recorded by libdlo on
+the streams the work runs on), the dominant kernel's roofline position, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+LINK_PEAK_GBS = 32.0 * 16 * 128 / 130 / 8   # PCIe 5.0 x16, one direction: 63.0 GB/s
+
+
+def kernel_work(name, d, T):
+    """Algorithmic work of one launch: (amount, unit, bound)."""
+    if name == "adaln_gemv":
+        return (6 * d * d * 2 + 6 * d * 4 * 2 + d * 4) / 1e9, "GB", "hbm"
+    if name in ("ln1_modulate", "ln2_modulate"):
+        return (T * d * 4 + T * d * 2) / 1e9, "GB", "hbm"
+    flops = {"gemm_qkv": 2 * T * d * 3 * d, "attention": 4 * T * T * d,
+             "gemm_out_residual": 2 * T * d * d, "gemm_fc1_gelu": 8 * T * d * d,
+             "gemm_fc2_residual": 8 * T * d * d}[name]
+    return flops / 1e12, "TFLOP", "mfma"
+
+
+def block_flops(d, T):
+    return 24 * T * d * d + 4 * T * T * d + 12 * d * d
+
+
+def union(iv):
+    iv = sorted((a, b) for a, b in iv if b > a)
+    out = []
+    for a, b in iv:
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def length(u):
+    return sum(b - a for a, b in u)
+
+
+def intersect(u, v):
+    i = j = 0
+    tot = 0.0
+    while i < len(u) and j < len(v):
+        a, b = max(u[i][0], v[j][0]), min(u[i][1], v[j][1])
+        if b > a:
+            tot += b - a
+        if u[i][1] < v[j][1]:
+            i += 1
+        else:
+            j += 1
+    return tot
+
+
+def clip(u, lo, hi):
+    return [[max(a, lo), min(b, hi)] for a, b in u if min(b, hi) > max(a, lo)]
+
+
+def overlap_metrics(trace, copy_bytes, flops):
+    """Steady window: from the start of copy(1) to the end of compute(last - 1)."""
+    n = len(trace)
+    if n < 3:
+        return None
+    lo, hi = trace[1]["t_copy_begin"], trace[n - 2]["t_compute_end"]
+    C = clip(union([(e["t_compute_begin"], e["t_compute_end"]) for e in trace]), lo, hi)
+    M = clip(union([(e["t_copy_begin"], e["t_copy_end"]) for e in trace[1:]]), lo, hi)
+    c, m, W = length(C), length(M), hi - lo
+    in_w = [e for e in trace[1:n - 1]]
+    bytes_w = sum(copy_bytes[e["block"]] for e in in_w)
+    flops_w = sum(flops[e["block"]] for e in in_w)
+    return {
+        "window_ms": W, "compute_busy_ms": c, "copy_busy_ms": m,
+        "overlap_eff": intersect(C, M) / max(min(c, m), 1e-9),
+        "wall_eff": max(c, m) / W,
+        "h2d_busy_GBps": bytes_w / (m * 1e-3) / 1e9,
+        "h2d_delivered_GBps": bytes_w / (W * 1e-3) / 1e9,
+        "mfma_util_busy": flops_w / (c * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "mfma_util_wall": flops_w / (W * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "bound": "h2d" if m > c else "compute",
+    }
+
+
+def measure_link(torch, dev, gib=1, reps=4):
+    """Pinned host -> device copy rate of one large buffer (practical link peak)."""
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        dst.copy_(src, non_blocking=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        e1.record(s)
+    s.synchronize()
+    ms = e0.elapsed_time(e1)
+    del src, dst
+    return reps * n / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(w, seed, rows=128):
+    """The oracle, untouched, on a bounded sample: sampled output rows of the first block.
+
+    dit_block_rows computes LN1 and the k/v projections for every token and the
+    rest of the block for ``rows`` query rows; its FLOPs are counted and the
+    rate is scaled to whole blocks by the ratio of FLOPs.
+    """
+    import synth
+    from oracle import forward as of
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    d, T, H = w.width(0), w.tokens, w.heads(0)
+    params = synth.block_params(seed, 0, d)
+    x = synth.activations(seed, T, w.D)
+    c = synth.conditioning(seed, w.D)
+    idx = np.linspace(0, T - 1, rows).astype(np.int64)
+    t0 = time.perf_counter()
+    of.dit_block_rows(x, c, of.param_dict(params), H, idx)
+    dt = time.perf_counter() - t0
+    f_sample = 2 * T * d * 2 * d + rows * (2 * d * d + 4 * T * d + 2 * d * d + 16 * d * d) + 12 * d * d
+    frac = f_sample / block_flops(d, T)
+    blocks_per_s = frac / dt
+    return {"value": blocks_per_s, "unit": "blocks/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 oracle, first block of the {w.name} stack (d={d}, T={T}): "
+                       f"k/v for all tokens + {rows} sampled query rows, {dt:.1f} s for "
+                       f"{frac * 100:.2f}% of a block's FLOPs, scaled by that FLOP fraction")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="super")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--k", type=int, default=None)
+    ap.add_argument("--blocks", type=int, default=None, help="use only the first N blocks")
+    ap.add_argument("--pinned-limit-gib", type=float, default=56.0,
+                    help="ceiling on pinned block memory; blocks beyond it are staged")
+    ap.add_argument("--store", default="auto", choices=["auto", "pinned", "pageable"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the streamed == resident bit-exact check")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the stack is streamed from this host into this "
+              "GPU's two slots; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import layerwise_weight_streaming_amd as dlo
+    from layerwise_weight_streaming_amd.runner import StackRunner
+
+    def log(*a):
+        print("[bench]", *a, file=sys.stderr, flush=True)
+
+    dlo.lib()
+    dev = torch.device("cuda", 0)
+    w = synth.WORKLOADS[args.config]
+    if args.k:
+        w = w.with_(k=args.k)
+    n = args.blocks or w.n_blocks
+    T, P = w.tokens, w.passes
+    specs = [(w.width(b), w.heads(b), [(nm, dt, int(np.prod(s))) for nm, dt, s in synth.block_schema(w.width(b))])
+             for b in range(n)]
+
+    t_setup = time.perf_counter()
+    r = StackRunner(specs, w.k, T, w.D, store_mode=args.store,
+                    pinned_limit=int(args.pinned_limit_gib * (1 << 30)))
+    t_alloc = time.perf_counter() - t_setup
+    store_info = r.store.info()
+    log(f"{w.name}: {n} blocks, slot {r.plan.slot_bytes / 1e6:.1f} MB, store {store_info} "
+        f"allocated in {t_alloc:.1f} s")
+    bufs = {}
+    t_gen = t_pack = 0.0
+    for b in range(n):
+        d = w.width(b)
+        key = d
+        if key not in bufs:
+            bufs[key] = {nm: np.empty(s, dtype=np.uint16 if dt == "bf16" else np.float32)
+                         for nm, dt, s in synth.block_schema(d)}
+        t0 = time.perf_counter()
+        ps = synth.block_params(args.seed, b, d, out_buffers=bufs[key])
+        t1 = time.perf_counter()
+        r.pack(b, [(d, w.heads(b), ps)])
+        t2 = time.perf_counter()
+        t_gen += t1 - t0
+        t_pack += t2 - t1
+        if b % 32 == 31:
+            log(f"packed {b + 1}/{n} blocks")
+    del bufs
+    x0 = synth.activations(args.seed, T, w.D)
+    c0 = synth.conditioning(args.seed, w.D)
+    r.set_inputs(x0, c0)
+    log(f"generated in {t_gen:.1f} s, packed in {t_pack:.1f} s")
+
+    link = measure_link(torch, dev)
+    log(f"pinned H2D microbenchmark: {link:.1f} GB/s")
+
+    for i in range(args.warmup):
+        r.forward(P, want_run=False)
+        r.synchronize()
+        log(f"warmup step {i + 1} done")
+
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    runs = [r.forward(P, flags=dlo.TRACE_TIMING) for _ in range(args.steps)]
+    r.synchronize()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.2f} s")
+
+    infos = [r.plan.block_info(b) for b in range(n)]
+    copy_bytes = [i["copy_bytes"] for i in infos]
+    flops = [block_flops(i["d_model"], T) for i in infos]
+    names = dlo.kernel_names()
+    per_kernel = np.zeros(len(names))
+    launches = 0
+    work = np.zeros(len(names))
+    ov = []
+    for run in runs:
+        tr = run.trace()
+        kt = run.kernel_times()
+        per_kernel += kt.sum(axis=0)
+        launches += kt.shape[0]
+        for e, row in zip(tr, kt):
+            d = infos[e["block"]]["d_model"]
+            for j, nm in enumerate(names):
+                work[j] += kernel_work(nm, d, T)[0]
+        m = overlap_metrics(tr, copy_bytes, flops)
+        if m:
+            ov.append(m)
+        run.close()
+    avg = {k: float(np.median([m[k] for m in ov])) for k in ov[0] if k != "bound"} if ov else {}
+    bound = ov[0]["bound"] if ov else None
+    jdom = int(np.argmax(per_kernel))
+    dname = names[jdom]
+    _, unit, kbound = kernel_work(dname, w.width(0), T)
+    avg_ms = per_kernel[jdom] / launches
+    achieved = work[jdom] / launches / (avg_ms * 1e-3)
+    peak = PEAK_BF16_TFLOPS if kbound == "mfma" else PEAK_HBM_GBS
+    roofline = {"kernel": dname, "bound": kbound, "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s" if kbound == "mfma" else "GB/s", "frac": achieved / peak,
+                "traffic": None, "avg_launch_ms": avg_ms,
+                "per_launch": f"{work[jdom] / launches:.4g} {unit}"}
+
+    blocks_done = n * P * args.steps
+    result = {
+        "metric": "DiT blocks/s with streaming",
+        "value": blocks_done / wall,
+        "unit": "blocks/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "n_blocks": n,
+                   "widths": list(w.widths), "head_dim": w.head_dim, "tokens": T, "batch": 1,
+                   "k": w.k, "passes": P, "slot_bytes": r.plan.slot_bytes,
+                   "block_copy_bytes": max(copy_bytes), "host_store_bytes": sum(copy_bytes),
+                   "parallelism": "single GPU", "store": args.store,
+                   "pinned_blocks": store_info["pinned_blocks"],
+                   "staged_blocks": store_info["staged_blocks"]},
+        "tokens_per_s": T * P * args.steps / wall,
+        "h2d": {"busy_GBps": avg.get("h2d_busy_GBps"), "delivered_GBps": avg.get("h2d_delivered_GBps"),
+                "link_peak_GBps": LINK_PEAK_GBS, "measured_link_GBps": link,
+                "frac_of_link_peak": (avg.get("h2d_busy_GBps") or 0) / LINK_PEAK_GBS},
+        "mfma_util": {"busy": avg.get("mfma_util_busy"), "wall": avg.get("mfma_util_wall"),
+                      "peak_TFLOPs": PEAK_BF16_TFLOPS},
+        "overlap_eff": avg.get("overlap_eff"), "wall_eff": avg.get("wall_eff"),
+        "bound_resource": bound,
+        "steady_window": {k: avg.get(k) for k in ("window_ms", "compute_busy_ms", "copy_busy_ms")},
+        "per_kernel_ms_per_block": {nm: per_kernel[j] / launches for j, nm in enumerate(names)},
+        "roofline": roofline,
+        "setup_s": {"pin_alloc": t_alloc, "generate": t_gen, "pack": t_pack},
+    }
+
+    if not args.no_verify:
+        # the pages' own correctness criterion at full scale: streamed == resident, bit-exact
+        log("verify: streamed vs resident, one step each from the same inputs")
+        r.set_inputs(x0, c0)
+        r.forward(P, want_run=False)
+        xs = r.x_host()
+        r.set_inputs(x0, c0)
+        t0 = time.perf_counter()
+        r.make_resident()
+        r.forward(P, resident=True, want_run=False)
+        r.synchronize()
+        t_res = time.perf_counter() - t0
+        xr = r.x_host()
+        r.free_resident()
+        result["streamed_equals_resident"] = bool(np.array_equal(xs.view(np.uint32), xr.view(np.uint32)))
+        result["finite"] = bool(np.isfinite(xs).all())
+        log(f"verify: equal={result['streamed_equals_resident']} (resident place+step {t_res:.1f} s)")
+
+    r.close()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        result["cpu_baseline"] = cpu_baseline(w, args.seed)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

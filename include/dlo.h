@@ -142,13 +142,35 @@ int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens);
  * Host store ([Aug] s.2: each shard is a pinned DMA buffer)
  * ------------------------------------------------------------------------- */
 
-#define DLO_STORE_PINNED 0u     /* hipHostMalloc'd shards (DMA-capable; the default) */
-#define DLO_STORE_PAGEABLE 1u   /* ordinary aligned host memory (no GPU needed) */
+#define DLO_STORE_PINNED 0u     /* every shard in hipHostMalloc'd memory (the default) */
+#define DLO_STORE_PAGEABLE 1u   /* every shard in ordinary host memory (no GPU needed) */
+#define DLO_STORE_AUTO 2u       /* pin blocks while the pinned ceiling allows, rest pageable */
 
-/* Allocates every shard of every block of the plan (zero-filled).  Shards start
- * on 4096-byte boundaries.  Fails with DLO_E_PIN / DLO_E_HOSTMEM after freeing
- * whatever it had allocated. */
+/* Allocates every shard of every block of the plan.  Shards start on 4096-byte
+ * boundaries; their bytes are undefined until packed.  Fails with DLO_E_PIN /
+ * DLO_E_HOSTMEM after freeing whatever it had allocated.
+ *
+ * Blocks held in ordinary (pageable) memory reach the GPU through two bounded
+ * pinned staging buffers of one slot each ([Doc] "Rank-local path without DLO
+ * AllGather": complete blocks from host views through two bounded pinned host
+ * staging slots): the host copies the block's shards into a staging buffer at
+ * their slot offsets, then the DMA engine copies them into the slot.  The
+ * staging buffers are allocated on the first forward that needs them (GPU
+ * required then). */
 int dlo_host_store_create(const dlo_plan *plan, uint32_t flags, dlo_host_store **out);
+
+/* As dlo_host_store_create; with DLO_STORE_AUTO, `pinned_limit_bytes` (> 0) caps
+ * the pinned bytes of block shards (the two staging buffers are reserved first and
+ * not counted) -- the analogue of a per-worker registration ceiling ([Doc]
+ * "Registered mmap transport").  Blocks are pinned in order until the next one
+ * would cross the ceiling or the pinned allocation fails; the rest are pageable.
+ * pinned_limit_bytes = 0 means no ceiling. */
+int dlo_host_store_create_ex(const dlo_plan *plan, uint32_t flags, int64_t pinned_limit_bytes,
+                             dlo_host_store **out);
+
+/* Number of blocks whose shards are pinned, their bytes, and the number staged. */
+int dlo_host_store_info(const dlo_host_store *store, int32_t *pinned_blocks,
+                        int64_t *pinned_bytes, int32_t *staged_blocks);
 
 /* Destroys the store.  Copies that read it must have completed: the caller
  * synchronises the copy stream of every run that used it first. */
@@ -181,11 +203,12 @@ int32_t dlo_host_store_complete(const dlo_host_store *store);
  * Program per run: RECORD(compute, START), WAIT(copy, START),
  * COPY(block 0 -> slot 0), RECORD(copy, COPIED[0]); then for step t (pass p,
  * block i, read slot s):
+ *   WAIT(compute, COPIED[s]), COMPUTE(block i, slot s), RECORD(compute, COMPUTED[s])
  *   if t is not the last step:  [t >= 1: WAIT(copy, COMPUTED[s'])]
  *                               COPY(next block -> s'), RECORD(copy, COPIED[s'])
- *   WAIT(compute, COPIED[s]), COMPUTE(block i, slot s), RECORD(compute, COMPUTED[s])
- * where s' = 1 - s.  COPY issues 2k hipMemcpyAsync calls (k shards per dtype
- * group) to slot + region_g + r * S_g * elt_g.
+ * where s' = 1 - s: the copy into s' waits for step t-1, the last reader of s'.
+ * COPY issues 2k hipMemcpyAsync calls (k shards per dtype group) to
+ * slot + region_g + r * S_g * elt_g.
  * ------------------------------------------------------------------------- */
 
 enum { DLO_OP_COPY = 0, DLO_OP_COMPUTE = 1, DLO_OP_RECORD = 2, DLO_OP_WAIT = 3 };
@@ -246,13 +269,16 @@ typedef struct {
                                          block's slot image (see dlo_place_block) */
 } dlo_forward_args;
 
-/* Enqueues `passes` passes of the stack and returns without waiting.  x is
- * updated on the compute stream; everything the caller enqueued on the compute
- * stream before the call happens before the run, and the copy stream waits for
- * it too.  Each call starts afresh at block 0 in slot 0.  Caller memory must stay
- * valid until the compute stream has drained.  If run_out is non-NULL it receives
- * a handle for dlo_slot_trace (free with dlo_run_destroy); otherwise the library
- * releases the run's resources once it has completed. */
+/* Enqueues `passes` passes of the stack.  x is updated on the compute stream;
+ * everything the caller enqueued on the compute stream before the call happens
+ * before the run, and the copy stream waits for it too.  Each call starts afresh
+ * at block 0 in slot 0.  Caller memory must stay valid until the compute stream
+ * has drained.  With a fully pinned store the call returns without waiting; when
+ * blocks are staged, the host fills each staging buffer in step order, so the
+ * call returns once the last staged block has been handed to the copy stream.
+ * If run_out is non-NULL it receives a handle for dlo_slot_trace (free with
+ * dlo_run_destroy); otherwise the library releases the run's resources once it
+ * has completed. */
 int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
                       const dlo_forward_args *args, dlo_run **run_out);
 

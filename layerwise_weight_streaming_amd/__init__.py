@@ -23,7 +23,7 @@ STATUS = {0: "DLO_OK", -1: "DLO_E_ARG", -2: "DLO_E_HOSTMEM", -3: "DLO_E_PIN",
           -7: "DLO_E_STATE", -8: "DLO_E_UNSUPPORTED", -9: "DLO_E_WORKSPACE"}
 DTYPES = {"bf16": 0, "f32": 1}
 DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
-STORE_PINNED, STORE_PAGEABLE = 0, 1
+STORE_PINNED, STORE_PAGEABLE, STORE_AUTO = 0, 1, 2
 TRACE_DIGEST, TRACE_TIMING, RESIDENT = 1, 2, 4
 EPI_BIAS, EPI_BIAS_GELU, EPI_GATED_RESIDUAL = 0, 1, 2
 KERNELS_PER_BLOCK = 8
@@ -105,6 +105,10 @@ _SIGS = {
                                          ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "dlo_host_store_create": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint32,
                                              ctypes.POINTER(ctypes.c_void_p)]),
+    "dlo_host_store_create_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int64,
+                                                ctypes.POINTER(ctypes.c_void_p)]),
+    "dlo_host_store_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]),
     "dlo_host_store_destroy": (None, [ctypes.c_void_p]),
     "dlo_pack_host_shards": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(Block)]),
@@ -275,14 +279,27 @@ class Plan:
 
 
 class HostStore:
-    """dlo_host_store_create + dlo_pack_host_shards."""
+    """dlo_host_store_create_ex + dlo_pack_host_shards.
 
-    def __init__(self, plan: Plan, pinned: bool = True):
+    mode: "pinned" (every block pinned), "pageable" (every block staged through two
+    pinned buffers), or "auto" (pin blocks up to ``pinned_limit`` bytes, stage the rest).
+    ``pinned=True/False`` is shorthand for "pinned" / "pageable".
+    """
+
+    def __init__(self, plan: Plan, pinned: bool = True, mode: str = None, pinned_limit: int = 0):
+        if mode is None:
+            mode = "pinned" if pinned else "pageable"
+        flags = {"pinned": STORE_PINNED, "pageable": STORE_PAGEABLE, "auto": STORE_AUTO}[mode]
         h = ctypes.c_void_p()
-        _check(lib().dlo_host_store_create(plan.h, STORE_PINNED if pinned else STORE_PAGEABLE,
-                                           ctypes.byref(h)))
+        _check(lib().dlo_host_store_create_ex(plan.h, flags, int(pinned_limit), ctypes.byref(h)))
         self.h = h
         self.plan = plan
+        self.mode = mode
+
+    def info(self):
+        pb, by, sb = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
+        _check(lib().dlo_host_store_info(self.h, ctypes.byref(pb), ctypes.byref(by), ctypes.byref(sb)))
+        return {"pinned_blocks": pb.value, "pinned_bytes": by.value, "staged_blocks": sb.value}
 
     def close(self):
         if self.h:

@@ -124,11 +124,15 @@ struct dlo_plan {
 struct dlo_host_store {
   const dlo_plan *plan = nullptr;
   uint64_t plan_id = 0;
-  bool pinned = true;
   std::vector<char *> mem;                     // per block
+  std::vector<uint8_t> pinned;                 // per block: shards in pinned memory
   std::vector<std::vector<int64_t>> shard_at;  // per block: byte offset of (g * k + r)
-  std::vector<int64_t> shard_bytes_g;          // scratch
   std::vector<uint8_t> packed;                 // per block flag
+  // two bounded pinned staging buffers (one slot each) for pageable blocks
+  char *staging[2] = {nullptr, nullptr};
+  hipEvent_t staging_free[2] = {nullptr, nullptr};
+  int64_t staging_bytes = 0;
+  int64_t staged_uses = 0;
   const void *shard(int b, int g, int r) const {
     return mem[b] + shard_at[b][g * plan->k + r];
   }
@@ -229,15 +233,17 @@ std::vector<dlo_sched_op> build_program(const std::vector<Step> &steps, bool res
   op(DLO_OP_COPY, DLO_STREAM_COPY, steps[0].block, steps[0].slot, -1, 0);
   op(DLO_OP_RECORD, DLO_STREAM_COPY, -1, -1, DLO_EV_COPIED0 + steps[0].slot, -1);
   for (const Step &s : steps) {
+    // step t's block, from its slot, once the copy that placed it is done
+    op(DLO_OP_WAIT, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_COPIED0 + s.slot, -1);
+    op(DLO_OP_COMPUTE, DLO_STREAM_COMPUTE, s.block, s.slot, -1, s.t);
+    op(DLO_OP_RECORD, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_COMPUTED0 + s.slot, -1);
+    // prefetch the next block into the other slot, whose last reader was step t-1.
+    // Enqueued after step t's compute so that a host-staged copy never delays it.
     if (s.next_block >= 0) {
-      // the slot being refilled was last read by step t-1: wait for that compute
       if (s.t >= 1) op(DLO_OP_WAIT, DLO_STREAM_COPY, -1, -1, DLO_EV_COMPUTED0 + s.next_slot, -1);
       op(DLO_OP_COPY, DLO_STREAM_COPY, s.next_block, s.next_slot, -1, s.t + 1);
       op(DLO_OP_RECORD, DLO_STREAM_COPY, -1, -1, DLO_EV_COPIED0 + s.next_slot, -1);
     }
-    op(DLO_OP_WAIT, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_COPIED0 + s.slot, -1);
-    op(DLO_OP_COMPUTE, DLO_STREAM_COMPUTE, s.block, s.slot, -1, s.t);
-    op(DLO_OP_RECORD, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_COMPUTED0 + s.slot, -1);
   }
   return prog;
 }
@@ -473,9 +479,17 @@ int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, i
 
 void dlo_host_store_destroy(dlo_host_store *store) {
   if (!store) return;
-  for (char *m : store->mem) {
+  for (int j = 0; j < 2; ++j) {
+    if (store->staging_free[j]) {
+      (void)hipEventSynchronize(store->staging_free[j]);
+      (void)hipEventDestroy(store->staging_free[j]);
+    }
+    if (store->staging[j]) (void)hipHostFree(store->staging[j]);
+  }
+  for (size_t b = 0; b < store->mem.size(); ++b) {
+    char *m = store->mem[b];
     if (!m) continue;
-    if (store->pinned)
+    if (store->pinned[b])
       (void)hipHostFree(m);
     else
       std::free(m);
@@ -483,20 +497,51 @@ void dlo_host_store_destroy(dlo_host_store *store) {
   delete store;
 }
 
-int dlo_host_store_create(const dlo_plan *plan, uint32_t flags, dlo_host_store **out) {
+namespace {
+int ensure_staging(dlo_host_store *st) {
+  if (st->staging[0]) return DLO_OK;
+  const int64_t bytes = std::max<int64_t>(st->plan->slot_bytes, 4096);
+  for (int j = 0; j < 2; ++j) {
+    void *m = nullptr;
+    hipError_t e = hipHostMalloc(&m, (size_t)bytes, hipHostMallocDefault);
+    if (e != hipSuccess)
+      return fail(DLO_E_PIN, "pinned staging buffer of %lld bytes: %s", (long long)bytes,
+                  hipGetErrorString(e));
+    st->staging[j] = static_cast<char *>(m);
+    e = hipEventCreateWithFlags(&st->staging_free[j], hipEventDisableTiming);
+    if (e != hipSuccess) return fail(DLO_E_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+  }
+  st->staging_bytes = bytes;
+  return DLO_OK;
+}
+}  // namespace
+
+int dlo_host_store_create_ex(const dlo_plan *plan, uint32_t flags, int64_t pinned_limit_bytes,
+                             dlo_host_store **out) {
   if (!out) return fail(DLO_E_ARG, "out is NULL");
   *out = nullptr;
   if (!plan) return fail(DLO_E_ARG, "plan is NULL");
-  if (flags & ~DLO_STORE_PAGEABLE) return fail(DLO_E_ARG, "unknown store flags 0x%x", flags);
+  if (flags > DLO_STORE_AUTO) return fail(DLO_E_ARG, "unknown store flags 0x%x", flags);
+  if (pinned_limit_bytes < 0) return fail(DLO_E_ARG, "negative pinned limit");
   dlo_host_store *st = new (std::nothrow) dlo_host_store;
   if (!st) return fail(DLO_E_HOSTMEM, "out of host memory");
   st->plan = plan;
   st->plan_id = plan->id;
-  st->pinned = !(flags & DLO_STORE_PAGEABLE);
   const int nb = (int)plan->blocks.size(), k = plan->k;
   st->mem.assign(nb, nullptr);
+  st->pinned.assign(nb, 0);
   st->shard_at.resize(nb);
   st->packed.assign(nb, 0);
+  if (flags == DLO_STORE_AUTO) {
+    // reserve the staging buffers first: pageable blocks cannot move without them
+    int rc = ensure_staging(st);
+    if (rc) {
+      dlo_host_store_destroy(st);
+      return rc;
+    }
+  }
+  bool may_pin = flags != DLO_STORE_PAGEABLE;
+  int64_t pinned_total = 0;
   for (int b = 0; b < nb; ++b) {
     const BlockPlan &bp = plan->blocks[b];
     int64_t cursor = 0;
@@ -508,16 +553,27 @@ int dlo_host_store_create(const dlo_plan *plan, uint32_t flags, dlo_host_store *
       }
     const size_t bytes = (size_t)std::max<int64_t>(cursor, 4096);
     void *m = nullptr;
-    if (st->pinned) {
+    if (may_pin && flags == DLO_STORE_AUTO && pinned_limit_bytes > 0 &&
+        pinned_total + (int64_t)bytes > pinned_limit_bytes)
+      may_pin = false;
+    if (may_pin) {
       // [Aug] s.2: the shard is a pinned DMA buffer for fast H2D
       hipError_t e = hipHostMalloc(&m, bytes, hipHostMallocDefault);
       if (e != hipSuccess) {
         m = nullptr;
-        dlo_host_store_destroy(st);
-        return fail(DLO_E_PIN, "hipHostMalloc(%zu) for block %d failed: %s", bytes, b,
-                    hipGetErrorString(e));
+        (void)hipGetLastError();
+        if (flags == DLO_STORE_PINNED) {
+          dlo_host_store_destroy(st);
+          return fail(DLO_E_PIN, "hipHostMalloc(%zu) for block %d failed: %s", bytes, b,
+                      hipGetErrorString(e));
+        }
+        may_pin = false;   // AUTO: this and every later block is staged
+      } else {
+        st->pinned[b] = 1;
+        pinned_total += (int64_t)bytes;
       }
-    } else {
+    }
+    if (!m) {
       m = std::aligned_alloc(4096, align_up((int64_t)bytes, 4096));
       if (!m) {
         dlo_host_store_destroy(st);
@@ -527,6 +583,32 @@ int dlo_host_store_create(const dlo_plan *plan, uint32_t flags, dlo_host_store *
     st->mem[b] = static_cast<char *>(m);
   }
   *out = st;
+  return ok();
+}
+
+int dlo_host_store_create(const dlo_plan *plan, uint32_t flags, dlo_host_store **out) {
+  return dlo_host_store_create_ex(plan, flags, 0, out);
+}
+
+int dlo_host_store_info(const dlo_host_store *store, int32_t *pinned_blocks,
+                        int64_t *pinned_bytes, int32_t *staged_blocks) {
+  if (!store) return fail(DLO_E_ARG, "store is NULL");
+  int32_t pb = 0, sb = 0;
+  int64_t bytes = 0;
+  for (size_t b = 0; b < store->mem.size(); ++b) {
+    if (store->pinned[b]) {
+      ++pb;
+      const BlockPlan &bp = store->plan->blocks[b];
+      int64_t c = 0;
+      for (int g = 0; g < bp.n_groups; ++g) c += store->plan->k * align_up(bp.gshard[g] * elt_bytes(bp.gdtype[g]), 4096);
+      bytes += std::max<int64_t>(c, 4096);
+    } else {
+      ++sb;
+    }
+  }
+  if (pinned_blocks) *pinned_blocks = pb;
+  if (pinned_bytes) *pinned_bytes = bytes;
+  if (staged_blocks) *staged_blocks = sb;
   return ok();
 }
 
@@ -600,18 +682,66 @@ int32_t dlo_host_store_complete(const dlo_host_store *store) {
 namespace {
 // the k shards of every group at region_g + r * S_g * elt_g ([Jul] "Weight
 // Sharding + AllGather": the all-gather output is the rank-ordered concatenation)
-hipError_t place(const dlo_plan *plan, const dlo_host_store *st, int b, char *dst, hipStream_t s) {
+hipError_t place_from(const dlo_plan *plan, int b, const void *(*src)(const dlo_host_store *, const char *, int, int, int, int64_t),
+                      const dlo_host_store *st, const char *staging, char *dst, hipStream_t s) {
   const BlockPlan &bp = plan->blocks[b];
   for (int g = 0; g < bp.n_groups; ++g) {
     const int64_t sb = bp.gshard[g] * elt_bytes(bp.gdtype[g]);
     if (sb == 0) continue;
     for (int r = 0; r < plan->k; ++r) {
-      hipError_t e = hipMemcpyAsync(dst + bp.gregion[g] + r * sb, st->shard(b, g, r), (size_t)sb,
+      const int64_t off = bp.gregion[g] + r * sb;
+      hipError_t e = hipMemcpyAsync(dst + off, src(st, staging, b, g, r, off), (size_t)sb,
                                     hipMemcpyHostToDevice, s);
       if (e != hipSuccess) return e;
     }
   }
   return hipSuccess;
+}
+
+const void *from_store(const dlo_host_store *st, const char *, int b, int g, int r, int64_t) {
+  return st->shard(b, g, r);
+}
+
+const void *from_staging(const dlo_host_store *, const char *staging, int, int, int, int64_t off) {
+  return staging + off;
+}
+
+// One block into `dst` on stream s.  A pinned block is copied directly; a pageable
+// block first goes (host memcpy, several threads) into the staging buffer whose
+// previous DMA has completed, laid out as the slot image, then is DMA'd from there.
+// Returns a dlo status (host-side waits can fail too).
+// `begin` (optional) is recorded on s just before the DMAs are enqueued.
+int place(const dlo_plan *plan, dlo_host_store *st, int b, char *dst, hipStream_t s,
+          hipEvent_t begin = nullptr) {
+  if (st->pinned[b]) {
+    if (begin) {
+      int rc = check_hip(hipEventRecord(begin, s), "hipEventRecord");
+      if (rc) return rc;
+    }
+    return check_hip(place_from(plan, b, from_store, st, nullptr, dst, s), "hipMemcpyAsync");
+  }
+  int rc = ensure_staging(st);
+  if (rc) return rc;
+  const int j = (int)(st->staged_uses++ & 1);
+  // wait on the host until the staging buffer's previous DMA has drained
+  rc = check_hip(hipEventSynchronize(st->staging_free[j]), "hipEventSynchronize(staging)");
+  if (rc) return rc;
+  const BlockPlan &bp = plan->blocks[b];
+  std::vector<CopyTask> tasks;
+  for (int g = 0; g < bp.n_groups; ++g) {
+    const int64_t sb = bp.gshard[g] * elt_bytes(bp.gdtype[g]);
+    for (int r = 0; r < plan->k && sb > 0; ++r)
+      tasks.push_back({st->staging[j] + bp.gregion[g] + r * sb,
+                       static_cast<const char *>(st->shard(b, g, r)), sb});
+  }
+  run_copies(tasks);
+  if (begin) {
+    rc = check_hip(hipEventRecord(begin, s), "hipEventRecord");
+    if (rc) return rc;
+  }
+  rc = check_hip(place_from(plan, b, from_staging, st, st->staging[j], dst, s), "hipMemcpyAsync");
+  if (rc) return rc;
+  return check_hip(hipEventRecord(st->staging_free[j], s), "hipEventRecord(staging)");
 }
 }  // namespace
 
@@ -624,7 +754,8 @@ int dlo_place_block(const dlo_plan *plan, const dlo_host_store *store, int32_t b
   if (dst_bytes < plan->blocks[b].extent)
     return fail(DLO_E_SLOT_SMALL, "destination %lld < extent %lld", (long long)dst_bytes,
                 (long long)plan->blocks[b].extent);
-  int rc = check_hip(place(plan, store, b, static_cast<char *>(dst), (hipStream_t)stream), "hipMemcpyAsync");
+  int rc = place(plan, const_cast<dlo_host_store *>(store), b, static_cast<char *>(dst),
+                 (hipStream_t)stream);
   return rc ? rc : ok();
 }
 
@@ -795,6 +926,7 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
   hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
   auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
   hipError_t e = hipSuccess;
+  int place_rc = DLO_OK;
   auto HIP = [&](hipError_t x) {
     if (e == hipSuccess && x != hipSuccess) e = x;
     return e == hipSuccess;
@@ -818,8 +950,15 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
         HIP(hipStreamWaitEvent(s, run->ev[op.event], 0));
         break;
       case DLO_OP_COPY: {
-        if (run->timing) HIP(hipEventRecord(tev(op.step, 0), ps));
-        HIP(place(plan, store, op.block, static_cast<char *>(a->slot[op.slot]), ps));
+        if (e == hipSuccess) {
+          int prc = place(plan, const_cast<dlo_host_store *>(store), op.block,
+                          static_cast<char *>(a->slot[op.slot]), ps,
+                          run->timing ? tev(op.step, 0) : nullptr);
+          if (prc) {
+            place_rc = prc;
+            e = hipErrorUnknown;
+          }
+        }
         if (run->timing) HIP(hipEventRecord(tev(op.step, 1), ps));
         break;
       }
@@ -848,6 +987,7 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
   if (e != hipSuccess) {
     // work may already be enqueued: keep the run until it drains
     plan->detached.push_back(run);
+    if (place_rc) return place_rc;
     return fail(DLO_E_HIP, "enqueue failed: %s (synchronise both streams; x is undefined)",
                 hipGetErrorString(e));
   }

@@ -17,13 +17,13 @@ class StackRunner:
     blocks: [(d_model, n_heads, [(name, dtype, numel)])] -- the plan's shapes.
     """
 
-    def __init__(self, blocks, k, tokens, D, pinned=True, device=0):
+    def __init__(self, blocks, k, tokens, D, pinned=True, device=0, store_mode=None, pinned_limit=0):
         import torch
 
         self.torch = torch
         self.dev = torch.device("cuda", device)
         self.plan = Plan(blocks, k)
-        self.store = HostStore(self.plan, pinned=pinned)
+        self.store = HostStore(self.plan, pinned=pinned, mode=store_mode, pinned_limit=pinned_limit)
         self.tokens, self.D = tokens, D
         self.n_blocks = len(blocks)
         sb = self.plan.slot_bytes

@@ -187,21 +187,24 @@ WEIGHT_STD = 0.02
 EPS_VALUE = 1e-6
 
 
-def block_params(seed: int, b: int, d: int):
+def block_params(seed: int, b: int, d: int, out_buffers=None):
     """Seeded parameters of block ``b`` (width ``d``): list of (name, dtype, ndarray).
 
-    bf16 tensors are uint16 arrays of bf16 bit patterns.
+    bf16 tensors are uint16 arrays of bf16 bit patterns.  ``out_buffers`` (a
+    dict name -> array of the right shape and dtype) lets a caller reuse memory
+    across blocks.
     """
     out = []
     for p, (name, dt, shape) in enumerate(block_schema(d)):
+        buf = None if out_buffers is None else out_buffers.get(name)
         if dt == BF16:
-            arr = normal_bf16(seed, 0, b, p, shape, 0.0, WEIGHT_STD)
+            arr = normal_bf16(seed, 0, b, p, shape, 0.0, WEIGHT_STD, out=buf)
         elif name.endswith(".eps"):
             arr = np.full(shape, EPS_VALUE, dtype=np.float32)
         elif name.startswith("norm") and name.endswith(".weight"):
-            arr = normal_f32(seed, 0, b, p, shape, 1.0, WEIGHT_STD)
+            arr = normal_f32(seed, 0, b, p, shape, 1.0, WEIGHT_STD, out=buf)
         else:
-            arr = normal_f32(seed, 0, b, p, shape, 0.0, WEIGHT_STD)
+            arr = normal_f32(seed, 0, b, p, shape, 0.0, WEIGHT_STD, out=buf)
         out.append((name, dt, arr))
     return out
 

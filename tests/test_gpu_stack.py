@@ -188,3 +188,35 @@ def test_timing_trace_is_ordered():
     for t in range(2, len(tr)):
         assert tr[t]["t_copy_begin"] >= tr[t - 2]["t_compute_end"] - 1e-3
     r.close()
+
+
+@pytest.mark.parametrize("mode,limit_blocks", [("pageable", 0), ("auto", 3)])
+def test_staged_store_matches_pinned(mode, limit_blocks):
+    """Blocks staged through the two pinned staging buffers give the pinned result, bit for bit."""
+    torch = require_gpu()
+    from layerwise_weight_streaming_amd.runner import StackRunner
+    w = synth.WORKLOADS["8blk"]
+    say(f"staged store {mode}")
+    stack = synth.make_stack(w, 6)
+    blocks = [(w.width(b), w.heads(b), ps) for b, ps in enumerate(stack.blocks)]
+    specs = spec_blocks(w, w.n_blocks)
+    ref = make_runner(w, stack)
+    ref.forward(w.passes, want_run=False)
+    x_ref = ref.x_host()
+    ref.close()
+    limit = 0
+    if limit_blocks:
+        limit = limit_blocks * (op.plan_block(op.specs_of(stack.blocks[0]), w.k).extent + 16 * 4096)
+    r = StackRunner(specs, w.k, w.tokens, w.D, store_mode=mode, pinned_limit=limit)
+    info = r.store.info()
+    if mode == "pageable":
+        assert info["pinned_blocks"] == 0 and info["staged_blocks"] == w.n_blocks
+    else:
+        assert info["pinned_blocks"] == limit_blocks and info["staged_blocks"] == w.n_blocks - limit_blocks
+    r.pack(0, blocks)
+    r.set_inputs(stack.x, stack.c)
+    run = r.forward(w.passes, flags=dlo.TRACE_DIGEST)
+    tr = run.trace()
+    _check_trace(tr, w.n_blocks, w.passes, _expected_regions(w, stack, w.k))
+    assert np.array_equal(r.x_host().view(np.uint32), x_ref.view(np.uint32))
+    r.close()
