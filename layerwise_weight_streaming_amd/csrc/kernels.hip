@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace dlo {
@@ -130,22 +132,21 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// GEMM tiles: 256 rows of A per workgroup, 4 waves of 256 threads.
+// GEMM tiles: 256 rows of A per workgroup.
 // ---------------------------------------------------------------------------
 
 constexpr int GBM = 256;
-constexpr int G_THREADS = 256;
 
 // ---------------------------------------------------------------------------
 // GEMM: C[M, N] = A[M, K] B[N, K]^T, bf16 in, fp32 accumulate (direct-to-LDS).
-// Workgroup tile 256 x 256 x 32, 4 waves in 2 x 2 (128 x 128 each, 4 x 4 MFMA
-// 32x32 tiles).  Operand tiles travel HBM/L2 -> LDS with buffer_load ... lds
+// Workgroup tile 256 x 256 x 32, 2 x WN waves (128 x 256/WN each, in MFMA
+// 32x32 tiles; WN = 4 on every DiT launch).  Operand tiles travel HBM/L2 -> LDS with buffer_load ... lds
 // (no register staging) into a ring of 4 LDS stages, up to four tiles ahead of
 // the one being multiplied.  One LDS stage = A and B tiles of 256 rows x 64 B;
 // a row holds 4 chunks of 16 B whose order is XOR-swizzled (dl_swz) so that
 // the MFMA operand reads are free of bank conflicts.  A load instruction fills
-// 1 KB of LDS: 64 lanes x 16 B at M0 + 16 * lane, i.e. 16 rows; each wave
-// issues 4 of them per operand per tile.
+// 1 KB of LDS: 64 lanes x 16 B at M0 + 16 * lane, i.e. 16 rows; the waves
+// share the 16 such loads per operand per tile.
 // ---------------------------------------------------------------------------
 
 constexpr int DL_BK = 32;
@@ -189,23 +190,25 @@ __device__ __forceinline__ void vmcnt_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// BN: workgroup tile width (256: waves 128 x 128; 128: waves 128 x 64, two
-// workgroups per CU).  STAGES: depth of the LDS ring.
-template <int EPI, int BN, int STAGES>
-__global__ __launch_bounds__(G_THREADS, BN == 128 ? 2 : 1) void gemm_nt_dl_kernel(
+// BN: workgroup tile width; STAGES: depth of the LDS ring; WN: waves along N
+// (the wave grid is 2 x WN, each wave owns 128 x BN / WN).
+template <int EPI, int BN, int STAGES, int WN = 2>
+__global__ __launch_bounds__(128 * WN, (BN == 128 && WN == 2) ? 2 : 1) void gemm_nt_dl_kernel(
     const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
     int M, int N, int K, const float *__restrict__ bias, const float *__restrict__ gate,
     void *__restrict__ Cv, int64_t ldc) {
-  constexpr int NJ = BN / 64;                 // 32-wide column tiles per wave
+  constexpr int NW = 2 * WN;                  // waves per workgroup
+  constexpr int NJ = BN / WN / 32;            // 32-wide column tiles per wave
   constexpr int B_TILE = BN * DL_BK;          // bf16 elements of the B tile
   constexpr int STAGE = DL_TILE + B_TILE;     // bf16 elements of one stage
-  constexpr int BLOADS = BN / 64;             // B load instructions per wave per tile
-  constexpr int LPT = 4 + BLOADS;             // load instructions per lane per tile
+  constexpr int ALOADS = 16 / NW;             // A load instructions per wave per tile
+  constexpr int BLOADS = BN / 16 / NW;        // B load instructions per wave per tile
+  constexpr int LPT = ALOADS + BLOADS;        // load instructions per lane per tile
   constexpr int READS = 4 + NJ;               // fragment reads per half step
   __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * STAGE];
 
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / WN, wn = wv % WN;
 
   const int tiles_m = (M + GBM - 1) / GBM, tiles_n = N / BN;
   const int total = tiles_m * tiles_n;
@@ -222,11 +225,12 @@ __global__ __launch_bounds__(G_THREADS, BN == 128 ? 2 : 1) void gemm_nt_dl_kerne
   const i32x4 a_rsrc = dl_rsrc(A + (int64_t)m0 * lda, (uint32_t)(a_rows * lda * 2));
   const i32x4 b_rsrc = dl_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(BN * ldb * 2));
 
-  // this lane's source offsets: A blocks wv*4 + i, B blocks wv*BLOADS + i (16 rows each)
-  int a_voff[4], b_voff[BLOADS];
+  // this lane's source offsets: A blocks wv*ALOADS + i, B blocks wv*BLOADS + i
+  // (16 rows each)
+  int a_voff[ALOADS], b_voff[BLOADS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wv * 4 + i) * 16 + (lane >> 2);
+  for (int i = 0; i < ALOADS; ++i) {
+    const int r = (wv * ALOADS + i) * 16 + (lane >> 2);
     a_voff[i] = (r * (int)lda + ((lane & 3) ^ dl_swz(r)) * 8) * 2;
   }
 #pragma unroll
@@ -238,8 +242,8 @@ __global__ __launch_bounds__(G_THREADS, BN == 128 ? 2 : 1) void gemm_nt_dl_kerne
   auto issue = [&](int kt) {
     const uint32_t sbase = lds0 + (uint32_t)((kt % STAGES) * STAGE * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dl_load(a_rsrc, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wv * 4 + i) * 1024)),
+    for (int i = 0; i < ALOADS; ++i)
+      dl_load(a_rsrc, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wv * ALOADS + i) * 1024)),
               a_voff[i] + kt * DL_BK * 2);
 #pragma unroll
     for (int i = 0; i < BLOADS; ++i)
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(G_THREADS, BN == 128 ? 2 : 1) void gemm_nt_dl_kerne
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       f.b[j] = *reinterpret_cast<const bf16x8 *>(
-          &Bs[dl_lds_off(wn * (BN / 2) + j * 32 + frow, kk * 2 + fk)]);
+          &Bs[dl_lds_off(wn * (BN / WN) + j * 32 + frow, kk * 2 + fk)]);
   };
   auto mma = [&](const Frags &f) {
 #pragma unroll
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(G_THREADS, BN == 128 ? 2 : 1) void gemm_nt_dl_kerne
   const int ldc32 = (int)ldc;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn * (BN / 2) + j * 32 + frow;
+    const int n = n0 + wn * (BN / WN) + j * 32 + frow;
     const float bn = bias[n];
     float gn = 0.f;
     if (EPI == EPI_GATED_RESIDUAL) gn = gate[n];
@@ -479,10 +483,24 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     }
   };
 
-  // per-lane pieces of the transposed V reads: group g = lane / 16, li = lane % 16
+  // Loop-invariant per-lane LDS byte offsets: the K operand read of each k-step
+  // (the 32-key half adds a constant) and the transposed V read of each 32-row
+  // dh tile (the 16-key chunk, the second read and the stage add constants).
+  // Transposed V reads, group g = lane / 16, li = lane % 16: keys
+  // 16 c + 4 hf + li / 4 (+ 8), dh 32 t + 16 (g & 1) + 4 (li & 3).
   const int g16 = lane >> 4, li = lane & 15;
-  const int vt_key = 4 * hf + (li >> 2);          // + 16 c (+ 8 for the second read)
-  const int vt_dh = 16 * (g16 & 1) + 4 * (li & 3);  // + 32 dt
+  const int vt_key = 4 * hf + (li >> 2);
+  const int vt_dh = 16 * (g16 & 1) + 4 * (li & 3);
+  int k_lane[KK], v_lane[DT];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    k_lane[kk] = (ql * DH + (((kk * 2 + hf) ^ k_swz<DH>(ql)) << 3)) * 2;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    const int dh = 32 * t + vt_dh;
+    v_lane[t] = (vt_key * DH + (((dh >> 3) ^ v_swz<DH>(vt_key)) << 3) + (dh & 7)) * 2;
+  }
+  const char *lds_bytes = reinterpret_cast<const char *>(&smem[0][0][0]);
 
   f32x16 o[DT];
 #pragma unroll
@@ -497,15 +515,18 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
   for (int b = 0; b < A_STAGES - 1; ++b)
     if (b < nkb) issue(b);
 
-  for (int j = 0; j < nkb; ++j) {
+  // one key block from stage S (a compile-time constant, so every LDS address
+  // below is a loop-invariant register plus an immediate)
+  auto block = [&](int j, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
     // block j landed once at most block j+1's loads are in flight
-    if (j + 1 < nkb && A_STAGES > 2)
+    if (A_STAGES > 2 && j + 1 < nkb)
       vmcnt_barrier<LPB>();
     else
       vmcnt_barrier<0>();
     if (j + A_STAGES - 1 < nkb) issue(j + A_STAGES - 1);
-    const uint16_t *Ks = smem[j % A_STAGES][0];
-    const uint16_t *Vs = smem[j % A_STAGES][1];
+    const char *Kb = lds_bytes + S * 2 * TILE * 2;
+    const char *Vb = Kb + TILE * 2;
 
     // S^T = K Q^T for the block's two 32-key halves
     f32x16 s[2];
@@ -513,11 +534,9 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int kr = kb * 32 + ql;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
-            &Ks[kr * DH + (((kk * 2 + hf) ^ k_swz<DH>(kr)) << 3)]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Kb + kb * 32 * DH * 2 + k_lane[kk]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
       }
     }
@@ -562,14 +581,23 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const int k1 = 16 * c + vt_key, k2 = k1 + 8, dh = 32 * t + vt_dh;
+        const char *p1 = Vb + c * 16 * DH * 2 + v_lane[t];
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(Vs + k1 * DH + (((dh >> 3) ^ v_swz<DH>(k1)) << 3) + (dh & 7)));
+            (__attribute__((address_space(3))) v4i16 *)(p1));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(Vs + k2 * DH + (((dh >> 3) ^ v_swz<DH>(k2)) << 3) + (dh & 7)));
+            (__attribute__((address_space(3))) v4i16 *)(p1 + 8 * DH * 2));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
       }
+  };
+  for (int j = 0; j < nkb; j += A_STAGES) {
+    block(j, std::integral_constant<int, 0>{});
+    if constexpr (A_STAGES > 1) {
+      if (j + 1 < nkb) block(j + 1, std::integral_constant<int, 1>{});
+    }
+    if constexpr (A_STAGES > 2) {
+      if (j + 2 < nkb) block(j + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, WAVE);
@@ -676,23 +704,23 @@ hipError_t launch_ln_modulate(const float *x, int64_t ldx, int T, int d, const f
 }
 
 namespace {
-template <int BN, int STAGES>
+template <int BN, int STAGES, int WN>
 hipError_t gemm_launch(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int M, int N,
                        int K, const float *bias, const float *gate, void *C, int64_t ldc,
                        int epilogue, hipStream_t s) {
   const int tiles = ((M + GBM - 1) / GBM) * (N / BN);
   switch (epilogue) {
     case EPI_BIAS:
-      hipLaunchKernelGGL((gemm_nt_dl_kernel<EPI_BIAS, BN, STAGES>), dim3(tiles), dim3(G_THREADS), 0,
+      hipLaunchKernelGGL((gemm_nt_dl_kernel<EPI_BIAS, BN, STAGES, WN>), dim3(tiles), dim3(128 * WN), 0,
                          s, A, lda, B, ldb, M, N, K, bias, gate, C, ldc);
       break;
     case EPI_BIAS_GELU:
-      hipLaunchKernelGGL((gemm_nt_dl_kernel<EPI_BIAS_GELU, BN, STAGES>), dim3(tiles),
-                         dim3(G_THREADS), 0, s, A, lda, B, ldb, M, N, K, bias, gate, C, ldc);
+      hipLaunchKernelGGL((gemm_nt_dl_kernel<EPI_BIAS_GELU, BN, STAGES, WN>), dim3(tiles),
+                         dim3(128 * WN), 0, s, A, lda, B, ldb, M, N, K, bias, gate, C, ldc);
       break;
     case EPI_GATED_RESIDUAL:
-      hipLaunchKernelGGL((gemm_nt_dl_kernel<EPI_GATED_RESIDUAL, BN, STAGES>), dim3(tiles),
-                         dim3(G_THREADS), 0, s, A, lda, B, ldb, M, N, K, bias, gate, C, ldc);
+      hipLaunchKernelGGL((gemm_nt_dl_kernel<EPI_GATED_RESIDUAL, BN, STAGES, WN>), dim3(tiles),
+                         dim3(128 * WN), 0, s, A, lda, B, ldb, M, N, K, bias, gate, C, ldc);
       break;
     default:
       return hipErrorInvalidValue;
@@ -704,9 +732,11 @@ hipError_t gemm_launch(const uint16_t *A, int64_t lda, const uint16_t *B, int64_
 hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int M,
                        int N, int K, const float *bias, const float *gate, void *C, int64_t ldc,
                        int epilogue, hipStream_t s) {
-  // 256 x 256 tiles with a 4-deep ring measured faster than 256 x 128 tiles at
-  // two workgroups per CU on every DiT shape but the fc1 one
-  return gemm_launch<256, 4>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, s);
+  // 256 x 256 tiles, a 4-deep ring and eight waves (2 x 4, 128 x 64 each):
+  // faster than four 128 x 128 waves (5-12 % on the DiT shapes: two waves per
+  // SIMD hide the LDS latency of each other's fragment reads) and than
+  // 256 x 128 tiles at two workgroups per CU
+  return gemm_launch<256, 4, 4>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, s);
 }
 
 hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, int T, int H, int dh,
