@@ -261,7 +261,8 @@ typedef struct {
   int64_t workspace_bytes;
   void *compute_stream;     /* hipStream_t */
   void *copy_stream;        /* hipStream_t, distinct from compute_stream */
-  int32_t tokens;           /* rows of x (batch 1), >= 1 */
+  int32_t tokens;           /* rows of x (batch 1), >= 1; (tokens + 64) * 3 * widest d * 2
+                               < 2^31, else DLO_E_UNSUPPORTED */
   int32_t passes;           /* chained passes over the stack, >= 1 */
   uint32_t flags;           /* DLO_TRACE_* | DLO_RESIDENT */
   int32_t pad;
@@ -361,7 +362,8 @@ int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, 
 
 /* Per head j < H: out[:, j*dh:(j+1)*dh] = softmax(q_j k_j^T / sqrt(dh)) v_j, with
  * q, k, v read from qkv bf16 [T, 3*H*dh] (row stride ldqkv) at column offsets 0,
- * H*dh, 2*H*dh; out bf16 [T, H*dh] (row stride ldo).  dh in {64, 128}. */
+ * H*dh, 2*H*dh; out bf16 [T, H*dh] (row stride ldo).  dh in {64, 128}.
+ * DLO_E_UNSUPPORTED when (T + 64) * ldqkv * 2 >= 2^31 (32-bit buffer offsets). */
 int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t H, int32_t dh,
                      uint16_t *out, int64_t ldo, void *stream);
 

@@ -846,7 +846,7 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
   }
   if (a->x_row_stride < plan->max_d)
     return fail(DLO_E_ARG, "x_row_stride %lld < widest block %d", (long long)a->x_row_stride, plan->max_d);
-  if ((int64_t)a->tokens * 3 * plan->max_d * 2 >= ((int64_t)1 << 31))
+  if (((int64_t)a->tokens + 64) * 3 * plan->max_d * 2 >= ((int64_t)1 << 31))
     return fail(DLO_E_UNSUPPORTED, "tokens x 3 d too large for 32-bit buffer offsets");
   const int64_t need = workspace_bytes_for(plan->max_d, a->tokens);
   if (a->workspace_bytes < need)
@@ -1110,7 +1110,7 @@ int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t H, i
   if (T < 1 || H < 1 || (dh != 64 && dh != 128) || ldqkv < 3LL * H * dh || ldo < (int64_t)H * dh ||
       ldqkv % 8 || ldo % 4)
     return fail(DLO_E_UNSUPPORTED, "attention: dh in {64,128}, ldqkv >= 3 H dh (multiple of 8)");
-  if ((int64_t)T * ldqkv * 2 >= ((int64_t)1 << 31))
+  if (((int64_t)T + 64) * ldqkv * 2 >= ((int64_t)1 << 31))
     return fail(DLO_E_UNSUPPORTED, "attention: T * ldqkv too large for 32-bit buffer offsets");
   int rc = check_hip(dlo::launch_attention(qkv, ldqkv, T, H, dh, out, ldo, (hipStream_t)stream),
                      "attention");
