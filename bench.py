@@ -44,38 +44,51 @@ def kernel_work(name, d, T):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dit_block_kernels_super_hbm_traffic.md")
-KERNELS_SRC = os.path.join(ROOT, "layerwise_weight_streaming_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "layerwise_weight_streaming_amd", "csrc")
 TRAFFIC_KEY = {"adaln_gemv": "adaln_gemv", "ln1_modulate": "ln1", "ln2_modulate": "ln1",
                "gemm_qkv": "gemm_qkv", "attention": "attention", "gemm_out_residual": "gemm_out",
                "gemm_fc1_gelu": "gemm_fc1", "gemm_fc2_residual": "gemm_fc2"}
 
 
+def kernel_source_sha(fname):
+    """sha256 of a kernel source file followed by the shared device header."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (fname, "device_common.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def counted_traffic(kernel, workload):
     """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary, or None.
 
-    The summary holds bytes already scaled by the plain-copy calibration; they
-    describe the kernel source they were counted on, so a changed source (its
-    sha256 differs) or another workload gives None.
+    The summary holds bytes already scaled by the plain-copy calibration and,
+    per kernel, the hash of the source file it was counted on; a changed source
+    or another workload gives None.
     """
-    import hashlib
+    key = TRAFFIC_KEY.get(kernel)
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
-        src = hashlib.sha256(open(KERNELS_SRC, "rb").read()).hexdigest()
     except OSError:
         return None
-    sha = wl = None
-    table = {}
+    wl, src, val = None, None, None
     for ln in lines:
         f = ln.split()
-        if len(f) == 2 and f[0] == "kernels_source_sha256":
-            sha = f[1]
-        elif len(f) == 2 and f[0] == "workload":
+        if len(f) == 2 and f[0] == "workload":
             wl = f[1]
-        elif len(f) == 3 and f[0] == "traffic_bytes_per_launch":
-            table[f[1]] = float(f[2])
-    if sha != src or wl != workload:
+        elif len(f) == 4 and f[0] == "kernel_source" and f[1] == key:
+            src = (f[2], f[3])
+        elif len(f) == 3 and f[0] == "traffic_bytes_per_launch" and f[1] == key:
+            val = float(f[2])
+    if wl != workload or src is None or val is None:
         return None
-    return table.get(TRAFFIC_KEY.get(kernel))
+    try:
+        if kernel_source_sha(src[0]) != src[1]:
+            return None
+    except OSError:
+        return None
+    return val
 
 
 def block_flops(d, T):

@@ -1,0 +1,287 @@
+// gfx950 flash attention forward of the DiT block (non-causal softmax
+// attention over all tokens, per head).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dlo {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Flash attention forward (non-causal), one head per workgroup column.
+// Workgroup: 8 waves, 256 queries (32 per wave).  Keys/values in blocks of 64
+// travel HBM/L2 -> LDS by buffer_load ... lds, both key-major, into separate
+// two-slot rings for K and V, K one block ahead of V.  Each wave computes
+// S^T = K Q^T on MFMA, so a lane owns one query and the online-softmax
+// statistics stay in the lane (one exchange with lane l ^ 32, by
+// v_permlane32_swap).  P^T in that layout is the B operand of O^T += V^T P^T;
+// the V^T operand comes straight from the key-major V tile via
+// ds_read_b64_tr_b16 (for a group of 16 lanes, lane j receives element j % 4
+// of the 4-element loads of lanes 4t + j / 4, t = 0..3).
+//
+// Software pipeline: block j's scores are computed one iteration ahead, so
+// while the MFMAs of S_{j+1} = K_{j+1} Q^T run, the same wave takes the softmax
+// of block j on the VALU (max, exp2, bf16 packing); then O^T += V_j^T P_j^T,
+// with the row sums of P_j taken by v_dot2 (on the bf16 P the MFMA uses) in the
+// shadow of those MFMAs.  One barrier per block; every load has a whole block
+// of compute to land in.
+//
+// Softmax in base 2 on raw scores s: p = exp2(s * c - m * c), c = log2(e)/sqrt(dh).
+// The running max m is raised only when a block's max exceeds it by more than
+// 8 / c (so p <= 2^8), which leaves the rescale of O and l out of most blocks;
+// the result is the same softmax, normalised by the same running sum.
+// ---------------------------------------------------------------------------
+
+constexpr int AK = 64;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// 16-B chunk swizzles of the key-major K and V tiles (rows of DH bf16).
+// K: MFMA A reads of 16 consecutive key rows at one chunk hit 16 distinct bank
+// groups.  V: a transposed read touches 4 consecutive keys x 32 B; the swizzle
+// moves each key's 32 B to its own quarter of the 256-B bank window.
+template <int DH>
+__device__ __forceinline__ int k_swz(int key) {
+  return DH == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+template <int DH>
+__device__ __forceinline__ int v_swz(int key) {
+  return (key & 3) * (DH / 32);
+}
+
+// A_WAVES waves of 32 queries per workgroup.
+template <int DH, int A_WAVES>
+__global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_kernel(
+    const uint16_t *__restrict__ qkv, int64_t ldq, int T, int H, uint16_t *__restrict__ out,
+    int64_t ldo, float scale_log2) {
+  constexpr int AQ = 32 * A_WAVES;
+  constexpr int KCH = DH / 8;
+  constexpr int TILE = AK * DH;
+  constexpr int ROWS_PER_LD = 1024 / (DH * 2);
+  constexpr int LD_PER_WAVE = AK / ROWS_PER_LD / A_WAVES;
+  constexpr int DT = DH / 32;
+  constexpr int KK = DH / 16;
+  // tiles: K slot 0, K slot 1, V slot 0, V slot 1
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
+
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int nqb = (T + AQ - 1) / AQ;
+  const int lid = xcd_remap(blockIdx.x, nqb * H);
+  const int head = lid / nqb, qb = lid % nqb;
+  const int HD = H * DH;
+
+  const int ql = lane & 31, hf = lane >> 5;
+  const int q = qb * AQ + wv * 32 + ql;
+  const int qc = q < T ? q : T - 1;
+
+  bf16x8 qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8 *>(qkv + (int64_t)qc * ldq + head * DH + kk * 16 + hf * 8);
+
+  const uint32_t rec = (uint32_t)((int64_t)T * ldq * 2);
+  const i32x4 k_rsrc = dl_rsrc(qkv + HD + head * DH, rec);
+  const i32x4 v_rsrc = dl_rsrc(qkv + 2 * HD + head * DH, rec);
+  int k_voff[LD_PER_WAVE], v_voff[LD_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < LD_PER_WAVE; ++i) {
+    const int row = (wv * LD_PER_WAVE + i) * ROWS_PER_LD + lane / KCH;
+    const int p = lane % KCH;
+    k_voff[i] = (row * (int)ldq + (p ^ k_swz<DH>(row)) * 8) * 2;
+    v_voff[i] = (row * (int)ldq + (p ^ v_swz<DH>(row)) * 8) * 2;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&smem[0];
+  auto issue_k = [&](int j, int tile) {
+    const uint32_t sb = lds0 + (uint32_t)(tile * TILE * 2);
+    const int off = j * AK * (int)ldq * 2;
+#pragma unroll
+    for (int i = 0; i < LD_PER_WAVE; ++i)
+      dl_load(k_rsrc, __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wv * LD_PER_WAVE + i) * 1024)),
+              k_voff[i] + off);
+  };
+  auto issue_v = [&](int j, int tile) {
+    const uint32_t sb = lds0 + (uint32_t)(tile * TILE * 2);
+    const int off = j * AK * (int)ldq * 2;
+#pragma unroll
+    for (int i = 0; i < LD_PER_WAVE; ++i)
+      dl_load(v_rsrc, __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wv * LD_PER_WAVE + i) * 1024)),
+              v_voff[i] + off);
+  };
+
+  const int g16 = lane >> 4, li = lane & 15;
+  const int vt_key = 4 * hf + (li >> 2);
+  const int vt_dh = 16 * (g16 & 1) + 4 * (li & 3);
+  int k_lane[KK], v_lane[DT];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    k_lane[kk] = (ql * DH + (((kk * 2 + hf) ^ k_swz<DH>(ql)) << 3)) * 2;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    const int dh = 32 * t + vt_dh;
+    v_lane[t] = (vt_key * DH + (((dh >> 3) ^ v_swz<DH>(vt_key)) << 3) + (dh & 7)) * 2;
+  }
+  const char *lds_bytes = reinterpret_cast<const char *>(&smem[0]);
+
+  // S^T of one block: two 32-key halves, their MFMA chains interleaved
+  auto qk = [&](const char *Kb, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Kb + kb * 32 * DH * 2 + k_lane[kk]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+      }
+  };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float tau = 8.0f / scale_log2;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  const int nkb = (T + AK - 1) / AK;
+  issue_k(0, 0);
+  issue_v(0, 2);
+  if (nkb > 1) issue_k(1, 1);
+  vmcnt_barrier<0>();
+  f32x16 sa[2], sb[2];
+  qk(lds_bytes, sa);
+
+  // block j (parity P = j & 1): scores sc (computed one iteration earlier),
+  // next block's scores into sn; K_{j+1} in K slot 1 - P, V_j in V slot P
+  auto iter = [&](int j, auto par_c, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr int P = decltype(par_c)::value;
+    // K_{j+1} and V_j landed, and every wave is done with block j - 1
+    vmcnt_barrier<0>();
+    if (j + 2 < nkb) issue_k(j + 2, P);         // K_j's slot
+    if (j + 1 < nkb) issue_v(j + 1, 2 + 1 - P); // V_{j-1}'s slot
+    const char *Kn = lds_bytes + (1 - P) * TILE * 2;
+    const char *Vb = lds_bytes + (2 + P) * TILE * 2;
+
+    const int kbase = j * AK;
+    if (kbase + AK > T) {  // last, partial block: keys >= T do not exist
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3) >= T) sc[kb][r] = -INFINITY;
+    }
+    float mx = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const bool need = __any(mx > m_run + tau);
+    const float m_new = need ? fmaxf(m_run, mx) : m_run;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    m_run = m_new;
+    const float mc = m_new * scale_log2;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], scale_log2, -mc));
+
+    qk(Kn, sn);  // next block's scores (unused after the last block)
+    // interleave the 16 MFMAs with the K operand reads (two ahead) and the
+    // softmax VALU work
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+    }
+    // P_j is complete here, ahead of the rescale branch (keeps the exp2 work in
+    // this block, next to the MFMAs it overlaps)
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
+
+    if (need) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+    }
+
+    // O^T += V^T P^T over the four 16-key chunks; row sums of P on the VALU
+    float ls = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const char *p1 = Vb + c * 16 * DH * 2 + v_lane[t];
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16 *)(p1));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16 *)(p1 + 8 * DH * 2));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[c][2 * e], pf[c][2 * e + 1]}, ones, ls, false);
+    }
+    l_run = l_run * alpha + ls;
+  };
+  int j = 0;
+  for (; j + 1 < nkb; j += 2) {
+    iter(j, std::integral_constant<int, 0>{}, sa, sb);
+    iter(j + 1, std::integral_constant<int, 1>{}, sb, sa);
+  }
+  if (j < nkb) iter(j, std::integral_constant<int, 0>{}, sa, sb);
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, WAVE);
+  const float inv = 1.0f / l_tot;
+  if (q < T) {
+    uint16_t *orow = out + (int64_t)q * ldo + head * DH;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[t][g * 4 + e] * inv);
+        *reinterpret_cast<bf16x4 *>(orow + t * 32 + g * 8 + hf * 4) = v;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, int T, int H, int dh,
+                            uint16_t *out, int64_t ldo, hipStream_t s) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
+  // 8 waves (256 queries) per workgroup, one workgroup per CU: faster than
+  // 4 waves at two workgroups per CU (each K/V tile then serves twice the
+  // queries; 3.6 % on the Super attention shape)
+  const int nqb = (T + 255) / 256;
+  if (dh == 128) {
+    hipLaunchKernelGGL((attention_kernel<128, 8>), dim3(nqb * H), dim3(512), 0, s, qkv, ldqkv, T,
+                       H, out, ldo, scale_log2);
+  } else if (dh == 64) {
+    hipLaunchKernelGGL((attention_kernel<64, 8>), dim3(nqb * H), dim3(512), 0, s, qkv, ldqkv, T, H,
+                       out, ldo, scale_log2);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dlo

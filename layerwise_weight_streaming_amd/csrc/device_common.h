@@ -1,0 +1,78 @@
+// Device-side helpers shared by the gfx950 kernels of the DiT block forward.
+//
+// Wave size 64.  MFMA: v_mfma_f32_32x32x16_bf16.  For that instruction lane l
+// supplies row (l % 32) of A and column (l % 32) of B, each as eight bf16 at
+// k = 8 * (l / 32) .. +7, and receives column (l % 32) of the 32x32 fp32
+// result at rows (r / 4) * 8 + (l / 32) * 4 + r % 4, r = 0..15.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dlo {
+namespace {
+
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int WAVE = 64;
+
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+}
+
+// XCD-aware tile order.  Workgroup w is dispatched to XCD w % 8; renumber so
+// that the workgroups one XCD receives get consecutive logical ids and hence
+// neighbouring tiles that share operands in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  constexpr int NX = 8;
+  int x = pid % NX, idx = pid / NX;
+  int base = total / NX, rem = total % NX;
+  return x * base + (x < rem ? x : rem) + idx;
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+// raw buffer descriptor: base, no stride, num_records bytes (reads past it return 0)
+__device__ __forceinline__ i32x4 dl_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 B per lane from rsrc + voff into LDS at lds_base + 16 * lane (M0 = lds_base).
+// Issued as inline asm so that the compiler does not add its own (over-strict)
+// counter waits before the LDS reads; the kernel waits on vmcnt explicitly.
+__device__ __forceinline__ void dl_load(i32x4 rsrc, uint32_t lds_base, int voff) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(voff), "s"(lds_base), "s"(rsrc)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N) then s_barrier (N an immediate)
+template <int N>
+__device__ __forceinline__ void vmcnt_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+}  // namespace
+}  // namespace dlo
