@@ -254,7 +254,8 @@ int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, i
 typedef struct {
   void *slot[2];            /* device, slot_bytes each, distinct (unused if DLO_RESIDENT) */
   int64_t slot_bytes;       /* capacity of each slot */
-  float *x;                 /* device fp32 [tokens, x_row_stride], updated in place */
+  float *x;                 /* device fp32 [tokens, x_row_stride], updated in place; 16-B
+                               aligned, x_row_stride % 4 == 0 (else DLO_E_ARG) */
   int64_t x_row_stride;     /* elements; >= the widest block's d */
   const float *cond;        /* device fp32 [>= widest d]: conditioning vector */
   void *workspace;          /* device, >= dlo_plan_workspace_bytes(plan, tokens) */
@@ -354,7 +355,8 @@ int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const 
  *   epilogue 0: C bf16 [M, N] (ldc)
  *   epilogue 1: C bf16 = GELU_erf(A B^T + bias)
  *   epilogue 2: X fp32 (ldc) += gate[n] * (A B^T + bias)  (C points at X)
- * N % 256 == 0, K % 64 == 0, M >= 1. */
+ * N % 256 == 0, K % 64 == 0, M >= 1; lda, ldb multiples of 8; C, bias and gate
+ * 16-B aligned and ldc % 4 == 0 (else DLO_E_UNSUPPORTED). */
 enum { DLO_EPI_BIAS = 0, DLO_EPI_BIAS_GELU = 1, DLO_EPI_GATED_RESIDUAL = 2 };
 int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int32_t M,
                 int32_t N, int32_t K, const float *bias, const float *gate, void *C, int64_t ldc,

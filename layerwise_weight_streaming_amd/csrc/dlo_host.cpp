@@ -846,6 +846,10 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
   }
   if (a->x_row_stride < plan->max_d)
     return fail(DLO_E_ARG, "x_row_stride %lld < widest block %d", (long long)a->x_row_stride, plan->max_d);
+  if (a->x_row_stride % 4 || (uintptr_t)a->x % 16)
+    return fail(DLO_E_ARG, "x must be 16-B aligned with x_row_stride %% 4 == 0");
+  if ((int64_t)256 * a->x_row_stride * 4 >= ((int64_t)1 << 31))
+    return fail(DLO_E_UNSUPPORTED, "x_row_stride too large for 32-bit tile offsets");
   if (((int64_t)a->tokens + 64) * 3 * plan->max_d * 2 >= ((int64_t)1 << 31))
     return fail(DLO_E_UNSUPPORTED, "tokens x 3 d too large for 32-bit buffer offsets");
   const int64_t need = workspace_bytes_for(plan->max_d, a->tokens);
@@ -1097,8 +1101,11 @@ int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, 
   if (M < 1 || N < 256 || N % 256 || K < 64 || K % 64 || lda < K || ldb < K || ldc < N ||
       lda % 8 || ldb % 8)
     return fail(DLO_E_UNSUPPORTED, "gemm: N %% 256 == 0, K %% 64 == 0, ld >= extent, ld %% 8 == 0");
-  if ((int64_t)256 * lda * 2 >= (int64_t)1 << 31 || (int64_t)256 * ldb * 2 >= (int64_t)1 << 31)
+  if ((int64_t)256 * lda * 2 >= (int64_t)1 << 31 || (int64_t)256 * ldb * 2 >= (int64_t)1 << 31 ||
+      (int64_t)256 * ldc * 4 >= (int64_t)1 << 31)
     return fail(DLO_E_UNSUPPORTED, "gemm: leading dimension too large for 32-bit tile offsets");
+  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 16 || (gate && (uintptr_t)gate % 16))
+    return fail(DLO_E_UNSUPPORTED, "gemm: C, bias and gate must be 16-B aligned and ldc %% 4 == 0");
   int rc = check_hip(dlo::launch_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue,
                                       (hipStream_t)stream), "gemm");
   return rc ? rc : ok();

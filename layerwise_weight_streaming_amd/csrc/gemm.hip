@@ -54,7 +54,13 @@ __global__ __launch_bounds__(128 * WN, (BN == 128 && WN == 2) ? 2 : 1) void gemm
   constexpr int BLOADS = BN / 16 / NW;        // B load instructions per wave per tile
   constexpr int LPT = ALOADS + BLOADS;        // load instructions per lane per tile
   constexpr int READS = 4 + NJ;               // fragment reads per half step
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * STAGE];
+  // the epilogue reuses the ring as a staging tile: 256 rows of bf16 (row
+  // stride C_LD) or 128 rows of fp32 (row stride X_LD)
+  constexpr int C_LD = BN + 8;                // bf16 elements
+  constexpr int X_LD = BN + 4;                // fp32 elements
+  constexpr int RING = STAGES * STAGE;
+  constexpr int CSTAGE = EPI == EPI_GATED_RESIDUAL ? 128 * X_LD * 2 : GBM * C_LD;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[RING > CSTAGE ? RING : CSTAGE];
 
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int wm = wv / WN, wn = wv % WN;
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(128 * WN, (BN == 128 && WN == 2) ? 2 : 1) void gemm
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
   // wait until at most `younger` tiles' loads (LPT per tile per lane) are in
   // flight, then barrier.  The wave's own LDS reads of the stage about to be
@@ -195,51 +201,97 @@ __global__ __launch_bounds__(128 * WN, (BN == 128 && WN == 2) ? 2 : 1) void gemm
     asm volatile("" ::: "memory");
   }
 
-  // Epilogue, one 32x32 sub-tile at a time.  Offsets are 32-bit from the tile's
-  // first row; a residual sub-tile's 16 loads all issue before any of its stores;
-  // only the last row tile checks rows against M.
+  // Epilogue, staged through LDS so that global accesses are whole rows.
+  // acc[i][j] holds the transposed 32x32 sub-tile (the MFMA took B as its first
+  // operand): lane l has row i*32 + l%32 of the wave's rows and, for g = 0..3,
+  // the four consecutive columns j*32 + 8g + 4(l/32) + 0..3 -- one 8-B (bf16)
+  // or 16-B (fp32) piece of a row, written to LDS as such.  Then every thread
+  // moves 16-B row segments between LDS and global memory; only the last row
+  // tile checks rows against M.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // ring no longer read
   const bool full = m0 + GBM <= M;
   const int ldc32 = (int)ldc;
+  constexpr int NT = 128 * WN;                // threads
+  if (EPI != EPI_GATED_RESIDUAL) {
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn * (BN / WN) + j * 32 + frow;
-    const float bn = bias[n];
-    float gn = 0.f;
-    if (EPI == EPI_GATED_RESIDUAL) gn = gate[n];
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int mr0 = wm * 128 + i * 32 + fk * 4;  // row of r = 0, relative to m0
-      if (EPI == EPI_GATED_RESIDUAL) {
-        float *X = reinterpret_cast<float *>(Cv) + (int64_t)m0 * ldc;
-        float xv[16];
-        if (full) {
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * (BN / WN) + j * 32 + g * 8 + fk * 4;
+        const float4 bv = *reinterpret_cast<const float4 *>(&bias[n0 + col]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) xv[r] = X[(mr0 + (r >> 2) * 8 + (r & 3)) * ldc32 + n];
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            X[(mr0 + (r >> 2) * 8 + (r & 3)) * ldc32 + n] = xv[r] + gn * (acc[i][j][r] + bn);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int mr = mr0 + (r >> 2) * 8 + (r & 3);
-            xv[r] = m0 + mr < M ? X[mr * ldc32 + n] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          float v0 = acc[i][j][g * 4 + 0] + bv.x, v1 = acc[i][j][g * 4 + 1] + bv.y;
+          float v2 = acc[i][j][g * 4 + 2] + bv.z, v3 = acc[i][j][g * 4 + 3] + bv.w;
+          if (EPI == EPI_BIAS_GELU) {
+            v0 = gelu_erf(v0);
+            v1 = gelu_erf(v1);
+            v2 = gelu_erf(v2);
+            v3 = gelu_erf(v3);
           }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int mr = mr0 + (r >> 2) * 8 + (r & 3);
-            if (m0 + mr < M) X[mr * ldc32 + n] = xv[r] + gn * (acc[i][j][r] + bn);
-          }
-        }
-      } else {
-        uint16_t *C = reinterpret_cast<uint16_t *>(Cv) + (int64_t)m0 * ldc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mr = mr0 + (r >> 2) * 8 + (r & 3);
-          float v = acc[i][j][r] + bn;
-          if (EPI == EPI_BIAS_GELU) v = gelu_erf(v);
-          if (full || m0 + mr < M) C[mr * ldc32 + n] = f32_to_bf16(v);
+          bf16x4 o;
+          o[0] = (__bf16)v0;
+          o[1] = (__bf16)v1;
+          o[2] = (__bf16)v2;
+          o[3] = (__bf16)v3;
+          *reinterpret_cast<bf16x4 *>(&smem[(wm * 128 + i * 32 + frow) * C_LD + col]) = o;
         }
       }
+    __syncthreads();
+    constexpr int SEG = BN / 8;               // 16-B segments per row
+    uint16_t *C = reinterpret_cast<uint16_t *>(Cv) + (int64_t)m0 * ldc + n0;
+#pragma unroll
+    for (int it = 0; it < GBM * SEG / NT; ++it) {
+      const int e = it * NT + tid, row = e / SEG, c8 = (e % SEG) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&smem[row * C_LD + c8]);
+      if (full || m0 + row < M) *reinterpret_cast<u32x4 *>(&C[row * ldc32 + c8]) = v;
+    }
+  } else {
+    float *xs = reinterpret_cast<float *>(smem);
+    constexpr int SEG = BN / 4;               // 16-B segments per row
+    float *X = reinterpret_cast<float *>(Cv) + (int64_t)m0 * ldc + n0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = wn * (BN / WN) + j * 32 + g * 8 + fk * 4;
+            const float4 bv = *reinterpret_cast<const float4 *>(&bias[n0 + col]);
+            const float4 gv = *reinterpret_cast<const float4 *>(&gate[n0 + col]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float4 v;
+              v.x = gv.x * (acc[i][j][g * 4 + 0] + bv.x);
+              v.y = gv.y * (acc[i][j][g * 4 + 1] + bv.y);
+              v.z = gv.z * (acc[i][j][g * 4 + 2] + bv.z);
+              v.w = gv.w * (acc[i][j][g * 4 + 3] + bv.w);
+              *reinterpret_cast<float4 *>(&xs[(i * 32 + frow) * X_LD + col]) = v;
+            }
+          }
+      }
+      __syncthreads();
+      constexpr int PER = 128 * SEG / NT;     // segments per thread
+      float4 xv[PER];
+#pragma unroll
+      for (int it = 0; it < PER; ++it) {
+        const int e = it * NT + tid, row = half * 128 + e / SEG, c4 = (e % SEG) * 4;
+        xv[it] = (full || m0 + row < M) ? *reinterpret_cast<const float4 *>(&X[row * ldc32 + c4])
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int it = 0; it < PER; ++it) {
+        const int e = it * NT + tid, row = half * 128 + e / SEG, c4 = (e % SEG) * 4;
+        const float4 u = *reinterpret_cast<const float4 *>(&xs[(e / SEG) * X_LD + c4]);
+        float4 v = xv[it];
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+        if (full || m0 + row < M) *reinterpret_cast<float4 *>(&X[row * ldc32 + c4]) = v;
+      }
+      if (half == 0) __syncthreads();
     }
   }
 }

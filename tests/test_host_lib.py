@@ -235,6 +235,8 @@ def test_forward_validation_errors():
     assert _status(F, copy_stream=0x10) == "DLO_E_ARG"          # aliased streams
     assert _status(F, copy_stream=0) == "DLO_E_ARG"
     assert _status(F, x_row_stride=128) == "DLO_E_ARG"
+    assert _status(F, x_row_stride=258) == "DLO_E_ARG"          # rows not 16-B aligned
+    assert _status(F, x=0x1004) == "DLO_E_ARG"                  # x not 16-B aligned
     assert _status(F, workspace_bytes=100) == "DLO_E_WORKSPACE"
     assert _status(F, slot_bytes=p.slot_bytes - 1) == "DLO_E_SLOT_SMALL"
     assert _status(F, slots=(0x100000, 0x100000 + 256)) == "DLO_E_ARG"   # overlapping slots
@@ -271,6 +273,10 @@ def test_op_validation_errors():
     assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 100, 64, 1, 0, 1, 100, 0, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 256, 60, 1, 0, 1, 256, 0, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 256, 64, 1, 0, 1, 256, 2, 0) == "DLO_E_ARG"  # no gate
+    # epilogue stores are 8/16-B vectors: C, bias, gate 16-B aligned, ldc % 4 == 0
+    assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 16, 16, 0x1008, 256, 2, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 16, 16, 0x1000, 258, 2, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 0x1004, 16, 0x1000, 256, 0, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_attention, 1, 3 * 4 * 32, 10, 4, 32, 1, 128, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_ln_modulate, 1, 300, 4, 300, 1, 1, 1, 1, 1, 1, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_digest, 1, [3], [8], 1, 0) == "DLO_E_ARG"
