@@ -28,25 +28,41 @@ class SlotEvent:
     prefetch_slot: int    # -1 on the last step
 
 
-def simulate_hooks(n: int, passes: int):
-    """The per-step slot trace produced by n circularly linked hooks over ``passes`` passes."""
-    if n < 1 or passes < 1:
-        raise ValueError("n and passes must be >= 1")
-    current = [i % 2 for i in range(n)]
-    prefetched = [None] * n
-    total = n * passes
+def simulate_hooks(n: int, passes: int, n_resident: int = 0):
+    """The per-step slot trace produced by n circularly linked hooks over ``passes`` passes.
+
+    With ``n_resident`` = R > 0 (the pages' resident-layer setting, [Doc]
+    "Validation coverage" and the smoke-test setup that names
+    dlo_resident_layers), the first R blocks of the stack stay in device memory:
+    their steps read no slot (-1) and prefetch nothing.  The other n - R blocks
+    carry the hooks, linked circularly among themselves, and stream through the
+    two slots by the same rule; the last streamed step of the run prefetches
+    nothing.
+    """
+    if n < 1 or passes < 1 or not 0 <= n_resident <= n:
+        raise ValueError("n, passes >= 1 and 0 <= n_resident <= n required")
+    m = n - n_resident
+    current = [h % 2 for h in range(m)]
+    prefetched = [None] * m
+    streamed_total = m * passes
+    u = 0
     trace = []
-    for t in range(total):
+    for t in range(n * passes):
         p, i = divmod(t, n)
-        prev = (i - 1) % n
+        if i < n_resident:
+            trace.append(SlotEvent(t, p, i, -1, -1, -1))
+            continue
+        h = i - n_resident
+        prev = (h - 1) % m
         if prefetched[prev] is not None:
-            current[i] = prefetched[prev]
-        if t + 1 < total:
-            nxt, ps = (i + 1) % n, 1 - current[i]
-            prefetched[i] = ps
+            current[h] = prefetched[prev]
+        if u + 1 < streamed_total:
+            nxt, ps = n_resident + (h + 1) % m, 1 - current[h]
+            prefetched[h] = ps
         else:
             nxt, ps = -1, -1
-        trace.append(SlotEvent(t, p, i, current[i], nxt, ps))
+        trace.append(SlotEvent(t, p, i, current[h], nxt, ps))
+        u += 1
     return trace
 
 
@@ -83,6 +99,8 @@ def trace_hazards(trace, n_slots: int = 2, first_block: int = 0, first_slot: int
     holds = {first_slot: first_block}
     problems = []
     for ev in trace:
+        if ev.read_slot == -1 and ev.prefetch_block == -1:
+            continue   # a resident block: reads no slot
         if not (0 <= ev.read_slot < n_slots):
             problems.append((ev.step, "slot out of range"))
         if holds.get(ev.read_slot) != ev.block:
@@ -158,6 +176,8 @@ def program_hazards(program, initial=None):
     problems = []
     for kc in computes:
         _, _, block, slot, step = program[kc]
+        if slot == -1:
+            continue   # a resident block: reads no slot
         before = []
         for c in copies:
             if program[c][3] != slot:

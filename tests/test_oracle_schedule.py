@@ -35,6 +35,47 @@ def test_closed_form_and_no_hazards(passes):
         assert sc.trace_hazards(tr) == []
 
 
+def test_hand_worked_trace_n3_one_resident_layer():
+    want = []
+    for line in open(os.path.join(GOLDEN, "slot_trace_n3_r1_p2.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            want.append(tuple(int(v) for v in line.split()))
+    got = [(e.step, e.pass_, e.block, e.read_slot, e.prefetch_block, e.prefetch_slot)
+           for e in sc.simulate_hooks(3, 2, n_resident=1)]
+    assert got == want
+
+
+@pytest.mark.parametrize("passes", [1, 2, 3])
+def test_resident_layers_reduce_to_the_plain_rule(passes):
+    # the streamed steps of an n-block stack with R resident layers are exactly the
+    # trace of an (n - R)-block stack, shifted by R; resident steps read nothing
+    for n in range(1, 41):
+        for R in range(0, n + 1):
+            tr = sc.simulate_hooks(n, passes, n_resident=R)
+            assert len(tr) == n * passes
+            res = [e for e in tr if e.block < R]
+            assert all((e.read_slot, e.prefetch_block, e.prefetch_slot) == (-1, -1, -1) for e in res)
+            streamed = [e for e in tr if e.block >= R]
+            if R == n:
+                assert not streamed
+                continue
+            ref = sc.simulate_hooks(n - R, passes)
+            assert len(streamed) == len(ref)
+            for u, (e, r) in enumerate(zip(streamed, ref)):
+                assert e.read_slot == r.read_slot == u % 2
+                assert e.block == r.block + R
+                assert e.prefetch_slot == r.prefetch_slot
+                assert e.prefetch_block == (r.prefetch_block + R if r.prefetch_block >= 0 else -1)
+            assert sc.trace_hazards(tr, first_block=R) == []
+
+
+def test_resident_layer_count_is_validated():
+    for bad in (-1, 4):
+        with pytest.raises(ValueError):
+            sc.simulate_hooks(3, 1, n_resident=bad)
+
+
 def test_static_rule_fails_for_odd_counts():
     # negative control: without the correction the tail -> head prefetch of an odd stack
     # lands in the slot the tail is reading
