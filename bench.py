@@ -129,27 +129,63 @@ def clip(u, lo, hi):
 
 
 def overlap_metrics(trace, copy_bytes, flops):
-    """Steady window: from the start of copy(1) to the end of compute(last - 1)."""
+    """Steady window: from the start of the second streamed step's copy to the end of
+    compute(last - 1).  Resident steps (read_slot -1) have no copy."""
     n = len(trace)
     if n < 3:
         return None
-    lo, hi = trace[1]["t_copy_begin"], trace[n - 2]["t_compute_end"]
+    streamed = [e for e in trace if e["read_slot"] >= 0]
+    lo = streamed[1]["t_copy_begin"] if len(streamed) > 1 else trace[1]["t_compute_begin"]
+    hi = trace[n - 2]["t_compute_end"]
     C = clip(union([(e["t_compute_begin"], e["t_compute_end"]) for e in trace]), lo, hi)
-    M = clip(union([(e["t_copy_begin"], e["t_copy_end"]) for e in trace[1:]]), lo, hi)
+    M = clip(union([(e["t_copy_begin"], e["t_copy_end"]) for e in streamed[1:]]), lo, hi)
     c, m, W = length(C), length(M), hi - lo
     in_w = [e for e in trace[1:n - 1]]
-    bytes_w = sum(copy_bytes[e["block"]] for e in in_w)
+    bytes_w = sum(copy_bytes[e["block"]] for e in in_w if e["read_slot"] >= 0)
     flops_w = sum(flops[e["block"]] for e in in_w)
+    all_copy = length(union([(e["t_copy_begin"], e["t_copy_end"]) for e in streamed]))
     return {
-        "window_ms": W, "compute_busy_ms": c, "copy_busy_ms": m,
+        "window_ms": W, "compute_busy_ms": c, "copy_busy_ms": m, "copy_busy_step_ms": all_copy,
         "overlap_eff": intersect(C, M) / max(min(c, m), 1e-9),
         "wall_eff": max(c, m) / W,
-        "h2d_busy_GBps": bytes_w / (m * 1e-3) / 1e9,
+        "h2d_busy_GBps": bytes_w / (max(m, 1e-9) * 1e-3) / 1e9,
         "h2d_delivered_GBps": bytes_w / (W * 1e-3) / 1e9,
         "mfma_util_busy": flops_w / (c * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "mfma_util_wall": flops_w / (W * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "bound": "h2d" if m > c else "compute",
     }
+
+
+def environment(torch, dev):
+    """Software, GPU, host-link and CPU facts of the machine the run is on."""
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        env["rocm"] = None
+    p = torch.cuda.get_device_properties(dev)
+    env["gpu"] = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+                  "compute_units": p.multi_processor_count, "hbm_GiB": round(p.total_memory / 2**30, 1)}
+    bus = getattr(p, "pci_bus_id", None)
+    if bus is not None:
+        bdf = "%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0), bus, getattr(p, "pci_device_id", 0))
+        link = {"bdf": bdf}
+        for key in ("current_link_speed", "current_link_width", "max_link_speed", "max_link_width", "numa_node"):
+            try:
+                link[key] = open(f"/sys/bus/pci/devices/{bdf}/{key}").read().strip()
+            except OSError:
+                link[key] = None
+        env["pcie"] = link
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    env["cpu"] = {"model": model, "threads_available": len(os.sched_getaffinity(0))}
+    return env
 
 
 def measure_link(torch, dev, gib=1, reps=4):
@@ -214,6 +250,8 @@ def main():
     ap.add_argument("--pinned-limit-gib", type=float, default=56.0,
                     help="ceiling on pinned block memory; blocks beyond it are staged")
     ap.add_argument("--store", default="auto", choices=["auto", "pinned", "pageable"])
+    ap.add_argument("--resident-layers", type=int, default=0,
+                    help="keep blocks 0 .. R-1 in device memory; stream the rest")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB "
                          "(a known-size kernel to scale HBM counters by)")
@@ -286,14 +324,18 @@ def main():
     link = measure_link(torch, dev)
     log(f"pinned H2D microbenchmark: {link:.1f} GB/s")
 
+    R = args.resident_layers
+    if R:
+        r.make_resident(R)
+        log(f"{R} resident layers placed")
     for i in range(args.warmup):
-        r.forward(P, want_run=False)
+        r.forward(P, n_resident=R, want_run=False)
         r.synchronize()
         log(f"warmup step {i + 1} done")
 
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    runs = [r.forward(P, flags=dlo.TRACE_TIMING) for _ in range(args.steps)]
+    runs = [r.forward(P, flags=dlo.TRACE_TIMING, n_resident=R) for _ in range(args.steps)]
     r.synchronize()
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
@@ -348,7 +390,7 @@ def main():
                    "widths": list(w.widths), "head_dim": w.head_dim, "tokens": T, "batch": 1,
                    "k": w.k, "passes": P, "slot_bytes": r.plan.slot_bytes,
                    "block_copy_bytes": max(copy_bytes), "host_store_bytes": sum(copy_bytes),
-                   "parallelism": "single GPU", "store": args.store,
+                   "parallelism": "single GPU", "store": args.store, "resident_layers": R,
                    "pinned_blocks": store_info["pinned_blocks"],
                    "staged_blocks": store_info["staged_blocks"]},
         "tokens_per_s": T * P * args.steps / wall,
@@ -363,25 +405,40 @@ def main():
         "per_kernel_ms_per_block": {nm: per_kernel[j] / launches for j, nm in enumerate(names)},
         "roofline": roofline,
         "setup_s": {"pin_alloc": t_alloc, "generate": t_gen, "pack": t_pack},
+        "env": environment(torch, dev),
     }
 
     if not args.no_verify:
         # the pages' own correctness criterion at full scale: streamed == resident, bit-exact
         log("verify: streamed vs resident, one step each from the same inputs")
         r.set_inputs(x0, c0)
-        r.forward(P, want_run=False)
+        r.forward(P, n_resident=R, want_run=False)
         xs = r.x_host()
         r.set_inputs(x0, c0)
-        t0 = time.perf_counter()
         r.make_resident()
+        r.synchronize()
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
         r.forward(P, resident=True, want_run=False)
         r.synchronize()
+        torch.cuda.synchronize(dev)
         t_res = time.perf_counter() - t0
         xr = r.x_host()
         r.free_resident()
         result["streamed_equals_resident"] = bool(np.array_equal(xs.view(np.uint32), xr.view(np.uint32)))
         result["finite"] = bool(np.isfinite(xs).all())
-        log(f"verify: equal={result['streamed_equals_resident']} (resident place+step {t_res:.1f} s)")
+        # run-based cross-check of the overlap: a resident step is the compute
+        # alone; the copy stream's busy time per streamed step is the copy alone
+        t_str = wall / args.steps
+        t_copy = avg.get("copy_busy_step_ms", 0.0) * 1e-3
+        result["cross_check"] = {
+            "streamed_step_ms": t_str * 1e3, "resident_step_ms": t_res * 1e3,
+            "copy_busy_step_ms": t_copy * 1e3,
+            "run_overlap": (t_copy + t_res - t_str) / max(min(t_copy, t_res), 1e-9),
+            "streaming_cost": t_str / t_res - 1.0,
+        }
+        log(f"verify: equal={result['streamed_equals_resident']}; resident step {t_res * 1e3:.0f} ms "
+            f"vs streamed {t_str * 1e3:.0f} ms")
 
     r.close()
     if not args.no_cpu_baseline:

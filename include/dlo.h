@@ -231,6 +231,16 @@ typedef struct {
 int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, int64_t cap,
                       int64_t *n_ops);
 
+/* As dlo_plan_schedule with the first n_resident blocks resident (0 <= n_resident
+ * <= n, else DLO_E_ARG): their steps are a lone COMPUTE(block, slot -1) each, with
+ * no waits or copies.  The other blocks follow the hook rule among themselves:
+ * the first streamed block is copied to slot 0 before the run, the u-th
+ * streamed step reads slot u % 2 and prefetches the next streamed block
+ * (circularly) into the other slot, and a COPY's step is the streamed step that
+ * reads it.  n_resident = n gives n COMPUTE ops and nothing else. */
+int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_resident,
+                         dlo_sched_op *ops, int64_t cap, int64_t *n_ops);
+
 /* ---------------------------------------------------------------------------
  * Forward ([Jul] "How It Works"; [Aug] s.3 "Double-Buffered Prefetch")
  *
@@ -249,10 +259,11 @@ int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, i
 
 #define DLO_TRACE_DIGEST 1u  /* digest the slot's regions before and after each block */
 #define DLO_TRACE_TIMING 2u  /* timestamp copies, block computes and every kernel */
-#define DLO_RESIDENT 4u      /* no streaming: block b is read from resident_blocks[b] */
+#define DLO_RESIDENT 4u      /* no streaming: block b is read from resident_blocks[b] (same as
+                                n_resident = number of blocks) */
 
 typedef struct {
-  void *slot[2];            /* device, slot_bytes each, distinct (unused if DLO_RESIDENT) */
+  void *slot[2];            /* device, slot_bytes each, distinct (unused if nothing streams) */
   int64_t slot_bytes;       /* capacity of each slot */
   float *x;                 /* device fp32 [tokens, x_row_stride], updated in place; 16-B
                                aligned, x_row_stride % 4 == 0 (else DLO_E_ARG) */
@@ -261,14 +272,21 @@ typedef struct {
   void *workspace;          /* device, >= dlo_plan_workspace_bytes(plan, tokens) */
   int64_t workspace_bytes;
   void *compute_stream;     /* hipStream_t */
-  void *copy_stream;        /* hipStream_t, distinct from compute_stream */
+  void *copy_stream;        /* hipStream_t, distinct from compute_stream (unused if nothing
+                               streams) */
   int32_t tokens;           /* rows of x (batch 1), >= 1; (tokens + 64) * 3 * widest d * 2
                                < 2^31, else DLO_E_UNSUPPORTED */
   int32_t passes;           /* chained passes over the stack, >= 1 */
   uint32_t flags;           /* DLO_TRACE_* | DLO_RESIDENT */
-  int32_t pad;
-  const void *const *resident_blocks; /* DLO_RESIDENT: device pointer per block, holding the
-                                         block's slot image (see dlo_place_block) */
+  int32_t n_resident;       /* resident layers R in [0, n] ([Doc] "Validation coverage":
+                               resident-layer requests): blocks 0 .. R-1 are read from
+                               resident_blocks[b] and never copied; blocks R .. n-1 stream
+                               through the two slots by the hook rule, their hooks linked
+                               circularly among themselves (see dlo_plan_schedule_ex).
+                               Ignored with DLO_RESIDENT.  Outside [0, n]: DLO_E_ARG. */
+  const void *const *resident_blocks; /* device pointer per resident block (entries 0 .. R-1,
+                                         or all with DLO_RESIDENT), holding the block's slot
+                                         image (see dlo_place_block); NULL entry: DLO_E_ARG */
 } dlo_forward_args;
 
 /* Enqueues `passes` passes of the stack.  x is updated on the compute stream;
@@ -293,8 +311,8 @@ int dlo_place_block(const dlo_plan *plan, const dlo_host_store *store, int32_t b
 typedef struct {
   int64_t step;
   int32_t pass, block;
-  int32_t read_slot;        /* -1 for a resident run */
-  int32_t prefetch_block;   /* -1 on the last step and for a resident run */
+  int32_t read_slot;        /* -1 for a resident block */
+  int32_t prefetch_block;   /* -1 on the last streamed step and for a resident block */
   int32_t prefetch_slot;    /* -1 likewise */
   int32_t pad;
   int64_t prefetch_bytes;   /* bytes copied by this step's prefetch (0 if none) */

@@ -70,7 +70,7 @@ class ForwardArgs(ctypes.Structure):
                 ("cond", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_int64), ("compute_stream", ctypes.c_void_p),
                 ("copy_stream", ctypes.c_void_p), ("tokens", ctypes.c_int32),
-                ("passes", ctypes.c_int32), ("flags", ctypes.c_uint32), ("pad", ctypes.c_int32),
+                ("passes", ctypes.c_int32), ("flags", ctypes.c_uint32), ("n_resident", ctypes.c_int32),
                 ("resident_blocks", ctypes.POINTER(ctypes.c_void_p))]
 
 
@@ -103,6 +103,9 @@ _SIGS = {
     "dlo_plan_workspace_bytes": (ctypes.c_int64, [ctypes.c_void_p, ctypes.c_int32]),
     "dlo_plan_schedule": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(SchedOp),
                                          ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "dlo_plan_schedule_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.POINTER(SchedOp), ctypes.c_int64,
+                                            ctypes.POINTER(ctypes.c_int64)]),
     "dlo_host_store_create": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint32,
                                              ctypes.POINTER(ctypes.c_void_p)]),
     "dlo_host_store_create_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int64,
@@ -260,12 +263,12 @@ class Plan:
             raise DLOError(-1, last_error())
         return v
 
-    def schedule(self, passes):
-        """The enqueued program as oracle-style tuples."""
+    def schedule(self, passes, n_resident=0):
+        """The enqueued program as oracle-style tuples (dlo_plan_schedule_ex)."""
         n = ctypes.c_int64()
-        _check(lib().dlo_plan_schedule(self.h, passes, None, 0, ctypes.byref(n)))
+        _check(lib().dlo_plan_schedule_ex(self.h, passes, n_resident, None, 0, ctypes.byref(n)))
         ops = (SchedOp * n.value)()
-        _check(lib().dlo_plan_schedule(self.h, passes, ops, n.value, ctypes.byref(n)))
+        _check(lib().dlo_plan_schedule_ex(self.h, passes, n_resident, ops, n.value, ctypes.byref(n)))
         out = []
         for o in ops:
             kind, stream = OP_KIND[o.kind], OP_STREAM[o.stream]
@@ -364,7 +367,7 @@ class Run:
 
 def forward_stack(plan, store, *, x, x_row_stride, cond, workspace, workspace_bytes,
                   compute_stream, copy_stream, tokens, passes, slots=(0, 0), slot_bytes=0,
-                  flags=0, resident_blocks=None, want_run=True):
+                  flags=0, resident_blocks=None, n_resident=0, want_run=True):
     """dlo_forward_stack; device pointers and streams as integers."""
     a = ForwardArgs()
     a.slot[0], a.slot[1] = slots
@@ -373,6 +376,7 @@ def forward_stack(plan, store, *, x, x_row_stride, cond, workspace, workspace_by
     a.workspace, a.workspace_bytes = workspace, workspace_bytes
     a.compute_stream, a.copy_stream = compute_stream, copy_stream
     a.tokens, a.passes, a.flags = tokens, passes, flags
+    a.n_resident = n_resident
     keep = None
     if resident_blocks is not None:
         keep = (ctypes.c_void_p * len(resident_blocks))(*resident_blocks)

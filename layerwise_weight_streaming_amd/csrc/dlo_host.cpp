@@ -189,33 +189,50 @@ void reap_detached(const dlo_plan *p, bool wait) {
 
 struct Step {
   int64_t t;
-  int32_t pass, block, slot, next_block, next_slot;
+  int32_t pass, block, slot, next_block, next_slot;  // slot -1: a resident block
+  int64_t next_step;                                  // step that reads the prefetch, -1 if none
 };
 
 // [Jul] "Slot Tracking: i%2 + Dynamic Correction": each hook starts at i % 2 and
 // takes the slot its predecessor (circularly) prefetched into, once there is one.
-std::vector<Step> hook_steps(int n, int passes) {
-  std::vector<int> cur(n), pref(n, -1);
-  for (int i = 0; i < n; ++i) cur[i] = i % 2;
-  const int64_t total = (int64_t)n * passes;
+// With n_res resident blocks ([Doc] "Validation coverage": resident-layer
+// requests), blocks 0 .. n_res-1 read no slot; the hooks of the streamed blocks
+// are linked circularly among themselves and follow the same rule.
+std::vector<Step> hook_steps(int n, int passes, int n_res) {
+  const int m = n - n_res;
+  std::vector<int> cur((size_t)std::max(m, 1)), pref((size_t)std::max(m, 1), -1);
+  for (int h = 0; h < m; ++h) cur[h] = h % 2;
+  const int64_t total = (int64_t)n * passes, streamed_total = (int64_t)m * passes;
   std::vector<Step> out;
   out.reserve((size_t)total);
+  int64_t u = 0;
   for (int64_t t = 0; t < total; ++t) {
     const int i = (int)(t % n), p = (int)(t / n);
-    const int prev = (i + n - 1) % n;
-    if (pref[prev] >= 0) cur[i] = pref[prev];
-    Step s{t, p, i, cur[i], -1, -1};
-    if (t + 1 < total) {
-      s.next_block = (i + 1) % n;
-      s.next_slot = 1 - cur[i];
-      pref[i] = s.next_slot;
+    Step s{t, p, i, -1, -1, -1, -1};
+    if (i >= n_res) {
+      const int h = i - n_res, prev = (h + m - 1) % m;
+      if (pref[prev] >= 0) cur[h] = pref[prev];
+      s.slot = cur[h];
+      if (u + 1 < streamed_total) {
+        s.next_block = n_res + (h + 1) % m;
+        s.next_slot = 1 - cur[h];
+        pref[h] = s.next_slot;
+      }
+      ++u;
     }
     out.push_back(s);
+  }
+  // the step that reads each prefetch: the next streamed step
+  int64_t next_streamed = -1;
+  for (int64_t t = total - 1; t >= 0; --t) {
+    Step &s = out[(size_t)t];
+    if (s.next_block >= 0) s.next_step = next_streamed;
+    if (s.slot >= 0) next_streamed = t;
   }
   return out;
 }
 
-std::vector<dlo_sched_op> build_program(const std::vector<Step> &steps, bool resident) {
+std::vector<dlo_sched_op> build_program(const std::vector<Step> &steps, bool all_resident) {
   std::vector<dlo_sched_op> prog;
   auto op = [&](int kind, int stream, int block, int slot, int event, int64_t step) {
     dlo_sched_op o;
@@ -223,27 +240,41 @@ std::vector<dlo_sched_op> build_program(const std::vector<Step> &steps, bool res
     o.pad = 0; o.step = step;
     prog.push_back(o);
   };
-  if (resident) {
+  const Step *first = nullptr;
+  for (const Step &s : steps)
+    if (s.slot >= 0) {
+      first = &s;
+      break;
+    }
+  if (all_resident || !first) {
     for (const Step &s : steps) op(DLO_OP_COMPUTE, DLO_STREAM_COMPUTE, s.block, -1, -1, s.t);
     return prog;
   }
   op(DLO_OP_RECORD, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_START, -1);
   op(DLO_OP_WAIT, DLO_STREAM_COPY, -1, -1, DLO_EV_START, -1);
-  // initial prefetch: block 0 into slot 0 ([Doc] "Pre-service transaction boundary")
-  op(DLO_OP_COPY, DLO_STREAM_COPY, steps[0].block, steps[0].slot, -1, 0);
-  op(DLO_OP_RECORD, DLO_STREAM_COPY, -1, -1, DLO_EV_COPIED0 + steps[0].slot, -1);
+  // initial prefetch: the first streamed block into slot 0 ([Doc] "Pre-service
+  // transaction boundary")
+  op(DLO_OP_COPY, DLO_STREAM_COPY, first->block, first->slot, -1, first->t);
+  op(DLO_OP_RECORD, DLO_STREAM_COPY, -1, -1, DLO_EV_COPIED0 + first->slot, -1);
+  bool first_streamed = true;
   for (const Step &s : steps) {
+    if (s.slot < 0) {  // resident block: reads no slot, nothing to wait for
+      op(DLO_OP_COMPUTE, DLO_STREAM_COMPUTE, s.block, -1, -1, s.t);
+      continue;
+    }
     // step t's block, from its slot, once the copy that placed it is done
     op(DLO_OP_WAIT, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_COPIED0 + s.slot, -1);
     op(DLO_OP_COMPUTE, DLO_STREAM_COMPUTE, s.block, s.slot, -1, s.t);
     op(DLO_OP_RECORD, DLO_STREAM_COMPUTE, -1, -1, DLO_EV_COMPUTED0 + s.slot, -1);
-    // prefetch the next block into the other slot, whose last reader was step t-1.
-    // Enqueued after step t's compute so that a host-staged copy never delays it.
+    // prefetch the next streamed block into the other slot, whose last reader
+    // was the previous streamed step.  Enqueued after this step's compute so
+    // that a host-staged copy never delays it.
     if (s.next_block >= 0) {
-      if (s.t >= 1) op(DLO_OP_WAIT, DLO_STREAM_COPY, -1, -1, DLO_EV_COMPUTED0 + s.next_slot, -1);
-      op(DLO_OP_COPY, DLO_STREAM_COPY, s.next_block, s.next_slot, -1, s.t + 1);
+      if (!first_streamed) op(DLO_OP_WAIT, DLO_STREAM_COPY, -1, -1, DLO_EV_COMPUTED0 + s.next_slot, -1);
+      op(DLO_OP_COPY, DLO_STREAM_COPY, s.next_block, s.next_slot, -1, s.next_step);
       op(DLO_OP_RECORD, DLO_STREAM_COPY, -1, -1, DLO_EV_COPIED0 + s.next_slot, -1);
     }
+    first_streamed = false;
   }
   return prog;
 }
@@ -464,9 +495,16 @@ int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens) {
 
 int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, int64_t cap,
                       int64_t *n_ops) {
+  return dlo_plan_schedule_ex(plan, passes, 0, ops, cap, n_ops);
+}
+
+int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_resident,
+                         dlo_sched_op *ops, int64_t cap, int64_t *n_ops) {
   if (!plan || !n_ops) return fail(DLO_E_ARG, "NULL argument");
   if (passes < 1) return fail(DLO_E_ARG, "passes must be >= 1");
-  const std::vector<Step> steps = hook_steps((int)plan->blocks.size(), passes);
+  const int n = (int)plan->blocks.size();
+  if (n_resident < 0 || n_resident > n) return fail(DLO_E_ARG, "n_resident %d not in [0, %d]", n_resident, n);
+  const std::vector<Step> steps = hook_steps(n, passes, n_resident);
   const std::vector<dlo_sched_op> prog = build_program(steps, false);
   *n_ops = (int64_t)prog.size();
   if (!ops) return ok();
@@ -819,9 +857,13 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
 
 int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dlo_forward_args *a) {
   if (!plan || !a) return fail(DLO_E_ARG, "NULL plan or args");
-  const bool resident = a->flags & DLO_RESIDENT;
   if (a->flags & ~(DLO_TRACE_DIGEST | DLO_TRACE_TIMING | DLO_RESIDENT))
     return fail(DLO_E_ARG, "unknown flags 0x%x", a->flags);
+  const int n = (int)plan->blocks.size();
+  if (!(a->flags & DLO_RESIDENT) && (a->n_resident < 0 || a->n_resident > n))
+    return fail(DLO_E_ARG, "n_resident %d not in [0, %d]", a->n_resident, n);
+  const int n_res = (a->flags & DLO_RESIDENT) ? n : a->n_resident;
+  const bool resident = n_res == n;  // nothing streams
   if (!resident) {
     if (!store) return fail(DLO_E_ARG, "store is NULL");
     if (store->plan_id != plan->id)
@@ -863,10 +905,11 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
     const char *s0 = static_cast<const char *>(a->slot[0]), *s1 = static_cast<const char *>(a->slot[1]);
     const int64_t gap = s0 < s1 ? s1 - s0 : s0 - s1;
     if (gap < plan->slot_bytes) return fail(DLO_E_ARG, "the two slots overlap");
-  } else {
-    if (!a->resident_blocks) return fail(DLO_E_ARG, "DLO_RESIDENT needs resident_blocks");
-    for (size_t b = 0; b < plan->blocks.size(); ++b)
-      if (!a->resident_blocks[b]) return fail(DLO_E_ARG, "resident block %zu is NULL", b);
+  }
+  if (n_res > 0) {
+    if (!a->resident_blocks) return fail(DLO_E_ARG, "resident blocks need resident_blocks");
+    for (int b = 0; b < n_res; ++b)
+      if (!a->resident_blocks[b]) return fail(DLO_E_ARG, "resident block %d is NULL", b);
   }
   return DLO_OK;
 }
@@ -881,9 +924,10 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
   std::lock_guard<std::mutex> lk(plan->mu);
   reap_detached(plan, false);
 
-  const bool resident = a->flags & DLO_RESIDENT;
   const int n = (int)plan->blocks.size();
-  const std::vector<Step> steps = hook_steps(n, a->passes);
+  const int n_res = (a->flags & DLO_RESIDENT) ? n : a->n_resident;
+  const bool resident = n_res == n;  // nothing streams
+  const std::vector<Step> steps = hook_steps(n, a->passes, n_res);
   const std::vector<dlo_sched_op> prog = build_program(steps, resident);
   hipStream_t cs = (hipStream_t)a->compute_stream, ps = (hipStream_t)a->copy_stream;
 
@@ -921,10 +965,10 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
     r.step = s.t;
     r.pass = s.pass;
     r.block = s.block;
-    r.read_slot = resident ? -1 : s.slot;
-    r.prefetch_block = resident ? -1 : s.next_block;
-    r.prefetch_slot = resident ? -1 : s.next_slot;
-    r.prefetch_bytes = (resident || s.next_block < 0) ? 0 : plan->blocks[s.next_block].copy_bytes;
+    r.read_slot = s.slot;
+    r.prefetch_block = s.next_block;
+    r.prefetch_slot = s.next_slot;
+    r.prefetch_bytes = s.next_block < 0 ? 0 : plan->blocks[s.next_block].copy_bytes;
     r.t_copy_begin = r.t_copy_end = r.t_compute_begin = r.t_compute_end = -1.f;
   }
 
@@ -970,8 +1014,8 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
       }
       case DLO_OP_COMPUTE: {
         const BlockPlan &bp = plan->blocks[op.block];
-        const char *base = resident ? static_cast<const char *>(a->resident_blocks[op.block])
-                                    : static_cast<const char *>(a->slot[op.slot]);
+        const char *base = op.slot < 0 ? static_cast<const char *>(a->resident_blocks[op.block])
+                                       : static_cast<const char *>(a->slot[op.slot]);
         int64_t offs[DLO_MAX_GROUPS], lens[DLO_MAX_GROUPS];
         for (int g = 0; g < bp.n_groups; ++g) {
           offs[g] = bp.gregion[g];
@@ -1030,11 +1074,10 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
         return ms;
       };
       run->kernel_ms.assign((size_t)(total * DLO_KERNELS_PER_BLOCK), -1.f);
-      const bool resident = total > 0 && run->recs[0].read_slot < 0;
       for (int64_t t = 0; t < total; ++t) {
         dlo_slot_event &r = run->recs[(size_t)t];
         auto ev = [&](int j) { return run->tev[(size_t)(t * TEV + j)]; };
-        if (!resident) {
+        if (r.read_slot >= 0) {  // a streamed step: the copy that fed it
           r.t_copy_begin = since(ev(0));
           r.t_copy_end = since(ev(1));
         }

@@ -47,11 +47,12 @@ class StackRunner:
         self.cond.copy_(torch.from_numpy(np.ascontiguousarray(c, dtype=np.float32)))
         torch.cuda.synchronize(self.dev)
 
-    def make_resident(self):
-        """Every block's slot image in its own device buffer (for resident runs)."""
+    def make_resident(self, count=None):
+        """Slot images of blocks 0 .. count-1 (all by default) in device buffers of their own."""
         torch = self.torch
+        count = self.n_blocks if count is None else count
         self.resident = []
-        for b in range(self.n_blocks):
+        for b in range(count):
             ext = self.plan.block_info(b)["extent"]
             buf = torch.empty(max(ext, 256), dtype=torch.uint8, device=self.dev)
             place_block(self.plan, self.store, b, buf.data_ptr(), buf.numel(), self.copy.cuda_stream)
@@ -62,14 +63,18 @@ class StackRunner:
         self.resident = None
 
     # -- runs -------------------------------------------------------------------
-    def forward(self, passes, flags=0, resident=False, want_run=True):
+    def forward(self, passes, flags=0, resident=False, n_resident=0, want_run=True):
+        """One dlo_forward_stack call.  resident=True: nothing streams; n_resident=R:
+        blocks 0 .. R-1 resident, the rest streamed (resident images made on demand)."""
         from . import RESIDENT
 
         res_ptrs = None
-        if resident:
-            if self.resident is None:
-                self.make_resident()
-            flags |= RESIDENT
+        if resident or n_resident:
+            need = self.n_blocks if resident else n_resident
+            if self.resident is None or len(self.resident) < need:
+                self.make_resident(need)
+            if resident:
+                flags |= RESIDENT
             res_ptrs = [b.data_ptr() for b in self.resident]
         return forward_stack(
             self.plan, None if resident else self.store,
@@ -79,7 +84,7 @@ class StackRunner:
             tokens=self.tokens, passes=passes,
             slots=(self.slots[0].data_ptr(), self.slots[1].data_ptr()),
             slot_bytes=self.plan.slot_bytes, flags=flags, resident_blocks=res_ptrs,
-            want_run=want_run)
+            n_resident=n_resident, want_run=want_run)
 
     def synchronize(self):
         self.compute.synchronize()

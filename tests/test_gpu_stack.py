@@ -31,8 +31,8 @@ def _expected_regions(w, stack, k):
     return regs
 
 
-def _check_trace(tr, n, passes, regs=None):
-    ref = sc.simulate_hooks(n, passes)
+def _check_trace(tr, n, passes, regs=None, n_resident=0):
+    ref = sc.simulate_hooks(n, passes, n_resident=n_resident)
     assert len(tr) == len(ref)
     for got, e in zip(tr, ref):
         assert (got["step"], got["pass_"], got["block"], got["read_slot"], got["prefetch_block"],
@@ -219,4 +219,29 @@ def test_staged_store_matches_pinned(mode, limit_blocks):
     tr = run.trace()
     _check_trace(tr, w.n_blocks, w.passes, _expected_regions(w, stack, w.k))
     assert np.array_equal(r.x_host().view(np.uint32), x_ref.view(np.uint32))
+    r.close()
+
+
+@pytest.mark.parametrize("n_resident", [1, 3, 7, 8])
+def test_resident_layers_match_full_streaming(n_resident):
+    """Blocks 0 .. R-1 resident, the rest streamed: the slot trace and digests follow
+    the oracle's hook rule over the streamed blocks, and x equals the fully
+    streamed result bit for bit (the streamed subset has an odd count for R = 1, 3, 7)."""
+    torch = require_gpu()
+    w = synth.WORKLOADS["8blk"]
+    say(f"resident layers R={n_resident}")
+    stack = synth.make_stack(w, 11)
+    r = make_runner(w, stack)
+    r.forward(w.passes, want_run=False)
+    x_stream = r.x_host()
+    r.set_inputs(stack.x, stack.c)
+    run = r.forward(w.passes, flags=dlo.TRACE_DIGEST, n_resident=n_resident)
+    tr = run.trace()
+    _check_trace(tr, w.n_blocks, w.passes, _expected_regions(w, stack, w.k), n_resident=n_resident)
+    assert np.array_equal(r.x_host().view(np.uint32), x_stream.view(np.uint32))
+    # repeated calls with resident layers chain like passes
+    r.set_inputs(stack.x, stack.c)
+    r.forward(1, n_resident=n_resident, want_run=False)
+    r.forward(w.passes - 1, n_resident=n_resident, want_run=False)
+    assert np.array_equal(r.x_host().view(np.uint32), x_stream.view(np.uint32))
     r.close()

@@ -145,6 +145,34 @@ def test_schedule_program_is_race_free_and_follows_the_hook_rule(passes):
         assert {o[3] for o in prog if o[0] in ("copy", "compute")} <= {0, 1}
 
 
+@pytest.mark.parametrize("passes", [1, 2, 3])
+def test_schedule_with_resident_layers_is_race_free_and_follows_the_oracle(passes):
+    for n in list(range(1, 13)) + [72, 127]:
+        blocks = [(256, 4, [("w", "bf16", 10)]) for _ in range(n)]
+        plan = dlo.Plan(blocks, 2)
+        for R in sorted({0, 1, n // 2, n - 1, n}):
+            prog = plan.schedule(passes, n_resident=R)
+            ref = sc.simulate_hooks(n, passes, n_resident=R)
+            computes = [o for o in prog if o[0] == "compute"]
+            assert [(o[2], o[3], o[4]) for o in computes] == [(e.block, e.read_slot, e.step) for e in ref]
+            copies = [o for o in prog if o[0] == "copy"]
+            if R == n:
+                assert len(prog) == n * passes and not copies
+                continue
+            assert sc.program_hazards(prog) == [], (n, R, passes)
+            want = [(R, 0)] + [(e.prefetch_block, e.prefetch_slot) for e in ref if e.prefetch_block >= 0]
+            assert [(o[2], o[3]) for o in copies] == want
+            # resident blocks are never copied and never wait
+            assert all(o[2] >= R for o in copies)
+            assert all(o[3] == -1 for o in computes if o[2] < R)
+
+
+def test_schedule_resident_count_out_of_range():
+    plan = dlo.Plan([(256, 4, [("w", "bf16", 10)]) for _ in range(3)], 2)
+    for bad in (-1, 4):
+        assert _status(plan.schedule, 1, bad) == "DLO_E_ARG"
+
+
 def test_schedule_negative_control_detected():
     # dropping the copy stream's wait on the previous reader must be flagged by the checker
     blocks = [(256, 4, [("w", "bf16", 10)]) for _ in range(3)]
@@ -243,6 +271,10 @@ def test_forward_validation_errors():
     assert _status(F, slots=(0, 0x100000)) == "DLO_E_ARG"
     assert _status(F, flags=64) == "DLO_E_ARG"
     assert _status(F, flags=dlo.RESIDENT) == "DLO_E_ARG"        # no resident pointers
+    assert _status(F, n_resident=-1) == "DLO_E_ARG"
+    assert _status(F, n_resident=4) == "DLO_E_ARG"              # more than the 3 blocks
+    assert _status(F, n_resident=1) == "DLO_E_ARG"              # resident layers need pointers
+    assert _status(F, n_resident=2, resident_blocks=[0x200000, 0]) == "DLO_E_ARG"  # NULL entry
     # a store made by another plan is the analogue of double sharding: rejected
     p2, st2 = _tiny_plan_and_store()
     assert _status(lambda: dlo.forward_stack(p, st2, **_args(p))) == "DLO_E_PLAN_MISMATCH"
