@@ -42,10 +42,25 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
 
 
 def param_dict(params):
-    """[(name, dtype, array)] -> {name: float64 array} (bf16 widened)."""
-    out = {}
+    """[(name, dtype, array)] -> {name: float64 array} (bf16 widened).
+
+    An FP8 block carries each linear as ``X.weight`` (E4M3 codes) plus
+    ``X.weight_scale`` (one fp32 value); ``X.weight`` is then the dequantised
+    weight code_value * scale (see oracle.fp8), and the scale entry is dropped.
+    """
+    from . import fp8
+
+    out, codes = {}, {}
     for name, dt, arr in params:
-        out[name] = widen_bf16(arr) if dt == "bf16" else np.asarray(arr, dtype=np.float64)
+        if dt == "fp8":
+            codes[name] = np.asarray(arr, dtype=np.uint8)
+        elif dt == "bf16":
+            out[name] = widen_bf16(arr)
+        else:
+            out[name] = np.asarray(arr, dtype=np.float64)
+    for name, c in codes.items():
+        scale = out.pop(name + "_scale")
+        out[name] = fp8.dequantize(c, np.float32(scale.reshape(-1)[0]))
     return out
 
 

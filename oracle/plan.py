@@ -23,8 +23,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-ELEMENT_BYTES = {"bf16": 2, "f32": 4}
-NUMPY_DTYPE = {"bf16": np.uint16, "f32": np.float32}
+ELEMENT_BYTES = {"bf16": 2, "f32": 4, "fp8": 1}
+NUMPY_DTYPE = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}
 
 
 def ceil_div(a: int, b: int) -> int:

@@ -1,0 +1,100 @@
+"""Pins for oracle.fp8: E4M3 code values from the format definition, nearest-even
+encoding with saturation, per-tensor scaling, and the FP8 block's parameter form."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import fp8
+from oracle import forward as of
+
+
+def test_code_values_from_the_format_definition():
+    # OCP FP8 E4M3: bias 7, subnormals m * 2^-9, S.1111.111 = NaN, max 448
+    assert fp8.DECODE[0x00] == 0.0 and np.signbit(fp8.DECODE[0x80])
+    assert fp8.DECODE[0x38] == 1.0
+    assert fp8.DECODE[0x7E] == 448.0 and fp8.DECODE[0xFE] == -448.0
+    assert fp8.DECODE[0x08] == 2.0 ** -6          # smallest normal
+    assert fp8.DECODE[0x07] == 7 * 2.0 ** -9      # largest subnormal
+    assert fp8.DECODE[0x01] == 2.0 ** -9          # smallest subnormal
+    assert fp8.DECODE[0x3C] == 1.5 and fp8.DECODE[0x40] == 2.0
+    assert np.isnan(fp8.DECODE[0x7F]) and np.isnan(fp8.DECODE[0xFF])
+    assert np.sum(np.isnan(fp8.DECODE)) == 2      # no infinities, two NaN codes
+
+
+def test_round_trip_of_every_finite_code():
+    codes = np.array([c for c in range(256) if not np.isnan(fp8.DECODE[c])], dtype=np.uint8)
+    vals = fp8.DECODE[codes].astype(np.float32)
+    assert np.array_equal(fp8.encode_e4m3(vals), codes)
+
+
+def test_nearest_even_ties_and_saturation():
+    # midpoints between neighbouring codes go to the even code
+    pos = [c for c in range(0x7F)]
+    for c in pos[:-1]:
+        mid = np.float32((fp8.DECODE[c] + fp8.DECODE[c + 1]) / 2)
+        want = c if c % 2 == 0 else c + 1
+        assert fp8.encode_e4m3(mid)[()] == want, hex(c)
+        assert fp8.encode_e4m3(-mid)[()] == want | 0x80
+    # beyond the largest finite value: saturate, never NaN
+    for v in (448.0, 460.0, 464.0, 480.0, 1e6, np.float32(3e38)):
+        assert fp8.encode_e4m3(np.float32(v))[()] == 0x7E
+    assert fp8.encode_e4m3(np.float32(np.nan))[()] == 0x7F
+
+
+def test_encoding_is_nearest_against_brute_force():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.normal(0, 3, 4000), rng.normal(0, 0.01, 2000), rng.uniform(-500, 500, 2000)])
+    x = x.astype(np.float32)
+    codes = fp8.encode_e4m3(x)
+    finite = np.array([c for c in range(256) if not np.isnan(fp8.DECODE[c])])
+    for xi, ci in zip(x, codes):
+        a = min(abs(float(xi)), 448.0)
+        best = np.min(np.abs(np.abs(fp8.DECODE[finite]) - a))
+        assert abs(abs(fp8.DECODE[ci]) - a) == best
+        assert (fp8.DECODE[ci] < 0) == (xi < 0) or fp8.DECODE[ci] == 0
+
+
+def test_tensor_scale_maps_amax_to_448_and_error_bound():
+    rng = np.random.default_rng(1)
+    w = (rng.normal(0, 0.02, (64, 96)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    codes, scale = fp8.quantize_tensor(w)
+    wf = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    amax = np.max(np.abs(wf))
+    assert scale == np.float32(np.float32(amax) / np.float32(448.0))
+    assert np.max(np.abs(fp8.DECODE[codes])) == 448.0
+    deq = fp8.dequantize(codes, scale)
+    # 3 mantissa bits: relative error <= 2^-4 for normal codes; absolute error
+    # <= half the subnormal step below
+    err = np.abs(deq - wf)
+    bound = np.maximum(np.abs(wf) * 2.0 ** -4, 2.0 ** -10 * float(scale))
+    assert np.all(err <= bound * (1 + 1e-12))
+    # an all-zero tensor keeps scale 1 and zero codes
+    z, s = fp8.quantize_tensor(np.zeros(10, np.uint16))
+    assert s == 1.0 and not z.any()
+
+
+def test_fp8_block_form_and_forward_plumbing():
+    d, T = 256, 16
+    ps = synth.block_params(3, 0, d)
+    q = fp8.quantize_block(ps)
+    names = [n for n, _, _ in q]
+    # registration order: weight, weight_scale, bias for each linear
+    for lin in ("adaln", "attn.qkv", "attn.out", "mlp.fc1", "mlp.fc2"):
+        i = names.index(lin + ".weight")
+        assert names[i + 1] == lin + ".weight_scale" and names[i + 2] == lin + ".bias"
+    assert len(q) == len(ps) + 5
+    # the FP8 block's forward is the bf16 block's forward with the dequantised weights
+    P = of.param_dict(q)
+    P_ref = of.param_dict(ps)
+    for n, dt, a in q:
+        if dt == "fp8":
+            scale = dict((m, b) for m, _, b in q)[n + "_scale"][0]
+            P_ref[n] = fp8.dequantize(a, scale)
+            assert np.array_equal(P[n], P_ref[n])
+    x = np.random.default_rng(2).normal(size=(T, d))
+    c = np.random.default_rng(3).normal(size=d)
+    assert np.array_equal(of.dit_block(x, c, P, 4), of.dit_block(x, c, P_ref, 4))
+    # and it differs from the bf16 block by the quantisation only (a few percent of the update)
+    y_bf16, y_fp8 = of.dit_block(x, c, of.param_dict(ps), 4), of.dit_block(x, c, P, 4)
+    upd = np.max(np.abs(y_bf16 - x))
+    assert 0 < np.max(np.abs(y_fp8 - y_bf16)) < 0.2 * upd

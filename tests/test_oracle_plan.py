@@ -76,10 +76,12 @@ def test_param_offsets_follow_registration_order():
 def _random_params(rng, n_params):
     params = []
     for p in range(n_params):
-        dt = rng.choice(["bf16", "f32"])
+        dt = rng.choice(["bf16", "f32", "fp8"])
         numel = rng.choice([0, 1, 2, 3, 5, 7, 31, 64, 257, rng.randint(0, 5000)])
         if dt == "bf16":
             a = np.array([rng.getrandbits(16) for _ in range(numel)], dtype=np.uint16)
+        elif dt == "fp8":
+            a = np.array([rng.getrandbits(8) for _ in range(numel)], dtype=np.uint8)
         else:
             a = np.array([rng.uniform(-1, 1) for _ in range(numel)], dtype=np.float32)
         params.append((f"p{p}", dt, a))
