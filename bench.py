@@ -31,8 +31,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 LINK_PEAK_GBS = 32.0 * 16 * 128 / 130 / 8   # PCIe 5.0 x16, one direction: 63.0 GB/s
 
 
-def kernel_work(name, d, T):
+def kernel_work(name, d, T, fp8=False):
     """Algorithmic work of one launch: (amount, unit, bound)."""
+    if name == "dequant_fp8":   # E4M3 codes in, bf16 weights out (nothing for a bf16 block)
+        return (18 * d * d * 3 if fp8 else 0) / 1e9, "GB", "hbm"
     if name == "adaln_gemv":
         return (6 * d * d * 2 + 6 * d * 4 * 2 + d * 4) / 1e9, "GB", "hbm"
     if name in ("ln1_modulate", "ln2_modulate"):
@@ -250,6 +252,9 @@ def main():
     ap.add_argument("--pinned-limit-gib", type=float, default=56.0,
                     help="ceiling on pinned block memory; blocks beyond it are staged")
     ap.add_argument("--store", default="auto", choices=["auto", "pinned", "pageable"])
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
+                    help="fp8: per-tensor E4M3 weights + fp32 scales (quantized on the host before "
+                         "packing), dequantised on the device after each copy")
     ap.add_argument("--resident-layers", type=int, default=0,
                     help="keep blocks 0 .. R-1 in device memory; stream the rest")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -288,8 +293,12 @@ def main():
         w = w.with_(k=args.k)
     n = args.blocks or w.n_blocks
     T, P = w.tokens, w.passes
-    specs = [(w.width(b), w.heads(b), [(nm, dt, int(np.prod(s))) for nm, dt, s in synth.block_schema(w.width(b))])
-             for b in range(n)]
+    fp8 = args.weights == "fp8"
+    if fp8:
+        specs = [(w.width(b), w.heads(b), dlo.block_schema(w.width(b), fp8=True)) for b in range(n)]
+    else:
+        specs = [(w.width(b), w.heads(b), [(nm, dt, int(np.prod(s))) for nm, dt, s in synth.block_schema(w.width(b))])
+                 for b in range(n)]
 
     t_setup = time.perf_counter()
     r = StackRunner(specs, w.k, T, w.D, store_mode=args.store,
@@ -308,6 +317,15 @@ def main():
                          for nm, dt, s in synth.block_schema(d)}
         t0 = time.perf_counter()
         ps = synth.block_params(args.seed, b, d, out_buffers=bufs[key])
+        if fp8:   # the loader's finalisation: per-tensor E4M3 codes + fp32 scale
+            q = []
+            for nm, dt, a in ps:
+                if dt == "bf16":
+                    codes, scale = dlo.quantize_fp8(a)
+                    q += [(nm, "fp8", codes), (nm + "_scale", "f32", np.array([scale], np.float32))]
+                else:
+                    q.append((nm, dt, a))
+            ps = q
         t1 = time.perf_counter()
         r.pack(b, [(d, w.heads(b), ps)])
         t2 = time.perf_counter()
@@ -355,9 +373,9 @@ def main():
         per_kernel += kt.sum(axis=0)
         launches += kt.shape[0]
         for e, row in zip(tr, kt):
-            d = infos[e["block"]]["d_model"]
+            d, f8 = infos[e["block"]]["d_model"], infos[e["block"]]["fp8"]
             for j, nm in enumerate(names):
-                work[j] += kernel_work(nm, d, T)[0]
+                work[j] += kernel_work(nm, d, T, f8)[0]
         m = overlap_metrics(tr, copy_bytes, flops)
         if m:
             ov.append(m)
@@ -391,6 +409,7 @@ def main():
                    "k": w.k, "passes": P, "slot_bytes": r.plan.slot_bytes,
                    "block_copy_bytes": max(copy_bytes), "host_store_bytes": sum(copy_bytes),
                    "parallelism": "single GPU", "store": args.store, "resident_layers": R,
+                   "weights": args.weights,
                    "pinned_blocks": store_info["pinned_blocks"],
                    "staged_blocks": store_info["staged_blocks"]},
         "tokens_per_s": T * P * args.steps / wall,

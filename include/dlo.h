@@ -66,9 +66,9 @@ typedef enum {
 } dlo_status;
 
 /* element types of parameter groups */
-enum { DLO_BF16 = 0, DLO_F32 = 1 };
+enum { DLO_BF16 = 0, DLO_F32 = 1, DLO_FP8_E4M3 = 2 /* OCP FP8 E4M3, 1 byte */ };
 
-#define DLO_MAX_GROUPS 2   /* one group per element type */
+#define DLO_MAX_GROUPS 3   /* one group per element type */
 #define DLO_ALIGN 256      /* byte alignment of regions and extents inside a slot */
 
 /* One parameter, in the block's registration order.  `src` is a host pointer to
@@ -108,7 +108,8 @@ typedef struct dlo_run dlo_run;
  * large whatever the block count.
  * ------------------------------------------------------------------------- */
 
-/* Plans n_blocks blocks for k shards.  k >= 1, n_blocks >= 1, every dtype known,
+/* Plans n_blocks blocks for k shards.  k >= 1, n_blocks >= 1, every dtype known
+ * (DLO_BF16, DLO_F32, DLO_FP8_E4M3: groups of 2, 4 and 1 bytes per element),
  * numel >= 0.  The plan copies names and sizes and never keeps `src`.  *out is
  * set to a new plan (free with dlo_plan_destroy) or NULL on error. */
 int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_plan **out);
@@ -126,7 +127,8 @@ typedef struct {
   int64_t region[DLO_MAX_GROUPS];  /* byte offset of the group in the slot */
   int64_t extent;                  /* bytes of the slot the block occupies */
   int64_t copy_bytes;              /* sum_g k * S_g * elt_g: bytes moved per placement */
-  int32_t is_dit;                  /* 1 if the parameter list is the DiT block schema */
+  int32_t is_dit;                  /* 1: the DiT block schema (bf16 weights); 2: its FP8
+                                      form (dlo_block_schema_fp8); 0: neither */
 } dlo_block_info;
 
 int dlo_plan_block_info(const dlo_plan *plan, int32_t b, dlo_block_info *out);
@@ -135,7 +137,9 @@ int dlo_plan_block_info(const dlo_plan *plan, int32_t b, dlo_block_info *out);
 int dlo_plan_param_offset(const dlo_plan *plan, int32_t b, int32_t p, int64_t *byte_offset);
 
 /* Device workspace needed by dlo_forward_stack for `tokens` rows (batch 1):
- * activations of one block at the widest d; -1 on error. */
+ * activations of one block at the widest d, plus, when the plan holds FP8
+ * blocks, the bf16 weights of the widest FP8 block (18 d^2 elements) that its
+ * forward dequantises into; -1 on error. */
 int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens);
 
 /* ---------------------------------------------------------------------------
@@ -244,7 +248,8 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 /* ---------------------------------------------------------------------------
  * Forward ([Jul] "How It Works"; [Aug] s.3 "Double-Buffered Prefetch")
  *
- * Block forward (every block must carry the DiT schema of dlo_block_schema;
+ * Block forward (every block must carry the DiT schema of dlo_block_schema or its
+ * FP8 form, dlo_block_schema_fp8 -- whose weights are first dequantised to bf16;
  * width d % 256 == 0, d <= 8192, head dim d / n_heads in {64, 128}):
  *   mod = SiLU(cond[:d]) W_ada^T + b_ada -> shift1, scale1, gate1, shift2, scale2, gate2
  *   h   = LN1(x[:, :d]) * (1 + scale1) + shift1                      (bf16)
@@ -331,8 +336,9 @@ typedef struct {
 int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_out);
 
 /* DLO_TRACE_TIMING: per step, the duration in ms of each of the block's kernels in
- * launch order (DLO_KERNELS_PER_BLOCK per step), after the run completed. */
-#define DLO_KERNELS_PER_BLOCK 8
+ * launch order (DLO_KERNELS_PER_BLOCK per step), after the run completed.  Entry 0
+ * is the FP8 weight dequantisation (0 for a bf16 block). */
+#define DLO_KERNELS_PER_BLOCK 9
 int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
 /* name of kernel j (0 <= j < DLO_KERNELS_PER_BLOCK) of a block forward */
 const char *dlo_kernel_name(int32_t j);
@@ -354,6 +360,27 @@ const char *dlo_last_error(void);
  * mlp.fc2.bias; all others fp32).  Returns DLO_E_ARG for i out of range. */
 #define DLO_DIT_N_PARAMS 16
 int dlo_block_schema(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel);
+
+/* Parameter i (0 <= i < 21) of the FP8 form of the DiT block ([Doc] "Request and
+ * loading constraints": per-tensor online FP8 linears keep a 1-byte weight plus
+ * an fp32 scale and are sharded like any other dtype group): every bf16 matrix
+ * X.weight of dlo_block_schema becomes X.weight (DLO_FP8_E4M3, same shape)
+ * followed by X.weight_scale (fp32, 1 element); the other parameters are
+ * unchanged, so each linear registers weight, weight_scale, bias.  The block's
+ * dtype groups are then FP8 (18 d^2 elements) and fp32 (19 d + 7).  Its forward
+ * dequantises each weight to bf16(code_value * scale) into the workspace on the
+ * compute stream, then runs the bf16 block forward.  DLO_E_ARG for i out of
+ * range. */
+#define DLO_DIT_FP8_N_PARAMS 21
+int dlo_block_schema_fp8(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel);
+
+/* The loader's finalisation of one weight for the FP8 block (host memory, not
+ * on the streamed path): scale = amax|w| / 448 in fp32 (1 for an all-zero or
+ * empty tensor); codes[i] = the OCP E4M3 code nearest to float(w[i]) / scale,
+ * ties to the even code, saturating at +-448 (never NaN for finite input; NaN
+ * input gives 0x7F).  w: n bf16 values; codes: n bytes; n >= 0.  DLO_E_ARG for
+ * NULL pointers or n < 0. */
+int dlo_quantize_fp8(const uint16_t *w, int64_t n, uint8_t *codes, float *scale);
 
 /* The kernels the block forward is made of, callable one at a time (device
  * pointers, row-major, enqueued on `stream`, asynchronous).  Each validates its
@@ -386,6 +413,12 @@ int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, 
  * DLO_E_UNSUPPORTED when (T + 64) * ldqkv * 2 >= 2^31 (32-bit buffer offsets). */
 int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t H, int32_t dh,
                      uint16_t *out, int64_t ldo, void *stream);
+
+/* out[i] = bf16_rne(e4m3_value(codes[i]) * *scale), i < n (device pointers; scale
+ * is read on the device).  n % 16 == 0, codes 16-B and out 32-B aligned, else
+ * DLO_E_UNSUPPORTED.  The FP8 block's forward runs this on each weight. */
+int dlo_op_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
+                       void *stream);
 
 /* Slot digest (see dlo_slot_trace) of up to DLO_MAX_GROUPS regions of `base`,
  * written to *out (device uint64). */

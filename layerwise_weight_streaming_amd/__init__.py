@@ -21,12 +21,13 @@ DLO_OK = 0
 STATUS = {0: "DLO_OK", -1: "DLO_E_ARG", -2: "DLO_E_HOSTMEM", -3: "DLO_E_PIN",
           -4: "DLO_E_SLOT_SMALL", -5: "DLO_E_PLAN_MISMATCH", -6: "DLO_E_HIP",
           -7: "DLO_E_STATE", -8: "DLO_E_UNSUPPORTED", -9: "DLO_E_WORKSPACE"}
-DTYPES = {"bf16": 0, "f32": 1}
+DTYPES = {"bf16": 0, "f32": 1, "fp8": 2}   # fp8: OCP E4M3, one byte
 DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
 STORE_PINNED, STORE_PAGEABLE, STORE_AUTO = 0, 1, 2
 TRACE_DIGEST, TRACE_TIMING, RESIDENT = 1, 2, 4
 EPI_BIAS, EPI_BIAS_GELU, EPI_GATED_RESIDUAL = 0, 1, 2
-KERNELS_PER_BLOCK = 8
+KERNELS_PER_BLOCK = 9
+MAX_GROUPS = 3
 OP_KIND = {0: "copy", 1: "compute", 2: "record", 3: "wait"}
 OP_STREAM = {0: "compute", 1: "copy"}
 OP_EVENT = {0: "copied0", 1: "copied1", 2: "computed0", 3: "computed1", 4: "start"}
@@ -52,8 +53,8 @@ class Block(ctypes.Structure):
 class BlockInfo(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_params", ctypes.c_int32), ("n_groups", ctypes.c_int32),
-                ("dtype", ctypes.c_int32 * 2), ("numel", ctypes.c_int64 * 2),
-                ("shard", ctypes.c_int64 * 2), ("region", ctypes.c_int64 * 2),
+                ("dtype", ctypes.c_int32 * MAX_GROUPS), ("numel", ctypes.c_int64 * MAX_GROUPS),
+                ("shard", ctypes.c_int64 * MAX_GROUPS), ("region", ctypes.c_int64 * MAX_GROUPS),
                 ("extent", ctypes.c_int64), ("copy_bytes", ctypes.c_int64),
                 ("is_dit", ctypes.c_int32)]
 
@@ -139,6 +140,12 @@ _SIGS = {
     "dlo_op_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_void_p]),
+    "dlo_block_schema_fp8": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
+                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
+    "dlo_quantize_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.POINTER(ctypes.c_float)]),
+    "dlo_op_dequant_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]),
     "dlo_op_digest": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_void_p]),
@@ -171,14 +178,25 @@ def last_error() -> str:
     return (lib().dlo_last_error() or b"").decode()
 
 
-def block_schema(d: int):
-    """[(name, dtype, numel)] of the DiT block schema as libdlo defines it."""
+def block_schema(d: int, fp8: bool = False):
+    """[(name, dtype, numel)] of the DiT block schema (or its FP8 form) as libdlo defines it."""
+    fn, count = (lib().dlo_block_schema_fp8, 21) if fp8 else (lib().dlo_block_schema, 16)
     out = []
-    for i in range(16):
+    for i in range(count):
         name, dt, n = ctypes.c_char_p(), ctypes.c_int32(), ctypes.c_int64()
-        _check(lib().dlo_block_schema(d, i, ctypes.byref(name), ctypes.byref(dt), ctypes.byref(n)))
+        _check(fn(d, i, ctypes.byref(name), ctypes.byref(dt), ctypes.byref(n)))
         out.append((name.value.decode(), DTYPE_NAMES[dt.value], n.value))
     return out
+
+
+def quantize_fp8(w_bf16):
+    """dlo_quantize_fp8 on a host array of bf16 bit patterns -> (E4M3 codes, float32 scale)."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    codes = np.empty(w.shape, dtype=np.uint8)
+    scale = ctypes.c_float()
+    _check(lib().dlo_quantize_fp8(w.ctypes.data_as(ctypes.c_void_p), w.size,
+                                  codes.ctypes.data_as(ctypes.c_void_p), ctypes.byref(scale)))
+    return codes, np.float32(scale.value)
 
 
 def kernel_names():
@@ -250,7 +268,7 @@ class Plan:
                 "n_groups": g, "dtype": [DTYPE_NAMES[bi.dtype[i]] for i in range(g)],
                 "numel": list(bi.numel[:g]), "shard": list(bi.shard[:g]),
                 "region": list(bi.region[:g]), "extent": bi.extent,
-                "copy_bytes": bi.copy_bytes, "is_dit": bool(bi.is_dit)}
+                "copy_bytes": bi.copy_bytes, "is_dit": bool(bi.is_dit), "fp8": bi.is_dit == 2}
 
     def param_offset(self, b, p):
         v = ctypes.c_int64()
@@ -405,6 +423,10 @@ def op_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, stream):
 
 def op_attention(qkv, ldqkv, T, H, dh, out, ldo, stream):
     _check(lib().dlo_op_attention(qkv, ldqkv, T, H, dh, out, ldo, stream))
+
+
+def op_dequant_fp8(codes, n, scale, out, stream):
+    _check(lib().dlo_op_dequant_fp8(codes, n, scale, out, stream))
 
 
 def op_digest(base, offsets, lengths, out, stream):

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -40,9 +41,34 @@ int ok() {
   return DLO_OK;
 }
 
-int64_t elt_bytes(int dtype) { return dtype == DLO_BF16 ? 2 : 4; }
+int64_t elt_bytes(int dtype) { return dtype == DLO_BF16 ? 2 : dtype == DLO_FP8_E4M3 ? 1 : 4; }
+bool known_dtype(int dtype) { return dtype == DLO_BF16 || dtype == DLO_F32 || dtype == DLO_FP8_E4M3; }
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// OCP FP8 E4M3 code nearest to x: ties to the even code, magnitudes of 448 and
+// above saturate to 448, NaN -> 0x7F.  Arithmetic on the exponent and the
+// 3-bit mantissa: every scaling by a power of two is exact, and nearbyintf
+// rounds ties to even in the default rounding mode.
+uint8_t e4m3_encode(float x) {
+  uint32_t bits;
+  std::memcpy(&bits, &x, 4);
+  const uint8_t sign = (uint8_t)((bits >> 24) & 0x80);
+  if (std::isnan(x)) return 0x7F;
+  const float a = std::fabs(x);
+  if (a >= 448.0f) return sign | 0x7E;
+  if (a < 0.015625f)  // below 2^-6: subnormal steps of 2^-9; 8 steps is the smallest normal
+    return sign | (uint8_t)std::nearbyintf(a * 512.0f);
+  int e2;
+  (void)std::frexp(a, &e2);  // a = f * 2^e2, f in [0.5, 1)
+  int E = e2 - 1;            // a in [2^E, 2^(E+1)), E in [-6, 8]
+  int m = (int)std::nearbyintf(std::ldexp(a, -E) * 8.0f) - 8;
+  if (m == 8) {
+    m = 0;
+    ++E;
+  }
+  return sign | (uint8_t)(((E + 7) << 3) | m);
+}
 
 // ---------------------------------------------------------------------------
 // DiT block schema (registration order)
@@ -67,10 +93,35 @@ const SchemaEntry kDit[DLO_DIT_N_PARAMS] = {
     {"mlp.fc1.weight", DLO_BF16, 4, 1, 0},  {"mlp.fc1.bias", DLO_F32, 4, 0, 0},
     {"mlp.fc2.weight", DLO_BF16, 1, 4, 0},  {"mlp.fc2.bias", DLO_F32, 1, 0, 0},
 };
+// FP8 form ([Doc] "Request and loading constraints": per-tensor online FP8
+// linears keep a 1-byte weight and an fp32 scale): each bf16 matrix becomes an
+// E4M3 matrix followed by its one-element scale.
+const SchemaEntry kDitFp8[DLO_DIT_FP8_N_PARAMS] = {
+    {"adaln.weight", DLO_FP8_E4M3, 6, 1, 0},    {"adaln.weight_scale", DLO_F32, 0, 0, 1},
+    {"adaln.bias", DLO_F32, 6, 0, 0},           {"norm1.weight", DLO_F32, 1, 0, 0},
+    {"norm1.bias", DLO_F32, 1, 0, 0},           {"norm1.eps", DLO_F32, 0, 0, 1},
+    {"attn.qkv.weight", DLO_FP8_E4M3, 3, 1, 0}, {"attn.qkv.weight_scale", DLO_F32, 0, 0, 1},
+    {"attn.qkv.bias", DLO_F32, 3, 0, 0},        {"attn.out.weight", DLO_FP8_E4M3, 1, 1, 0},
+    {"attn.out.weight_scale", DLO_F32, 0, 0, 1}, {"attn.out.bias", DLO_F32, 1, 0, 0},
+    {"norm2.weight", DLO_F32, 1, 0, 0},         {"norm2.bias", DLO_F32, 1, 0, 0},
+    {"norm2.eps", DLO_F32, 0, 0, 1},            {"mlp.fc1.weight", DLO_FP8_E4M3, 4, 1, 0},
+    {"mlp.fc1.weight_scale", DLO_F32, 0, 0, 1}, {"mlp.fc1.bias", DLO_F32, 4, 0, 0},
+    {"mlp.fc2.weight", DLO_FP8_E4M3, 1, 4, 0},  {"mlp.fc2.weight_scale", DLO_F32, 0, 0, 1},
+    {"mlp.fc2.bias", DLO_F32, 1, 0, 0},
+};
+// logical parameters of the block forward (indices into kDit)
 enum {
   P_ADA_W, P_ADA_B, P_N1_W, P_N1_B, P_N1_EPS, P_QKV_W, P_QKV_B, P_OUT_W, P_OUT_B, P_N2_W, P_N2_B,
   P_N2_EPS, P_FC1_W, P_FC1_B, P_FC2_W, P_FC2_B
 };
+// where each logical parameter sits in the FP8 schema
+const int kFp8Index[DLO_DIT_N_PARAMS] = {0, 2, 3, 4, 5, 6, 8, 9, 11, 12, 13, 14, 15, 17, 18, 20};
+// the five weights (ada, qkv, out, fc1, fc2): logical index, scale index in the
+// FP8 schema, and numel / d^2
+const int kWeightP[5] = {P_ADA_W, P_QKV_W, P_OUT_W, P_FC1_W, P_FC2_W};
+const int kFp8Scale[5] = {1, 7, 10, 16, 19};
+const int64_t kWeightD2[5] = {6, 3, 1, 4, 4};
+enum { KIND_NONE = 0, KIND_DIT = 1, KIND_DIT_FP8 = 2 };
 
 int64_t schema_numel(const SchemaEntry &e, int64_t d) {
   if (e.fixed > 0) return e.fixed;
@@ -78,7 +129,7 @@ int64_t schema_numel(const SchemaEntry &e, int64_t d) {
 }
 
 const char *kKernelNames[DLO_KERNELS_PER_BLOCK] = {
-    "adaln_gemv", "ln1_modulate", "gemm_qkv", "attention",
+    "dequant_fp8", "adaln_gemv", "ln1_modulate", "gemm_qkv", "attention",
     "gemm_out_residual", "ln2_modulate", "gemm_fc1_gelu", "gemm_fc2_residual"};
 
 }  // namespace
@@ -100,12 +151,14 @@ struct BlockPlan {
   int64_t gshard[DLO_MAX_GROUPS] = {0, 0};
   int64_t gregion[DLO_MAX_GROUPS] = {0, 0};
   int64_t extent = 0, copy_bytes = 0;
-  bool is_dit = false;
+  int kind = KIND_NONE;            // KIND_DIT: bf16 weights; KIND_DIT_FP8: E4M3 weights
 
   int64_t param_byte(int p) const {
     const int g = pgroup[p];
     return gregion[g] + poff[p] * elt_bytes(gdtype[g]);
   }
+  // slot byte offset of a logical parameter (P_*) of either schema
+  int64_t logical_byte(int lp) const { return param_byte(kind == KIND_DIT_FP8 ? kFp8Index[lp] : lp); }
 };
 
 struct dlo_run;
@@ -115,6 +168,7 @@ struct dlo_plan {
   std::vector<BlockPlan> blocks;
   int64_t slot_bytes = 0;
   int32_t max_d = 0;
+  int32_t max_fp8_d = 0;   // widest FP8 block (0: none)
   uint64_t id = 0;
   mutable std::mutex mu;
   mutable std::vector<dlo_run *> detached;   // runs started without a handle
@@ -322,10 +376,10 @@ void run_copies(std::vector<CopyTask> &tasks) {
   for (auto &t : th) t.join();
 }
 
-int64_t workspace_bytes_for(int32_t max_d, int64_t T) {
-  const int64_t d = max_d;
+int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d) {
+  const int64_t d = max_d, f = fp8_d;
   return align_up(4 * d, DLO_ALIGN) + align_up(24 * d, DLO_ALIGN) + align_up(2 * T * d, DLO_ALIGN) +
-         align_up(8 * T * d, DLO_ALIGN);
+         align_up(8 * T * d, DLO_ALIGN) + align_up(36 * f * f, DLO_ALIGN);
 }
 
 int validate_block_against(const BlockPlan &bp, const dlo_block &blk, int b, bool need_src) {
@@ -362,6 +416,51 @@ int dlo_block_schema(int32_t d, int32_t i, const char **name, int32_t *dtype, in
   return ok();
 }
 
+int dlo_block_schema_fp8(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel) {
+  if (i < 0 || i >= DLO_DIT_FP8_N_PARAMS || d < 1) return fail(DLO_E_ARG, "schema index out of range");
+  if (name) *name = kDitFp8[i].name;
+  if (dtype) *dtype = kDitFp8[i].dtype;
+  if (numel) *numel = schema_numel(kDitFp8[i], d);
+  return ok();
+}
+
+int dlo_quantize_fp8(const uint16_t *w, int64_t n, uint8_t *codes, float *scale) {
+  if (!scale || n < 0 || (n > 0 && (!w || !codes))) return fail(DLO_E_ARG, "bad arguments");
+  auto widen = [](uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+  };
+  // large tensors on up to 16 threads (a max and an elementwise map: the result
+  // does not depend on the split)
+  const int nt = (int)std::min<int64_t>(16, std::max<int64_t>(1, n >> 20));
+  const int64_t chunk = (n + nt - 1) / nt;
+  std::vector<float> part((size_t)nt, 0.f);
+  auto run = [&](auto &&fn) {
+    std::vector<std::thread> th;
+    for (int t = 1; t < nt; ++t) th.emplace_back(fn, t);
+    fn(0);
+    for (auto &x : th) x.join();
+  };
+  run([&](int t) {
+    float m = 0.f;
+    for (int64_t i = t * chunk; i < std::min(n, (t + 1) * chunk); ++i) {
+      const float a = std::fabs(widen(w[i]));
+      if (a > m) m = a;  // NaN never compares greater
+    }
+    part[(size_t)t] = m;
+  });
+  float amax = 0.f;
+  for (float m : part) amax = std::max(amax, m);
+  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  *scale = sc;
+  run([&](int t) {
+    for (int64_t i = t * chunk; i < std::min(n, (t + 1) * chunk); ++i) codes[i] = e4m3_encode(widen(w[i]) / sc);
+  });
+  return ok();
+}
+
 const char *dlo_kernel_name(int32_t j) {
   return (j >= 0 && j < DLO_KERNELS_PER_BLOCK) ? kKernelNames[j] : nullptr;
 }
@@ -394,7 +493,7 @@ int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_pl
         delete pl;
         return fail(DLO_E_ARG, "block %d parameter %d has no name", b, p);
       }
-      if (pr.dtype != DLO_BF16 && pr.dtype != DLO_F32) {
+      if (!known_dtype(pr.dtype)) {
         delete pl;
         return fail(DLO_E_ARG, "block %d parameter %s: unknown dtype %d", b, pr.name, pr.dtype);
       }
@@ -427,13 +526,19 @@ int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_pl
     }
     bp.extent = cursor;
     pl->slot_bytes = std::max(pl->slot_bytes, bp.extent);
-    // DiT schema?
-    bool dit = blk.n_params == DLO_DIT_N_PARAMS && bp.d > 0;
-    for (int p = 0; dit && p < DLO_DIT_N_PARAMS; ++p)
-      dit = bp.names[p] == kDit[p].name && bp.dtypes[p] == kDit[p].dtype &&
-            bp.numels[p] == schema_numel(kDit[p], bp.d);
-    bp.is_dit = dit;
+    // DiT schema, bf16 or FP8 form?
+    auto matches = [&](const SchemaEntry *sch, int np) {
+      bool ok_ = blk.n_params == np && bp.d > 0;
+      for (int p = 0; ok_ && p < np; ++p)
+        ok_ = bp.names[p] == sch[p].name && bp.dtypes[p] == sch[p].dtype &&
+              bp.numels[p] == schema_numel(sch[p], bp.d);
+      return ok_;
+    };
+    bp.kind = matches(kDit, DLO_DIT_N_PARAMS)          ? KIND_DIT
+              : matches(kDitFp8, DLO_DIT_FP8_N_PARAMS) ? KIND_DIT_FP8
+                                                       : KIND_NONE;
     pl->max_d = std::max(pl->max_d, bp.d);
+    if (bp.kind == KIND_DIT_FP8) pl->max_fp8_d = std::max(pl->max_fp8_d, bp.d);
   }
   pl->id = g_plan_ids++;
   *out = pl;
@@ -471,7 +576,7 @@ int dlo_plan_block_info(const dlo_plan *plan, int32_t b, dlo_block_info *out) {
   }
   out->extent = bp.extent;
   out->copy_bytes = bp.copy_bytes;
-  out->is_dit = bp.is_dit ? 1 : 0;
+  out->is_dit = bp.kind;
   return ok();
 }
 
@@ -490,7 +595,7 @@ int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens) {
     return -1;
   }
   g_err.clear();
-  return workspace_bytes_for(plan->max_d, tokens);
+  return workspace_bytes_for(plan->max_d, tokens, plan->max_fp8_d);
 }
 
 int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, int64_t cap,
@@ -803,7 +908,7 @@ namespace {
 
 struct Workspace {
   float *silu_c, *mod;
-  uint16_t *h, *big;
+  uint16_t *h, *big, *dq;
 };
 
 Workspace carve(void *ws, int32_t max_d, int64_t T) {
@@ -816,6 +921,8 @@ Workspace carve(void *ws, int32_t max_d, int64_t T) {
   w.h = reinterpret_cast<uint16_t *>(p);
   p += align_up(2 * T * max_d, DLO_ALIGN);
   w.big = reinterpret_cast<uint16_t *>(p);  // qkv [T,3d] then a [T,d]; later u [T,4d]
+  p += align_up(8 * T * max_d, DLO_ALIGN);
+  w.dq = reinterpret_cast<uint16_t *>(p);   // an FP8 block's weights, dequantised to bf16
   return w;
 }
 
@@ -824,36 +931,53 @@ Workspace carve(void *ws, int32_t max_d, int64_t T) {
 hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forward_args *a,
                          const Workspace &w, hipStream_t s, hipEvent_t *kernel_end) {
   const int d = bp.d, H = bp.heads, dh = d / H, T = a->tokens;
-  auto P = [&](int p) { return base + bp.param_byte(p); };
-  auto W = [&](int p) { return reinterpret_cast<const uint16_t *>(P(p)); };
-  auto F = [&](int p) { return reinterpret_cast<const float *>(P(p)); };
+  auto P = [&](int lp) { return base + bp.logical_byte(lp); };
+  auto F = [&](int lp) { return reinterpret_cast<const float *>(P(lp)); };
+  hipError_t e;
+  // bf16 weights: in the slot, or (FP8 block) dequantised into the workspace
+  const uint16_t *Wt[5];
+  if (bp.kind == KIND_DIT_FP8) {
+    uint16_t *dst = w.dq;
+    for (int i = 0; i < 5; ++i) {
+      const int64_t n = kWeightD2[i] * d * d;
+      const float *scale = reinterpret_cast<const float *>(base + bp.param_byte(kFp8Scale[i]));
+      if ((e = dlo::launch_dequant_fp8(reinterpret_cast<const uint8_t *>(P(kWeightP[i])), n, scale,
+                                       dst, s)) != hipSuccess)
+        return e;
+      Wt[i] = dst;
+      dst += n;
+    }
+  } else {
+    for (int i = 0; i < 5; ++i) Wt[i] = reinterpret_cast<const uint16_t *>(P(kWeightP[i]));
+  }
+  if (kernel_end && (e = hipEventRecord(kernel_end[0], s)) != hipSuccess) return e;
   float *x = a->x;
   const int64_t ldx = a->x_row_stride;
   const float *mod = w.mod;
   uint16_t *qkv = w.big;
   uint16_t *attn = w.big + (int64_t)T * 3 * d;
   uint16_t *u = w.big;
-  hipError_t e;
 #define DLO_STEP(call, j)                                                   \
   if ((e = (call)) != hipSuccess) return e;                                 \
   if (kernel_end && (e = hipEventRecord(kernel_end[j], s)) != hipSuccess) return e;
-  DLO_STEP(dlo::launch_adaln_gemv(W(P_ADA_W), w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 0)
+  DLO_STEP(dlo::launch_adaln_gemv(Wt[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 1)
   DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N1_W), F(P_N1_B), F(P_N1_EPS), mod + 0 * d,
-                                   mod + 1 * d, w.h, s), 1)
-  DLO_STEP(dlo::launch_gemm(w.h, d, W(P_QKV_W), d, T, 3 * d, d, F(P_QKV_B), nullptr, qkv, 3 * d,
-                            dlo::EPI_BIAS, s), 2)
-  DLO_STEP(dlo::launch_attention(qkv, 3 * d, T, H, dh, attn, d, s), 3)
-  DLO_STEP(dlo::launch_gemm(attn, d, W(P_OUT_W), d, T, d, d, F(P_OUT_B), mod + 2 * d, x, ldx,
-                            dlo::EPI_GATED_RESIDUAL, s), 4)
+                                   mod + 1 * d, w.h, s), 2)
+  DLO_STEP(dlo::launch_gemm(w.h, d, Wt[1], d, T, 3 * d, d, F(P_QKV_B), nullptr, qkv, 3 * d,
+                            dlo::EPI_BIAS, s), 3)
+  DLO_STEP(dlo::launch_attention(qkv, 3 * d, T, H, dh, attn, d, s), 4)
+  DLO_STEP(dlo::launch_gemm(attn, d, Wt[2], d, T, d, d, F(P_OUT_B), mod + 2 * d, x, ldx,
+                            dlo::EPI_GATED_RESIDUAL, s), 5)
   DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N2_W), F(P_N2_B), F(P_N2_EPS), mod + 3 * d,
-                                   mod + 4 * d, w.h, s), 5)
-  DLO_STEP(dlo::launch_gemm(w.h, d, W(P_FC1_W), d, T, 4 * d, d, F(P_FC1_B), nullptr, u, 4 * d,
-                            dlo::EPI_BIAS_GELU, s), 6)
-  DLO_STEP(dlo::launch_gemm(u, 4 * d, W(P_FC2_W), 4 * d, T, d, 4 * d, F(P_FC2_B), mod + 5 * d, x,
-                            ldx, dlo::EPI_GATED_RESIDUAL, s), 7)
+                                   mod + 4 * d, w.h, s), 6)
+  DLO_STEP(dlo::launch_gemm(w.h, d, Wt[3], d, T, 4 * d, d, F(P_FC1_B), nullptr, u, 4 * d,
+                            dlo::EPI_BIAS_GELU, s), 7)
+  DLO_STEP(dlo::launch_gemm(u, 4 * d, Wt[4], 4 * d, T, d, 4 * d, F(P_FC2_B), mod + 5 * d, x,
+                            ldx, dlo::EPI_GATED_RESIDUAL, s), 8)
 #undef DLO_STEP
   return hipSuccess;
 }
+
 
 int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dlo_forward_args *a) {
   if (!plan || !a) return fail(DLO_E_ARG, "NULL plan or args");
@@ -878,7 +1002,8 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
     return fail(DLO_E_ARG, "copy_stream must be non-NULL and distinct from compute_stream");
   for (size_t b = 0; b < plan->blocks.size(); ++b) {
     const BlockPlan &bp = plan->blocks[b];
-    if (!bp.is_dit) return fail(DLO_E_UNSUPPORTED, "block %zu does not carry the DiT block schema", b);
+    if (bp.kind == KIND_NONE)
+      return fail(DLO_E_UNSUPPORTED, "block %zu does not carry the DiT block schema (bf16 or FP8)", b);
     if (bp.d % 256 || bp.d > 8192)
       return fail(DLO_E_UNSUPPORTED, "block %zu: d = %d (need a multiple of 256, at most 8192)", b, bp.d);
     if (bp.heads < 1 || bp.d % bp.heads)
@@ -894,7 +1019,7 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
     return fail(DLO_E_UNSUPPORTED, "x_row_stride too large for 32-bit tile offsets");
   if (((int64_t)a->tokens + 64) * 3 * plan->max_d * 2 >= ((int64_t)1 << 31))
     return fail(DLO_E_UNSUPPORTED, "tokens x 3 d too large for 32-bit buffer offsets");
-  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens);
+  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens, plan->max_fp8_d);
   if (a->workspace_bytes < need)
     return fail(DLO_E_WORKSPACE, "workspace %lld < %lld bytes", (long long)a->workspace_bytes, (long long)need);
   if (!resident) {
@@ -1164,6 +1289,15 @@ int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t H, i
     return fail(DLO_E_UNSUPPORTED, "attention: T * ldqkv too large for 32-bit buffer offsets");
   int rc = check_hip(dlo::launch_attention(qkv, ldqkv, T, H, dh, out, ldo, (hipStream_t)stream),
                      "attention");
+  return rc ? rc : ok();
+}
+
+int dlo_op_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
+                       void *stream) {
+  if (!codes || !scale || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (n < 0 || n % 16 || (uintptr_t)codes % 16 || (uintptr_t)out % 32)
+    return fail(DLO_E_UNSUPPORTED, "dequant: n %% 16 == 0, codes 16-B and out 32-B aligned required");
+  int rc = check_hip(dlo::launch_dequant_fp8(codes, n, scale, out, (hipStream_t)stream), "dequant_fp8");
   return rc ? rc : ok();
 }
 

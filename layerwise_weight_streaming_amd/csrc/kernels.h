@@ -28,6 +28,11 @@ hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_
 hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, int T, int H, int dh,
                             uint16_t *out, int64_t ldo, hipStream_t s);
 
+// out[i] = bf16_rne(e4m3_value(codes[i]) * *scale), i < n; n % 16 == 0, codes 16-B
+// and out 32-B aligned
+hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
+                              hipStream_t s);
+
 // *out = digest of the regions (base + offsets[i], lengths[i]); offsets multiples of 8
 hipError_t launch_digest(const void *base, const int64_t *offsets, const int64_t *lengths,
                          int n, uint64_t *out, hipStream_t s);

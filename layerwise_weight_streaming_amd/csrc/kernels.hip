@@ -149,8 +149,45 @@ hipError_t ln_launch(const float *x, int64_t ldx, int T, int d, const float *gam
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// FP8 weights: E4M3 codes -> bf16(code value * scale).  gfx950's
+// v_cvt_pk_f32_fp8 decodes OCP E4M3 exactly to fp32; one fp32 multiply and a
+// round-to-nearest-even to bf16 follow.  16 codes per thread: one 16-B load,
+// two 16-B stores.
+// ---------------------------------------------------------------------------
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint32_t *__restrict__ codes,
+                                                          const float *__restrict__ scale,
+                                                          u32x4 *__restrict__ out, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const float sc = *scale;
+  const u32x4 w = *reinterpret_cast<const u32x4 *>(codes + 4 * i);
+  uint32_t o[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);  // bytes 0, 1
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);   // bytes 2, 3
+    o[2 * k] = (uint32_t)f32_to_bf16(lo[0] * sc) | ((uint32_t)f32_to_bf16(lo[1] * sc) << 16);
+    o[2 * k + 1] = (uint32_t)f32_to_bf16(hi[0] * sc) | ((uint32_t)f32_to_bf16(hi[1] * sc) << 16);
+  }
+  out[2 * i] = u32x4{o[0], o[1], o[2], o[3]};
+  out[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 }  // namespace
 
+hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
+                              hipStream_t s) {
+  const int64_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = (n16 + 255) / 256;
+  hipLaunchKernelGGL(dequant_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t *>(codes), scale, reinterpret_cast<u32x4 *>(out), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_silu(const float *c, float *out, int n, hipStream_t s) {
   hipLaunchKernelGGL(silu_kernel, dim3((n + 255) / 256), dim3(256), 0, s, c, out, n);

@@ -79,7 +79,7 @@ def encode_e4m3(x) -> np.ndarray:
 def tensor_scale(w_bf16_bits: np.ndarray) -> np.float32:
     """Per-tensor scale amax / 448 in float32 (1.0 if the tensor is all zero)."""
     w = (np.asarray(w_bf16_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
-    amax = np.float32(np.max(np.abs(w))) if w.size else np.float32(0)
+    amax = np.float32(np.nanmax(np.abs(w))) if w.size else np.float32(0)   # NaN entries ignored
     if amax == 0:
         return np.float32(1.0)
     return np.float32(amax / np.float32(E4M3_MAX))

@@ -54,3 +54,39 @@ def make_runner(w, stack, k=None, pinned=True):
     r.pack(0, stack_blocks(w, stack))
     r.set_inputs(stack.x, stack.c)
     return r
+
+
+def fp8_blocks(w, stack, which=None):
+    """Per block, the FP8 parameter list made by libdlo's quantizer (checked equal,
+    byte for byte, to the oracle's).  which: block indices to quantize (default all);
+    the others keep their bf16 lists."""
+    from oracle import fp8 as ofp8
+    import layerwise_weight_streaming_amd as dlo
+    out = []
+    for b, ps in enumerate(stack.blocks):
+        if which is not None and b not in which:
+            out.append(ps)
+            continue
+        ref = ofp8.quantize_block(ps)
+        got = []
+        for name, dt, arr in ps:
+            if dt == "bf16":
+                codes, scale = dlo.quantize_fp8(arr)
+                got.append((name, "fp8", codes))
+                got.append((name + "_scale", "f32", np.array([scale], dtype=np.float32)))
+            else:
+                got.append((name, dt, arr))
+        assert [(n, d) for n, d, _ in got] == [(n, d) for n, d, _ in ref]
+        for (_, _, a), (_, _, b2) in zip(got, ref):
+            assert a.tobytes() == b2.tobytes()
+        out.append(got)
+    return out
+
+
+def make_runner_params(w, blocks, k=None, pinned=True):
+    """A runner over explicit per-block parameter lists (any schema form)."""
+    from layerwise_weight_streaming_amd.runner import StackRunner
+    specs = [(w.width(b), w.heads(b), [(nm, dt, int(a.size)) for nm, dt, a in ps]) for b, ps in enumerate(blocks)]
+    r = StackRunner(specs, w.k if k is None else k, w.tokens, w.D, pinned=pinned)
+    r.pack(0, [(w.width(b), w.heads(b), ps) for b, ps in enumerate(blocks)])
+    return r

@@ -183,3 +183,39 @@ def test_digest_matches_oracle_definition():
         got = int(out.cpu().numpy().view(np.uint64)[0])
         want = op.digest_regions([(o, buf[o:o + n]) for o, n in zip(offs, lens)])
         assert got == want
+
+
+def _bf16_rne(x32):
+    """float32 -> bf16 bit pattern, round to nearest even (finite inputs)."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0371, 3.5e-5])
+def test_dequant_fp8_every_code(scale):
+    """All 256 E4M3 codes: the kernel's bf16(value * scale) equals the oracle's code
+    value times the scale in float32, rounded to nearest even; NaN codes give NaN."""
+    torch = require_gpu()
+    from oracle import fp8
+    codes = np.tile(np.arange(256, dtype=np.uint8), 24)              # 6144 codes
+    dc = torch.from_numpy(codes).cuda()
+    ds = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    out = torch.empty(codes.size, dtype=torch.int16, device="cuda")
+    dlo.op_dequant_fp8(dc.data_ptr(), codes.size, ds.data_ptr(), out.data_ptr(), 0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    vals = fp8.DECODE[codes]
+    nan = np.isnan(vals)
+    want = _bf16_rne(vals[~nan].astype(np.float32) * np.float32(scale))
+    assert np.array_equal(got[~nan], want)
+    gotf = (got[nan].astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isnan(gotf))
+
+
+def test_dequant_fp8_rejects_misaligned_sizes():
+    torch = require_gpu()
+    c = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    s_ = torch.ones(1, device="cuda")
+    o = torch.empty(64, dtype=torch.int16, device="cuda")
+    with pytest.raises(dlo.DLOError):
+        dlo.op_dequant_fp8(c.data_ptr(), 63, s_.data_ptr(), o.data_ptr(), 0)

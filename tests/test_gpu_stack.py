@@ -18,7 +18,8 @@ import layerwise_weight_streaming_amd as dlo
 from oracle import forward as of
 from oracle import plan as op
 from oracle import schedule as sc
-from tests.gpu_util import TOL, make_runner, rel_err, require_gpu, say, spec_blocks
+from tests.gpu_util import (TOL, fp8_blocks, make_runner, make_runner_params, rel_err, require_gpu,
+                            say, spec_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -244,4 +245,49 @@ def test_resident_layers_match_full_streaming(n_resident):
     r.forward(1, n_resident=n_resident, want_run=False)
     r.forward(w.passes - 1, n_resident=n_resident, want_run=False)
     assert np.array_equal(r.x_host().view(np.uint32), x_stream.view(np.uint32))
+    r.close()
+
+
+def _regions_of(blocks, k):
+    regs = []
+    for ps in blocks:
+        bp = op.plan_block(op.specs_of(ps), k)
+        regs.append(op.slot_regions(bp, op.pack_block(ps, bp)))
+    return regs
+
+
+@pytest.mark.parametrize("name,n_blocks,tokens,which", [
+    ("tiny", None, None, None),                 # every block FP8, 2 passes, odd count
+    ("8blk", None, None, {0, 2, 3, 5}),         # FP8 and bf16 blocks mixed in one plan
+    ("irregular", 3, 256, None),                # widths 2048/3072/4096, k = 4 (uneven fp32 padding)
+])
+def test_fp8_weight_groups_streamed(name, n_blocks, tokens, which):
+    """FP8 (E4M3 + fp32 scale) blocks: 1-byte groups sharded, streamed and placed at the
+    all-gather offsets (slot bytes and digests = oracle), forward within tolerance of the
+    oracle on the dequantised weights, and streamed == resident bit for bit."""
+    torch = require_gpu()
+    w = synth.WORKLOADS[name]
+    if tokens is not None:
+        w = w.with_(tokens=tokens)
+    n = w.n_blocks if n_blocks is None else n_blocks
+    say(f"fp8 stack {name} n={n} T={w.tokens} which={which}")
+    stack = synth.make_stack(w, 21, n)
+    blocks = fp8_blocks(w, stack, which)
+    r = make_runner_params(w, blocks)
+    for b in range(n):
+        assert r.plan.block_info(b)["fp8"] == (which is None or b in which)
+    r.set_inputs(stack.x, stack.c)
+    run = r.forward(w.passes, flags=dlo.TRACE_DIGEST)
+    tr = run.trace()
+    regs = _regions_of(blocks, w.k)
+    _check_trace(tr, n, w.passes, regs)
+    x_gpu = r.x_host()
+    say("oracle forward (dequantised weights)")
+    x_ref = of.forward_stack(stack.x, stack.c, blocks, [w.heads(b) for b in range(n)], w.passes)
+    e_abs, e_upd = rel_err(x_gpu, x_ref), rel_err(x_gpu - stack.x, x_ref - stack.x)
+    say(f"rel err {e_abs:.3e}, update rel err {e_upd:.3e}")
+    assert e_abs <= TOL and e_upd <= TOL
+    r.set_inputs(stack.x, stack.c)
+    r.forward(w.passes, resident=True, want_run=False)
+    assert np.array_equal(r.x_host().view(np.uint32), x_gpu.view(np.uint32))
     r.close()

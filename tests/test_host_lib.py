@@ -78,10 +78,12 @@ def test_plan_matches_oracle_on_workloads(name):
 def _random_params(rng, n):
     out = []
     for i in range(n):
-        dt = rng.choice(["bf16", "f32"])
+        dt = rng.choice(["bf16", "f32", "fp8"])
         numel = rng.choice([0, 1, 3, 7, 64, 255, rng.randint(0, 3000)])
         if dt == "bf16":
             a = np.frombuffer(rng.randbytes(2 * numel), dtype=np.uint16).copy()
+        elif dt == "fp8":
+            a = np.frombuffer(rng.randbytes(numel), dtype=np.uint8).copy()
         else:
             a = np.array([rng.uniform(-3, 3) for _ in range(numel)], dtype=np.float32)
         out.append((f"p{i}", dt, a))
@@ -312,3 +314,79 @@ def test_op_validation_errors():
     assert _status(dlo.op_attention, 1, 3 * 4 * 32, 10, 4, 32, 1, 128, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_ln_modulate, 1, 300, 4, 300, 1, 1, 1, 1, 1, 1, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_digest, 1, [3], [8], 1, 0) == "DLO_E_ARG"
+
+
+# ---------------------------------------------------------------------------
+# FP8 weight groups
+# ---------------------------------------------------------------------------
+
+def _bf16(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_quantizer_matches_oracle_byte_for_byte():
+    from oracle import fp8
+    rng = np.random.default_rng(5)
+    cases = [
+        _bf16(rng.normal(0, 0.02, 5000)),
+        _bf16(rng.normal(0, 0.5, 3_000_001)),                                    # threaded path
+        _bf16(rng.normal(0, 1.0, 4096) * np.exp(rng.uniform(-12, 12, 4096))),   # wide dynamic range
+        _bf16(np.array([0.0, -0.0, 1e-30, -3e-38, 448.0, 1.0, -1.0, 65504.0])),
+        np.frombuffer(rng.bytes(2 * 3000), dtype=np.uint16).copy(),              # any bf16 bits
+        np.zeros(17, np.uint16),
+        np.zeros(0, np.uint16),
+    ]
+    for w in cases:
+        finite = np.isfinite((w.astype(np.uint32) << 16).view(np.float32))
+        if not finite.all():    # weights are finite; NaN/inf bit patterns go separately below
+            w = w[finite]
+        codes, scale = dlo.quantize_fp8(w)
+        ocodes, oscale = fp8.quantize_tensor(w)
+        assert scale == oscale
+        assert codes.tobytes() == ocodes.tobytes()
+    # NaN entries are ignored by the scale and encode as 0x7F
+    w = np.concatenate([_bf16(rng.normal(0, 1, 100)), np.array([0x7FC0], np.uint16)])
+    codes, scale = dlo.quantize_fp8(w)
+    ocodes, oscale = fp8.quantize_tensor(w)
+    assert scale == oscale and codes.tobytes() == ocodes.tobytes() and codes[-1] == 0x7F
+
+
+def test_fp8_schema_matches_the_oracle_block_form():
+    from oracle import fp8
+    for d in (256, 1024, 5120):
+        ps = synth.block_params(0, 0, 256) if d == 256 else None
+        sch = dlo.block_schema(d, fp8=True)
+        assert len(sch) == 21
+        bf = dlo.block_schema(d)
+        names = [n for n, _, _ in sch]
+        for n, dt, numel in bf:
+            i = names.index(n)
+            assert sch[i][2] == numel and sch[i][1] == ("fp8" if dt == "bf16" else dt)
+            if dt == "bf16":
+                assert sch[i + 1] == (n + "_scale", "f32", 1)
+        if ps is not None:
+            q = fp8.quantize_block(ps)
+            assert [(n, dt, int(a.size)) for n, dt, a in q] == sch
+
+
+def test_fp8_block_plan_pack_and_workspace():
+    from oracle import fp8
+    d, k = 256, 4
+    q = fp8.quantize_block(synth.block_params(1, 0, d))
+    p = dlo.Plan([(d, 4, q), (d, 4, synth.block_params(1, 1, d))], k)
+    info = p.block_info(0)
+    assert info["fp8"] and info["is_dit"] and info["dtype"] == ["fp8", "f32"]
+    assert info["numel"] == [18 * d * d, 19 * d + 7]
+    assert not p.block_info(1)["fp8"] and p.block_info(1)["is_dit"]
+    bp = op.plan_block(op.specs_of(q), k)
+    assert info["extent"] == bp.extent and info["region"] == [g.region for g in bp.groups]
+    assert info["copy_bytes"] * 2 < p.block_info(1)["copy_bytes"] * 1.01   # about half the bytes
+    st = dlo.HostStore(p, pinned=False)
+    st.pack(0, [(d, 4, q), (d, 4, synth.block_params(1, 1, d))])
+    sh = op.pack_block(q, bp)
+    for g in range(2):
+        for r in range(k):
+            assert st.shard(0, g, r).tobytes() == sh[g][r].tobytes()
+    # the workspace grows by the widest FP8 block's bf16 weights
+    p_bf = dlo.Plan([(d, 4, synth.block_params(1, 1, d))], k)
+    assert p.workspace_bytes(64) - p_bf.workspace_bytes(64) == 36 * d * d
