@@ -211,8 +211,9 @@ int32_t dlo_host_store_complete(const dlo_host_store *store);
  *   if t is not the last step:  [t >= 1: WAIT(copy, COMPUTED[s'])]
  *                               COPY(next block -> s'), RECORD(copy, COPIED[s'])
  * where s' = 1 - s: the copy into s' waits for step t-1, the last reader of s'.
- * COPY issues 2k hipMemcpyAsync calls (k shards per dtype group) to
- * slot + region_g + r * S_g * elt_g.
+ * COPY places the k shards of every dtype group at slot + region_g + r * S_g * elt_g
+ * with hipMemcpyAsync, one call per run of shards whose host bytes are adjacent
+ * (at most k calls per group).
  * ------------------------------------------------------------------------- */
 
 enum { DLO_OP_COPY = 0, DLO_OP_COMPUTE = 1, DLO_OP_RECORD = 2, DLO_OP_WAIT = 3 };

@@ -831,11 +831,18 @@ hipError_t place_from(const dlo_plan *plan, int b, const void *(*src)(const dlo_
   for (int g = 0; g < bp.n_groups; ++g) {
     const int64_t sb = bp.gshard[g] * elt_bytes(bp.gdtype[g]);
     if (sb == 0) continue;
-    for (int r = 0; r < plan->k; ++r) {
+    // shard r goes to region_g + r * sb; consecutive shards whose host bytes are
+    // also consecutive move in one DMA (the same bytes to the same offsets)
+    for (int r = 0; r < plan->k;) {
       const int64_t off = bp.gregion[g] + r * sb;
-      hipError_t e = hipMemcpyAsync(dst + off, src(st, staging, b, g, r, off), (size_t)sb,
-                                    hipMemcpyHostToDevice, s);
+      const char *from = static_cast<const char *>(src(st, staging, b, g, r, off));
+      int r2 = r + 1;
+      while (r2 < plan->k &&
+             static_cast<const char *>(src(st, staging, b, g, r2, bp.gregion[g] + r2 * sb)) == from + (r2 - r) * sb)
+        ++r2;
+      hipError_t e = hipMemcpyAsync(dst + off, from, (size_t)((r2 - r) * sb), hipMemcpyHostToDevice, s);
       if (e != hipSuccess) return e;
+      r = r2;
     }
   }
   return hipSuccess;
