@@ -25,9 +25,10 @@ namespace {
 //
 // Software pipeline: block j's scores are computed one iteration ahead, so
 // while the MFMAs of S_{j+1} = K_{j+1} Q^T run, the same wave takes the softmax
-// of block j on the VALU (max, exp2, bf16 packing); then O^T += V_j^T P_j^T,
-// with the row sums of P_j taken by v_dot2 (on the bf16 P the MFMA uses) in the
-// shadow of those MFMAs.  One barrier per block; every load has a whole block
+// statistics of block j and the P of its first 32 keys on the VALU (max,
+// exp2, bf16 packing); then O^T += V_j^T P_j^T, with the second half's P and
+// the row sums of P_j (v_dot2 on the bf16 P the MFMA uses) in the shadow of
+// those MFMAs.  One barrier per block; every load has a whole block
 // of compute to land in.
 //
 // Softmax in base 2 on raw scores s: p = exp2(s * c - m * c), c = log2(e)/sqrt(dh).
@@ -192,12 +193,13 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
     m_run = m_new;
     const float mc = m_new * scale_log2;
+    // P of the first 32-key half here; the second half's exp2 work moves to
+    // phase B, under the PV MFMAs of the first half (1.2 % faster than all of
+    // it here: phase A was VALU-bound, phase B MFMA-bound)
     bf16x8 pf[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], scale_log2, -mc));
+    for (int r = 0; r < 16; ++r)
+      pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][r], scale_log2, -mc));
 
     qk(Kn, sn);  // next block's scores (unused after the last block)
     // interleave the 16 MFMAs with the K operand reads (two ahead) and the
@@ -207,11 +209,11 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
     }
-    // P_j is complete here, ahead of the rescale branch (keeps the exp2 work in
-    // this block, next to the MFMAs it overlaps)
-    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
+    // the first half's P is complete here, ahead of the rescale branch (keeps
+    // its exp2 work in this block, next to the MFMAs it overlaps)
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
 
     if (need) {
 #pragma unroll
@@ -220,7 +222,11 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     }
 
-    // O^T += V^T P^T over the four 16-key chunks; row sums of P on the VALU
+    // O^T += V^T P^T over the four 16-key chunks; the second half's P and the
+    // row sums of P on the VALU meanwhile
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      pf[2 + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][r], scale_log2, -mc));
     float ls = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
