@@ -87,6 +87,13 @@ def test_tiny_stack_three_passes_odd_tail():
     _run_and_compare("tiny", passes=3, seed=5)
 
 
+@pytest.mark.parametrize("tokens", [1, 129])
+def test_tiny_stack_ragged_token_counts(tokens):
+    # one token (attention over a single key) and a count that leaves partial
+    # 64-key blocks, 128-row LN/attention tiles and 256-row GEMM tiles
+    _run_and_compare("tiny", passes=3, seed=8, tokens=tokens)
+
+
 def test_8blk_stack_streamed():
     _run_and_compare("8blk")
 
