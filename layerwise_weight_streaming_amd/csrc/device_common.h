@@ -82,6 +82,15 @@ __device__ __forceinline__ void dl_load(i32x4 rsrc, uint32_t lds_base, int voff)
                : "memory");
 }
 
+// as dl_load, with a wave-uniform byte offset soff added by the buffer unit
+// (the per-lane offset stays loop-invariant)
+__device__ __forceinline__ void dl_load_so(i32x4 rsrc, uint32_t lds_base, int voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+               :
+               : "v"(voff), "s"(lds_base), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
 // s_waitcnt vmcnt(N) then s_barrier (N an immediate)
 template <int N>
 __device__ __forceinline__ void vmcnt_barrier() {

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -199,17 +201,21 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     b_voff[i] = (r * (int)ldb + ((lane & 3) ^ dl_swz(r)) * 8) * 2;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&smem[0];
-  auto issue = [&](int kt) {
-    const uint32_t sbase = lds0 + (uint32_t)((kt % STAGES) * STAGE * 2);
+  // loads of k-tile kt into stage S (a compile-time constant): per-lane
+  // offsets fixed, the k offset in the buffer instruction's scalar offset
+  auto issue = [&](int kt, auto st_c) {
+    constexpr int S = decltype(st_c)::value;
+    const uint32_t sbase = lds0 + (uint32_t)(S * STAGE * 2);
+    const uint32_t koff = __builtin_amdgcn_readfirstlane(kt * DL_BK * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      dl_load(a_rsrc, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((grp * 8 + wq * 2 + i) * 1024)),
-              a_voff[i] + kt * DL_BK * 2);
+      dl_load_so(a_rsrc, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((grp * 8 + wq * 2 + i) * 1024)),
+                 a_voff[i], koff);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      dl_load(b_rsrc,
-              __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(DL_TILE * 2 + (grp * 8 + wq * 2 + i) * 1024)),
-              b_voff[i] + kt * DL_BK * 2);
+      dl_load_so(b_rsrc,
+                 __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(DL_TILE * 2 + (grp * 8 + wq * 2 + i) * 1024)),
+                 b_voff[i], koff);
   };
 
   f32x16 acc[4][NJ];
@@ -227,17 +233,26 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   struct Frags {
     bf16x8 a[2][4], b[2][NJ];
   };
-  auto read_tile = [&](int st, Frags &f) {
-    const uint16_t *As = smem + st * STAGE;
-    const uint16_t *Bs = As + DL_TILE;
+  // fragment byte offsets inside a stage: the XOR swizzle depends on row bits
+  // 1..3 only, so rows 32 apart share it and the 32-row steps are immediates
+  const char *lds_bytes = reinterpret_cast<const char *>(&smem[0]);
+  int a_lane[2], b_lane[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    a_lane[kk] = dl_lds_off(wm * 128 + frow, kk * 2 + fk) * 2;
+    b_lane[kk] = (DL_TILE + dl_lds_off(wn * 64 + frow, kk * 2 + fk)) * 2;
+  }
+  auto read_tile = [&](auto st_c, Frags &f) {
+    constexpr int S = decltype(st_c)::value;
+    const char *base = lds_bytes + S * STAGE * 2;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        f.a[kk][i] = *reinterpret_cast<const bf16x8 *>(&As[dl_lds_off(wm * 128 + i * 32 + frow, kk * 2 + fk)]);
+        f.a[kk][i] = *reinterpret_cast<const bf16x8 *>(base + a_lane[kk] + i * 32 * DL_BK * 2);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        f.b[kk][j] = *reinterpret_cast<const bf16x8 *>(&Bs[dl_lds_off(wn * 64 + j * 32 + frow, kk * 2 + fk)]);
+        f.b[kk][j] = *reinterpret_cast<const bf16x8 *>(base + b_lane[kk] + j * 32 * DL_BK * 2);
     }
   };
   auto drained = [&](const Frags &f) {
@@ -276,24 +291,32 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-#pragma unroll
-  for (int t = 0; t < 3; ++t)
-    if (t < nk) issue(t);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (0 < nk) issue(0, I0{});
+  if (1 < nk) issue(1, I1{});
+  if (2 < nk) issue(2, I2{});
   Frags f0, f1;
-  auto step = [&](int s, Frags &f) {
+  // k-tile s in stage S = s % 4 (compile-time: the loop is unrolled by the ring depth)
+  auto step = [&](int s, auto st_c, Frags &f) {
+    constexpr int S = decltype(st_c)::value;
     const int pm = 2 * s + grp;  // this wave's memory phase
     phase_barrier(pm);
-    if (s + 3 < nk) issue(s + 3);
-    read_tile(s % STAGES, f);
+    if (s + 3 < nk) issue(s + 3, std::integral_constant<int, (S + 3) % STAGES>{});
+    read_tile(st_c, f);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     drained(f);
     phase_barrier(pm + 1);
     compute(f);
   };
   if (grp == 1) phase_barrier(0);
-  for (int s = 0; s < nk; s += 2) {
-    step(s, f0);
-    if (s + 1 < nk) step(s + 1, f1);
+  for (int s = 0; s < nk; s += 4) {
+    step(s, I0{}, f0);
+    if (s + 1 < nk) step(s + 1, I1{}, f1);
+    if (s + 2 < nk) step(s + 2, I2{}, f0);
+    if (s + 3 < nk) step(s + 3, I3{}, f1);
   }
   if (grp == 0) phase_barrier(2 * nk);
 
