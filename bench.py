@@ -39,7 +39,7 @@ def kernel_work(name, d, T, fp8=False):
         return (6 * d * d * 2 + 6 * d * 4 * 2 + d * 4) / 1e9, "GB", "hbm"
     if name in ("ln1_modulate", "ln2_modulate"):
         return (T * d * 4 + T * d * 2) / 1e9, "GB", "hbm"
-    flops = {"gemm_qkv": 2 * T * d * 3 * d, "attention": 4 * T * T * d,
+    flops = {"gemm_qk": 2 * T * d * 2 * d, "gemm_v_t": 2 * T * d * d, "attention": 4 * T * T * d,
              "gemm_out_residual": 2 * T * d * d, "gemm_fc1_gelu": 8 * T * d * d,
              "gemm_fc2_residual": 8 * T * d * d}[name]
     return flops / 1e12, "TFLOP", "mfma"
@@ -48,7 +48,8 @@ def kernel_work(name, d, T, fp8=False):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dit_block_kernels_super_hbm_traffic.md")
 CSRC = os.path.join(ROOT, "layerwise_weight_streaming_amd", "csrc")
 TRAFFIC_KEY = {"adaln_gemv": "adaln_gemv", "ln1_modulate": "ln1", "ln2_modulate": "ln1",
-               "gemm_qkv": "gemm_qkv", "attention": "attention", "gemm_out_residual": "gemm_out",
+               "gemm_qk": "gemm_qk", "gemm_v_t": "gemm_v_t", "attention": "attention",
+               "gemm_out_residual": "gemm_out",
                "gemm_fc1_gelu": "gemm_fc1", "gemm_fc2_residual": "gemm_fc2"}
 
 

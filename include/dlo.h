@@ -338,8 +338,10 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
 
 /* DLO_TRACE_TIMING: per step, the duration in ms of each of the block's kernels in
  * launch order (DLO_KERNELS_PER_BLOCK per step), after the run completed.  Entry 0
- * is the FP8 weight dequantisation (0 for a bf16 block). */
-#define DLO_KERNELS_PER_BLOCK 9
+ * is the FP8 weight dequantisation (0 for a bf16 block); then adaln_gemv,
+ * ln1_modulate, gemm_qkv, v_transpose, attention, gemm_out, ln2_modulate,
+ * gemm_fc1, gemm_fc2 (dlo_kernel_name). */
+#define DLO_KERNELS_PER_BLOCK 10
 int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
 /* name of kernel j (0 <= j < DLO_KERNELS_PER_BLOCK) of a block forward */
 const char *dlo_kernel_name(int32_t j);
@@ -401,19 +403,38 @@ int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const 
  *   epilogue 0: C bf16 [M, N] (ldc)
  *   epilogue 1: C bf16 = GELU_erf(A B^T + bias)
  *   epilogue 2: X fp32 (ldc) += gate[n] * (A B^T + bias)  (C points at X)
+ *   epilogue 3: C bf16 [N, ldc] = (A B^T + bias)^T, i.e. C[n, m]; columns m in
+ *               [M, M64) (M rounded up to 64) are 0, columns from M64 on are
+ *               not written; ldc >= M64 and ldc % 8 == 0.  The block computes
+ *               its v part this way, in the layout dlo_op_attention reads.
  * N % 256 == 0, K % 64 == 0, M >= 1; lda, ldb multiples of 8; C, bias and gate
  * 16-B aligned and ldc % 4 == 0 (else DLO_E_UNSUPPORTED). */
-enum { DLO_EPI_BIAS = 0, DLO_EPI_BIAS_GELU = 1, DLO_EPI_GATED_RESIDUAL = 2 };
+enum { DLO_EPI_BIAS = 0, DLO_EPI_BIAS_GELU = 1, DLO_EPI_GATED_RESIDUAL = 2, DLO_EPI_BIAS_T = 3 };
 int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int32_t M,
                 int32_t N, int32_t K, const float *bias, const float *gate, void *C, int64_t ldc,
                 int32_t epilogue, void *stream);
 
-/* Per head j < H: out[:, j*dh:(j+1)*dh] = softmax(q_j k_j^T / sqrt(dh)) v_j, with
- * q, k, v read from qkv bf16 [T, 3*H*dh] (row stride ldqkv) at column offsets 0,
- * H*dh, 2*H*dh; out bf16 [T, H*dh] (row stride ldo).  dh in {64, 128}.
+/* Feature-major copy of the v part of a fused qkv buffer, the layout the
+ * block's attention reads its values in:
+ * vt[f, t] = qkv[t, 2 d + f] for f < d, t < T, and vt[f, t] = 0 for
+ * T <= t < T64 (T rounded up to 64); columns from T64 to ldvt are not written.
+ * qkv bf16 [T, >= 3 d] (row stride ldqkv), vt bf16 [d, ldvt], both device,
+ * caller-owned, 16-B aligned.  d % 64 == 0, ldqkv >= 3 d, ldvt >= T64, ldqkv
+ * and ldvt multiples of 8, else DLO_E_UNSUPPORTED.  (The block forward gets the
+ * same layout straight from its v GEMM, dlo_op_gemm epilogue 3.) */
+int dlo_op_v_transpose(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t d, uint16_t *vt,
+                       int64_t ldvt, void *stream);
+
+/* Per head j < H: out[:, j*dh:(j+1)*dh] = softmax(q_j k_j^T / sqrt(dh)) v_j (the
+ * block's non-causal self-attention), with q, k read from qkv bf16
+ * [T, >= 2*H*dh] (row stride ldqkv) at column offsets 0 and H*dh, and v from a
+ * feature-major copy vt bf16 [H*dh, ldvt] as dlo_op_v_transpose writes it
+ * (columns T .. T64-1 must hold finite values; that op writes zeros there);
+ * out bf16 [T, H*dh] (row stride ldo).  All device, caller-owned; qkv and vt
+ * 16-B aligned.  dh in {64, 128}; ldqkv and ldvt multiples of 8, ldvt >= T64.
  * DLO_E_UNSUPPORTED when (T + 64) * ldqkv * 2 >= 2^31 (32-bit buffer offsets). */
-int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t H, int32_t dh,
-                     uint16_t *out, int64_t ldo, void *stream);
+int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, const uint16_t *vt, int64_t ldvt,
+                     int32_t T, int32_t H, int32_t dh, uint16_t *out, int64_t ldo, void *stream);
 
 /* out[i] = bf16_rne(e4m3_value(codes[i]) * *scale), i < n (device pointers; scale
  * is read on the device).  n % 16 == 0, codes 16-B and out 32-B aligned, else

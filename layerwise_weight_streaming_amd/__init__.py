@@ -25,8 +25,8 @@ DTYPES = {"bf16": 0, "f32": 1, "fp8": 2}   # fp8: OCP E4M3, one byte
 DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
 STORE_PINNED, STORE_PAGEABLE, STORE_AUTO = 0, 1, 2
 TRACE_DIGEST, TRACE_TIMING, RESIDENT = 1, 2, 4
-EPI_BIAS, EPI_BIAS_GELU, EPI_GATED_RESIDUAL = 0, 1, 2
-KERNELS_PER_BLOCK = 9
+EPI_BIAS, EPI_BIAS_GELU, EPI_GATED_RESIDUAL, EPI_BIAS_T = 0, 1, 2, 3
+KERNELS_PER_BLOCK = 10
 MAX_GROUPS = 3
 OP_KIND = {0: "copy", 1: "compute", 2: "record", 3: "wait"}
 OP_STREAM = {0: "compute", 1: "copy"}
@@ -137,9 +137,13 @@ _SIGS = {
                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_void_p]),
-    "dlo_op_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                        ctypes.c_int64, ctypes.c_void_p]),
+    "dlo_op_v_transpose": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p]),
+    "dlo_op_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_void_p]),
     "dlo_block_schema_fp8": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
                                             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
     "dlo_quantize_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
@@ -421,8 +425,17 @@ def op_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, stream):
     _check(lib().dlo_op_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, stream))
 
 
-def op_attention(qkv, ldqkv, T, H, dh, out, ldo, stream):
-    _check(lib().dlo_op_attention(qkv, ldqkv, T, H, dh, out, ldo, stream))
+def v_t_stride(T):
+    """Row stride (elements) of the feature-major V^T the attention reads: T rounded up to 64."""
+    return (T + 63) // 64 * 64
+
+
+def op_v_transpose(qkv, ldqkv, T, d, vt, ldvt, stream):
+    _check(lib().dlo_op_v_transpose(qkv, ldqkv, T, d, vt, ldvt, stream))
+
+
+def op_attention(qkv, ldqkv, vt, ldvt, T, H, dh, out, ldo, stream):
+    _check(lib().dlo_op_attention(qkv, ldqkv, vt, ldvt, T, H, dh, out, ldo, stream))
 
 
 def op_dequant_fp8(codes, n, scale, out, stream):

@@ -13,15 +13,18 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Flash attention forward (non-causal), one head per workgroup column.
-// Workgroup: 8 waves, 256 queries (32 per wave).  Keys/values in blocks of 64
-// travel HBM/L2 -> LDS by buffer_load ... lds, both key-major, into separate
-// two-slot rings for K and V, K one block ahead of V.  Each wave computes
-// S^T = K Q^T on MFMA, so a lane owns one query and the online-softmax
-// statistics stay in the lane (one exchange with lane l ^ 32, by
-// v_permlane32_swap).  P^T in that layout is the B operand of O^T += V^T P^T;
-// the V^T operand comes straight from the key-major V tile via
-// ds_read_b64_tr_b16 (for a group of 16 lanes, lane j receives element j % 4
-// of the 4-element loads of lanes 4t + j / 4, t = 0..3).
+// Workgroup: 8 waves, 256 queries (32 per wave).  Keys in blocks of 64 travel
+// HBM/L2 -> LDS by buffer_load ... lds into a two-slot ring, key-major; values
+// come from a feature-major copy V^T (rows of the head's dh features, T keys
+// each) into a second two-slot ring, K one block ahead of V.  Each wave
+// computes S^T = K Q^T on MFMA, so a lane owns one query and the
+// online-softmax statistics stay in the lane (one exchange with lane l ^ 32, by
+// v_permlane32_swap).  P^T in that layout is the B operand of O^T += V^T P^T,
+// whose A operand (32 features x 16 keys) is one 16-B LDS read per lane in the
+// feature-major tile.  Every operand read is a ds_read_b128: on gfx950 the LDS
+// moves about 140 B/clk per CU with 16-B reads but only about 76 B/clk with
+// 8-B reads (measured), and the reads of K and V for 32 queries per wave come
+// close to the MFMA time of the block.
 //
 // Software pipeline: block j's scores are computed one iteration ahead, so
 // while the MFMAs of S_{j+1} = K_{j+1} Q^T run, the same wave takes the softmax
@@ -39,34 +42,31 @@ namespace {
 
 constexpr int AK = 64;
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// 16-B chunk swizzles of the key-major K and V tiles (rows of DH bf16).
-// K: MFMA A reads of 16 consecutive key rows at one chunk hit 16 distinct bank
-// groups.  V: a transposed read touches 4 consecutive keys x 32 B; the swizzle
-// moves each key's 32 B to its own quarter of the 256-B bank window.
+// 16-B chunk swizzles.  K (key-major, rows of DH bf16): MFMA A reads of 16
+// consecutive key rows at one chunk hit 16 distinct bank groups.  V^T
+// (feature-major, rows of 64 keys = 128 B): 16 consecutive feature rows at one
+// chunk cover both 128-B halves of the 256-B bank window and, within a half,
+// 8 distinct chunks.
 template <int DH>
 __device__ __forceinline__ int k_swz(int key) {
   return DH == 128 ? (key & 15) : ((key >> 1) & 7);
 }
-template <int DH>
-__device__ __forceinline__ int v_swz(int key) {
-  return (key & 3) * (DH / 32);
-}
+__device__ __forceinline__ int vt_swz(int feature) { return (feature >> 1) & 7; }
 
 // A_WAVES waves of 32 queries per workgroup.
 template <int DH, int A_WAVES>
 __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_kernel(
-    const uint16_t *__restrict__ qkv, int64_t ldq, int T, int H, uint16_t *__restrict__ out,
-    int64_t ldo, float scale_log2) {
+    const uint16_t *__restrict__ qkv, int64_t ldq, const uint16_t *__restrict__ vt, int64_t ldvt,
+    int T, int H, uint16_t *__restrict__ out, int64_t ldo, float scale_log2) {
   constexpr int AQ = 32 * A_WAVES;
   constexpr int KCH = DH / 8;
   constexpr int TILE = AK * DH;
   constexpr int ROWS_PER_LD = 1024 / (DH * 2);
   constexpr int LD_PER_WAVE = AK / ROWS_PER_LD / A_WAVES;
+  constexpr int VLD_PER_WAVE = DH / 8 / A_WAVES;  // 1 KB = 8 feature rows of 64 keys
   constexpr int DT = DH / 32;
   constexpr int KK = DH / 16;
-  // tiles: K slot 0, K slot 1, V slot 0, V slot 1
+  // tiles: K slot 0, K slot 1, V^T slot 0, V^T slot 1
   __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
 
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
@@ -86,14 +86,18 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
 
   const uint32_t rec = (uint32_t)((int64_t)T * ldq * 2);
   const i32x4 k_rsrc = dl_rsrc(qkv + HD + head * DH, rec);
-  const i32x4 v_rsrc = dl_rsrc(qkv + 2 * HD + head * DH, rec);
-  int k_voff[LD_PER_WAVE], v_voff[LD_PER_WAVE];
+  const i32x4 v_rsrc = dl_rsrc(vt + (int64_t)head * DH * ldvt, (uint32_t)(DH * ldvt * 2));
+  int k_voff[LD_PER_WAVE], v_voff[VLD_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LD_PER_WAVE; ++i) {
     const int row = (wv * LD_PER_WAVE + i) * ROWS_PER_LD + lane / KCH;
     const int p = lane % KCH;
     k_voff[i] = (row * (int)ldq + (p ^ k_swz<DH>(row)) * 8) * 2;
-    v_voff[i] = (row * (int)ldq + (p ^ v_swz<DH>(row)) * 8) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < VLD_PER_WAVE; ++i) {
+    const int f = (wv * VLD_PER_WAVE + i) * 8 + lane / 8;
+    v_voff[i] = (f * (int)ldvt + ((lane % 8) ^ vt_swz(f)) * 8) * 2;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&smem[0];
   auto issue_k = [&](int j, int tile) {
@@ -106,25 +110,26 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
   };
   auto issue_v = [&](int j, int tile) {
     const uint32_t sb = lds0 + (uint32_t)(tile * TILE * 2);
-    const int off = j * AK * (int)ldq * 2;
+    const int off = j * AK * 2;
 #pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; ++i)
-      dl_load(v_rsrc, __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wv * LD_PER_WAVE + i) * 1024)),
+    for (int i = 0; i < VLD_PER_WAVE; ++i)
+      dl_load(v_rsrc, __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wv * VLD_PER_WAVE + i) * 1024)),
               v_voff[i] + off);
   };
 
-  const int g16 = lane >> 4, li = lane & 15;
-  const int vt_key = 4 * hf + (li >> 2);
-  const int vt_dh = 16 * (g16 & 1) + 4 * (li & 3);
-  int k_lane[KK], v_lane[DT];
+  // Key order: MFMA row i of a 32-key half reads key row i with bits 2 and 3
+  // swapped.  Accumulator r of lane (ql, hf) then holds key 16 (r / 8) + 8 hf +
+  // r % 8, so the eight bf16 P values a lane packs per 16-key chunk are eight
+  // consecutive keys: the layout of one 16-B read of a V^T row.
+  const int kr = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);
+  int k_lane[KK], v_lane[4];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    k_lane[kk] = (ql * DH + (((kk * 2 + hf) ^ k_swz<DH>(ql)) << 3)) * 2;
+    k_lane[kk] = (kr * DH + (((kk * 2 + hf) ^ k_swz<DH>(kr)) << 3)) * 2;
+  // V^T operand of key chunk c (16 keys): feature row ql (+ 32 t), keys
+  // 16 c + 8 hf .. + 7; the 32 t rows add 4096 B
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    const int dh = 32 * t + vt_dh;
-    v_lane[t] = (vt_key * DH + (((dh >> 3) ^ v_swz<DH>(vt_key)) << 3) + (dh & 7)) * 2;
-  }
+  for (int c = 0; c < 4; ++c) v_lane[c] = ql * AK * 2 + (((2 * c + hf) ^ vt_swz(ql)) << 4);
   const char *lds_bytes = reinterpret_cast<const char *>(&smem[0]);
 
   // S^T of one block: two 32-key halves, their MFMA chains interleaved
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kbase + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3) >= T) sc[kb][r] = -INFINITY;
+          if (kbase + kb * 32 + (r >> 3) * 16 + hf * 8 + (r & 7) >= T) sc[kb][r] = -INFINITY;
     }
     float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
@@ -232,12 +237,7 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const char *p1 = Vb + c * 16 * DH * 2 + v_lane[t];
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(p1));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(p1 + 8 * DH * 2));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vb + t * 32 * AK * 2 + v_lane[c]);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
       }
 #pragma unroll
@@ -269,21 +269,63 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
   }
 }
 
+// V^T for the attention: vt[f, t] = v[t, f] for t < T, 0 for T <= t < T64
+// (T64 = T rounded up to 64, so every 64-key block of V^T holds finite values).
+// One workgroup per 64 tokens x 64 features: 16-B row loads into an LDS tile
+// whose 132-B rows put the eight 2-B reads of a 16-B output segment on eight
+// distinct banks, then 16-B stores along the feature rows.
+__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t *__restrict__ v, int64_t ldv,
+                                                          int T, uint16_t *__restrict__ vt,
+                                                          int64_t ldvt) {
+  constexpr int LDT = 66;  // u16 per LDS row (132 B)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * LDT];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * 64, f0 = blockIdx.y * 64;
+#pragma unroll
+  for (int L = 0; L < 2; ++L) {
+    const int idx = L * 256 + tid, r = idx >> 3, c = idx & 7;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (t0 + r < T) val = *reinterpret_cast<const u32x4 *>(v + (int64_t)(t0 + r) * ldv + f0 + c * 8);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(tile + r * LDT + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = val[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int L = 0; L < 2; ++L) {
+    const int idx = L * 256 + tid, f = idx >> 3, c = idx & 7;
+    u32x4 val;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      val[e] = (uint32_t)tile[(c * 8 + 2 * e) * LDT + f] | ((uint32_t)tile[(c * 8 + 2 * e + 1) * LDT + f] << 16);
+    *reinterpret_cast<u32x4 *>(vt + (int64_t)(f0 + f) * ldvt + t0 + c * 8) = val;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, int T, int H, int dh,
-                            uint16_t *out, int64_t ldo, hipStream_t s) {
+hipError_t launch_v_transpose(const uint16_t *v, int64_t ldv, int T, int d, uint16_t *vt,
+                              int64_t ldvt, hipStream_t s) {
+  if (T < 1 || d % 64 || ldv % 8 || ldvt % 8 || ldvt < (int64_t)(T + 63) / 64 * 64)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(v_transpose_kernel, dim3((T + 63) / 64, d / 64), dim3(256), 0, s, v, ldv, T, vt,
+                     ldvt);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, const uint16_t *vt, int64_t ldvt,
+                            int T, int H, int dh, uint16_t *out, int64_t ldo, hipStream_t s) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
   // 8 waves (256 queries) per workgroup, one workgroup per CU: faster than
   // 4 waves at two workgroups per CU (each K/V tile then serves twice the
   // queries; 3.6 % on the Super attention shape)
   const int nqb = (T + 255) / 256;
   if (dh == 128) {
-    hipLaunchKernelGGL((attention_kernel<128, 8>), dim3(nqb * H), dim3(512), 0, s, qkv, ldqkv, T,
-                       H, out, ldo, scale_log2);
+    hipLaunchKernelGGL((attention_kernel<128, 8>), dim3(nqb * H), dim3(512), 0, s, qkv, ldqkv, vt,
+                       ldvt, T, H, out, ldo, scale_log2);
   } else if (dh == 64) {
-    hipLaunchKernelGGL((attention_kernel<64, 8>), dim3(nqb * H), dim3(512), 0, s, qkv, ldqkv, T, H,
-                       out, ldo, scale_log2);
+    hipLaunchKernelGGL((attention_kernel<64, 8>), dim3(nqb * H), dim3(512), 0, s, qkv, ldqkv, vt,
+                       ldvt, T, H, out, ldo, scale_log2);
   } else {
     return hipErrorInvalidValue;
   }

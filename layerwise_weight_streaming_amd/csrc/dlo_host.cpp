@@ -129,7 +129,7 @@ int64_t schema_numel(const SchemaEntry &e, int64_t d) {
 }
 
 const char *kKernelNames[DLO_KERNELS_PER_BLOCK] = {
-    "dequant_fp8", "adaln_gemv", "ln1_modulate", "gemm_qkv", "attention",
+    "dequant_fp8", "adaln_gemv", "ln1_modulate", "gemm_qk", "gemm_v_t", "attention",
     "gemm_out_residual", "ln2_modulate", "gemm_fc1_gelu", "gemm_fc2_residual"};
 
 }  // namespace
@@ -376,10 +376,12 @@ void run_copies(std::vector<CopyTask> &tasks) {
   for (auto &t : th) t.join();
 }
 
+int64_t round_up64(int64_t T) { return (T + 63) / 64 * 64; }
+
 int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d) {
   const int64_t d = max_d, f = fp8_d;
   return align_up(4 * d, DLO_ALIGN) + align_up(24 * d, DLO_ALIGN) + align_up(2 * T * d, DLO_ALIGN) +
-         align_up(8 * T * d, DLO_ALIGN) + align_up(36 * f * f, DLO_ALIGN);
+         align_up(8 * round_up64(T) * d, DLO_ALIGN) + align_up(36 * f * f, DLO_ALIGN);
 }
 
 int validate_block_against(const BlockPlan &bp, const dlo_block &blk, int b, bool need_src) {
@@ -925,10 +927,10 @@ Workspace carve(void *ws, int32_t max_d, int64_t T) {
   p += align_up(4 * (int64_t)max_d, DLO_ALIGN);
   w.mod = reinterpret_cast<float *>(p);
   p += align_up(24 * (int64_t)max_d, DLO_ALIGN);
-  w.h = reinterpret_cast<uint16_t *>(p);
+  w.h = reinterpret_cast<uint16_t *>(p);    // h [T,d]
   p += align_up(2 * T * max_d, DLO_ALIGN);
-  w.big = reinterpret_cast<uint16_t *>(p);  // qkv [T,3d] then a [T,d]; later u [T,4d]
-  p += align_up(8 * T * max_d, DLO_ALIGN);
+  w.big = reinterpret_cast<uint16_t *>(p);  // qk [T,2d], V^T [d,T64], a [T,d]; later u [T,4d]
+  p += align_up(8 * round_up64(T) * max_d, DLO_ALIGN);
   w.dq = reinterpret_cast<uint16_t *>(p);   // an FP8 block's weights, dequantised to bf16
   return w;
 }
@@ -961,8 +963,12 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   float *x = a->x;
   const int64_t ldx = a->x_row_stride;
   const float *mod = w.mod;
-  uint16_t *qkv = w.big;
-  uint16_t *attn = w.big + (int64_t)T * 3 * d;
+  // q and k from one GEMM; v from a second one that stores V^T, the layout the
+  // attention reads its values in
+  const int64_t ldvt = round_up64(T);
+  uint16_t *qk = w.big;
+  uint16_t *vt = w.big + (int64_t)T * 2 * d;
+  uint16_t *attn = vt + (int64_t)d * ldvt;
   uint16_t *u = w.big;
 #define DLO_STEP(call, j)                                                   \
   if ((e = (call)) != hipSuccess) return e;                                 \
@@ -970,17 +976,19 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   DLO_STEP(dlo::launch_adaln_gemv(Wt[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 1)
   DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N1_W), F(P_N1_B), F(P_N1_EPS), mod + 0 * d,
                                    mod + 1 * d, w.h, s), 2)
-  DLO_STEP(dlo::launch_gemm(w.h, d, Wt[1], d, T, 3 * d, d, F(P_QKV_B), nullptr, qkv, 3 * d,
+  DLO_STEP(dlo::launch_gemm(w.h, d, Wt[1], d, T, 2 * d, d, F(P_QKV_B), nullptr, qk, 2 * d,
                             dlo::EPI_BIAS, s), 3)
-  DLO_STEP(dlo::launch_attention(qkv, 3 * d, T, H, dh, attn, d, s), 4)
+  DLO_STEP(dlo::launch_gemm(w.h, d, Wt[1] + (int64_t)2 * d * d, d, T, d, d, F(P_QKV_B) + 2 * d,
+                            nullptr, vt, ldvt, dlo::EPI_BIAS_T, s), 4)
+  DLO_STEP(dlo::launch_attention(qk, 2 * d, vt, ldvt, T, H, dh, attn, d, s), 5)
   DLO_STEP(dlo::launch_gemm(attn, d, Wt[2], d, T, d, d, F(P_OUT_B), mod + 2 * d, x, ldx,
-                            dlo::EPI_GATED_RESIDUAL, s), 5)
+                            dlo::EPI_GATED_RESIDUAL, s), 6)
   DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N2_W), F(P_N2_B), F(P_N2_EPS), mod + 3 * d,
-                                   mod + 4 * d, w.h, s), 6)
+                                   mod + 4 * d, w.h, s), 7)
   DLO_STEP(dlo::launch_gemm(w.h, d, Wt[3], d, T, 4 * d, d, F(P_FC1_B), nullptr, u, 4 * d,
-                            dlo::EPI_BIAS_GELU, s), 7)
+                            dlo::EPI_BIAS_GELU, s), 8)
   DLO_STEP(dlo::launch_gemm(u, 4 * d, Wt[4], 4 * d, T, d, 4 * d, F(P_FC2_B), mod + 5 * d, x,
-                            ldx, dlo::EPI_GATED_RESIDUAL, s), 8)
+                            ldx, dlo::EPI_GATED_RESIDUAL, s), 9)
 #undef DLO_STEP
   return hipSuccess;
 }
@@ -1271,10 +1279,11 @@ int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, 
                 int32_t N, int32_t K, const float *bias, const float *gate, void *C, int64_t ldc,
                 int32_t epilogue, void *stream) {
   if (!A || !B || !bias || !C) return fail(DLO_E_ARG, "NULL argument");
-  if (epilogue < 0 || epilogue > 2) return fail(DLO_E_ARG, "unknown epilogue %d", epilogue);
+  if (epilogue < 0 || epilogue > 3) return fail(DLO_E_ARG, "unknown epilogue %d", epilogue);
   if (epilogue == DLO_EPI_GATED_RESIDUAL && !gate) return fail(DLO_E_ARG, "gate is required");
-  if (M < 1 || N < 256 || N % 256 || K < 64 || K % 64 || lda < K || ldb < K || ldc < N ||
-      lda % 8 || ldb % 8)
+  const bool trans = epilogue == DLO_EPI_BIAS_T;
+  if (M < 1 || N < 256 || N % 256 || K < 64 || K % 64 || lda < K || ldb < K ||
+      ldc < (trans ? round_up64(M) : N) || lda % 8 || ldb % 8 || (trans && ldc % 8))
     return fail(DLO_E_UNSUPPORTED, "gemm: N %% 256 == 0, K %% 64 == 0, ld >= extent, ld %% 8 == 0");
   if ((int64_t)256 * lda * 2 >= (int64_t)1 << 31 || (int64_t)256 * ldb * 2 >= (int64_t)1 << 31 ||
       (int64_t)256 * ldc * 4 >= (int64_t)1 << 31)
@@ -1286,16 +1295,32 @@ int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, 
   return rc ? rc : ok();
 }
 
-int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t H, int32_t dh,
-                     uint16_t *out, int64_t ldo, void *stream) {
-  if (!qkv || !out) return fail(DLO_E_ARG, "NULL argument");
-  if (T < 1 || H < 1 || (dh != 64 && dh != 128) || ldqkv < 3LL * H * dh || ldo < (int64_t)H * dh ||
-      ldqkv % 8 || ldo % 4)
-    return fail(DLO_E_UNSUPPORTED, "attention: dh in {64,128}, ldqkv >= 3 H dh (multiple of 8)");
-  if (((int64_t)T + 64) * ldqkv * 2 >= ((int64_t)1 << 31))
+int dlo_op_v_transpose(const uint16_t *qkv, int64_t ldqkv, int32_t T, int32_t d, uint16_t *vt,
+                       int64_t ldvt, void *stream) {
+  if (!qkv || !vt) return fail(DLO_E_ARG, "NULL argument");
+  if (T < 1 || d < 64 || d % 64 || ldqkv < 3LL * d || ldqkv % 8 || ldvt % 8 || ldvt < round_up64(T))
+    return fail(DLO_E_UNSUPPORTED,
+                "v_transpose: d %% 64 == 0, ldqkv >= 3 d and ldvt >= T rounded up to 64 (multiples of 8)");
+  if ((uintptr_t)qkv % 16 || (uintptr_t)vt % 16)
+    return fail(DLO_E_UNSUPPORTED, "v_transpose: qkv and vt must be 16-B aligned");
+  int rc = check_hip(dlo::launch_v_transpose(qkv + 2 * (int64_t)d, ldqkv, T, d, vt, ldvt,
+                                             (hipStream_t)stream), "v_transpose");
+  return rc ? rc : ok();
+}
+
+int dlo_op_attention(const uint16_t *qkv, int64_t ldqkv, const uint16_t *vt, int64_t ldvt, int32_t T,
+                     int32_t H, int32_t dh, uint16_t *out, int64_t ldo, void *stream) {
+  if (!qkv || !vt || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (T < 1 || H < 1 || (dh != 64 && dh != 128) || ldqkv < 2LL * H * dh || ldo < (int64_t)H * dh ||
+      ldqkv % 8 || ldo % 4 || ldvt % 8 || ldvt < round_up64(T))
+    return fail(DLO_E_UNSUPPORTED,
+                "attention: dh in {64,128}, ldqkv >= 2 H dh, ldvt >= T rounded up to 64 (multiples of 8)");
+  if (((int64_t)T + 64) * ldqkv * 2 >= ((int64_t)1 << 31) || (int64_t)dh * ldvt * 2 >= ((int64_t)1 << 31))
     return fail(DLO_E_UNSUPPORTED, "attention: T * ldqkv too large for 32-bit buffer offsets");
-  int rc = check_hip(dlo::launch_attention(qkv, ldqkv, T, H, dh, out, ldo, (hipStream_t)stream),
-                     "attention");
+  if ((uintptr_t)qkv % 16 || (uintptr_t)vt % 16)
+    return fail(DLO_E_UNSUPPORTED, "attention: qkv and vt must be 16-B aligned");
+  int rc = check_hip(dlo::launch_attention(qkv, ldqkv, vt, ldvt, T, H, dh, out, ldo,
+                                           (hipStream_t)stream), "attention");
   return rc ? rc : ok();
 }
 

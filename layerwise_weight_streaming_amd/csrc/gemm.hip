@@ -1,5 +1,6 @@
 // gfx950 GEMM of the DiT block linears: C = A B^T with bf16 operands, fp32
-// accumulation and fused epilogues (bias, bias + GELU, gated residual).
+// accumulation and fused epilogues (bias, bias + GELU, gated residual, and bias
+// with the result stored transposed).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,8 +42,9 @@ __device__ __forceinline__ int dl_lds_off(int row, int chunk) {  // element offs
 }
 
 // Epilogue of a 256 x BN tile held by 2 x WN waves (acc: the wave's 128 x BN/WN
-// sub-tile in transposed 32x32 MFMA tiles).  smem: at least 256 x (BN + 8) bf16
-// (bias epilogues) or 128 x (BN + 4) fp32 (gated residual), no longer in use.
+// sub-tile in 32x32 MFMA tiles, transposed except for EPI_BIAS_T).  smem: at
+// least 256 x (BN + 8) bf16 (bias epilogues; BN x (256 + 8) for EPI_BIAS_T) or
+// 128 x (BN + 4) fp32 (gated residual), no longer in use.
 template <int EPI, int BN, int WN>
 __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 32], uint16_t *smem,
                                               int tid, int wm, int wn, int lane, int m0, int n0,
@@ -63,7 +65,38 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
   constexpr int NJ = BN / WN / 32;
   constexpr int C_LD = BN + 8, X_LD = BN + 4;
   const int frow = lane & 31, fk = lane >> 5;
-  if (EPI != EPI_GATED_RESIDUAL) {
+  if (EPI == EPI_BIAS_T) {
+    // acc[i][j] holds the 32x32 sub-tile as the MFMA lays it out with A first:
+    // lane l has column j*32 + l%32 and, for g = 0..3, the four consecutive
+    // rows i*32 + 8g + 4(l/32) + 0..3: one 8-B piece of a row of C^T.  Rows
+    // m >= M become 0; rows of C^T are stored up to M rounded up to 64.
+    const int M64 = (M + 63) & ~63;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = wn * (BN / WN) + j * 32 + frow;
+      const float bv = bias[n0 + col];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row = wm * 128 + i * 32 + g * 8 + fk * 4;
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = (full || m0 + row + e < M) ? (__bf16)(acc[i][j][g * 4 + e] + bv) : (__bf16)0.0f;
+          *reinterpret_cast<bf16x4 *>(&smem[col * (GBM + 8) + row]) = o;
+        }
+    }
+    __syncthreads();
+    constexpr int SEG = GBM / 8;              // 16-B segments per row of C^T
+    uint16_t *C = reinterpret_cast<uint16_t *>(Cv) + (int64_t)n0 * ldc + m0;
+#pragma unroll
+    for (int it = 0; it < BN * SEG / NT; ++it) {
+      const int e = it * NT + tid, row = e / SEG, c8 = (e % SEG) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&smem[row * (GBM + 8) + c8]);
+      if (full || m0 + c8 < M64) *reinterpret_cast<u32x4 *>(&C[row * ldc32 + c8]) = v;
+    }
+  } else if (EPI != EPI_GATED_RESIDUAL) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -269,7 +302,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][j], f.a[kk][i], acc[i][j], 0, 0, 0);
+          acc[i][j] = EPI == EPI_BIAS_T
+                          ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][j], f.a[kk][i], acc[i][j], 0, 0, 0);
   };
   // Barrier opening global phase p.  Before it, this wave's loads of the tile
   // read in phase p (tile p / 2) have landed: younger tiles of this wave's
@@ -342,6 +377,10 @@ hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_
     case EPI_GATED_RESIDUAL:
       hipLaunchKernelGGL((gemm_pp_kernel<EPI_GATED_RESIDUAL>), dim3(tiles), dim3(512), 0, s, A, lda, B,
                          ldb, M, N, K, bias, gate, C, ldc);
+      break;
+    case EPI_BIAS_T:
+      hipLaunchKernelGGL((gemm_pp_kernel<EPI_BIAS_T>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb,
+                         M, N, K, bias, gate, C, ldc);
       break;
     default:
       return hipErrorInvalidValue;

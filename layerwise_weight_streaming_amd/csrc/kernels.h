@@ -17,16 +17,23 @@ hipError_t launch_ln_modulate(const float *x, int64_t ldx, int T, int d, const f
                               const float *beta, const float *eps, const float *shift,
                               const float *scale, uint16_t *out, hipStream_t s);
 
-enum GemmEpilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_GATED_RESIDUAL = 2 };
+enum GemmEpilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_GATED_RESIDUAL = 2, EPI_BIAS_T = 3 };
 
-// C = A B^T + bias (see dlo_op_gemm); N % 256 == 0, K % 64 == 0
+// C = A B^T + bias (see dlo_op_gemm); N % 256 == 0, K % 64 == 0.  EPI_BIAS_T
+// stores C^T [N, ldc]: rows m in [M, M rounded up to 64) as 0, nothing beyond
 hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int M,
                        int N, int K, const float *bias, const float *gate, void *C, int64_t ldc,
                        int epilogue, hipStream_t s);
 
-// per-head softmax(q k^T / sqrt(dh)) v from a fused qkv buffer; dh in {64, 128}
-hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, int T, int H, int dh,
-                            uint16_t *out, int64_t ldo, hipStream_t s);
+// vt[f, t] = v[t, f] (f < d, t < T), 0 for T <= t < T rounded up to 64;
+// d % 64 == 0, ldv and ldvt multiples of 8, ldvt >= T rounded up to 64
+hipError_t launch_v_transpose(const uint16_t *v, int64_t ldv, int T, int d, uint16_t *vt,
+                              int64_t ldvt, hipStream_t s);
+
+// per-head softmax(q k^T / sqrt(dh)) v: q, k from a fused qkv buffer, v from
+// its feature-major copy vt (launch_v_transpose); dh in {64, 128}
+hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, const uint16_t *vt, int64_t ldvt,
+                            int T, int H, int dh, uint16_t *out, int64_t ldo, hipStream_t s);
 
 // out[i] = bf16_rne(e4m3_value(codes[i]) * *scale), i < n; n % 16 == 0, codes 16-B
 // and out 32-B aligned

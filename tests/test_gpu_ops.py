@@ -88,15 +88,67 @@ def test_gemm_full_size_sampled():
     assert nbad == 0, (nbad, worst)
 
 
+@pytest.mark.parametrize("M,N,K,extra", [(300, 512, 128, 0), (64, 768, 256, 8), (1000, 256, 320, 64),
+                                         (1, 256, 64, 0), (513, 256, 64, 0)])
+def test_gemm_transposed_store(M, N, K, extra):
+    """Epilogue 3: C[n, m] = (A B^T + bias)[m, n]; zeros for M <= m < M64, nothing written beyond."""
+    torch = require_gpu()
+    say("gemm transposed", M, N, K, extra)
+    A = _bf16_rand(M * 3 + 7, (M, K))
+    B = _bf16_rand(N * 11 + 5, (N, K), 0.05)
+    bias = synth.normal_f32(6, 9, 1, 0, (N,), 0.0, 0.1)
+    ref = of.linear(bf16_to_f64(A), bf16_to_f64(B), bias.astype(np.float64))
+    M64 = (M + 63) // 64 * 64
+    ldc = M64 + extra
+    dA, dB, db = _dev(torch, A), _dev(torch, B), _dev(torch, bias)
+    s = torch.cuda.current_stream().cuda_stream
+    dCt = torch.full((N, ldc), 0x7FC0, dtype=torch.int16, device="cuda")
+    dlo.op_gemm(dA.data_ptr(), K, dB.data_ptr(), K, M, N, K, db.data_ptr(), 0, dCt.data_ptr(), ldc,
+                dlo.EPI_BIAS_T, s)
+    dC = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    dlo.op_gemm(dA.data_ptr(), K, dB.data_ptr(), K, M, N, K, db.data_ptr(), 0, dC.data_ptr(), N,
+                dlo.EPI_BIAS, s)
+    torch.cuda.synchronize()
+    ct = dCt.cpu().numpy().view(np.uint16)
+    nbad, worst = _close_bf16(bf16_to_f64(ct[:, :M].T), ref)
+    assert nbad == 0, (nbad, worst)
+    assert np.all(ct[:, M:M64] == 0)
+    assert np.all(ct[:, M64:] == 0x7FC0)
+    # the same products as the row-major store, element for element
+    assert np.array_equal(ct[:, :M].T, dC.cpu().numpy().view(np.uint16))
+
+
 def _attention_case(torch, T, H, dh, seed):
     d = H * dh
     qkv = _bf16_rand(seed, (T, 3 * d), 1.0)
     dq = _dev(torch, qkv)
+    ldvt = dlo.v_t_stride(T)
+    # V^T starts as NaN everywhere: the attention must only see what the transpose wrote
+    dvt = torch.full((d, ldvt), 0x7FC0, dtype=torch.int16, device="cuda")
     dout = torch.zeros((T, d), dtype=torch.int16, device="cuda")
-    dlo.op_attention(dq.data_ptr(), 3 * d, T, H, dh, dout.data_ptr(), d,
-                     torch.cuda.current_stream().cuda_stream)
+    s = torch.cuda.current_stream().cuda_stream
+    dlo.op_v_transpose(dq.data_ptr(), 3 * d, T, d, dvt.data_ptr(), ldvt, s)
+    dlo.op_attention(dq.data_ptr(), 3 * d, dvt.data_ptr(), ldvt, T, H, dh, dout.data_ptr(), d, s)
     torch.cuda.synchronize()
     return qkv, bf16_to_f64(dout.cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("T,d,extra", [(1, 64, 0), (64, 256, 8), (300, 1024, 64), (777, 192, 0)])
+def test_v_transpose_bit_exact(T, d, extra):
+    """V^T holds the v columns of qkv transposed, zeros up to T rounded to 64, nothing beyond."""
+    torch = require_gpu()
+    say("v_transpose", T, d, extra)
+    qkv = _bf16_rand(T + d, (T, 3 * d), 1.0)
+    ldvt = dlo.v_t_stride(T) + extra
+    dvt = torch.full((d, ldvt), 0x7FC0, dtype=torch.int16, device="cuda")
+    dlo.op_v_transpose(_dev(torch, qkv).data_ptr(), 3 * d, T, d, dvt.data_ptr(), ldvt,
+                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    vt = dvt.cpu().numpy().view(np.uint16)
+    T64 = dlo.v_t_stride(T)
+    assert np.array_equal(vt[:, :T], qkv[:, 2 * d:].T)
+    assert np.all(vt[:, T:T64] == 0)
+    assert np.all(vt[:, T64:] == 0x7FC0)
 
 
 @pytest.mark.parametrize("T,H,dh", [(1, 1, 64), (64, 4, 64), (300, 2, 128), (1000, 3, 64), (777, 2, 128)])

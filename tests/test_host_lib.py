@@ -311,7 +311,15 @@ def test_op_validation_errors():
     assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 16, 16, 0x1008, 256, 2, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 16, 16, 0x1000, 258, 2, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 0x1004, 16, 0x1000, 256, 0, 0) == "DLO_E_UNSUPPORTED"
-    assert _status(dlo.op_attention, 1, 3 * 4 * 32, 10, 4, 32, 1, 128, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_attention, 16, 3 * 4 * 32, 16, 64, 10, 4, 32, 16, 128, 0) == "DLO_E_UNSUPPORTED"
+    # V^T row stride below T rounded up to 64, and misaligned V^T
+    assert _status(dlo.op_attention, 16, 3 * 4 * 64, 16, 56, 10, 4, 64, 16, 256, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_attention, 16, 3 * 4 * 64, 0x1008, 64, 10, 4, 64, 16, 256, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_attention, 16, 3 * 4 * 64, 0, 64, 10, 4, 64, 16, 256, 0) == "DLO_E_ARG"
+    assert _status(dlo.op_v_transpose, 16, 3 * 96, 10, 96, 16, 64, 0) == "DLO_E_UNSUPPORTED"   # d % 64
+    assert _status(dlo.op_v_transpose, 16, 3 * 128, 65, 128, 16, 64, 0) == "DLO_E_UNSUPPORTED"  # ldvt < 128
+    assert _status(dlo.op_v_transpose, 16, 3 * 128, 10, 128, 0x1008, 64, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_v_transpose, 16, 3 * 128 - 8, 10, 128, 16, 64, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_ln_modulate, 1, 300, 4, 300, 1, 1, 1, 1, 1, 1, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_digest, 1, [3], [8], 1, 0) == "DLO_E_ARG"
 
