@@ -27,20 +27,25 @@ namespace {
 // close to the MFMA time of the block.
 //
 // Software pipeline: block j's scores are computed one iteration ahead, so
-// while the MFMAs of S_{j+1} = K_{j+1} Q^T run, the same wave takes the softmax
-// statistics of block j and the P of its first 32 keys on the VALU (max,
-// exp2, bf16 packing); then O^T += V_j^T P_j^T, with the second half's P and
-// the row sums of P_j (v_dot2 on the bf16 P the MFMA uses) in the shadow of
-// those MFMAs.  One barrier per block; every load has a whole block
-// of compute to land in.
+// while the MFMAs of S_{j+1} = K_{j+1} Q^T run, the same wave turns the first
+// 32 keys of block j into P on the VALU (exp2, bf16 packing, row sums by
+// v_dot2 on the bf16 P the MFMA uses); then O^T += V_j^T P_j^T, with the
+// second half's P in the shadow of the first half's MFMAs.  One barrier per
+// block; every load has a whole block of compute to land in.
 //
-// Softmax in base 2 on raw scores s: p = exp2(s * c - m * c), c = log2(e)/sqrt(dh).
-// The running max m is raised only when a block's max exceeds it by more than
-// 8 / c (so p <= 2^8), which leaves the rescale of O and l out of most blocks;
-// the result is the same softmax, normalised by the same running sum.
+// Softmax in base 2 on raw scores s: p = exp2(s * c - m * c), c = log2(e)/sqrt(dh),
+// against a running max m that is not recomputed per block.  Each 32-key half
+// is checked instead: while every lane's sum of p over the half stays below
+// 2^64, every p does too, and fp32 O and l cannot overflow over any T; when it
+// does not (the first block, where m = -inf, or a score more than 64 / c
+// above m), the wave raises m to the max over the half, rescales O and l and
+// redoes the half's P -- the online-softmax update with each half as a step.
+// The result is the same softmax, normalised by the same running sum, without
+// a max reduction on the common path.
 // ---------------------------------------------------------------------------
 
 constexpr int AK = 64;
+constexpr float P_LIMIT = 18446744073709551616.0f;  // 2^64
 
 // 16-B chunk swizzles.  K (key-major, rows of DH bf16): MFMA A reads of 16
 // consecutive key rows at one chunk hit 16 distinct bank groups.  V^T
@@ -152,10 +157,47 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float tau = 8.0f / scale_log2;
+  float m_run = -INFINITY, l_run = 0.f, mc = -INFINITY;  // mc = m_run * scale_log2
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // p of the 16 scores of one 32-key half held by this lane, as bf16
+  auto half_p = [&](const f32x16 &sv, bf16x8 &p0, bf16x8 &p1) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p0[r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -mc));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p1[r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 + r], scale_log2, -mc));
+  };
+  // their sum, from the bf16 values the MFMA multiplies
+  auto half_sum = [&](const bf16x8 &p0, const bf16x8 &p1) {
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * e], p0[2 * e + 1]}, ones, ls, false);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * e], p1[2 * e + 1]}, ones, ls, false);
+    return ls;
+  };
+  // Taken when some lane's p sum of the half is not below 2^64 (always at the
+  // first block, where m = -inf; later only if a score exceeds m by more than
+  // 64 / c): raise m to the half's max over both lane halves, rescale O and
+  // l, redo P.
+  auto raise = [&](const f32x16 &sv, bf16x8 &p0, bf16x8 &p1, float &ls) {
+    float mx = sv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+    mc = m_new * scale_log2;
+    half_p(sv, p0, p1);
+    ls = half_sum(p0, p1);
+  };
 
   const int nkb = (T + AK - 1) / AK;
   issue_k(0, 0);
@@ -184,27 +226,10 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
         for (int r = 0; r < 16; ++r)
           if (kbase + kb * 32 + (r >> 3) * 16 + hf * 8 + (r & 7) >= T) sc[kb][r] = -INFINITY;
     }
-    float mx = fmaxf(sc[0][0], sc[0][1]);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const bool need = __any(mx > m_run + tau);
-    const float m_new = need ? fmaxf(m_run, mx) : m_run;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    m_run = m_new;
-    const float mc = m_new * scale_log2;
-    // P of the first 32-key half here; the second half's exp2 work moves to
-    // phase B, under the PV MFMAs of the first half (1.2 % faster than all of
-    // it here: phase A was VALU-bound, phase B MFMA-bound)
+    // P of the first 32-key half against the running max, and its row sums
     bf16x8 pf[4];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][r], scale_log2, -mc));
+    half_p(sc[0], pf[0], pf[1]);
+    float ls0 = half_sum(pf[0], pf[1]);
 
     qk(Kn, sn);  // next block's scores (unused after the last block)
     // interleave the 16 MFMAs with the K operand reads (two ahead) and the
@@ -214,37 +239,32 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
     }
-    // the first half's P is complete here, ahead of the rescale branch (keeps
-    // its exp2 work in this block, next to the MFMAs it overlaps)
     asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+    if (__any(!(ls0 < P_LIMIT))) raise(sc[0], pf[0], pf[1], ls0);
+    l_run += ls0;
 
-    if (need) {
+    // O^T += V^T P^T over the four 16-key chunks; the second half's P and row
+    // sums on the VALU under the first two chunks' MFMAs
+    half_p(sc[1], pf[2], pf[3]);
+    float ls1 = half_sum(pf[2], pf[3]);
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-    }
-
-    // O^T += V^T P^T over the four 16-key chunks; the second half's P and the
-    // row sums of P on the VALU meanwhile
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      pf[2 + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][r], scale_log2, -mc));
-    float ls = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vb + t * 32 * AK * 2 + v_lane[c]);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
       }
+    if (__any(!(ls1 < P_LIMIT))) raise(sc[1], pf[2], pf[3], ls1);
+    l_run += ls1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[c][2 * e], pf[c][2 * e + 1]}, ones, ls, false);
-    }
-    l_run = l_run * alpha + ls;
+    for (int c = 2; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vb + t * 32 * AK * 2 + v_lane[c]);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
+      }
   };
   int j = 0;
   for (; j + 1 < nkb; j += 2) {
