@@ -33,15 +33,18 @@ namespace {
 // second half's P in the shadow of the first half's MFMAs.  One barrier per
 // block; every load has a whole block of compute to land in.
 //
-// Softmax in base 2 on raw scores s: p = exp2(s * c - m * c), c = log2(e)/sqrt(dh),
-// against a running max m that is not recomputed per block.  Each 32-key half
-// is checked instead: while every lane's sum of p over the half stays below
-// 2^64, every p does too, and fp32 O and l cannot overflow over any T; when it
-// does not (the first block, where m = -inf, or a score more than 64 / c
-// above m), the wave raises m to the max over the half, rescales O and l and
+// Softmax in base 2: q is scaled by c = log2(e)/sqrt(dh) once (rounded to
+// bf16, a relative change of at most 2^-9 per element), so the MFMA yields
+// scores in log2 units, and each block's accumulators start at -m, the running
+// max: the registers hold score - m and p = exp2 of them directly.  m starts at
+// block 0's max and is not recomputed per block.  Each 32-key half is checked
+// instead: while every lane's sum of p over the half stays below 2^64, every p
+// does too, and fp32 O and l cannot overflow over any T; when it does not (a
+// score more than 64 above m), the wave raises m to the half's max, rescales O
+// and l, shifts every score register still to be used by the same amount and
 // redoes the half's P -- the online-softmax update with each half as a step.
 // The result is the same softmax, normalised by the same running sum, without
-// a max reduction on the common path.
+// a max reduction or a scale-and-subtract per score on the common path.
 // ---------------------------------------------------------------------------
 
 constexpr int AK = 64;
@@ -84,10 +87,14 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
   const int q = qb * AQ + wv * 32 + ql;
   const int qc = q < T ? q : T - 1;
 
+  // q * c in bf16: scores come out of the MFMA in log2 units
   bf16x8 qf[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    qf[kk] = *reinterpret_cast<const bf16x8 *>(qkv + (int64_t)qc * ldq + head * DH + kk * 16 + hf * 8);
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(qkv + (int64_t)qc * ldq + head * DH + kk * 16 + hf * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)((float)raw[e] * scale_log2);
+  }
 
   const uint32_t rec = (uint32_t)((int64_t)T * ldq * 2);
   const i32x4 k_rsrc = dl_rsrc(qkv + HD + head * DH, rec);
@@ -137,12 +144,12 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
   for (int c = 0; c < 4; ++c) v_lane[c] = ql * AK * 2 + (((2 * c + hf) ^ vt_swz(ql)) << 4);
   const char *lds_bytes = reinterpret_cast<const char *>(&smem[0]);
 
-  // S^T of one block: two 32-key halves, their MFMA chains interleaved
-  auto qk = [&](const char *Kb, f32x16 (&s)[2]) {
+  // S^T - s0 of one block: two 32-key halves, their MFMA chains interleaved
+  auto qk = [&](const char *Kb, f32x16 (&s)[2], float s0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = s0;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
@@ -157,15 +164,16 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f, mc = -INFINITY;  // mc = m_run * scale_log2
+  float m_run = 0.f, l_run = 0.f;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // p of the 16 scores of one 32-key half held by this lane, as bf16
+  // p = exp2(score - m) of the 16 scores of one 32-key half held by this lane
+  // (the registers hold score - m), as bf16
   auto half_p = [&](const f32x16 &sv, bf16x8 &p0, bf16x8 &p1) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) p0[r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -mc));
+    for (int r = 0; r < 8; ++r) p0[r] = (__bf16)__builtin_amdgcn_exp2f(sv[r]);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) p1[r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 + r], scale_log2, -mc));
+    for (int r = 0; r < 8; ++r) p1[r] = (__bf16)__builtin_amdgcn_exp2f(sv[8 + r]);
   };
   // their sum, from the bf16 values the MFMA multiplies
   auto half_sum = [&](const bf16x8 &p0, const bf16x8 &p1) {
@@ -176,25 +184,30 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     for (int e = 0; e < 4; ++e) ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * e], p1[2 * e + 1]}, ones, ls, false);
     return ls;
   };
-  // Taken when some lane's p sum of the half is not below 2^64 (always at the
-  // first block, where m = -inf; later only if a score exceeds m by more than
-  // 64 / c): raise m to the half's max over both lane halves, rescale O and
-  // l, redo P.
-  auto raise = [&](const f32x16 &sv, bf16x8 &p0, bf16x8 &p1, float &ls) {
+  // max over both lane halves of one half's 16 values per lane
+  auto half_max = [&](const f32x16 &sv) {
     float mx = sv[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+  // Taken when some lane's p sum of the half is not below 2^64 (a score more
+  // than 64 above m, in log2 units): raise m to the half's max, rescale O and
+  // l, shift every score register still to be used (this half, then `more`)
+  // by the same amount, redo the half's P.
+  auto raise = [&](f32x16 &sv, bf16x8 &p0, bf16x8 &p1, float &ls, auto &&more) {
+    const float delta = fmaxf(half_max(sv), 0.f);
+    m_run += delta;
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     l_run *= alpha;
-    m_run = m_new;
-    mc = m_new * scale_log2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] -= delta;
+    more(delta);
     half_p(sv, p0, p1);
     ls = half_sum(p0, p1);
   };
@@ -205,7 +218,20 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
   if (nkb > 1) issue_k(1, 1);
   vmcnt_barrier<0>();
   f32x16 sa[2], sb[2];
-  qk(lds_bytes, sa);
+  qk(lds_bytes, sa, 0.f);
+  // m starts at block 0's max (over existing keys), the scores relative to it
+  if (T < AK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + (r >> 3) * 16 + hf * 8 + (r & 7) >= T) sa[kb][r] = -INFINITY;
+  }
+  m_run = fmaxf(half_max(sa[0]), half_max(sa[1]));
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sa[kb][r] -= m_run;
 
   // block j (parity P = j & 1): scores sc (computed one iteration earlier),
   // next block's scores into sn; K_{j+1} in K slot 1 - P, V_j in V slot P
@@ -231,7 +257,7 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
     half_p(sc[0], pf[0], pf[1]);
     float ls0 = half_sum(pf[0], pf[1]);
 
-    qk(Kn, sn);  // next block's scores (unused after the last block)
+    qk(Kn, sn, -m_run);  // next block's scores - m (unused after the last block)
     // interleave the 16 MFMAs with the K operand reads (two ahead) and the
     // softmax VALU work
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
@@ -242,7 +268,15 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
     }
     asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
-    if (__any(!(ls0 < P_LIMIT))) raise(sc[0], pf[0], pf[1], ls0);
+    if (__any(!(ls0 < P_LIMIT)))
+      raise(sc[0], pf[0], pf[1], ls0, [&](float delta) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[1][r] -= delta;
+          sn[0][r] -= delta;
+          sn[1][r] -= delta;
+        }
+      });
     l_run += ls0;
 
     // O^T += V^T P^T over the four 16-key chunks; the second half's P and row
@@ -256,7 +290,14 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
         const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vb + t * 32 * AK * 2 + v_lane[c]);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
       }
-    if (__any(!(ls1 < P_LIMIT))) raise(sc[1], pf[2], pf[3], ls1);
+    if (__any(!(ls1 < P_LIMIT)))
+      raise(sc[1], pf[2], pf[3], ls1, [&](float delta) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sn[0][r] -= delta;
+          sn[1][r] -= delta;
+        }
+      });
     l_run += ls1;
 #pragma unroll
     for (int c = 2; c < 4; ++c)
