@@ -21,10 +21,9 @@ namespace {
 // online-softmax statistics stay in the lane (one exchange with lane l ^ 32, by
 // v_permlane32_swap).  P^T in that layout is the B operand of O^T += V^T P^T,
 // whose A operand (32 features x 16 keys) is one 16-B LDS read per lane in the
-// feature-major tile.  Every operand read is a ds_read_b128: on gfx950 the LDS
-// moves about 140 B/clk per CU with 16-B reads but only about 76 B/clk with
-// 8-B reads (measured), and the reads of K and V for 32 queries per wave come
-// close to the MFMA time of the block.
+// feature-major tile.  Every operand read is one ds_read_b128 (the key-major
+// V tile needed two 8-B transposing reads per operand: twice the LDS
+// instructions and waits, 1.5 % slower on the Super shape).
 //
 // Software pipeline: block j's scores are computed one iteration ahead, so
 // while the MFMAs of S_{j+1} = K_{j+1} Q^T run, the same wave turns the first
