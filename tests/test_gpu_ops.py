@@ -165,6 +165,44 @@ def test_attention_small(T, H, dh):
     assert rel_err(got, ref) < 2.0 ** -7, rel_err(got, ref)
 
 
+# score offsets (log2 units) of successive 32-key halves: the running max must be
+# raised in a first half, in a second half only, several times in a row, and in
+# the partial last block; dips in between take the common path
+_RAISE_OFFSETS = [0, 5, 70, 65, 140, 130, 120, 200, 150, 100, 210, 205, 90, 80, 280, 350,
+                  100, 0, 10, 290, 300, 430]
+
+
+@pytest.mark.parametrize("dh", [128, 64])
+def test_attention_running_max_raises(dh):
+    """Keys whose scores jump by more than 64 log2 units above every earlier block's
+    (through one shared q/k coordinate per head), so the rescale-and-redo path runs."""
+    torch = require_gpu()
+    T, H = 64 * 11 - 20, 2
+    d = H * dh
+    say("attention raises", T, H, dh)
+    c = np.log2(np.e) / np.sqrt(dh)
+    q = bf16_to_f64(_bf16_rand(1, (T, d), 1.0))
+    k = bf16_to_f64(_bf16_rand(2, (T, d), 1.0))
+    v = bf16_to_f64(_bf16_rand(3, (T, d), 1.0))
+    alpha = np.array([np.round(o / (8 * c)) for o in _RAISE_OFFSETS])   # rounded to bf16 below, for both sides
+    for h in range(H):
+        q[:, h * dh] = 8.0
+        k[:, h * dh] = alpha[np.arange(T) // 32]
+    qkv = synth.f32_to_bf16(np.concatenate([q, k, v], axis=1).astype(np.float32))
+    dq = _dev(torch, qkv)
+    ldvt = dlo.v_t_stride(T)
+    dvt = torch.full((d, ldvt), 0x7FC0, dtype=torch.int16, device="cuda")
+    dout = torch.zeros((T, d), dtype=torch.int16, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    dlo.op_v_transpose(dq.data_ptr(), 3 * d, T, d, dvt.data_ptr(), ldvt, st)
+    dlo.op_attention(dq.data_ptr(), 3 * d, dvt.data_ptr(), ldvt, T, H, dh, dout.data_ptr(), d, st)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(dout.cpu().numpy().view(np.uint16))
+    ref = of.attention(bf16_to_f64(qkv[:, :d]), bf16_to_f64(qkv[:, d:2 * d]), bf16_to_f64(qkv[:, 2 * d:]), H)
+    assert np.all(np.isfinite(got))
+    assert rel_err(got, ref) < 2.0 ** -7, rel_err(got, ref)
+
+
 def test_attention_full_size_sampled():
     """Super-shaped attention: T=28800, 40 heads of 128, sampled query rows and heads."""
     torch = require_gpu()
