@@ -221,20 +221,26 @@ def test_attention_full_size_sampled():
         assert rel_err(got[rows][:, cols], ref) < 2.0 ** -7
 
 
-@pytest.mark.parametrize("T,d,ldx", [(1, 256, 256), (33, 1024, 1024), (17, 5120, 5120), (9, 2048, 4096)])
-def test_ln_modulate(T, d, ldx):
+# (T, d, ldx, goff): the 16-B path (d % 1024 == 0, ldx % 4 == 0) with gamma and beta
+# at 4-B offsets as in a slot's fp32 region (goff = 1), the per-element path for
+# other widths and for ldx % 4 != 0
+@pytest.mark.parametrize("T,d,ldx,goff", [(1, 256, 256, 0), (33, 1024, 1024, 0), (17, 5120, 5120, 1),
+                                          (9, 2048, 4096, 0), (5, 3072, 3076, 1), (7, 1024, 1030, 0),
+                                          (3, 768, 768, 1)])
+def test_ln_modulate(T, d, ldx, goff):
     torch = require_gpu()
-    say("ln_modulate", T, d, ldx)
+    say("ln_modulate", T, d, ldx, goff)
     x = synth.normal_f32(20, 9, 0, 0, (T, ldx), 0.5, 2.0)
     gamma = synth.normal_f32(21, 9, 0, 0, (d,), 1.0, 0.1)
     beta = synth.normal_f32(22, 9, 0, 0, (d,), 0.0, 0.1)
     shift = synth.normal_f32(23, 9, 0, 0, (d,), 0.0, 0.1)
     scale = synth.normal_f32(24, 9, 0, 0, (d,), 0.0, 0.1)
     eps = np.array([1e-6], np.float32)
-    dx, dg, db, de, dsh, dsc = (_dev(torch, a) for a in (x, gamma, beta, eps, shift, scale))
+    dx, de, dsh, dsc = (_dev(torch, a) for a in (x, eps, shift, scale))
+    dgb = _dev(torch, np.concatenate([np.zeros(goff, np.float32), gamma, beta]))
     dout = torch.zeros((T, d), dtype=torch.int16, device="cuda")
-    dlo.op_ln_modulate(dx.data_ptr(), ldx, T, d, dg.data_ptr(), db.data_ptr(), de.data_ptr(),
-                       dsh.data_ptr(), dsc.data_ptr(), dout.data_ptr(),
+    dlo.op_ln_modulate(dx.data_ptr(), ldx, T, d, dgb.data_ptr() + 4 * goff, dgb.data_ptr() + 4 * (goff + d),
+                       de.data_ptr(), dsh.data_ptr(), dsc.data_ptr(), dout.data_ptr(),
                        torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     got = bf16_to_f64(dout.cpu().numpy().view(np.uint16))
