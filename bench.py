@@ -179,6 +179,10 @@ def environment(torch, dev):
             except OSError:
                 link[key] = None
         env["pcie"] = link
+        try:  # engine clock levels (current one starred), as the driver lists them
+            env["sclk_levels"] = open(f"/sys/bus/pci/devices/{bdf}/pp_dpm_sclk").read().split("\n")[:8]
+        except OSError:
+            env["sclk_levels"] = None
     model = None
     try:
         for ln in open("/proc/cpuinfo"):
@@ -424,6 +428,8 @@ def main():
         "steady_window": {k: avg.get(k) for k in ("window_ms", "compute_busy_ms", "copy_busy_ms")},
         "per_kernel_ms_per_block": {nm: per_kernel[j] / launches for j, nm in enumerate(names)},
         "roofline": roofline,
+        # device weight memory of the streamed path: exactly two slots of the largest block
+        "weight_hbm": {"two_slots_bytes": 2 * r.plan.slot_bytes, "allocated_bytes": r.slot_alloc_bytes},
         "setup_s": {"pin_alloc": t_alloc, "generate": t_gen, "pack": t_pack},
         "env": environment(torch, dev),
     }

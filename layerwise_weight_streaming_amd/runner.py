@@ -28,7 +28,9 @@ class StackRunner:
         self.n_blocks = len(blocks)
         sb = self.plan.slot_bytes
         # exactly two slots, each the size of the largest block
+        before = torch.cuda.memory_allocated(self.dev)
         self.slots = [torch.empty(sb, dtype=torch.uint8, device=self.dev) for _ in range(2)]
+        self.slot_alloc_bytes = torch.cuda.memory_allocated(self.dev) - before
         self.ws_bytes = self.plan.workspace_bytes(tokens)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.dev)
         self.x = torch.zeros((tokens, D), dtype=torch.float32, device=self.dev)
