@@ -372,9 +372,11 @@ def main():
     launches = 0
     work = np.zeros(len(names))
     ov = []
+    step_ms = []   # each step's GPU time: its trace is relative to the step's own start event
     for run in runs:
         tr = run.trace()
         kt = run.kernel_times()
+        step_ms.append(max(e["t_compute_end"] for e in tr))
         per_kernel += kt.sum(axis=0)
         launches += kt.shape[0]
         for e, row in zip(tr, kt):
@@ -407,6 +409,7 @@ def main():
         "unit": "blocks/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall / args.steps * 1e3,
+        "step_ms": {"per_step": step_ms, "median": float(np.median(step_ms))},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "n_blocks": n,
