@@ -214,7 +214,7 @@ def measure_link(torch, dev, gib=1, reps=4):
     return reps * n / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(w, seed, rows=128):
+def cpu_baseline(w, seed, n_blocks, rows=128):
     """The oracle, untouched, on a bounded sample: sampled output rows of the first block.
 
     dit_block_rows computes LN1 and the k/v projections for every token and the
@@ -240,6 +240,8 @@ def cpu_baseline(w, seed, rows=128):
     frac = f_sample / block_flops(d, T)
     blocks_per_s = frac / dt
     return {"value": blocks_per_s, "unit": "blocks/s", "cores": cores, "kind": "oracle",
+            # a pass of the n-block stack moves T tokens
+            "tokens_per_s": blocks_per_s * T / n_blocks,
             "sample": (f"float64 oracle, first block of the {w.name} stack (d={d}, T={T}): "
                        f"k/v for all tokens + {rows} sampled query rows, {dt:.1f} s for "
                        f"{frac * 100:.2f}% of a block's FLOPs, scaled by that FLOP fraction")}
@@ -472,7 +474,7 @@ def main():
     r.close()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
-        result["cpu_baseline"] = cpu_baseline(w, args.seed)
+        result["cpu_baseline"] = cpu_baseline(w, args.seed, n)
     print(json.dumps(result), flush=True)
 
 
