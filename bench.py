@@ -232,10 +232,16 @@ def cpu_baseline(w, seed, n_blocks, rows=128):
     params = synth.block_params(seed, 0, d)
     x = synth.activations(seed, T, w.D)
     c = synth.conditioning(seed, w.D)
+    rows = min(rows, T)
     idx = np.linspace(0, T - 1, rows).astype(np.int64)
-    t0 = time.perf_counter()
-    of.dit_block_rows(x, c, of.param_dict(params), H, idx)
-    dt = time.perf_counter() - t0
+    P = of.param_dict(params)
+    reps, t0 = 0, time.perf_counter()
+    while True:   # at least ~2 s of work, so small blocks are timed over many repetitions
+        of.dit_block_rows(x, c, P, H, idx)
+        reps += 1
+        if time.perf_counter() - t0 >= 2.0 or reps >= 1000:
+            break
+    dt = (time.perf_counter() - t0) / reps
     f_sample = 2 * T * d * 2 * d + rows * (2 * d * d + 4 * T * d + 2 * d * d + 16 * d * d) + 12 * d * d
     frac = f_sample / block_flops(d, T)
     blocks_per_s = frac / dt
@@ -243,8 +249,9 @@ def cpu_baseline(w, seed, n_blocks, rows=128):
             # a pass of the n-block stack moves T tokens
             "tokens_per_s": blocks_per_s * T / n_blocks,
             "sample": (f"float64 oracle, first block of the {w.name} stack (d={d}, T={T}): "
-                       f"k/v for all tokens + {rows} sampled query rows, {dt:.1f} s for "
-                       f"{frac * 100:.2f}% of a block's FLOPs, scaled by that FLOP fraction")}
+                       f"k/v for all tokens + {rows} sampled query rows, {dt:.3g} s per sample "
+                       f"(mean of {reps}) for {frac * 100:.2f}% of a block's FLOPs, scaled by that "
+                       f"FLOP fraction")}
 
 
 def main():
