@@ -112,20 +112,28 @@ def modulation(c, P, d):
     return [mod[i * d:(i + 1) * d] for i in range(6)]
 
 
-def dit_block(x, c, P, n_heads):
-    """One block on residual x [T, D] (float64, updated copy returned)."""
+def dit_block(x, c, P, n_heads, act_fp8=False):
+    """One block on residual x [T, D] (float64, updated copy returned).
+
+    act_fp8: the four block linears take their input through per-token E4M3
+    quantization (oracle.fp8.quantize_rows), the W8A8 form of an FP8 block's
+    online FP8 linears; the adaLN linear keeps its float input.
+    """
+    from . import fp8
+
+    lin_in = fp8.fake_quant_rows if act_fp8 else (lambda t: t)
     d = P["norm1.weight"].shape[0]
     x = np.array(x, dtype=np.float64, copy=True)
     shift1, scale1, gate1, shift2, scale2, gate2 = modulation(c, P, d)
     xb = x[:, :d]
     h = layer_norm(xb, P["norm1.weight"], P["norm1.bias"], P["norm1.eps"][0]) * (1.0 + scale1) + shift1
-    qkv = linear(h, P["attn.qkv.weight"], P["attn.qkv.bias"])
+    qkv = linear(lin_in(h), P["attn.qkv.weight"], P["attn.qkv.bias"])
     q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
     a = attention(q, k, v, n_heads)
-    xb += gate1 * linear(a, P["attn.out.weight"], P["attn.out.bias"])
+    xb += gate1 * linear(lin_in(a), P["attn.out.weight"], P["attn.out.bias"])
     h2 = layer_norm(xb, P["norm2.weight"], P["norm2.bias"], P["norm2.eps"][0]) * (1.0 + scale2) + shift2
-    u = gelu_erf(linear(h2, P["mlp.fc1.weight"], P["mlp.fc1.bias"]))
-    xb += gate2 * linear(u, P["mlp.fc2.weight"], P["mlp.fc2.bias"])
+    u = gelu_erf(linear(lin_in(h2), P["mlp.fc1.weight"], P["mlp.fc1.bias"]))
+    xb += gate2 * linear(lin_in(u), P["mlp.fc2.weight"], P["mlp.fc2.bias"])
     return x
 
 
@@ -156,14 +164,17 @@ def dit_block_rows(x, c, P, n_heads, rows):
     return y
 
 
-def forward_stack(x, c, blocks, heads, passes):
+def forward_stack(x, c, blocks, heads, passes, act_fp8=False):
     """``passes`` chained passes over the blocks.
 
     blocks: list of [(name, dtype, array)] per block; heads: heads per block.
+    act_fp8: blocks with FP8 weights run their linears in the W8A8 form
+    (see dit_block); bf16 blocks are unaffected.
     """
     Ps = [param_dict(b) for b in blocks]
+    fp8_block = [any(dt == "fp8" for _, dt, _ in b) for b in blocks]
     y = np.asarray(x, dtype=np.float64)
     for _ in range(passes):
-        for P, H in zip(Ps, heads):
-            y = dit_block(y, c, P, H)
+        for P, H, f8 in zip(Ps, heads, fp8_block):
+            y = dit_block(y, c, P, H, act_fp8=act_fp8 and f8)
     return y

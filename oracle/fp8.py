@@ -97,6 +97,35 @@ def dequantize(codes: np.ndarray, scale) -> np.ndarray:
     return DECODE[np.asarray(codes, dtype=np.uint8)] * np.float64(np.float32(scale))
 
 
+def quantize_rows(x):
+    """Per-row (per-token) dynamic E4M3 of an activation matrix [M, K].
+
+    The reading of an online FP8 linear's input (the pages leave it open; listed
+    in the design doc): row r gets scale_r = amax_r / 448 in float32 (NaN entries
+    ignored, 1.0 for an all-zero row), and each element the E4M3 code nearest to
+    float32(x) / scale_r, the division in float32, ties to the even code,
+    saturating at +-448.  Returns (codes uint8 [M, K], scales float32 [M]).
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    if x32.ndim != 2:
+        raise ValueError("quantize_rows takes a matrix")
+    if x32.shape[1] == 0:
+        return np.zeros(x32.shape, dtype=np.uint8), np.ones(x32.shape[0], dtype=np.float32)
+    with np.errstate(invalid="ignore"):
+        amax = np.nanmax(np.abs(x32), axis=1).astype(np.float32)
+    amax = np.where(np.isnan(amax), np.float32(0), amax).astype(np.float32)
+    scale = np.where(amax == 0, np.float32(1.0), amax / np.float32(E4M3_MAX)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        codes = encode_e4m3((x32 / scale[:, None]).astype(np.float32))
+    return codes, scale
+
+
+def fake_quant_rows(x):
+    """What an FP8 linear multiplies: the per-row codes times their scales, in float64."""
+    codes, scale = quantize_rows(x)
+    return DECODE[codes] * scale.astype(np.float64)[:, None]
+
+
 def quantize_block(params):
     """A bf16 DiT block's parameter list -> its per-tensor FP8 form.
 

@@ -98,3 +98,71 @@ def test_fp8_block_form_and_forward_plumbing():
     y_bf16, y_fp8 = of.dit_block(x, c, of.param_dict(ps), 4), of.dit_block(x, c, P, 4)
     upd = np.max(np.abs(y_bf16 - x))
     assert 0 < np.max(np.abs(y_fp8 - y_bf16)) < 0.2 * upd
+
+
+# ---------------------------------------------------------------------------
+# per-token activation quantization (the W8A8 reading of an FP8 block's linears)
+# ---------------------------------------------------------------------------
+
+def _nearest_code_brute(v):
+    """Index of the finite E4M3 value nearest to v; ties to the even code (v finite)."""
+    best = None
+    for c in range(256):
+        val = fp8.DECODE[c]
+        if np.isnan(val) or (val == 0 and c == 0x80):
+            continue
+        dist = abs(val - v)
+        if best is None or dist < best[0] or (dist == best[0] and c % 2 == 0 and best[1] % 2 == 1):
+            best = (dist, c)
+    return best[1]
+
+
+def test_quantize_rows_against_brute_force_and_per_row_amax():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((6, 40)) * np.array([1e-3, 0.1, 1, 7, 300, 2e4])[:, None]).astype(np.float32)
+    codes, scale = fp8.quantize_rows(x)
+    for r in range(6):
+        amax = np.float32(np.max(np.abs(x[r])))
+        assert scale[r] == np.float32(amax / np.float32(448.0))
+        for j in range(40):
+            y = np.float32(x[r, j] / scale[r])
+            c = int(codes[r, j])
+            v = abs(float(y))
+            want = _nearest_code_brute(min(v, 448.0)) | (0x80 if y < 0 else 0)
+            assert c == want, (r, j, y, c, want)
+        # the largest magnitude maps to +-448 (code 0x7E / 0xFE)
+        jmax = int(np.argmax(np.abs(x[r])))
+        assert codes[r, jmax] & 0x7F == 0x7E
+
+
+def test_quantize_rows_zero_rows_scaling_and_error_bound():
+    x = np.zeros((3, 8), np.float32)
+    x[1] = [1, -2, 3, -4, 5, -6, 7, -8]
+    x[2] = x[1] * 64          # a power of two scales the scale, not the codes
+    codes, scale = fp8.quantize_rows(x)
+    assert scale[0] == 1.0 and np.all(codes[0] == 0)
+    assert scale[2] == scale[1] * 64 and np.array_equal(codes[1], codes[2])
+    # relative error of a normal-range element at most half a 3-bit mantissa step, 2^-4
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal((50, 64)).astype(np.float32)
+    deq = fp8.fake_quant_rows(y)
+    big = np.abs(y) >= (np.max(np.abs(y), axis=1, keepdims=True) / 448.0) * 2.0 ** -6
+    assert np.all(np.abs(deq - y)[big] <= 2.0 ** -4 * np.abs(y)[big] * (1 + 1e-6))
+
+
+def test_w8a8_block_is_close_to_the_bf16_block_and_keeps_the_identity():
+    d, H, T = 64, 2, 12
+    blk = fp8.quantize_block(synth.block_params(3, 0, d))
+    P = of.param_dict(blk)
+    rng = np.random.default_rng(13)
+    x, c = rng.standard_normal((T, d)), rng.standard_normal(d)
+    y = of.dit_block(x, c, P, H)
+    yq = of.dit_block(x, c, P, H, act_fp8=True)
+    upd, updq = y - x, yq - x
+    err = np.max(np.abs(updq - upd)) / np.max(np.abs(upd))
+    assert 0 < err < 0.1        # FP8 inputs move the update by a few percent, not more
+    # adaLN-zero: gates 0 => output == input, quantized or not
+    P0 = dict(P)
+    P0["adaln.weight"] = np.zeros_like(P["adaln.weight"])
+    P0["adaln.bias"] = np.zeros_like(P["adaln.bias"])
+    assert np.array_equal(of.dit_block(x, c, P0, H, act_fp8=True), x)
