@@ -5,7 +5,9 @@ computes: the pages verify it by byte-identical outputs across execution
 strategies ([Aug] "NVIDIA B300 GPU Results", correctness paragraph).  So the
 oracle is the plain resident forward.  It reads the same bf16 weights, widened
 exactly to float64, and computes every activation in float64 with no rounding
-to bf16 anywhere.
+to bf16 anywhere -- except where an activation decides an integer: the W8A8
+form of an FP8 block quantizes each linear's input to E4M3 codes, and takes
+that decision on the input as the model stores it, bf16 (round_bf16).
 
 The pages never spell out the block (the model code is used unchanged, [Jul]
 "Module Architecture").  The block below is the plainest adaLN-Zero DiT block
@@ -33,6 +35,16 @@ import math
 
 import numpy as np
 from scipy.special import erf
+
+
+def round_bf16(x) -> np.ndarray:
+    """float64 -> the nearest bfloat16 value (8 significant bits, ties to the even
+    significand), as float64.  Exponents below bfloat16's smallest normal keep its
+    subnormal spacing 2^-133; the values here never reach its overflow range."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                      # x = m 2^e with 1/2 <= |m| < 1
+    e = np.maximum(e, -125)
+    return np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
 
 
 def widen_bf16(bits: np.ndarray) -> np.ndarray:
@@ -117,11 +129,14 @@ def dit_block(x, c, P, n_heads, act_fp8=False):
 
     act_fp8: the four block linears take their input through per-token E4M3
     quantization (oracle.fp8.quantize_rows), the W8A8 form of an FP8 block's
-    online FP8 linears; the adaLN linear keeps its float input.
+    online FP8 linears; the adaLN linear keeps its float input.  The quantizer
+    reads the input as the model stores it, rounded to bf16 (round_bf16): the
+    pages fix no precision for this decision, so it is taken in the storage
+    precision of the activations it quantizes.
     """
     from . import fp8
 
-    lin_in = fp8.fake_quant_rows if act_fp8 else (lambda t: t)
+    lin_in = (lambda t: fp8.fake_quant_rows(round_bf16(t))) if act_fp8 else (lambda t: t)
     d = P["norm1.weight"].shape[0]
     x = np.array(x, dtype=np.float64, copy=True)
     shift1, scale1, gate1, shift2, scale2, gate2 = modulation(c, P, d)

@@ -166,3 +166,31 @@ def test_w8a8_block_is_close_to_the_bf16_block_and_keeps_the_identity():
     P0["adaln.weight"] = np.zeros_like(P["adaln.weight"])
     P0["adaln.bias"] = np.zeros_like(P["adaln.bias"])
     assert np.array_equal(of.dit_block(x, c, P0, H, act_fp8=True), x)
+
+
+def test_round_bf16_is_the_nearest_even_bf16_value():
+    """Against the input generator's float32 -> bf16 rounding (a bit-level routine, not
+    the oracle's frexp form) on float32 inputs, and by the definition on float64 ones:
+    the result is a bf16 value, no bf16 value lies closer, and exact midpoints go to
+    the even significand."""
+    rng = np.random.default_rng(5)
+    x32 = (rng.standard_normal(20000) * np.exp2(rng.uniform(-40, 40, 20000))).astype(np.float32)
+    want = (synth.f32_to_bf16(x32).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(of.round_bf16(x32.astype(np.float64)), want)
+    x = rng.standard_normal(20000) * np.exp2(rng.uniform(-20, 20, 20000))
+    r = of.round_bf16(x)
+    r32 = r.astype(np.float32)
+    assert np.array_equal(r32.astype(np.float64), r)                 # a float32 ...
+    assert np.all(r32.view(np.uint32) & 0xFFFF == 0)                  # ... with 8 significant bits
+    up = (r32.view(np.uint32) + np.where(r >= 0, 0x10000, -0x10000).astype(np.uint32)).view(np.float32)
+    dn = (r32.view(np.uint32) - np.where(r >= 0, 0x10000, -0x10000).astype(np.uint32)).view(np.float32)
+    for nb in (up, dn):                                                # neighbours are no closer
+        assert np.all(np.abs(x - r) <= np.abs(x - nb.astype(np.float64)))
+    # midpoints between consecutive bf16 values 1 + j/128 and 1 + (j+1)/128
+    j = np.arange(128)
+    mid = 1.0 + (j + 0.5) / 128.0
+    got = of.round_bf16(np.concatenate([mid, -mid * 2.0 ** -30]))
+    even = 1.0 + np.where(j % 2 == 0, j, j + 1) / 128.0
+    assert np.array_equal(got, np.concatenate([even, -even * 2.0 ** -30]))
+    assert of.round_bf16(0.0) == 0.0 and of.round_bf16(2.0 ** -140) == 0.0
+    assert of.round_bf16(3 * 2.0 ** -134) == 2.0 ** -132             # subnormal tie to even
