@@ -27,16 +27,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 LINK_PEAK_GBS = 32.0 * 16 * 128 / 130 / 8   # PCIe 5.0 x16, one direction: 63.0 GB/s
 
 
-def kernel_work(name, d, T, fp8=False):
-    """Algorithmic work of one launch: (amount, unit, bound)."""
-    if name == "dequant_fp8":   # E4M3 codes in, bf16 weights out (nothing for a bf16 block)
-        return (18 * d * d * 3 if fp8 else 0) / 1e9, "GB", "hbm"
-    if name == "adaln_gemv":
-        return (6 * d * d * 2 + 6 * d * 4 * 2 + d * 4) / 1e9, "GB", "hbm"
+def kernel_work(name, d, T, fp8=False, w8a8=False):
+    """Algorithmic work of one launch: (amount, unit, bound).  w8a8: an FP8 block
+    run with FP8 compute (only the adaLN weight dequantised, inputs quantised)."""
+    if name == "dequant_fp8":   # the four linears: E4M3 codes in, bf16 weights out (W8A16 only)
+        return (12 * d * d * 3 if fp8 and not w8a8 else 0) / 1e9, "GB", "hbm"
+    if name.startswith("quant_"):   # bf16 rows in, E4M3 codes + fp32 row scales out
+        K = 4 * d if name == "quant_u" else d
+        return ((T * K * 3 + T * 4) if (fp8 and w8a8) else 0) / 1e9, "GB", "hbm"
+    if name == "adaln_gemv":   # bf16 or E4M3 weight rows, silu(c), bias in, modulation out
+        return (6 * d * d * (1 if fp8 else 2) + 6 * d * 4 * 2 + d * 4) / 1e9, "GB", "hbm"
     if name in ("ln1_modulate", "ln2_modulate"):
         return (T * d * 4 + T * d * 2) / 1e9, "GB", "hbm"
     flops = {"gemm_qk": 2 * T * d * 2 * d, "gemm_v_t": 2 * T * d * d, "attention": 4 * T * T * d,
@@ -269,6 +274,9 @@ def main():
     ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: per-tensor E4M3 weights + fp32 scales (quantized on the host before "
                          "packing), dequantised on the device after each copy")
+    ap.add_argument("--compute", default="bf16", choices=["bf16", "fp8"],
+                    help="fp8 (needs --weights fp8): the four linears of each block as W8A8 "
+                         "FP8 products (per-row E4M3 inputs); attention stays bf16")
     ap.add_argument("--resident-layers", type=int, default=0,
                     help="keep blocks 0 .. R-1 in device memory; stream the rest")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -279,6 +287,9 @@ def main():
                     help="skip the streamed == resident bit-exact check")
     args = ap.parse_args()
 
+    if args.compute == "fp8" and args.weights != "fp8":
+        print("--compute fp8 needs --weights fp8", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the stack is streamed from this host into this "
               "GPU's two slots; run with --gpus 1", file=sys.stderr)
@@ -357,17 +368,19 @@ def main():
     log(f"pinned H2D microbenchmark: {link:.1f} GB/s")
 
     R = args.resident_layers
+    w8a8 = args.compute == "fp8"
+    cflags = dlo.FP8_COMPUTE if w8a8 else 0
     if R:
         r.make_resident(R)
         log(f"{R} resident layers placed")
     for i in range(args.warmup):
-        r.forward(P, n_resident=R, want_run=False)
+        r.forward(P, flags=cflags, n_resident=R, want_run=False)
         r.synchronize()
         log(f"warmup step {i + 1} done")
 
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    runs = [r.forward(P, flags=dlo.TRACE_TIMING, n_resident=R) for _ in range(args.steps)]
+    runs = [r.forward(P, flags=dlo.TRACE_TIMING | cflags, n_resident=R) for _ in range(args.steps)]
     r.synchronize()
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
@@ -391,7 +404,7 @@ def main():
         for e, row in zip(tr, kt):
             d, f8 = infos[e["block"]]["d_model"], infos[e["block"]]["fp8"]
             for j, nm in enumerate(names):
-                work[j] += kernel_work(nm, d, T, f8)[0]
+                work[j] += kernel_work(nm, d, T, f8, w8a8)[0]
         m = overlap_metrics(tr, copy_bytes, flops)
         if m:
             ov.append(m)
@@ -403,7 +416,8 @@ def main():
     _, unit, kbound = kernel_work(dname, w.width(0), T)
     avg_ms = per_kernel[jdom] / launches
     achieved = work[jdom] / launches / (avg_ms * 1e-3)
-    peak = PEAK_BF16_TFLOPS if kbound == "mfma" else PEAK_HBM_GBS
+    fp8_mfma = w8a8 and dname.startswith("gemm_") and any(i["fp8"] for i in infos)
+    peak = (PEAK_FP8_TFLOPS if fp8_mfma else PEAK_BF16_TFLOPS) if kbound == "mfma" else PEAK_HBM_GBS
     roofline = {"kernel": dname, "bound": kbound, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s" if kbound == "mfma" else "GB/s", "frac": achieved / peak,
                 "traffic": counted_traffic(dname, w.name),
@@ -420,13 +434,13 @@ def main():
         "ms_per_step": wall / args.steps * 1e3,
         "step_ms": {"per_step": step_ms, "median": float(np.median(step_ms))},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "fp8e4m3+bf16" if w8a8 else "bf16", "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "n_blocks": n,
                    "widths": list(w.widths), "head_dim": w.head_dim, "tokens": T, "batch": 1,
                    "k": w.k, "passes": P, "slot_bytes": r.plan.slot_bytes,
                    "block_copy_bytes": max(copy_bytes), "host_store_bytes": sum(copy_bytes),
                    "parallelism": "single GPU", "store": args.store, "resident_layers": R,
-                   "weights": args.weights,
+                   "weights": args.weights, "compute": args.compute,
                    "pinned_blocks": store_info["pinned_blocks"],
                    "staged_blocks": store_info["staged_blocks"]},
         "tokens_per_s": T * P * args.steps / wall,
@@ -450,14 +464,14 @@ def main():
         # the pages' own correctness criterion at full scale: streamed == resident, bit-exact
         log("verify: streamed vs resident, one step each from the same inputs")
         r.set_inputs(x0, c0)
-        r.forward(P, n_resident=R, want_run=False)
+        r.forward(P, flags=cflags, n_resident=R, want_run=False)
         xs = r.x_host()
         r.set_inputs(x0, c0)
         r.make_resident()
         r.synchronize()
         torch.cuda.synchronize(dev)
         t0 = time.perf_counter()
-        r.forward(P, resident=True, want_run=False)
+        r.forward(P, flags=cflags, resident=True, want_run=False)
         r.synchronize()
         torch.cuda.synchronize(dev)
         t_res = time.perf_counter() - t0

@@ -138,8 +138,10 @@ int dlo_plan_param_offset(const dlo_plan *plan, int32_t b, int32_t p, int64_t *b
 
 /* Device workspace needed by dlo_forward_stack for `tokens` rows (batch 1):
  * activations of one block at the widest d, plus, when the plan holds FP8
- * blocks, the bf16 weights of the widest FP8 block (18 d^2 elements) that its
- * forward dequantises into; -1 on error. */
+ * blocks, the bf16 weights of the widest FP8 block's four linears (12 d^2
+ * elements) that its forward dequantises into and the E4M3 codes (tokens x 4 d
+ * bytes) and row scales of a W8A8 linear's input (DLO_FP8_COMPUTE); -1 on
+ * error. */
 int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens);
 
 /* ---------------------------------------------------------------------------
@@ -267,6 +269,15 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 #define DLO_TRACE_TIMING 2u  /* timestamp copies, block computes and every kernel */
 #define DLO_RESIDENT 4u      /* no streaming: block b is read from resident_blocks[b] (same as
                                 n_resident = number of blocks) */
+#define DLO_FP8_COMPUTE 8u   /* FP8 blocks run their qkv, out, fc1 and fc2 linears as W8A8
+                                products ([Doc] "Request and loading constraints", online FP8
+                                linears): the input quantised per row to E4M3 as by
+                                dlo_op_quantize_rows_fp8, then dlo_op_gemm_fp8 with the
+                                weight's codes and scale read in place from the slot.
+                                Without it an FP8 block dequantises its four linears'
+                                weights to bf16 (W8A16).  Either way an FP8 block's adaLN
+                                GEMV reads its codes (dlo_op_adaln_fp8), and bf16 blocks are
+                                unaffected. */
 
 typedef struct {
   void *slot[2];            /* device, slot_bytes each, distinct (unused if nothing streams) */
@@ -283,7 +294,7 @@ typedef struct {
   int32_t tokens;           /* rows of x (batch 1), >= 1; (tokens + 64) * 3 * widest d * 2
                                < 2^31, else DLO_E_UNSUPPORTED */
   int32_t passes;           /* chained passes over the stack, >= 1 */
-  uint32_t flags;           /* DLO_TRACE_* | DLO_RESIDENT */
+  uint32_t flags;           /* DLO_TRACE_* | DLO_RESIDENT | DLO_FP8_COMPUTE */
   int32_t n_resident;       /* resident layers R in [0, n] ([Doc] "Validation coverage":
                                resident-layer requests): blocks 0 .. R-1 are read from
                                resident_blocks[b] and never copied; blocks R .. n-1 stream
@@ -337,11 +348,13 @@ typedef struct {
 int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_out);
 
 /* DLO_TRACE_TIMING: per step, the duration in ms of each of the block's kernels in
- * launch order (DLO_KERNELS_PER_BLOCK per step), after the run completed.  Entry 0
- * is the FP8 weight dequantisation (0 for a bf16 block); then adaln_gemv,
- * ln1_modulate, gemm_qkv, v_transpose, attention, gemm_out, ln2_modulate,
- * gemm_fc1, gemm_fc2 (dlo_kernel_name). */
-#define DLO_KERNELS_PER_BLOCK 10
+ * launch order (DLO_KERNELS_PER_BLOCK per step), after the run completed: the FP8
+ * weight dequantisation (0 for a bf16 block), adaln_gemv, ln1_modulate, quant_h,
+ * gemm_qk, gemm_v_t, attention, quant_attn, gemm_out_residual, ln2_modulate,
+ * quant_h2, gemm_fc1_gelu, quant_u, gemm_fc2_residual (dlo_kernel_name).  The
+ * quant_* entries are the W8A8 input quantisations, 0 unless an FP8 block runs
+ * with DLO_FP8_COMPUTE. */
+#define DLO_KERNELS_PER_BLOCK 14
 int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
 /* name of kernel j (0 <= j < DLO_KERNELS_PER_BLOCK) of a block forward */
 const char *dlo_kernel_name(int32_t j);
@@ -393,6 +406,15 @@ int dlo_quantize_fp8(const uint16_t *w, int64_t n, uint8_t *codes, float *scale)
 int dlo_op_adaln(const uint16_t *W, const float *b, const float *cond, int32_t rows, int32_t d,
                  float *out, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* The same on an FP8 block's adaLN weight ([Doc] "Request and loading
+ * constraints": a 1-byte weight plus an fp32 scale): out[r] = w_scale[0] *
+ * sum_j value(W[r, j]) * silu(c[j]) + b[r], W OCP E4M3 codes [rows, d] (16-B
+ * aligned, d % 16 == 0, else DLO_E_UNSUPPORTED), w_scale one fp32 value; code
+ * values are exact in fp32, so the weights carry no bf16 rounding.  workspace
+ * >= 4 d bytes (silu(c)), else DLO_E_WORKSPACE. */
+int dlo_op_adaln_fp8(const uint8_t *W, const float *w_scale, const float *b, const float *cond, int32_t rows,
+                     int32_t d, float *out, void *workspace, int64_t workspace_bytes, void *stream);
+
 /* out[t, :] = bf16( LN(x[t, :d]; gamma, beta, *eps) * (1 + scale) + shift ), t < T;
  * x fp32 with row stride ldx; out bf16 [T, d]. */
 int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const float *gamma,
@@ -413,6 +435,32 @@ enum { DLO_EPI_BIAS = 0, DLO_EPI_BIAS_GELU = 1, DLO_EPI_GATED_RESIDUAL = 2, DLO_
 int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int32_t M,
                 int32_t N, int32_t K, const float *bias, const float *gate, void *C, int64_t ldc,
                 int32_t epilogue, void *stream);
+
+/* Per-row (per-token) dynamic E4M3 quantization of an activation matrix, the
+ * input side of an FP8 block's online FP8 linears in the W8A8 form (the pages
+ * only fix the weight side: [Doc] "Request and loading constraints"; the
+ * activation scaling is this library's reading): for each row r of x bf16
+ * [M, K] (row stride ldx), scales[r] = amax_r / 448 in fp32 (1 for an all-zero
+ * row; NaN entries ignored), codes[r, k] = the OCP E4M3 code nearest to
+ * x[r, k] / scales[r] (IEEE fp32 division), ties to the even code, saturating
+ * at 448, NaN -> 0x7F.  codes uint8 [M, ldq], scales fp32 [M]; all device,
+ * caller-owned.  K % 8 == 0, ldx and ldq multiples of 8 and >= K, x 16-B and
+ * codes 8-B aligned, else DLO_E_UNSUPPORTED. */
+int dlo_op_quantize_rows_fp8(const uint16_t *x, int64_t ldx, int32_t M, int32_t K, uint8_t *codes,
+                             int64_t ldq, float *scales, void *stream);
+
+/* The FP8 form of dlo_op_gemm: C = (A B^T) * a_scale[m] * b_scale[0] + bias, then
+ * the epilogue (0..3 as for dlo_op_gemm), with A [M, K] and B [N, K] OCP E4M3
+ * codes (row strides lda, ldb in bytes), a_scale fp32 [M] (per row, as
+ * dlo_op_quantize_rows_fp8 writes it) and b_scale one fp32 value (the weight's
+ * per-tensor scale, [Doc] "Request and loading constraints"); every product is
+ * exact and accumulates in fp32 on v_mfma_f32_32x32x64_f8f6f4.  All device,
+ * caller-owned.  N % 256 == 0, K % 64 == 0, lda and ldb multiples of 16, A, B,
+ * C, bias and gate 16-B aligned, ldc as for dlo_op_gemm, else
+ * DLO_E_UNSUPPORTED. */
+int dlo_op_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B, int64_t ldb,
+                    const float *b_scale, int32_t M, int32_t N, int32_t K, const float *bias,
+                    const float *gate, void *C, int64_t ldc, int32_t epilogue, void *stream);
 
 /* Feature-major copy of the v part of a fused qkv buffer, the layout the
  * block's attention reads its values in:

@@ -24,9 +24,9 @@ STATUS = {0: "DLO_OK", -1: "DLO_E_ARG", -2: "DLO_E_HOSTMEM", -3: "DLO_E_PIN",
 DTYPES = {"bf16": 0, "f32": 1, "fp8": 2}   # fp8: OCP E4M3, one byte
 DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
 STORE_PINNED, STORE_PAGEABLE, STORE_AUTO = 0, 1, 2
-TRACE_DIGEST, TRACE_TIMING, RESIDENT = 1, 2, 4
+TRACE_DIGEST, TRACE_TIMING, RESIDENT, FP8_COMPUTE = 1, 2, 4, 8
 EPI_BIAS, EPI_BIAS_GELU, EPI_GATED_RESIDUAL, EPI_BIAS_T = 0, 1, 2, 3
-KERNELS_PER_BLOCK = 10
+KERNELS_PER_BLOCK = 14
 MAX_GROUPS = 3
 OP_KIND = {0: "copy", 1: "compute", 2: "record", 3: "wait"}
 OP_STREAM = {0: "compute", 1: "copy"}
@@ -137,6 +137,16 @@ _SIGS = {
                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_void_p]),
+    "dlo_op_adaln_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p]),
+    "dlo_op_quantize_rows_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                                ctypes.c_void_p, ctypes.c_void_p]),
+    "dlo_op_gemm_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]),
     "dlo_op_v_transpose": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                           ctypes.c_void_p]),
@@ -423,6 +433,19 @@ def op_ln_modulate(x, ldx, T, d, gamma, beta, eps, shift, scale, out, stream):
 
 def op_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, stream):
     _check(lib().dlo_op_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, stream))
+
+
+def op_adaln_fp8(W, w_scale, b, cond, rows, d, out, workspace, workspace_bytes, stream):
+    _check(lib().dlo_op_adaln_fp8(W, w_scale, b, cond, rows, d, out, workspace, workspace_bytes, stream))
+
+
+def op_quantize_rows_fp8(x, ldx, M, K, codes, ldq, scales, stream):
+    _check(lib().dlo_op_quantize_rows_fp8(x, ldx, M, K, codes, ldq, scales, stream))
+
+
+def op_gemm_fp8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc, epilogue, stream):
+    _check(lib().dlo_op_gemm_fp8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc, epilogue,
+                                 stream))
 
 
 def v_t_stride(T):

@@ -129,8 +129,9 @@ int64_t schema_numel(const SchemaEntry &e, int64_t d) {
 }
 
 const char *kKernelNames[DLO_KERNELS_PER_BLOCK] = {
-    "dequant_fp8", "adaln_gemv", "ln1_modulate", "gemm_qk", "gemm_v_t", "attention",
-    "gemm_out_residual", "ln2_modulate", "gemm_fc1_gelu", "gemm_fc2_residual"};
+    "dequant_fp8", "adaln_gemv", "ln1_modulate", "quant_h", "gemm_qk", "gemm_v_t", "attention",
+    "quant_attn", "gemm_out_residual", "ln2_modulate", "quant_h2", "gemm_fc1_gelu", "quant_u",
+    "gemm_fc2_residual"};
 
 }  // namespace
 
@@ -380,8 +381,13 @@ int64_t round_up64(int64_t T) { return (T + 63) / 64 * 64; }
 
 int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d) {
   const int64_t d = max_d, f = fp8_d;
+  // FP8 blocks: the bf16 weights of their four linears (12 f^2 elements), and
+  // the E4M3 codes [T, 4f] and row scales [T] of a linear's input in the W8A8 form
+  const int64_t fp8 = f > 0 ? align_up(24 * f * f, DLO_ALIGN) + align_up(4 * T * f, DLO_ALIGN) +
+                                  align_up(4 * T, DLO_ALIGN)
+                            : 0;
   return align_up(4 * d, DLO_ALIGN) + align_up(24 * d, DLO_ALIGN) + align_up(2 * T * d, DLO_ALIGN) +
-         align_up(8 * round_up64(T) * d, DLO_ALIGN) + align_up(36 * f * f, DLO_ALIGN);
+         align_up(8 * round_up64(T) * d, DLO_ALIGN) + fp8;
 }
 
 int validate_block_against(const BlockPlan &bp, const dlo_block &blk, int b, bool need_src) {
@@ -916,11 +922,12 @@ int dlo_place_block(const dlo_plan *plan, const dlo_host_store *store, int32_t b
 namespace {
 
 struct Workspace {
-  float *silu_c, *mod;
+  float *silu_c, *mod, *act_scale;
   uint16_t *h, *big, *dq;
+  uint8_t *act_codes;
 };
 
-Workspace carve(void *ws, int32_t max_d, int64_t T) {
+Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d) {
   char *p = static_cast<char *>(ws);
   Workspace w;
   w.silu_c = reinterpret_cast<float *>(p);
@@ -931,28 +938,42 @@ Workspace carve(void *ws, int32_t max_d, int64_t T) {
   p += align_up(2 * T * max_d, DLO_ALIGN);
   w.big = reinterpret_cast<uint16_t *>(p);  // qk [T,2d], V^T [d,T64], a [T,d]; later u [T,4d]
   p += align_up(8 * round_up64(T) * max_d, DLO_ALIGN);
-  w.dq = reinterpret_cast<uint16_t *>(p);   // an FP8 block's weights, dequantised to bf16
+  w.dq = reinterpret_cast<uint16_t *>(p);   // an FP8 block's linear weights, dequantised to bf16
+  p += fp8_d > 0 ? align_up(24 * (int64_t)fp8_d * fp8_d, DLO_ALIGN) : 0;
+  w.act_codes = reinterpret_cast<uint8_t *>(p);  // W8A8: a linear input's E4M3 codes [T, <= 4d]
+  p += fp8_d > 0 ? align_up(4 * T * fp8_d, DLO_ALIGN) : 0;
+  w.act_scale = reinterpret_cast<float *>(p);    // ... and its per-row scales [T]
   return w;
 }
 
 // One block forward on the compute stream, parameters re-pointed into `base`
 // (a slot or a resident image) with no copy ([Jul] "How It Works", step 3).
+// An FP8 block's adaLN GEMV reads the E4M3 codes and scale in place; its four
+// linears either run on bf16 copies of their weights (dequantised into the
+// workspace) or, with fp8 compute, as W8A8 products: each input quantised per
+// row to E4M3, times the weight's codes and per-tensor scale ([Doc] "Request
+// and loading constraints", online FP8 linears).
 hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forward_args *a,
                          const Workspace &w, hipStream_t s, hipEvent_t *kernel_end) {
   const int d = bp.d, H = bp.heads, dh = d / H, T = a->tokens;
   auto P = [&](int lp) { return base + bp.logical_byte(lp); };
   auto F = [&](int lp) { return reinterpret_cast<const float *>(P(lp)); };
+  const bool fp8 = bp.kind == KIND_DIT_FP8;
+  const bool w8a8 = fp8 && (a->flags & DLO_FP8_COMPUTE);
   hipError_t e;
-  // bf16 weights: in the slot, or (FP8 block) dequantised into the workspace
-  const uint16_t *Wt[5];
-  if (bp.kind == KIND_DIT_FP8) {
+  // bf16 weights: in the slot, or (FP8 block) dequantised into the workspace;
+  // FP8 codes and scales: in the slot
+  const uint16_t *Wt[5] = {};
+  const uint8_t *W8[5] = {};
+  const float *S8[5] = {};
+  if (fp8) {
     uint16_t *dst = w.dq;
     for (int i = 0; i < 5; ++i) {
+      W8[i] = reinterpret_cast<const uint8_t *>(P(kWeightP[i]));
+      S8[i] = reinterpret_cast<const float *>(base + bp.param_byte(kFp8Scale[i]));
+      if (i == 0 || w8a8) continue;
       const int64_t n = kWeightD2[i] * d * d;
-      const float *scale = reinterpret_cast<const float *>(base + bp.param_byte(kFp8Scale[i]));
-      if ((e = dlo::launch_dequant_fp8(reinterpret_cast<const uint8_t *>(P(kWeightP[i])), n, scale,
-                                       dst, s)) != hipSuccess)
-        return e;
+      if ((e = dlo::launch_dequant_fp8(W8[i], n, S8[i], dst, s)) != hipSuccess) return e;
       Wt[i] = dst;
       dst += n;
     }
@@ -970,25 +991,38 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   uint16_t *vt = w.big + (int64_t)T * 2 * d;
   uint16_t *attn = vt + (int64_t)d * ldvt;
   uint16_t *u = w.big;
+  uint8_t *q8 = w.act_codes;
+  float *qs = w.act_scale;
+  // a linear: A [T, K] bf16 (row stride K) times weight i's rows n0 .. n0 + N - 1
+  auto linear = [&](const uint16_t *A, int K, int i, int64_t n0, int N, const float *bias,
+                    const float *gate, void *C, int64_t ldc, int epi) {
+    if (w8a8)
+      return dlo::launch_gemm_fp8(q8, K, qs, W8[i] + n0 * K, K, S8[i], T, N, K, bias, gate, C, ldc, epi, s);
+    return dlo::launch_gemm(A, K, Wt[i] + n0 * K, K, T, N, K, bias, gate, C, ldc, epi, s);
+  };
+  // W8A8: the per-row E4M3 codes of a linear's input; otherwise nothing
+  auto quant = [&](const uint16_t *A, int K) {
+    return w8a8 ? dlo::launch_quant_rows_fp8(A, K, T, K, q8, K, qs, s) : hipSuccess;
+  };
 #define DLO_STEP(call, j)                                                   \
   if ((e = (call)) != hipSuccess) return e;                                 \
   if (kernel_end && (e = hipEventRecord(kernel_end[j], s)) != hipSuccess) return e;
-  DLO_STEP(dlo::launch_adaln_gemv(Wt[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 1)
+  DLO_STEP(fp8 ? dlo::launch_adaln_gemv_fp8(W8[0], S8[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s)
+               : dlo::launch_adaln_gemv(Wt[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 1)
   DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N1_W), F(P_N1_B), F(P_N1_EPS), mod + 0 * d,
                                    mod + 1 * d, w.h, s), 2)
-  DLO_STEP(dlo::launch_gemm(w.h, d, Wt[1], d, T, 2 * d, d, F(P_QKV_B), nullptr, qk, 2 * d,
-                            dlo::EPI_BIAS, s), 3)
-  DLO_STEP(dlo::launch_gemm(w.h, d, Wt[1] + (int64_t)2 * d * d, d, T, d, d, F(P_QKV_B) + 2 * d,
-                            nullptr, vt, ldvt, dlo::EPI_BIAS_T, s), 4)
-  DLO_STEP(dlo::launch_attention(qk, 2 * d, vt, ldvt, T, H, dh, attn, d, s), 5)
-  DLO_STEP(dlo::launch_gemm(attn, d, Wt[2], d, T, d, d, F(P_OUT_B), mod + 2 * d, x, ldx,
-                            dlo::EPI_GATED_RESIDUAL, s), 6)
+  DLO_STEP(quant(w.h, d), 3)
+  DLO_STEP(linear(w.h, d, 1, 0, 2 * d, F(P_QKV_B), nullptr, qk, 2 * d, dlo::EPI_BIAS), 4)
+  DLO_STEP(linear(w.h, d, 1, 2 * d, d, F(P_QKV_B) + 2 * d, nullptr, vt, ldvt, dlo::EPI_BIAS_T), 5)
+  DLO_STEP(dlo::launch_attention(qk, 2 * d, vt, ldvt, T, H, dh, attn, d, s), 6)
+  DLO_STEP(quant(attn, d), 7)
+  DLO_STEP(linear(attn, d, 2, 0, d, F(P_OUT_B), mod + 2 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 8)
   DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N2_W), F(P_N2_B), F(P_N2_EPS), mod + 3 * d,
-                                   mod + 4 * d, w.h, s), 7)
-  DLO_STEP(dlo::launch_gemm(w.h, d, Wt[3], d, T, 4 * d, d, F(P_FC1_B), nullptr, u, 4 * d,
-                            dlo::EPI_BIAS_GELU, s), 8)
-  DLO_STEP(dlo::launch_gemm(u, 4 * d, Wt[4], 4 * d, T, d, 4 * d, F(P_FC2_B), mod + 5 * d, x,
-                            ldx, dlo::EPI_GATED_RESIDUAL, s), 9)
+                                   mod + 4 * d, w.h, s), 9)
+  DLO_STEP(quant(w.h, d), 10)
+  DLO_STEP(linear(w.h, d, 3, 0, 4 * d, F(P_FC1_B), nullptr, u, 4 * d, dlo::EPI_BIAS_GELU), 11)
+  DLO_STEP(quant(u, 4 * d), 12)
+  DLO_STEP(linear(u, 4 * d, 4, 0, d, F(P_FC2_B), mod + 5 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 13)
 #undef DLO_STEP
   return hipSuccess;
 }
@@ -996,7 +1030,7 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
 
 int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dlo_forward_args *a) {
   if (!plan || !a) return fail(DLO_E_ARG, "NULL plan or args");
-  if (a->flags & ~(DLO_TRACE_DIGEST | DLO_TRACE_TIMING | DLO_RESIDENT))
+  if (a->flags & ~(DLO_TRACE_DIGEST | DLO_TRACE_TIMING | DLO_RESIDENT | DLO_FP8_COMPUTE))
     return fail(DLO_E_ARG, "unknown flags 0x%x", a->flags);
   const int n = (int)plan->blocks.size();
   if (!(a->flags & DLO_RESIDENT) && (a->n_resident < 0 || a->n_resident > n))
@@ -1112,7 +1146,7 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
     r.t_copy_begin = r.t_copy_end = r.t_compute_begin = r.t_compute_end = -1.f;
   }
 
-  const Workspace w = carve(a->workspace, plan->max_d, a->tokens);
+  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d);
   hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
   auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
   hipError_t e = hipSuccess;
@@ -1264,6 +1298,20 @@ int dlo_op_adaln(const uint16_t *W, const float *b, const float *cond, int32_t r
   return rc ? rc : ok();
 }
 
+int dlo_op_adaln_fp8(const uint8_t *W, const float *w_scale, const float *b, const float *cond, int32_t rows,
+                     int32_t d, float *out, void *workspace, int64_t workspace_bytes, void *stream) {
+  if (!W || !w_scale || !b || !cond || !out || !workspace) return fail(DLO_E_ARG, "NULL argument");
+  if (rows < 1 || d < 16 || d % 16) return fail(DLO_E_UNSUPPORTED, "adaln_fp8: rows >= 1, d %% 16 == 0 required");
+  if ((uintptr_t)W % 16 || (uintptr_t)cond % 16)
+    return fail(DLO_E_UNSUPPORTED, "adaln_fp8: W and cond must be 16-B aligned");
+  if (workspace_bytes < 4 * (int64_t)d) return fail(DLO_E_WORKSPACE, "adaln_fp8: workspace < 4 d bytes");
+  hipStream_t s = (hipStream_t)stream;
+  float *sc = static_cast<float *>(workspace);
+  int rc = check_hip(dlo::launch_silu(cond, sc, d, s), "silu");
+  if (!rc) rc = check_hip(dlo::launch_adaln_gemv_fp8(W, w_scale, sc, b, out, rows, d, s), "adaln_gemv_fp8");
+  return rc ? rc : ok();
+}
+
 int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const float *gamma,
                        const float *beta, const float *eps, const float *shift,
                        const float *scale, uint16_t *out, void *stream) {
@@ -1292,6 +1340,40 @@ int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, 
     return fail(DLO_E_UNSUPPORTED, "gemm: C, bias and gate must be 16-B aligned and ldc %% 4 == 0");
   int rc = check_hip(dlo::launch_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue,
                                       (hipStream_t)stream), "gemm");
+  return rc ? rc : ok();
+}
+
+int dlo_op_quantize_rows_fp8(const uint16_t *x, int64_t ldx, int32_t M, int32_t K, uint8_t *codes,
+                             int64_t ldq, float *scales, void *stream) {
+  if (!x || !codes || !scales) return fail(DLO_E_ARG, "NULL argument");
+  if (M < 1 || K < 8 || K % 8 || ldx < K || ldq < K || ldx % 8 || ldq % 8)
+    return fail(DLO_E_UNSUPPORTED, "quantize_rows_fp8: K %% 8 == 0, ldx and ldq >= K and multiples of 8");
+  if ((uintptr_t)x % 16 || (uintptr_t)codes % 8 || (uintptr_t)scales % 4)
+    return fail(DLO_E_UNSUPPORTED, "quantize_rows_fp8: x 16-B, codes 8-B and scales 4-B aligned");
+  int rc = check_hip(dlo::launch_quant_rows_fp8(x, ldx, M, K, codes, ldq, scales, (hipStream_t)stream),
+                     "quantize_rows_fp8");
+  return rc ? rc : ok();
+}
+
+int dlo_op_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B, int64_t ldb,
+                    const float *b_scale, int32_t M, int32_t N, int32_t K, const float *bias,
+                    const float *gate, void *C, int64_t ldc, int32_t epilogue, void *stream) {
+  if (!A || !a_scale || !B || !b_scale || !bias || !C) return fail(DLO_E_ARG, "NULL argument");
+  if (epilogue < 0 || epilogue > 3) return fail(DLO_E_ARG, "unknown epilogue %d", epilogue);
+  if (epilogue == DLO_EPI_GATED_RESIDUAL && !gate) return fail(DLO_E_ARG, "gate is required");
+  const bool trans = epilogue == DLO_EPI_BIAS_T;
+  if (M < 1 || N < 256 || N % 256 || K < 64 || K % 64 || lda < K || ldb < K ||
+      ldc < (trans ? round_up64(M) : N) || lda % 16 || ldb % 16 || (trans && ldc % 8))
+    return fail(DLO_E_UNSUPPORTED,
+                "gemm_fp8: N %% 256 == 0, K %% 64 == 0, ld >= extent, lda and ldb multiples of 16");
+  if ((int64_t)256 * lda >= (int64_t)1 << 31 || (int64_t)256 * ldb >= (int64_t)1 << 31 ||
+      (int64_t)256 * ldc * 4 >= (int64_t)1 << 31)
+    return fail(DLO_E_UNSUPPORTED, "gemm_fp8: leading dimension too large for 32-bit tile offsets");
+  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 16 || (gate && (uintptr_t)gate % 16) ||
+      (uintptr_t)A % 16 || (uintptr_t)B % 16)
+    return fail(DLO_E_UNSUPPORTED, "gemm_fp8: A, B, C, bias and gate must be 16-B aligned and ldc %% 4 == 0");
+  int rc = check_hip(dlo::launch_gemm_fp8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc,
+                                          epilogue, (hipStream_t)stream), "gemm_fp8");
   return rc ? rc : ok();
 }
 

@@ -194,11 +194,21 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
 // accumulator sees the same k order).  Group g loads A rows and B rows
 // 128 g .. +127 of every k-tile; the 4-deep ring gives each load six phases
 // to land.
-template <int EPI>
+//
+// F8: A and B hold OCP E4M3 codes (1 byte per element) instead of bf16.  A
+// stage row is still 64 bytes, now 64 elements: one v_mfma_f32_32x32x64_f8f6f4
+// k-step per stage, whose operand (32 consecutive k-bytes of a row per lane)
+// is two 16-B chunks of the swizzled row; each phase issues 8 of these MFMAs,
+// the same MFMA time as 16 bf16 ones, over twice the K.  The fp32 result is
+// scaled by a_scale[row] * *b_scale before the epilogue.
+template <int EPI, bool F8>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
-    const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
+    const void *__restrict__ A, int64_t lda, const void *__restrict__ B, int64_t ldb,
     int M, int N, int K, const float *__restrict__ bias, const float *__restrict__ gate,
-    void *__restrict__ Cv, int64_t ldc) {
+    void *__restrict__ Cv, int64_t ldc, const float *__restrict__ a_scale,
+    const float *__restrict__ b_scale) {
+  constexpr int ES = F8 ? 1 : 2;             // bytes per element
+  constexpr int KSTAGE = 64 / ES;            // elements of k per stage
   constexpr int BN = 256, WN = 4, NJ = 2, STAGES = 4;
   constexpr int B_TILE = BN * DL_BK;
   constexpr int STAGE = DL_TILE + B_TILE;
@@ -224,16 +234,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   const int m0 = tm * GBM, n0 = tn * BN;
 
   const int a_rows = min(M - m0, GBM);
-  const i32x4 a_rsrc = dl_rsrc(A + (int64_t)m0 * lda, (uint32_t)(a_rows * lda * 2));
-  const i32x4 b_rsrc = dl_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(BN * ldb * 2));
+  const i32x4 a_rsrc = dl_rsrc(static_cast<const char *>(A) + (int64_t)m0 * lda * ES,
+                               (uint32_t)(a_rows * lda * ES));
+  const i32x4 b_rsrc = dl_rsrc(static_cast<const char *>(B) + (int64_t)n0 * ldb * ES,
+                               (uint32_t)(BN * ldb * ES));
 
   // 16-row load blocks 8 g + 2 wq + i (i < 2) of A and of B
   int a_voff[2], b_voff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = (grp * 8 + wq * 2 + i) * 16 + (lane >> 2);
-    a_voff[i] = (r * (int)lda + ((lane & 3) ^ dl_swz(r)) * 8) * 2;
-    b_voff[i] = (r * (int)ldb + ((lane & 3) ^ dl_swz(r)) * 8) * 2;
+    a_voff[i] = r * (int)lda * ES + ((lane & 3) ^ dl_swz(r)) * 16;
+    b_voff[i] = r * (int)ldb * ES + ((lane & 3) ^ dl_swz(r)) * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&smem[0];
   // loads of k-tile kt into stage S (a compile-time constant): per-lane
@@ -241,7 +253,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   auto issue = [&](int kt, auto st_c) {
     constexpr int S = decltype(st_c)::value;
     const uint32_t sbase = lds0 + (uint32_t)(S * STAGE * 2);
-    const uint32_t koff = __builtin_amdgcn_readfirstlane(kt * DL_BK * 2);
+    const uint32_t koff = __builtin_amdgcn_readfirstlane(kt * 64);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       dl_load_so(a_rsrc, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((grp * 8 + wq * 2 + i) * 1024)),
@@ -261,13 +273,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / DL_BK;
+  const int nk = K / KSTAGE;
   const int frow = lane & 31, fk = lane >> 5;
 
-  // all fragments of one 32-deep tile: 2 k-steps x (4 A rows, 2 B columns)
-  struct Frags {
+  // all fragments of one stage: bf16, 2 k-steps x (4 A rows, 2 B columns);
+  // F8, one k-step x (4 A rows, 2 B columns) of two 16-B halves each
+  struct FragsB {
     bf16x8 a[2][4], b[2][NJ];
   };
+  struct Frags8 {
+    u32x4 a[4][2], b[NJ][2];
+  };
+  using Frags = std::conditional_t<F8, Frags8, FragsB>;
   // fragment byte offsets inside a stage: the XOR swizzle depends on row bits
   // 1..3 only, so rows 32 apart share it and the 32-row steps are immediates
   const char *lds_bytes = reinterpret_cast<const char *>(&smem[0]);
@@ -277,36 +294,78 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     a_lane[kk] = dl_lds_off(wm * 128 + frow, kk * 2 + fk) * 2;
     b_lane[kk] = (DL_TILE + dl_lds_off(wn * 64 + frow, kk * 2 + fk)) * 2;
   }
+  // F8 operand of lane (row, fk): k-bytes 32 fk .. 32 fk + 31 = chunks 2 fk, 2 fk + 1
+  int a8_lane[2], b8_lane[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    a8_lane[h] = dl_lds_off(wm * 128 + frow, 2 * fk + h) * 2;
+    b8_lane[h] = (DL_TILE + dl_lds_off(wn * 64 + frow, 2 * fk + h)) * 2;
+  }
   auto read_tile = [&](auto st_c, Frags &f) {
     constexpr int S = decltype(st_c)::value;
     const char *base = lds_bytes + S * STAGE * 2;
+    if constexpr (F8) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f.a[kk][i] = *reinterpret_cast<const bf16x8 *>(base + a_lane[kk] + i * 32 * DL_BK * 2);
+        for (int i = 0; i < 4; ++i) f.a[i][h] = *reinterpret_cast<const u32x4 *>(base + a8_lane[h] + i * 32 * 64);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        f.b[kk][j] = *reinterpret_cast<const bf16x8 *>(base + b_lane[kk] + j * 32 * DL_BK * 2);
+        for (int j = 0; j < NJ; ++j) f.b[j][h] = *reinterpret_cast<const u32x4 *>(base + b8_lane[h] + j * 32 * 64);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          f.a[kk][i] = *reinterpret_cast<const bf16x8 *>(base + a_lane[kk] + i * 32 * DL_BK * 2);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          f.b[kk][j] = *reinterpret_cast<const bf16x8 *>(base + b_lane[kk] + j * 32 * DL_BK * 2);
+      }
     }
   };
   auto drained = [&](const Frags &f) {
+    if constexpr (F8) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      asm volatile("" ::"v"(f.a[kk][0]), "v"(f.a[kk][1]), "v"(f.a[kk][2]), "v"(f.a[kk][3]));
-      asm volatile("" ::"v"(f.b[kk][0]), "v"(f.b[kk][1]));
+      for (int h = 0; h < 2; ++h) {
+        asm volatile("" ::"v"(f.a[0][h]), "v"(f.a[1][h]), "v"(f.a[2][h]), "v"(f.a[3][h]));
+        asm volatile("" ::"v"(f.b[0][h]), "v"(f.b[1][h]));
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        asm volatile("" ::"v"(f.a[kk][0]), "v"(f.a[kk][1]), "v"(f.a[kk][2]), "v"(f.a[kk][3]));
+        asm volatile("" ::"v"(f.b[kk][0]), "v"(f.b[kk][1]));
+      }
     }
   };
   auto compute = [&](const Frags &f) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    if constexpr (F8) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < NJ; ++j) {
+          const u32x4 a0 = f.a[i][0], a1 = f.a[i][1], b0 = f.b[j][0], b1 = f.b[j][1];
+          const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                            (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          const i32x8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                            (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+          // format 0 (E4M3) for both operands, no block scales
           acc[i][j] = EPI == EPI_BIAS_T
-                          ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0)
-                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][j], f.a[kk][i], acc[i][j], 0, 0, 0);
+                          ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, 0, 0, 0)
+                          : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = EPI == EPI_BIAS_T
+                            ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0)
+                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][j], f.a[kk][i], acc[i][j], 0, 0, 0);
+    }
   };
   // Barrier opening global phase p.  Before it, this wave's loads of the tile
   // read in phase p (tile p / 2) have landed: younger tiles of this wave's
@@ -357,37 +416,66 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   }
   if (grp == 0) phase_barrier(2 * nk);
 
+  if constexpr (F8) {
+    // A's per-row scale times B's scale (rows past M read no scale)
+    const float sb = *b_scale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (EPI == EPI_BIAS_T) {  // lane holds rows 8 (r / 4) + 4 fk + r % 4 of row block i
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fk * 4 + (r & 3);
+          const float f = (row < M ? a_scale[row] : 0.f) * sb;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j][r] *= f;
+        }
+      } else {  // lane holds row frow of row block i
+        const int row = m0 + wm * 128 + i * 32 + frow;
+        const float f = (row < M ? a_scale[row] : 0.f) * sb;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= f;
+      }
+    }
+  }
   gemm_epilogue<EPI, BN, WN>(acc, smem, tid, wm, wn, lane, m0, n0, M, bias, gate, Cv, ldc);
 }
 
-}  // namespace
-
-
-hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int M,
-                       int N, int K, const float *bias, const float *gate, void *C, int64_t ldc,
-                       int epilogue, hipStream_t s) {
+template <bool F8>
+hipError_t launch_gemm_t(const void *A, int64_t lda, const void *B, int64_t ldb, int M, int N, int K,
+                         const float *bias, const float *gate, void *C, int64_t ldc, int epilogue,
+                         const float *a_scale, const float *b_scale, hipStream_t s) {
   const int tiles = ((M + GBM - 1) / GBM) * (N / 256);
   switch (epilogue) {
-    case EPI_BIAS:
-      hipLaunchKernelGGL((gemm_pp_kernel<EPI_BIAS>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb, M,
-                         N, K, bias, gate, C, ldc);
-      break;
-    case EPI_BIAS_GELU:
-      hipLaunchKernelGGL((gemm_pp_kernel<EPI_BIAS_GELU>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb,
-                         M, N, K, bias, gate, C, ldc);
-      break;
-    case EPI_GATED_RESIDUAL:
-      hipLaunchKernelGGL((gemm_pp_kernel<EPI_GATED_RESIDUAL>), dim3(tiles), dim3(512), 0, s, A, lda, B,
-                         ldb, M, N, K, bias, gate, C, ldc);
-      break;
-    case EPI_BIAS_T:
-      hipLaunchKernelGGL((gemm_pp_kernel<EPI_BIAS_T>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb,
-                         M, N, K, bias, gate, C, ldc);
-      break;
+#define DLO_GEMM_CASE(E)                                                                            \
+  case E:                                                                                           \
+    hipLaunchKernelGGL((gemm_pp_kernel<E, F8>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb, M, N, K, \
+                       bias, gate, C, ldc, a_scale, b_scale);                                       \
+    break;
+    DLO_GEMM_CASE(EPI_BIAS)
+    DLO_GEMM_CASE(EPI_BIAS_GELU)
+    DLO_GEMM_CASE(EPI_GATED_RESIDUAL)
+    DLO_GEMM_CASE(EPI_BIAS_T)
+#undef DLO_GEMM_CASE
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int M,
+                       int N, int K, const float *bias, const float *gate, void *C, int64_t ldc,
+                       int epilogue, hipStream_t s) {
+  return launch_gemm_t<false>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, nullptr, nullptr, s);
+}
+
+hipError_t launch_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B,
+                           int64_t ldb, const float *b_scale, int M, int N, int K, const float *bias,
+                           const float *gate, void *C, int64_t ldc, int epilogue, hipStream_t s) {
+  return launch_gemm_t<true>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, a_scale, b_scale, s);
 }
 
 }  // namespace dlo

@@ -11,6 +11,9 @@ hipError_t launch_silu(const float *c, float *out, int n, hipStream_t s);
 // out[r] = sum_j W[r, j] * sc[j] + b[r]   (W bf16 [rows, d], d % 8 == 0)
 hipError_t launch_adaln_gemv(const uint16_t *W, const float *sc, const float *b, float *out,
                              int rows, int d, hipStream_t s);
+// the adaLN GEMV on E4M3 codes W [rows, d] with per-tensor scale *wscale; d % 16 == 0
+hipError_t launch_adaln_gemv_fp8(const uint8_t *W, const float *wscale, const float *sc, const float *b,
+                                 float *out, int rows, int d, hipStream_t s);
 
 // out[t, :] = bf16(LN(x[t, :d]) * (1 + scale) + shift); d % 256 == 0, d <= 8192
 hipError_t launch_ln_modulate(const float *x, int64_t ldx, int T, int d, const float *gamma,
@@ -30,6 +33,12 @@ hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_
 hipError_t launch_v_transpose(const uint16_t *v, int64_t ldv, int T, int d, uint16_t *vt,
                               int64_t ldvt, hipStream_t s);
 
+// C = (A B^T) * a_scale[m] * *b_scale + bias with A, B OCP E4M3 codes ([M, K], [N, K],
+// row strides in bytes), the epilogues and constraints of launch_gemm
+hipError_t launch_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B,
+                           int64_t ldb, const float *b_scale, int M, int N, int K, const float *bias,
+                           const float *gate, void *C, int64_t ldc, int epilogue, hipStream_t s);
+
 // per-head softmax(q k^T / sqrt(dh)) v: q, k from a fused qkv buffer, v from
 // its feature-major copy vt (launch_v_transpose); dh in {64, 128}
 hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, const uint16_t *vt, int64_t ldvt,
@@ -39,6 +48,12 @@ hipError_t launch_attention(const uint16_t *qkv, int64_t ldqkv, const uint16_t *
 // and out 32-B aligned
 hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
                               hipStream_t s);
+
+// per-row dynamic E4M3 of bf16 x [M, K] (row stride ldx): scale[r] = amax_r / 448
+// (1 for a zero row), q[r, k] = E4M3 code nearest to x / scale[r]; K, ldx, ldq
+// multiples of 8, x 16-B and q 8-B aligned
+hipError_t launch_quant_rows_fp8(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,
+                                 float *scale, hipStream_t s);
 
 // *out = digest of the regions (base + offsets[i], lengths[i]); offsets multiples of 8
 hipError_t launch_digest(const void *base, const int64_t *offsets, const int64_t *lengths,

@@ -55,6 +55,34 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(const uint16_t *__restr
   if (lane == 0) out[row] = acc + b[row];
 }
 
+// The same GEMV on an FP8 block's E4M3 codes: each lane decodes 16 codes per
+// step (exact in fp32), and the per-tensor scale multiplies the row's sum, so
+// the weights enter as code value * scale with no bf16 rounding.
+__global__ __launch_bounds__(256) void adaln_gemv_fp8_kernel(const uint8_t *__restrict__ W,
+                                                             const float *__restrict__ wscale,
+                                                             const float *__restrict__ sc,
+                                                             const float *__restrict__ b,
+                                                             float *__restrict__ out, int rows, int d) {
+  const int lane = threadIdx.x % WAVE;
+  const int row = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+  if (row >= rows) return;
+  const uint8_t *w = W + (int64_t)row * d;
+  float acc = 0.f;
+  for (int c = lane * 16; c < d; c += WAVE * 16) {
+    const u32x4 q = *reinterpret_cast<const u32x4 *>(w + c);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[k], false);  // codes c + 4k, c + 4k + 1
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[k], true);   // codes c + 4k + 2, + 3
+      const float4 s4 = *reinterpret_cast<const float4 *>(sc + c + 4 * k);
+      acc += lo[0] * s4.x + lo[1] * s4.y;
+      acc += hi[0] * s4.z + hi[1] * s4.w;
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) out[row] = acc * *wscale + b[row];
+}
+
 template <int VPT>  // values per thread: d / 256
 __global__ __launch_bounds__(256) void ln_modulate_kernel(
     const float *__restrict__ x, int64_t ldx, int d, const float *__restrict__ gamma,
@@ -156,8 +184,6 @@ hipError_t ln_launch(const float *x, int64_t ldx, int T, int d, const float *gam
 // two 16-B stores.
 // ---------------------------------------------------------------------------
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
 __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint32_t *__restrict__ codes,
                                                           const float *__restrict__ scale,
                                                           u32x4 *__restrict__ out, int64_t n16) {
@@ -177,6 +203,75 @@ __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint32_t *__rest
   out[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// ---------------------------------------------------------------------------
+// Per-row (per-token) dynamic E4M3 quantization of a bf16 activation matrix,
+// the input side of an FP8 linear: scale_r = amax_r / 448 in fp32 (1 for an
+// all-zero row; NaN entries ignored), code = the E4M3 value nearest to
+// x / scale_r (IEEE fp32 division), ties to the even code, saturating at 448,
+// NaN -> 0x7F.  One workgroup per row: an amax pass, then a quantize pass over
+// the (cache-hot) row; 16-B loads of 8 bf16, 8-B stores of 8 codes.
+// ---------------------------------------------------------------------------
+
+// The encoder works on the fp32 exponent and a 3-bit mantissa rounded by
+// v_rndne (every scaling by a power of two is exact).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  if (x != x) return 0x7Fu;
+  const float a = fabsf(x);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f)  // below 2^-6: subnormal steps of 2^-9 (8 steps = the smallest normal)
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  int E = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;                      // a in [2^E, 2^(E+1))
+  const float f = __uint_as_float((__float_as_uint(a) & 0x7FFFFFu) | 0x3F800000u);  // a / 2^E in [1, 2)
+  int m = (int)__builtin_rintf(f * 8.0f) - 8;
+  if (m == 8) {
+    m = 0;
+    ++E;
+  }
+  return sign | (uint32_t)(((E + 7) << 3) | m);
+}
+
+__global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                             int K, uint8_t *__restrict__ q, int64_t ldq,
+                                                             float *__restrict__ scale) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int64_t row = blockIdx.x;
+  const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + row * ldx);
+  const int nch = K / 8;
+  float amax = 0.f;
+  for (int c = tid; c < nch; c += 256) {
+    const u32x4 v = xr[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(v[e] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(v[e] & 0xffff0000u)));
+    }
+  }
+#pragma unroll
+  for (int o = WAVE / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+  if (lane == 0) red[wv] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax == 0.f ? 1.0f : amax / 448.0f;
+  if (tid == 0) scale[row] = s;
+  uint2 *qr = reinterpret_cast<uint2 *>(q + row * ldq);
+  for (int c = tid; c < nch; c += 256) {
+    const u32x4 v = xr[c];
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c0 = e4m3_code(__uint_as_float(v[2 * h] << 16) / s);
+      const uint32_t c1 = e4m3_code(__uint_as_float(v[2 * h] & 0xffff0000u) / s);
+      const uint32_t c2 = e4m3_code(__uint_as_float(v[2 * h + 1] << 16) / s);
+      const uint32_t c3 = e4m3_code(__uint_as_float(v[2 * h + 1] & 0xffff0000u) / s);
+      w[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    qr[c] = make_uint2(w[0], w[1]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
@@ -189,6 +284,13 @@ hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scal
   return hipGetLastError();
 }
 
+hipError_t launch_quant_rows_fp8(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,
+                                 float *scale, hipStream_t s) {
+  if (M < 1 || K < 8 || K % 8 || ldx % 8 || ldq % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3(M), dim3(256), 0, s, x, ldx, K, q, ldq, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_silu(const float *c, float *out, int n, hipStream_t s) {
   hipLaunchKernelGGL(silu_kernel, dim3((n + 255) / 256), dim3(256), 0, s, c, out, n);
   return hipGetLastError();
@@ -197,6 +299,14 @@ hipError_t launch_silu(const float *c, float *out, int n, hipStream_t s) {
 hipError_t launch_adaln_gemv(const uint16_t *W, const float *sc, const float *b, float *out,
                              int rows, int d, hipStream_t s) {
   hipLaunchKernelGGL(adaln_gemv_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, W, sc, b, out,
+                     rows, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_adaln_gemv_fp8(const uint8_t *W, const float *wscale, const float *sc, const float *b,
+                                 float *out, int rows, int d, hipStream_t s) {
+  if (d % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(adaln_gemv_fp8_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, W, wscale, sc, b, out,
                      rows, d);
   return hipGetLastError();
 }

@@ -1,0 +1,197 @@
+"""The W8A8 forward of FP8 blocks (DLO_FP8_COMPUTE) through dlo_forward_stack.
+
+Why the checks against the oracle are looser here than for bf16 blocks: every
+W8A8 linear turns its input into E4M3 codes, and an input that moves by one
+bf16 step across a code boundary changes its code by a whole E4M3 step (up to
+2^-3 relative).  The GPU computes in fp32 with bf16 q, k, v and P in the
+attention, the oracle in float64; its attention output differs from the
+oracle's by about 0.2 % (rms), which flips about 5 % of that output's codes
+(measured), and the flips compound through the block's later linears and
+across blocks.  On one 256-wide block the update stays within 0.7 % (rms) of
+the W8A8 oracle, far from the 3.6 % that separates it from the W8A16 oracle;
+a single flipped code can still move one output element by 2 % of the update's
+maximum, so the max-norm bound is twice the bf16 one.  Wider blocks and
+multi-block stacks drift by 1-6 % (CPU stand-ins of the GPU's rounding points
+reproduce the single-block figures), as much as that separation.  So:
+
+* the FP8 ops themselves are checked exactly (codes and scales bit for bit, the
+  GEMM and the FP8 adaLN GEMV element by element) in test_gpu_fp8_ops.py;
+* the streamed W8A8 block is checked bit for bit against those ops called one
+  by one;
+* one tiny block is compared with the W8A8 oracle (rms of the update within
+  1 %, max-norm within 2 x the stack tolerance) and must sit at least four times
+  closer to it than to the W8A16 oracle;
+* stacks check the streaming (slot bytes and digests = oracle, hook schedule),
+  streamed == resident bit for bit, that the flag changes FP8 blocks and leaves
+  bf16 blocks alone, and a gross-error bound of 0.1 (rms of the update).
+"""
+import numpy as np
+import pytest
+
+import synth
+import layerwise_weight_streaming_amd as dlo
+from oracle import forward as of
+from oracle import plan as op
+from oracle import schedule as sc
+from tests.gpu_util import TOL, fp8_blocks, make_runner_params, rel_err, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rms_rel(got, ref):
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def _check_trace(tr, n, passes, regs):
+    ref = sc.simulate_hooks(n, passes)
+    assert len(tr) == len(ref)
+    for got, e in zip(tr, ref):
+        assert (got["step"], got["block"], got["read_slot"], got["prefetch_block"]) == \
+            (e.step, e.block, e.read_slot, e.prefetch_block)
+        want = op.digest_regions(regs[e.block])
+        assert got["digest_pre"] == want and got["digest_post"] == want, e.step
+
+
+def test_w8a8_single_block_matches_the_w8a8_oracle():
+    """One FP8 block (d = 256, 4 heads, 64 tokens), one pass."""
+    require_gpu()
+    w = synth.WORKLOADS["tiny"]
+    stack = synth.make_stack(w, 21, 1)
+    blocks = fp8_blocks(w, stack)
+    r = make_runner_params(w, blocks)
+    r.set_inputs(stack.x, stack.c)
+    r.forward(1, flags=dlo.FP8_COMPUTE, want_run=False)
+    x_gpu = r.x_host().astype(np.float64)
+    r.close()
+    x0 = np.asarray(stack.x, np.float64)
+    heads = [w.heads(0)]
+    ref8 = of.forward_stack(x0, stack.c, blocks, heads, 1, act_fp8=True)
+    ref16 = of.forward_stack(x0, stack.c, blocks, heads, 1)
+    e_max = rel_err(x_gpu - x0, ref8 - x0)
+    e8, e16 = _rms_rel(x_gpu - x0, ref8 - x0), _rms_rel(x_gpu - x0, ref16 - x0)
+    say(f"W8A8 block: update max {e_max:.3e}; rms vs W8A8 oracle {e8:.3e}, vs W8A16 oracle {e16:.3e}")
+    assert e8 <= 1e-2 and e_max <= 2 * TOL
+    assert e8 < 0.25 * e16
+
+
+def test_w8a8_block_is_the_op_sequence():
+    """The streamed W8A8 block computes, bit for bit, what the C-ABI ops compute when
+    called one by one in the block's order (each op is checked against the oracle in
+    test_gpu_fp8_ops.py and test_gpu_ops.py): adaLN on the E4M3 W_ada, LN1 +
+    modulate, per-row E4M3 of h, the q/k and V^T FP8 products, attention, E4M3 of a,
+    the gated out product, LN2 + modulate, E4M3 of h2, the fc1 product with GELU, E4M3
+    of u, the gated fc2 product."""
+    torch = require_gpu()
+    w = synth.WORKLOADS["tiny"]
+    stack = synth.make_stack(w, 23, 1)
+    blocks = fp8_blocks(w, stack)
+    r = make_runner_params(w, blocks)
+    r.set_inputs(stack.x, stack.c)
+    r.forward(1, flags=dlo.FP8_COMPUTE, want_run=False)
+    x_fwd = r.x_host()
+    r.close()
+
+    d, T, H, D = w.width(0), w.tokens, w.heads(0), w.D
+    dh = d // H
+    s = torch.cuda.current_stream().cuda_stream
+    dev = {nm: torch.from_numpy(np.ascontiguousarray(a)).cuda() for nm, _, a in blocks[0]}
+    ptr = lambda nm: dev[nm].data_ptr()
+    x = torch.from_numpy(np.ascontiguousarray(stack.x, dtype=np.float32)).cuda()
+    c = torch.from_numpy(np.ascontiguousarray(stack.c, dtype=np.float32)).cuda()
+    mod = torch.empty(6 * d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(4 * d, dtype=torch.uint8, device="cuda")
+    dlo.op_adaln_fp8(ptr("adaln.weight"), ptr("adaln.weight_scale"), ptr("adaln.bias"), c.data_ptr(), 6 * d, d,
+                     mod.data_ptr(), ws.data_ptr(), ws.numel(), s)
+    m = lambda i: mod.data_ptr() + 4 * i * d
+    h = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    codes = torch.empty((T, 4 * d), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(T, dtype=torch.float32, device="cuda")
+    ldvt = dlo.v_t_stride(T)
+    qk = torch.empty((T, 2 * d), dtype=torch.int16, device="cuda")
+    vt = torch.empty((d, ldvt), dtype=torch.int16, device="cuda")
+    att = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    u = torch.empty((T, 4 * d), dtype=torch.int16, device="cuda")
+
+    def quant(src, K):
+        dlo.op_quantize_rows_fp8(src.data_ptr(), K, T, K, codes.data_ptr(), K, scales.data_ptr(), s)
+
+    def lin(wname, K, row0, N, bias, gate, C, ldc, epi):
+        dlo.op_gemm_fp8(codes.data_ptr(), K, scales.data_ptr(), ptr(wname) + row0 * K, K, ptr(wname + "_scale"),
+                        T, N, K, bias, gate, C, ldc, epi, s)
+
+    dlo.op_ln_modulate(x.data_ptr(), D, T, d, ptr("norm1.weight"), ptr("norm1.bias"), ptr("norm1.eps"),
+                       m(0), m(1), h.data_ptr(), s)
+    quant(h, d)
+    lin("attn.qkv.weight", d, 0, 2 * d, ptr("attn.qkv.bias"), 0, qk.data_ptr(), 2 * d, dlo.EPI_BIAS)
+    lin("attn.qkv.weight", d, 2 * d, d, ptr("attn.qkv.bias") + 8 * d, 0, vt.data_ptr(), ldvt, dlo.EPI_BIAS_T)
+    dlo.op_attention(qk.data_ptr(), 2 * d, vt.data_ptr(), ldvt, T, H, dh, att.data_ptr(), d, s)
+    quant(att, d)
+    lin("attn.out.weight", d, 0, d, ptr("attn.out.bias"), m(2), x.data_ptr(), D, dlo.EPI_GATED_RESIDUAL)
+    dlo.op_ln_modulate(x.data_ptr(), D, T, d, ptr("norm2.weight"), ptr("norm2.bias"), ptr("norm2.eps"),
+                       m(3), m(4), h.data_ptr(), s)
+    quant(h, d)
+    lin("mlp.fc1.weight", d, 0, 4 * d, ptr("mlp.fc1.bias"), 0, u.data_ptr(), 4 * d, dlo.EPI_BIAS_GELU)
+    quant(u, 4 * d)
+    lin("mlp.fc2.weight", 4 * d, 0, d, ptr("mlp.fc2.bias"), m(5), x.data_ptr(), D, dlo.EPI_GATED_RESIDUAL)
+    torch.cuda.synchronize()
+    x_ops = x.cpu().numpy()
+    assert not np.array_equal(x_ops, stack.x)
+    assert np.array_equal(x_ops.view(np.uint32), x_fwd.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,n_blocks,tokens,which", [
+    ("tiny", None, None, None),                 # every block FP8, 2 passes, odd count
+    ("8blk", None, None, {0, 2, 3, 5}),         # FP8 and bf16 blocks mixed
+    ("irregular", 3, 256, None),                # widths 2048/3072/4096, k = 4
+])
+def test_w8a8_stack_streamed(name, n_blocks, tokens, which):
+    require_gpu()
+    w = synth.WORKLOADS[name]
+    if tokens is not None:
+        w = w.with_(tokens=tokens)
+    n = w.n_blocks if n_blocks is None else n_blocks
+    say(f"W8A8 stack {name} n={n} T={w.tokens} which={which}")
+    stack = synth.make_stack(w, 21, n)
+    blocks = fp8_blocks(w, stack, which)
+    r = make_runner_params(w, blocks)
+    r.set_inputs(stack.x, stack.c)
+    run = r.forward(w.passes, flags=dlo.TRACE_DIGEST | dlo.FP8_COMPUTE)
+    tr = run.trace()
+    regs = []
+    for ps in blocks:
+        bp = op.plan_block(op.specs_of(ps), w.k)
+        regs.append(op.slot_regions(bp, op.pack_block(ps, bp)))
+    _check_trace(tr, n, w.passes, regs)
+    x_gpu = r.x_host()
+    # streamed == resident, bit for bit
+    r.set_inputs(stack.x, stack.c)
+    r.forward(w.passes, flags=dlo.FP8_COMPUTE, resident=True, want_run=False)
+    assert np.array_equal(r.x_host().view(np.uint32), x_gpu.view(np.uint32))
+    # the flag changes what FP8 blocks compute: the W8A16 forward differs
+    r.set_inputs(stack.x, stack.c)
+    r.forward(w.passes, want_run=False)
+    x_w16 = r.x_host()
+    assert not np.array_equal(x_w16, x_gpu)
+    r.close()
+    say("oracle forward (W8A8)")
+    x0 = np.asarray(stack.x, np.float64)
+    heads = [w.heads(b) for b in range(n)]
+    ref = of.forward_stack(x0, stack.c, blocks, heads, w.passes, act_fp8=True)
+    e = _rms_rel(x_gpu - x0, ref - x0)
+    say(f"update rms rel err vs the W8A8 oracle {e:.3e}")
+    assert e < 0.1
+
+
+def test_w8a8_leaves_bf16_blocks_alone():
+    """A plan of bf16 blocks computes the same bits with and without the flag."""
+    require_gpu()
+    w = synth.WORKLOADS["tiny"]
+    stack = synth.make_stack(w, 22)
+    r = make_runner_params(w, stack.blocks)
+    r.set_inputs(stack.x, stack.c)
+    r.forward(w.passes, want_run=False)
+    a = r.x_host()
+    r.set_inputs(stack.x, stack.c)
+    r.forward(w.passes, flags=dlo.FP8_COMPUTE, want_run=False)
+    assert np.array_equal(r.x_host().view(np.uint32), a.view(np.uint32))
+    r.close()

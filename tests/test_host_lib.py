@@ -272,6 +272,7 @@ def test_forward_validation_errors():
     assert _status(F, slots=(0x100000, 0x100000 + 256)) == "DLO_E_ARG"   # overlapping slots
     assert _status(F, slots=(0, 0x100000)) == "DLO_E_ARG"
     assert _status(F, flags=64) == "DLO_E_ARG"
+    assert _status(F, flags=16) == "DLO_E_ARG"
     assert _status(F, flags=dlo.RESIDENT) == "DLO_E_ARG"        # no resident pointers
     assert _status(F, n_resident=-1) == "DLO_E_ARG"
     assert _status(F, n_resident=4) == "DLO_E_ARG"              # more than the 3 blocks
@@ -395,6 +396,23 @@ def test_fp8_block_plan_pack_and_workspace():
     for g in range(2):
         for r in range(k):
             assert st.shard(0, g, r).tobytes() == sh[g][r].tobytes()
-    # the workspace grows by the widest FP8 block's bf16 weights
+    # the workspace grows by the widest FP8 block's four bf16 linear weights and, for the W8A8
+    # form, a linear input's E4M3 codes [T, 4d] and row scales [T] (each region
+    # 256-B aligned)
     p_bf = dlo.Plan([(d, 4, synth.block_params(1, 1, d))], k)
-    assert p.workspace_bytes(64) - p_bf.workspace_bytes(64) == 36 * d * d
+    for T in (64, 1000):
+        al = lambda n: (n + 255) // 256 * 256
+        assert p.workspace_bytes(T) - p_bf.workspace_bytes(T) == al(24 * d * d) + al(4 * T * d) + al(4 * T)
+
+
+def test_kernel_slot_names():
+    """One name per timed kernel of a block forward, in launch order, the W8A8 input
+    quantisations just before the linears they feed; out of range gives NULL."""
+    names = dlo.kernel_names()
+    assert len(names) == dlo.KERNELS_PER_BLOCK == len(set(names))
+    order = ["dequant_fp8", "adaln_gemv", "ln1_modulate", "quant_h", "gemm_qk", "gemm_v_t", "attention",
+             "quant_attn", "gemm_out_residual", "ln2_modulate", "quant_h2", "gemm_fc1_gelu", "quant_u",
+             "gemm_fc2_residual"]
+    assert names == order
+    assert dlo.lib().dlo_kernel_name(dlo.KERNELS_PER_BLOCK) is None
+    assert dlo.lib().dlo_kernel_name(-1) is None
