@@ -56,23 +56,38 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
 def param_dict(params):
     """[(name, dtype, array)] -> {name: float64 array} (bf16 widened).
 
-    An FP8 block carries each linear as ``X.weight`` (E4M3 codes) plus
-    ``X.weight_scale`` (one fp32 value); ``X.weight`` is then the dequantised
-    weight code_value * scale (see oracle.fp8), and the scale entry is dropped.
+    A quantised block carries each linear as ``X.weight`` (codes) plus
+    ``X.weight_scale``; ``X.weight`` is then the dequantised weight and the
+    scale entry is dropped: E4M3 codes with one fp32 scale (per-tensor FP8,
+    oracle.fp8), int8 codes with one fp32 scale per output row, or E4M3 codes
+    with E8M0 scales per 32-element block (oracle.quant).
     """
-    from . import fp8
+    from . import fp8, quant
 
     out, codes = {}, {}
+    raw = {name: (dt, arr) for name, dt, arr in params}
     for name, dt, arr in params:
-        if dt == "fp8":
-            codes[name] = np.asarray(arr, dtype=np.uint8)
+        if name.endswith("_scale") and name[:-len("_scale")] in raw and \
+                raw[name[:-len("_scale")]][0] in ("fp8", "i8"):
+            continue
+        if dt in ("fp8", "i8"):
+            codes[name] = (dt, arr)
         elif dt == "bf16":
             out[name] = widen_bf16(arr)
         else:
             out[name] = np.asarray(arr, dtype=np.float64)
-    for name, c in codes.items():
-        scale = out.pop(name + "_scale")
-        out[name] = fp8.dequantize(c, np.float32(scale.reshape(-1)[0]))
+    for name, (dt, c) in codes.items():
+        sdt, sc = raw[name + "_scale"]
+        if dt == "fp8" and sdt == "f32":
+            out[name] = fp8.dequantize(c, np.float32(np.asarray(sc).reshape(-1)[0]))
+        elif dt == "i8" and sdt == "f32":
+            scl = np.asarray(sc, np.float32).reshape(-1)
+            out[name] = quant.dequantize_int8(np.asarray(c, np.int8).reshape(scl.size, -1), scl)
+        elif dt == "fp8" and sdt == "e8m0":
+            c2 = np.asarray(c, np.uint8)
+            out[name] = quant.dequantize_mxfp8(c2, np.asarray(sc, np.uint8).reshape(c2.shape[0], -1))
+        else:
+            raise ValueError(f"{name}: no dequantisation for {dt} codes with {sdt} scales")
     return out
 
 

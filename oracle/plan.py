@@ -23,8 +23,10 @@ from dataclasses import dataclass
 
 import numpy as np
 
-ELEMENT_BYTES = {"bf16": 2, "f32": 4, "fp8": 1}
-NUMPY_DTYPE = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}
+# element types of the block forms: bf16 and fp32 parameters, E4M3 ("fp8"),
+# int8 ("i8") and E8M0 block scales ("e8m0") of the online-quantised forms
+ELEMENT_BYTES = {"bf16": 2, "f32": 4, "fp8": 1, "i8": 1, "e8m0": 1}
+NUMPY_DTYPE = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8, "i8": np.int8, "e8m0": np.uint8}
 
 
 def ceil_div(a: int, b: int) -> int:
