@@ -32,11 +32,19 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 LINK_PEAK_GBS = 32.0 * 16 * 128 / 130 / 8   # PCIe 5.0 x16, one direction: 63.0 GB/s
 
 
-def kernel_work(name, d, T, fp8=False, w8a8=False):
-    """Algorithmic work of one launch: (amount, unit, bound).  w8a8: an FP8 block
-    run with FP8 compute (only the adaLN weight dequantised, inputs quantised)."""
-    if name == "dequant_fp8":   # the four linears: E4M3 codes in, bf16 weights out (W8A16 only)
-        return (12 * d * d * 3 if fp8 and not w8a8 else 0) / 1e9, "GB", "hbm"
+def kernel_work(name, d, T, form="bf16", w8a8=False):
+    """Algorithmic work of one launch: (amount, unit, bound).  form: the block's
+    weight form ("bf16", "fp8", "int8", "mxfp8"); w8a8: FP8 blocks run with FP8
+    compute (the linears' inputs quantised, no weight dequantised)."""
+    fp8 = form == "fp8"
+    if name == "dequant_weights":   # codes (+ scales) in, bf16 weights out
+        if fp8:     # the four linears, W8A16 only
+            return (12 * d * d * 3 if not w8a8 else 0) / 1e9, "GB", "hbm"
+        if form == "int8":   # all five weights, fp32 scale per row (15 d rows)
+            return (18 * d * d * 3 + 15 * d * 4) / 1e9, "GB", "hbm"
+        if form == "mxfp8":  # all five weights, one E8M0 per 32 codes
+            return (18 * d * d * 3 + 18 * d * d // 32) / 1e9, "GB", "hbm"
+        return 0.0, "GB", "hbm"
     if name.startswith("quant_"):   # bf16 rows in, E4M3 codes + fp32 row scales out
         K = 4 * d if name == "quant_u" else d
         return ((T * K * 3 + T * 4) if (fp8 and w8a8) else 0) / 1e9, "GB", "hbm"
@@ -271,8 +279,9 @@ def main():
     ap.add_argument("--pinned-limit-gib", type=float, default=56.0,
                     help="ceiling on pinned block memory; blocks beyond it are staged")
     ap.add_argument("--store", default="auto", choices=["auto", "pinned", "pageable"])
-    ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
-                    help="fp8: per-tensor E4M3 weights + fp32 scales (quantized on the host before "
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8", "int8", "mxfp8"],
+                    help="fp8: per-tensor E4M3 weights + fp32 scales; int8: int8 weights + fp32 "
+                         "scales per row; mxfp8: E4M3 weights + E8M0 scales per 32 (quantized on the host before "
                          "packing), dequantised on the device after each copy")
     ap.add_argument("--compute", default="bf16", choices=["bf16", "fp8"],
                     help="fp8 (needs --weights fp8): the four linears of each block as W8A8 "
@@ -318,9 +327,9 @@ def main():
         w = w.with_(k=args.k)
     n = args.blocks or w.n_blocks
     T, P = w.tokens, w.passes
-    fp8 = args.weights == "fp8"
-    if fp8:
-        specs = [(w.width(b), w.heads(b), dlo.block_schema(w.width(b), fp8=True)) for b in range(n)]
+    quantized = args.weights != "bf16"
+    if quantized:
+        specs = [(w.width(b), w.heads(b), dlo.block_schema(w.width(b), form=args.weights)) for b in range(n)]
     else:
         specs = [(w.width(b), w.heads(b), [(nm, dt, int(np.prod(s))) for nm, dt, s in synth.block_schema(w.width(b))])
                  for b in range(n)]
@@ -342,15 +351,8 @@ def main():
                          for nm, dt, s in synth.block_schema(d)}
         t0 = time.perf_counter()
         ps = synth.block_params(args.seed, b, d, out_buffers=bufs[key])
-        if fp8:   # the loader's finalisation: per-tensor E4M3 codes + fp32 scale
-            q = []
-            for nm, dt, a in ps:
-                if dt == "bf16":
-                    codes, scale = dlo.quantize_fp8(a)
-                    q += [(nm, "fp8", codes), (nm + "_scale", "f32", np.array([scale], np.float32))]
-                else:
-                    q.append((nm, dt, a))
-            ps = q
+        if quantized:   # the loader's finalisation: codes + scales by libdlo's quantizer
+            ps = dlo.quantize_block(ps, args.weights)
         t1 = time.perf_counter()
         r.pack(b, [(d, w.heads(b), ps)])
         t2 = time.perf_counter()
@@ -402,9 +404,9 @@ def main():
         per_kernel += kt.sum(axis=0)
         launches += kt.shape[0]
         for e, row in zip(tr, kt):
-            d, f8 = infos[e["block"]]["d_model"], infos[e["block"]]["fp8"]
+            d, form = infos[e["block"]]["d_model"], infos[e["block"]]["form"]
             for j, nm in enumerate(names):
-                work[j] += kernel_work(nm, d, T, f8, w8a8)[0]
+                work[j] += kernel_work(nm, d, T, form, w8a8)[0]
         m = overlap_metrics(tr, copy_bytes, flops)
         if m:
             ov.append(m)

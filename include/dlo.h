@@ -66,7 +66,13 @@ typedef enum {
 } dlo_status;
 
 /* element types of parameter groups */
-enum { DLO_BF16 = 0, DLO_F32 = 1, DLO_FP8_E4M3 = 2 /* OCP FP8 E4M3, 1 byte */ };
+enum {
+  DLO_BF16 = 0,
+  DLO_F32 = 1,
+  DLO_FP8_E4M3 = 2, /* OCP FP8 E4M3, 1 byte */
+  DLO_I8 = 3,       /* int8, 1 byte */
+  DLO_E8M0 = 4      /* OCP MX E8M0 block scale 2^(b - 127), 1 byte (255: NaN) */
+};
 
 #define DLO_MAX_GROUPS 3   /* one group per element type */
 #define DLO_ALIGN 256      /* byte alignment of regions and extents inside a slot */
@@ -109,7 +115,8 @@ typedef struct dlo_run dlo_run;
  * ------------------------------------------------------------------------- */
 
 /* Plans n_blocks blocks for k shards.  k >= 1, n_blocks >= 1, every dtype known
- * (DLO_BF16, DLO_F32, DLO_FP8_E4M3: groups of 2, 4 and 1 bytes per element),
+ * (DLO_BF16: groups of 2 bytes per element, DLO_F32: 4, DLO_FP8_E4M3, DLO_I8 and
+ * DLO_E8M0: 1),
  * numel >= 0.  The plan copies names and sizes and never keeps `src`.  *out is
  * set to a new plan (free with dlo_plan_destroy) or NULL on error. */
 int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_plan **out);
@@ -127,8 +134,9 @@ typedef struct {
   int64_t region[DLO_MAX_GROUPS];  /* byte offset of the group in the slot */
   int64_t extent;                  /* bytes of the slot the block occupies */
   int64_t copy_bytes;              /* sum_g k * S_g * elt_g: bytes moved per placement */
-  int32_t is_dit;                  /* 1: the DiT block schema (bf16 weights); 2: its FP8
-                                      form (dlo_block_schema_fp8); 0: neither */
+  int32_t is_dit;                  /* 1: the DiT block schema (bf16 weights); 2, 3, 4: its
+                                      FP8, INT8 and MXFP8 forms (dlo_block_schema_fp8,
+                                      _int8, _mxfp8); 0: none of these */
 } dlo_block_info;
 
 int dlo_plan_block_info(const dlo_plan *plan, int32_t b, dlo_block_info *out);
@@ -269,15 +277,16 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 #define DLO_TRACE_TIMING 2u  /* timestamp copies, block computes and every kernel */
 #define DLO_RESIDENT 4u      /* no streaming: block b is read from resident_blocks[b] (same as
                                 n_resident = number of blocks) */
-#define DLO_FP8_COMPUTE 8u   /* FP8 blocks run their qkv, out, fc1 and fc2 linears as W8A8
+#define DLO_FP8_COMPUTE 8u   /* Per-tensor FP8 blocks (dlo_block_schema_fp8) run their
+                                qkv, out, fc1 and fc2 linears as W8A8
                                 products ([Doc] "Request and loading constraints", online FP8
                                 linears): the input quantised per row to E4M3 as by
                                 dlo_op_quantize_rows_fp8, then dlo_op_gemm_fp8 with the
                                 weight's codes and scale read in place from the slot.
                                 Without it an FP8 block dequantises its four linears'
                                 weights to bf16 (W8A16).  Either way an FP8 block's adaLN
-                                GEMV reads its codes (dlo_op_adaln_fp8), and bf16 blocks are
-                                unaffected. */
+                                GEMV reads its codes (dlo_op_adaln_fp8).  bf16, INT8 and
+                                MXFP8 blocks are unaffected. */
 
 typedef struct {
   void *slot[2];            /* device, slot_bytes each, distinct (unused if nothing streams) */
@@ -348,8 +357,9 @@ typedef struct {
 int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_out);
 
 /* DLO_TRACE_TIMING: per step, the duration in ms of each of the block's kernels in
- * launch order (DLO_KERNELS_PER_BLOCK per step), after the run completed: the FP8
- * weight dequantisation (0 for a bf16 block), adaln_gemv, ln1_modulate, quant_h,
+ * launch order (DLO_KERNELS_PER_BLOCK per step), after the run completed: the
+ * weight dequantisation of a quantised block (dequant_weights; 0 for a bf16
+ * block and for W8A8), adaln_gemv, ln1_modulate, quant_h,
  * gemm_qk, gemm_v_t, attention, quant_attn, gemm_out_residual, ln2_modulate,
  * quant_h2, gemm_fc1_gelu, quant_u, gemm_fc2_residual (dlo_kernel_name).  The
  * quant_* entries are the W8A8 input quantisations, 0 unless an FP8 block runs
@@ -397,6 +407,39 @@ int dlo_block_schema_fp8(int32_t d, int32_t i, const char **name, int32_t *dtype
  * input gives 0x7F).  w: n bf16 values; codes: n bytes; n >= 0.  DLO_E_ARG for
  * NULL pointers or n < 0. */
 int dlo_quantize_fp8(const uint16_t *w, int64_t n, uint8_t *codes, float *scale);
+
+/* Parameter i (0 <= i < 21) of the INT8 form of the DiT block ([Doc] "Request and
+ * loading constraints": online INT8 linears keep an int8 weight plus an fp32
+ * scale, sharded like any other dtype group): every bf16 matrix X.weight
+ * [out, in] becomes X.weight (DLO_I8, same shape) followed by X.weight_scale
+ * (fp32, one per output row: out elements); the other parameters are
+ * unchanged.  Groups: int8 (18 d^2 elements) and fp32.  Its forward dequantises
+ * each weight to bf16(code * scale_row) into the workspace, then runs the bf16
+ * block forward.  DLO_E_ARG for i out of range. */
+int dlo_block_schema_int8(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel);
+
+/* Parameter i (0 <= i < 21) of the MXFP8 form (same passage: online MXFP8 keeps
+ * an fp8 weight plus an e8m0 block scale): X.weight [out, in] becomes X.weight
+ * (DLO_FP8_E4M3, same shape) followed by X.weight_scale (DLO_E8M0, one per 32
+ * consecutive elements of a row: out * in / 32 elements).  Groups: E4M3
+ * (18 d^2), E8M0 (18 d^2 / 32) and fp32.  Its forward dequantises each weight
+ * to bf16(code_value * 2^(e - 127)) (exact), then runs the bf16 block forward.
+ * DLO_E_ARG for i out of range or d % 32 != 0. */
+int dlo_block_schema_mxfp8(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel);
+
+/* The loader's finalisation of one weight [rows, cols] (bf16, row-major, host
+ * memory) for the INT8 block: scales[r] = amax_r|w| / 127 in fp32 (1 for an
+ * all-zero row); codes[r, j] = float(w[r, j]) / scales[r] rounded to the
+ * nearest integer, ties to even, clamped to [-127, 127] (NaN -> 0).  DLO_E_ARG
+ * for NULL pointers or negative sizes. */
+int dlo_quantize_int8(const uint16_t *w, int64_t rows, int64_t cols, int8_t *codes, float *scales);
+
+/* The same for the MXFP8 block (OCP MX, E4M3 elements): for each 32-element
+ * block of a row, X = floor(log2 amax) - 8 clamped to [-127, 127] (-127 for an
+ * all-zero block), scales[r * cols / 32 + b] = X + 127, codes = the E4M3 code
+ * nearest to float(w) / 2^X, ties to the even code, saturating at +-448.
+ * cols % 32 == 0, else DLO_E_ARG. */
+int dlo_quantize_mxfp8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *codes, uint8_t *scales);
 
 /* The kernels the block forward is made of, callable one at a time (device
  * pointers, row-major, enqueued on `stream`, asynchronous).  Each validates its
@@ -492,6 +535,19 @@ int dlo_op_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint
 
 /* Slot digest (see dlo_slot_trace) of up to DLO_MAX_GROUPS regions of `base`,
  * written to *out (device uint64). */
+/* INT8 weight dequantisation (the INT8 block's forward runs this on each
+ * weight): out[r, j] = bf16(code[r, j] * scales[r]) rounded to nearest even;
+ * codes int8 [rows, cols] (16-B aligned), scales fp32 [rows], out bf16 (32-B
+ * aligned).  cols % 16 == 0, else DLO_E_UNSUPPORTED. */
+int dlo_op_dequant_int8(const int8_t *codes, int64_t rows, int64_t cols, const float *scales, uint16_t *out,
+                        void *stream);
+
+/* MXFP8 weight dequantisation: out[i] = bf16(value(codes[i]) * 2^(scales[i / 32]
+ * - 127)), exact for scales whose products stay in bf16's normal range; E8M0
+ * byte 255 gives NaN.  n % 32 == 0, codes 16-B and out 32-B aligned, else
+ * DLO_E_UNSUPPORTED. */
+int dlo_op_dequant_mxfp8(const uint8_t *codes, int64_t n, const uint8_t *scales, uint16_t *out, void *stream);
+
 int dlo_op_digest(const void *base, const int64_t *offsets, const int64_t *lengths,
                   int32_t n_regions, uint64_t *out, void *stream);
 

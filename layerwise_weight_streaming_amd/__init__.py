@@ -21,7 +21,7 @@ DLO_OK = 0
 STATUS = {0: "DLO_OK", -1: "DLO_E_ARG", -2: "DLO_E_HOSTMEM", -3: "DLO_E_PIN",
           -4: "DLO_E_SLOT_SMALL", -5: "DLO_E_PLAN_MISMATCH", -6: "DLO_E_HIP",
           -7: "DLO_E_STATE", -8: "DLO_E_UNSUPPORTED", -9: "DLO_E_WORKSPACE"}
-DTYPES = {"bf16": 0, "f32": 1, "fp8": 2}   # fp8: OCP E4M3, one byte
+DTYPES = {"bf16": 0, "f32": 1, "fp8": 2, "i8": 3, "e8m0": 4}   # fp8: OCP E4M3; e8m0: MX block scale
 DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
 STORE_PINNED, STORE_PAGEABLE, STORE_AUTO = 0, 1, 2
 TRACE_DIGEST, TRACE_TIMING, RESIDENT, FP8_COMPUTE = 1, 2, 4, 8
@@ -158,6 +158,18 @@ _SIGS = {
                                             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
     "dlo_quantize_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.POINTER(ctypes.c_float)]),
+    "dlo_block_schema_int8": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
+                                             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
+    "dlo_block_schema_mxfp8": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
+                                              ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
+    "dlo_quantize_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p]),
+    "dlo_quantize_mxfp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p]),
+    "dlo_op_dequant_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]),
+    "dlo_op_dequant_mxfp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]),
     "dlo_op_dequant_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]),
     "dlo_op_digest": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
@@ -192,9 +204,15 @@ def last_error() -> str:
     return (lib().dlo_last_error() or b"").decode()
 
 
-def block_schema(d: int, fp8: bool = False):
-    """[(name, dtype, numel)] of the DiT block schema (or its FP8 form) as libdlo defines it."""
-    fn, count = (lib().dlo_block_schema_fp8, 21) if fp8 else (lib().dlo_block_schema, 16)
+FORMS = ("bf16", "fp8", "int8", "mxfp8")   # dlo_block_info.is_dit 1 .. 4
+
+
+def block_schema(d: int, fp8: bool = False, form: str | None = None):
+    """[(name, dtype, numel)] of the DiT block schema or one of its quantised forms
+    ("fp8", "int8", "mxfp8") as libdlo defines it."""
+    form = form or ("fp8" if fp8 else "bf16")
+    fn, count = {"bf16": (lib().dlo_block_schema, 16), "fp8": (lib().dlo_block_schema_fp8, 21),
+                 "int8": (lib().dlo_block_schema_int8, 21), "mxfp8": (lib().dlo_block_schema_mxfp8, 21)}[form]
     out = []
     for i in range(count):
         name, dt, n = ctypes.c_char_p(), ctypes.c_int32(), ctypes.c_int64()
@@ -211,6 +229,51 @@ def quantize_fp8(w_bf16):
     _check(lib().dlo_quantize_fp8(w.ctypes.data_as(ctypes.c_void_p), w.size,
                                   codes.ctypes.data_as(ctypes.c_void_p), ctypes.byref(scale)))
     return codes, np.float32(scale.value)
+
+
+def quantize_int8(w_bf16):
+    """dlo_quantize_int8 on a host matrix of bf16 bit patterns -> (int8 codes, float32 row scales)."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    if w.ndim != 2:
+        raise ValueError("quantize_int8 takes a matrix")
+    codes = np.empty(w.shape, dtype=np.int8)
+    scales = np.empty(w.shape[0], dtype=np.float32)
+    _check(lib().dlo_quantize_int8(w.ctypes.data_as(ctypes.c_void_p), w.shape[0], w.shape[1],
+                                   codes.ctypes.data_as(ctypes.c_void_p), scales.ctypes.data_as(ctypes.c_void_p)))
+    return codes, scales
+
+
+def quantize_mxfp8(w_bf16):
+    """dlo_quantize_mxfp8 on a host matrix of bf16 bit patterns -> (E4M3 codes, E8M0 scales [rows, cols / 32])."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    if w.ndim != 2:
+        raise ValueError("quantize_mxfp8 takes a matrix")
+    codes = np.empty(w.shape, dtype=np.uint8)
+    scales = np.empty((w.shape[0], w.shape[1] // 32), dtype=np.uint8)
+    _check(lib().dlo_quantize_mxfp8(w.ctypes.data_as(ctypes.c_void_p), w.shape[0], w.shape[1],
+                                    codes.ctypes.data_as(ctypes.c_void_p), scales.ctypes.data_as(ctypes.c_void_p)))
+    return codes, scales
+
+
+def quantize_block(params, form):
+    """A bf16 block's [(name, dtype, array)] -> its quantised form, with libdlo's quantizers
+    (the loader's finalisation): "fp8" (per-tensor), "int8" (per-row) or "mxfp8" (32-blocks)."""
+    out = []
+    for name, dt, arr in params:
+        if dt != "bf16":
+            out.append((name, dt, arr))
+        elif form == "fp8":
+            codes, scale = quantize_fp8(arr)
+            out += [(name, "fp8", codes), (name + "_scale", "f32", np.array([scale], np.float32))]
+        elif form == "int8":
+            codes, scales = quantize_int8(arr)
+            out += [(name, "i8", codes), (name + "_scale", "f32", scales)]
+        elif form == "mxfp8":
+            codes, scales = quantize_mxfp8(arr)
+            out += [(name, "fp8", codes), (name + "_scale", "e8m0", scales.reshape(-1))]
+        else:
+            raise ValueError(f"unknown form {form!r}")
+    return out
 
 
 def kernel_names():
@@ -282,7 +345,8 @@ class Plan:
                 "n_groups": g, "dtype": [DTYPE_NAMES[bi.dtype[i]] for i in range(g)],
                 "numel": list(bi.numel[:g]), "shard": list(bi.shard[:g]),
                 "region": list(bi.region[:g]), "extent": bi.extent,
-                "copy_bytes": bi.copy_bytes, "is_dit": bool(bi.is_dit), "fp8": bi.is_dit == 2}
+                "copy_bytes": bi.copy_bytes, "is_dit": bool(bi.is_dit), "fp8": bi.is_dit == 2,
+                "form": FORMS[bi.is_dit - 1] if bi.is_dit else None}
 
     def param_offset(self, b, p):
         v = ctypes.c_int64()
@@ -463,6 +527,14 @@ def op_attention(qkv, ldqkv, vt, ldvt, T, H, dh, out, ldo, stream):
 
 def op_dequant_fp8(codes, n, scale, out, stream):
     _check(lib().dlo_op_dequant_fp8(codes, n, scale, out, stream))
+
+
+def op_dequant_int8(codes, rows, cols, scales, out, stream):
+    _check(lib().dlo_op_dequant_int8(codes, rows, cols, scales, out, stream))
+
+
+def op_dequant_mxfp8(codes, n, scales, out, stream):
+    _check(lib().dlo_op_dequant_mxfp8(codes, n, scales, out, stream))
 
 
 def op_digest(base, offsets, lengths, out, stream):

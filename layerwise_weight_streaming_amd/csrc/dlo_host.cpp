@@ -41,10 +41,33 @@ int ok() {
   return DLO_OK;
 }
 
-int64_t elt_bytes(int dtype) { return dtype == DLO_BF16 ? 2 : dtype == DLO_FP8_E4M3 ? 1 : 4; }
-bool known_dtype(int dtype) { return dtype == DLO_BF16 || dtype == DLO_F32 || dtype == DLO_FP8_E4M3; }
+int64_t elt_bytes(int dtype) { return dtype == DLO_BF16 ? 2 : dtype == DLO_F32 ? 4 : 1; }
+bool known_dtype(int dtype) {
+  return dtype == DLO_BF16 || dtype == DLO_F32 || dtype == DLO_FP8_E4M3 || dtype == DLO_I8 || dtype == DLO_E8M0;
+}
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+float widen_bf16(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// rows [0, rows) split over up to 16 threads (each row's result is independent)
+template <typename Fn>
+void for_rows(int64_t rows, int64_t cols, Fn &&fn) {
+  const int nt = (int)std::min<int64_t>(16, std::max<int64_t>(1, (rows * cols) >> 20));
+  const int64_t chunk = (rows + nt - 1) / nt;
+  std::vector<std::thread> th;
+  for (int t = 1; t < nt; ++t)
+    th.emplace_back([&, t] {
+      for (int64_t r = t * chunk; r < std::min(rows, (t + 1) * chunk); ++r) fn(r);
+    });
+  for (int64_t r = 0; r < std::min(rows, chunk); ++r) fn(r);
+  for (auto &x : th) x.join();
+}
 
 // OCP FP8 E4M3 code nearest to x: ties to the even code, magnitudes of 448 and
 // above saturate to 448, NaN -> 0x7F.  Arithmetic on the exponent and the
@@ -77,12 +100,13 @@ uint8_t e4m3_encode(float x) {
 struct SchemaEntry {
   const char *name;
   int dtype;
-  int64_t rows_per_d;  // numel = rows_per_d * d * cols_per_d * d, or fixed
+  int64_t rows_per_d;  // numel = rows_per_d * d * cols_per_d * d / div, or fixed
   int64_t cols_per_d;
   int64_t fixed;       // > 0: numel is this constant
+  int64_t div = 1;     // MX block scales: one per 32 elements
 };
 
-// numel(d) = fixed if fixed > 0, else rows_per_d * d * (cols_per_d ? cols_per_d * d : 1)
+// numel(d) = fixed if fixed > 0, else rows_per_d * d * (cols_per_d ? cols_per_d * d : 1) / div
 const SchemaEntry kDit[DLO_DIT_N_PARAMS] = {
     {"adaln.weight", DLO_BF16, 6, 1, 0},    {"adaln.bias", DLO_F32, 6, 0, 0},
     {"norm1.weight", DLO_F32, 1, 0, 0},     {"norm1.bias", DLO_F32, 1, 0, 0},
@@ -109,27 +133,60 @@ const SchemaEntry kDitFp8[DLO_DIT_FP8_N_PARAMS] = {
     {"mlp.fc2.weight", DLO_FP8_E4M3, 1, 4, 0},  {"mlp.fc2.weight_scale", DLO_F32, 0, 0, 1},
     {"mlp.fc2.bias", DLO_F32, 1, 0, 0},
 };
+// INT8 form ([Doc] "Request and loading constraints": online INT8 keeps an int8
+// weight and an fp32 scale): each bf16 matrix becomes int8 codes followed by
+// one fp32 scale per output row.
+const SchemaEntry kDitInt8[DLO_DIT_FP8_N_PARAMS] = {
+    {"adaln.weight", DLO_I8, 6, 1, 0},          {"adaln.weight_scale", DLO_F32, 6, 0, 0},
+    {"adaln.bias", DLO_F32, 6, 0, 0},           {"norm1.weight", DLO_F32, 1, 0, 0},
+    {"norm1.bias", DLO_F32, 1, 0, 0},           {"norm1.eps", DLO_F32, 0, 0, 1},
+    {"attn.qkv.weight", DLO_I8, 3, 1, 0},       {"attn.qkv.weight_scale", DLO_F32, 3, 0, 0},
+    {"attn.qkv.bias", DLO_F32, 3, 0, 0},        {"attn.out.weight", DLO_I8, 1, 1, 0},
+    {"attn.out.weight_scale", DLO_F32, 1, 0, 0}, {"attn.out.bias", DLO_F32, 1, 0, 0},
+    {"norm2.weight", DLO_F32, 1, 0, 0},         {"norm2.bias", DLO_F32, 1, 0, 0},
+    {"norm2.eps", DLO_F32, 0, 0, 1},            {"mlp.fc1.weight", DLO_I8, 4, 1, 0},
+    {"mlp.fc1.weight_scale", DLO_F32, 4, 0, 0}, {"mlp.fc1.bias", DLO_F32, 4, 0, 0},
+    {"mlp.fc2.weight", DLO_I8, 1, 4, 0},        {"mlp.fc2.weight_scale", DLO_F32, 1, 0, 0},
+    {"mlp.fc2.bias", DLO_F32, 1, 0, 0},
+};
+// MXFP8 form (same passage: an fp8 weight and an e8m0 block scale): each bf16
+// matrix becomes E4M3 codes followed by one E8M0 scale per 32 elements of a row.
+const SchemaEntry kDitMx[DLO_DIT_FP8_N_PARAMS] = {
+    {"adaln.weight", DLO_FP8_E4M3, 6, 1, 0},          {"adaln.weight_scale", DLO_E8M0, 6, 1, 0, 32},
+    {"adaln.bias", DLO_F32, 6, 0, 0},                 {"norm1.weight", DLO_F32, 1, 0, 0},
+    {"norm1.bias", DLO_F32, 1, 0, 0},                 {"norm1.eps", DLO_F32, 0, 0, 1},
+    {"attn.qkv.weight", DLO_FP8_E4M3, 3, 1, 0},       {"attn.qkv.weight_scale", DLO_E8M0, 3, 1, 0, 32},
+    {"attn.qkv.bias", DLO_F32, 3, 0, 0},              {"attn.out.weight", DLO_FP8_E4M3, 1, 1, 0},
+    {"attn.out.weight_scale", DLO_E8M0, 1, 1, 0, 32}, {"attn.out.bias", DLO_F32, 1, 0, 0},
+    {"norm2.weight", DLO_F32, 1, 0, 0},               {"norm2.bias", DLO_F32, 1, 0, 0},
+    {"norm2.eps", DLO_F32, 0, 0, 1},                  {"mlp.fc1.weight", DLO_FP8_E4M3, 4, 1, 0},
+    {"mlp.fc1.weight_scale", DLO_E8M0, 4, 1, 0, 32},  {"mlp.fc1.bias", DLO_F32, 4, 0, 0},
+    {"mlp.fc2.weight", DLO_FP8_E4M3, 1, 4, 0},        {"mlp.fc2.weight_scale", DLO_E8M0, 1, 4, 0, 32},
+    {"mlp.fc2.bias", DLO_F32, 1, 0, 0},
+};
 // logical parameters of the block forward (indices into kDit)
 enum {
   P_ADA_W, P_ADA_B, P_N1_W, P_N1_B, P_N1_EPS, P_QKV_W, P_QKV_B, P_OUT_W, P_OUT_B, P_N2_W, P_N2_B,
   P_N2_EPS, P_FC1_W, P_FC1_B, P_FC2_W, P_FC2_B
 };
-// where each logical parameter sits in the FP8 schema
+// where each logical parameter sits in the FP8, INT8 and MXFP8 schemas
 const int kFp8Index[DLO_DIT_N_PARAMS] = {0, 2, 3, 4, 5, 6, 8, 9, 11, 12, 13, 14, 15, 17, 18, 20};
 // the five weights (ada, qkv, out, fc1, fc2): logical index, scale index in the
-// FP8 schema, and numel / d^2
+// quantised schemas, and rows / d, columns / d
 const int kWeightP[5] = {P_ADA_W, P_QKV_W, P_OUT_W, P_FC1_W, P_FC2_W};
 const int kFp8Scale[5] = {1, 7, 10, 16, 19};
+const int64_t kWeightRows[5] = {6, 3, 1, 4, 1};
+const int64_t kWeightCols[5] = {1, 1, 1, 1, 4};
 const int64_t kWeightD2[5] = {6, 3, 1, 4, 4};
-enum { KIND_NONE = 0, KIND_DIT = 1, KIND_DIT_FP8 = 2 };
+enum { KIND_NONE = 0, KIND_DIT = 1, KIND_DIT_FP8 = 2, KIND_DIT_INT8 = 3, KIND_DIT_MX = 4 };
 
 int64_t schema_numel(const SchemaEntry &e, int64_t d) {
   if (e.fixed > 0) return e.fixed;
-  return e.rows_per_d * d * (e.cols_per_d ? e.cols_per_d * d : 1);
+  return e.rows_per_d * d * (e.cols_per_d ? e.cols_per_d * d : 1) / e.div;
 }
 
 const char *kKernelNames[DLO_KERNELS_PER_BLOCK] = {
-    "dequant_fp8", "adaln_gemv", "ln1_modulate", "quant_h", "gemm_qk", "gemm_v_t", "attention",
+    "dequant_weights", "adaln_gemv", "ln1_modulate", "quant_h", "gemm_qk", "gemm_v_t", "attention",
     "quant_attn", "gemm_out_residual", "ln2_modulate", "quant_h2", "gemm_fc1_gelu", "quant_u",
     "gemm_fc2_residual"};
 
@@ -152,14 +209,14 @@ struct BlockPlan {
   int64_t gshard[DLO_MAX_GROUPS] = {0, 0};
   int64_t gregion[DLO_MAX_GROUPS] = {0, 0};
   int64_t extent = 0, copy_bytes = 0;
-  int kind = KIND_NONE;            // KIND_DIT: bf16 weights; KIND_DIT_FP8: E4M3 weights
+  int kind = KIND_NONE;            // KIND_DIT: bf16 weights; else a quantised form
 
   int64_t param_byte(int p) const {
     const int g = pgroup[p];
     return gregion[g] + poff[p] * elt_bytes(gdtype[g]);
   }
   // slot byte offset of a logical parameter (P_*) of either schema
-  int64_t logical_byte(int lp) const { return param_byte(kind == KIND_DIT_FP8 ? kFp8Index[lp] : lp); }
+  int64_t logical_byte(int lp) const { return param_byte(kind >= KIND_DIT_FP8 ? kFp8Index[lp] : lp); }
 };
 
 struct dlo_run;
@@ -169,7 +226,8 @@ struct dlo_plan {
   std::vector<BlockPlan> blocks;
   int64_t slot_bytes = 0;
   int32_t max_d = 0;
-  int32_t max_fp8_d = 0;   // widest FP8 block (0: none)
+  int32_t max_fp8_d = 0;   // widest per-tensor FP8 block (0: none)
+  int32_t max_q_d = 0;     // widest INT8 or MXFP8 block (0: none)
   uint64_t id = 0;
   mutable std::mutex mu;
   mutable std::vector<dlo_run *> detached;   // runs started without a handle
@@ -379,15 +437,18 @@ void run_copies(std::vector<CopyTask> &tasks) {
 
 int64_t round_up64(int64_t T) { return (T + 63) / 64 * 64; }
 
-int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d) {
+// bytes of the dequantised-weight region: a per-tensor FP8 block's four linear
+// weights (12 f^2 bf16), an INT8 or MXFP8 block's five (18 q^2 bf16)
+int64_t dequant_bytes(int64_t f, int64_t q) { return std::max(24 * f * f, 36 * q * q); }
+
+int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d) {
   const int64_t d = max_d, f = fp8_d;
-  // FP8 blocks: the bf16 weights of their four linears (12 f^2 elements), and
-  // the E4M3 codes [T, 4f] and row scales [T] of a linear's input in the W8A8 form
-  const int64_t fp8 = f > 0 ? align_up(24 * f * f, DLO_ALIGN) + align_up(4 * T * f, DLO_ALIGN) +
-                                  align_up(4 * T, DLO_ALIGN)
-                            : 0;
+  // quantised blocks: their dequantised weights; FP8 blocks also the E4M3 codes
+  // [T, 4f] and row scales [T] of a linear's input in the W8A8 form
+  const int64_t dq = align_up(dequant_bytes(f, q_d), DLO_ALIGN);
+  const int64_t w8a8 = f > 0 ? align_up(4 * T * f, DLO_ALIGN) + align_up(4 * T, DLO_ALIGN) : 0;
   return align_up(4 * d, DLO_ALIGN) + align_up(24 * d, DLO_ALIGN) + align_up(2 * T * d, DLO_ALIGN) +
-         align_up(8 * round_up64(T) * d, DLO_ALIGN) + fp8;
+         align_up(8 * round_up64(T) * d, DLO_ALIGN) + dq + w8a8;
 }
 
 int validate_block_against(const BlockPlan &bp, const dlo_block &blk, int b, bool need_src) {
@@ -429,6 +490,70 @@ int dlo_block_schema_fp8(int32_t d, int32_t i, const char **name, int32_t *dtype
   if (name) *name = kDitFp8[i].name;
   if (dtype) *dtype = kDitFp8[i].dtype;
   if (numel) *numel = schema_numel(kDitFp8[i], d);
+  return ok();
+}
+
+int dlo_block_schema_int8(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel) {
+  if (i < 0 || i >= DLO_DIT_FP8_N_PARAMS || d < 1) return fail(DLO_E_ARG, "schema index out of range");
+  if (name) *name = kDitInt8[i].name;
+  if (dtype) *dtype = kDitInt8[i].dtype;
+  if (numel) *numel = schema_numel(kDitInt8[i], d);
+  return ok();
+}
+
+int dlo_block_schema_mxfp8(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel) {
+  if (i < 0 || i >= DLO_DIT_FP8_N_PARAMS || d < 1) return fail(DLO_E_ARG, "schema index out of range");
+  if (d % 32) return fail(DLO_E_ARG, "MXFP8 blocks need d %% 32 == 0 (32-element scale blocks)");
+  if (name) *name = kDitMx[i].name;
+  if (dtype) *dtype = kDitMx[i].dtype;
+  if (numel) *numel = schema_numel(kDitMx[i], d);
+  return ok();
+}
+
+int dlo_quantize_int8(const uint16_t *w, int64_t rows, int64_t cols, int8_t *codes, float *scales) {
+  if (rows < 0 || cols < 0 || (rows > 0 && (!w || !codes || !scales)))
+    return fail(DLO_E_ARG, "bad arguments");
+  for_rows(rows, cols, [&](int64_t r) {
+    const uint16_t *wr = w + r * cols;
+    float amax = 0.f;
+    for (int64_t j = 0; j < cols; ++j) {
+      const float a = std::fabs(widen_bf16(wr[j]));
+      if (a > amax) amax = a;  // NaN never compares greater
+    }
+    const float sc = amax > 0.f ? amax / 127.0f : 1.0f;
+    scales[r] = sc;
+    for (int64_t j = 0; j < cols; ++j) {
+      const float q = std::nearbyintf(widen_bf16(wr[j]) / sc);  // default rounding: to nearest even
+      codes[r * cols + j] = q != q ? 0 : (int8_t)std::max(-127.0f, std::min(127.0f, q));
+    }
+  });
+  return ok();
+}
+
+int dlo_quantize_mxfp8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *codes, uint8_t *scales) {
+  if (rows < 0 || cols < 0 || cols % 32 || (rows > 0 && (!w || !codes || !scales)))
+    return fail(DLO_E_ARG, "bad arguments (cols must be a multiple of 32)");
+  const int64_t nb = cols / 32;
+  for_rows(rows, cols, [&](int64_t r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint16_t *wb = w + r * cols + b * 32;
+      float amax = 0.f;
+      for (int j = 0; j < 32; ++j) {
+        const float a = std::fabs(widen_bf16(wb[j]));
+        if (a > amax) amax = a;
+      }
+      // shared exponent floor(log2 amax) - 8: the exponent field of amax (bf16
+      // values are normal or zero), clamped to the E8M0 range
+      int X = -127;
+      if (amax > 0.f) {
+        uint32_t u;
+        std::memcpy(&u, &amax, 4);
+        X = std::max(-127, std::min(127, (int)((u >> 23) & 0xFF) - 127 - 8));
+      }
+      scales[r * nb + b] = (uint8_t)(X + 127);
+      for (int j = 0; j < 32; ++j) codes[r * cols + b * 32 + j] = e4m3_encode(std::ldexp(widen_bf16(wb[j]), -X));
+    }
+  });
   return ok();
 }
 
@@ -542,11 +667,14 @@ int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_pl
               bp.numels[p] == schema_numel(sch[p], bp.d);
       return ok_;
     };
-    bp.kind = matches(kDit, DLO_DIT_N_PARAMS)          ? KIND_DIT
-              : matches(kDitFp8, DLO_DIT_FP8_N_PARAMS) ? KIND_DIT_FP8
-                                                       : KIND_NONE;
+    bp.kind = matches(kDit, DLO_DIT_N_PARAMS)                              ? KIND_DIT
+              : matches(kDitFp8, DLO_DIT_FP8_N_PARAMS)                     ? KIND_DIT_FP8
+              : matches(kDitInt8, DLO_DIT_FP8_N_PARAMS)                    ? KIND_DIT_INT8
+              : bp.d % 32 == 0 && matches(kDitMx, DLO_DIT_FP8_N_PARAMS) ? KIND_DIT_MX
+                                                                           : KIND_NONE;
     pl->max_d = std::max(pl->max_d, bp.d);
     if (bp.kind == KIND_DIT_FP8) pl->max_fp8_d = std::max(pl->max_fp8_d, bp.d);
+    if (bp.kind == KIND_DIT_INT8 || bp.kind == KIND_DIT_MX) pl->max_q_d = std::max(pl->max_q_d, bp.d);
   }
   pl->id = g_plan_ids++;
   *out = pl;
@@ -603,7 +731,7 @@ int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens) {
     return -1;
   }
   g_err.clear();
-  return workspace_bytes_for(plan->max_d, tokens, plan->max_fp8_d);
+  return workspace_bytes_for(plan->max_d, tokens, plan->max_fp8_d, plan->max_q_d);
 }
 
 int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, int64_t cap,
@@ -927,7 +1055,7 @@ struct Workspace {
   uint8_t *act_codes;
 };
 
-Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d) {
+Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d) {
   char *p = static_cast<char *>(ws);
   Workspace w;
   w.silu_c = reinterpret_cast<float *>(p);
@@ -938,8 +1066,8 @@ Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d) {
   p += align_up(2 * T * max_d, DLO_ALIGN);
   w.big = reinterpret_cast<uint16_t *>(p);  // qk [T,2d], V^T [d,T64], a [T,d]; later u [T,4d]
   p += align_up(8 * round_up64(T) * max_d, DLO_ALIGN);
-  w.dq = reinterpret_cast<uint16_t *>(p);   // an FP8 block's linear weights, dequantised to bf16
-  p += fp8_d > 0 ? align_up(24 * (int64_t)fp8_d * fp8_d, DLO_ALIGN) : 0;
+  w.dq = reinterpret_cast<uint16_t *>(p);   // a quantised block's weights, dequantised to bf16
+  p += align_up(dequant_bytes(fp8_d, q_d), DLO_ALIGN);
   w.act_codes = reinterpret_cast<uint8_t *>(p);  // W8A8: a linear input's E4M3 codes [T, <= 4d]
   p += fp8_d > 0 ? align_up(4 * T * fp8_d, DLO_ALIGN) : 0;
   w.act_scale = reinterpret_cast<float *>(p);    // ... and its per-row scales [T]
@@ -976,6 +1104,22 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
       if ((e = dlo::launch_dequant_fp8(W8[i], n, S8[i], dst, s)) != hipSuccess) return e;
       Wt[i] = dst;
       dst += n;
+    }
+  } else if (bp.kind == KIND_DIT_INT8 || bp.kind == KIND_DIT_MX) {
+    // INT8 / MXFP8: all five weights dequantised (MXFP8 exactly: an E4M3 value
+    // times a power of two fits bf16)
+    uint16_t *dst = w.dq;
+    for (int i = 0; i < 5; ++i) {
+      const int64_t rows = kWeightRows[i] * d, cols = kWeightCols[i] * d;
+      const char *sc = base + bp.param_byte(kFp8Scale[i]);
+      e = bp.kind == KIND_DIT_INT8
+              ? dlo::launch_dequant_int8(reinterpret_cast<const int8_t *>(P(kWeightP[i])), rows, cols,
+                                         reinterpret_cast<const float *>(sc), dst, s)
+              : dlo::launch_dequant_mxfp8(reinterpret_cast<const uint8_t *>(P(kWeightP[i])), rows * cols,
+                                          reinterpret_cast<const uint8_t *>(sc), dst, s);
+      if (e != hipSuccess) return e;
+      Wt[i] = dst;
+      dst += rows * cols;
     }
   } else {
     for (int i = 0; i < 5; ++i) Wt[i] = reinterpret_cast<const uint16_t *>(P(kWeightP[i]));
@@ -1068,7 +1212,7 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
     return fail(DLO_E_UNSUPPORTED, "x_row_stride too large for 32-bit tile offsets");
   if (((int64_t)a->tokens + 64) * 3 * plan->max_d * 2 >= ((int64_t)1 << 31))
     return fail(DLO_E_UNSUPPORTED, "tokens x 3 d too large for 32-bit buffer offsets");
-  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens, plan->max_fp8_d);
+  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d);
   if (a->workspace_bytes < need)
     return fail(DLO_E_WORKSPACE, "workspace %lld < %lld bytes", (long long)a->workspace_bytes, (long long)need);
   if (!resident) {
@@ -1146,7 +1290,7 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
     r.t_copy_begin = r.t_copy_end = r.t_compute_begin = r.t_compute_end = -1.f;
   }
 
-  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d);
+  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d);
   hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
   auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
   hipError_t e = hipSuccess;
@@ -1412,6 +1556,23 @@ int dlo_op_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint
   if (n < 0 || n % 16 || (uintptr_t)codes % 16 || (uintptr_t)out % 32)
     return fail(DLO_E_UNSUPPORTED, "dequant: n %% 16 == 0, codes 16-B and out 32-B aligned required");
   int rc = check_hip(dlo::launch_dequant_fp8(codes, n, scale, out, (hipStream_t)stream), "dequant_fp8");
+  return rc ? rc : ok();
+}
+
+int dlo_op_dequant_int8(const int8_t *codes, int64_t rows, int64_t cols, const float *scales, uint16_t *out,
+                        void *stream) {
+  if (!codes || !scales || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (rows < 0 || cols < 16 || cols % 16 || (uintptr_t)codes % 16 || (uintptr_t)out % 32)
+    return fail(DLO_E_UNSUPPORTED, "dequant_int8: cols %% 16 == 0, codes 16-B and out 32-B aligned required");
+  int rc = check_hip(dlo::launch_dequant_int8(codes, rows, cols, scales, out, (hipStream_t)stream), "dequant_int8");
+  return rc ? rc : ok();
+}
+
+int dlo_op_dequant_mxfp8(const uint8_t *codes, int64_t n, const uint8_t *scales, uint16_t *out, void *stream) {
+  if (!codes || !scales || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (n < 0 || n % 32 || (uintptr_t)codes % 16 || (uintptr_t)out % 32)
+    return fail(DLO_E_UNSUPPORTED, "dequant_mxfp8: n %% 32 == 0, codes 16-B and out 32-B aligned required");
+  int rc = check_hip(dlo::launch_dequant_mxfp8(codes, n, scales, out, (hipStream_t)stream), "dequant_mxfp8");
   return rc ? rc : ok();
 }
 

@@ -203,6 +203,54 @@ __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint32_t *__rest
   out[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// INT8 weights ([Doc] "Request and loading constraints": online INT8 keeps an
+// int8 weight and an fp32 scale, here one per output row): bf16(code * scale_r),
+// round to nearest even.  16 codes per thread, all in one row (cols % 16 == 0).
+__global__ __launch_bounds__(256) void dequant_int8_kernel(const u32x4 *__restrict__ codes,
+                                                          const float *__restrict__ scales, int64_t cols16,
+                                                          u32x4 *__restrict__ out, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const float sc = scales[i / cols16];
+  const u32x4 w = codes[i];
+  uint32_t o[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float v0 = (float)(int8_t)(w[k] & 0xFF), v1 = (float)(int8_t)((w[k] >> 8) & 0xFF);
+    const float v2 = (float)(int8_t)((w[k] >> 16) & 0xFF), v3 = (float)(int8_t)(w[k] >> 24);
+    o[2 * k] = (uint32_t)f32_to_bf16(v0 * sc) | ((uint32_t)f32_to_bf16(v1 * sc) << 16);
+    o[2 * k + 1] = (uint32_t)f32_to_bf16(v2 * sc) | ((uint32_t)f32_to_bf16(v3 * sc) << 16);
+  }
+  out[2 * i] = u32x4{o[0], o[1], o[2], o[3]};
+  out[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// MXFP8 weights (same passage: an fp8 weight and an e8m0 block scale, here one
+// per 32 consecutive elements): code value * 2^(e - 127); the product is exact
+// in fp32 and fits bf16's 8-bit significand, so the rounding never changes it
+// for scales of normal range.  E8M0 byte 255 is NaN, 0 is 2^-127.  16 codes per
+// thread, all in one scale block.
+__global__ __launch_bounds__(256) void dequant_mxfp8_kernel(const u32x4 *__restrict__ codes,
+                                                           const uint8_t *__restrict__ scales,
+                                                           u32x4 *__restrict__ out, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const uint32_t eb = scales[i >> 1];
+  const float sc = eb == 255u ? __uint_as_float(0x7FC00000u)
+                              : eb == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(eb << 23);
+  const u32x4 w = codes[i];
+  uint32_t o[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);  // bytes 0, 1
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);   // bytes 2, 3
+    o[2 * k] = (uint32_t)f32_to_bf16(lo[0] * sc) | ((uint32_t)f32_to_bf16(lo[1] * sc) << 16);
+    o[2 * k + 1] = (uint32_t)f32_to_bf16(hi[0] * sc) | ((uint32_t)f32_to_bf16(hi[1] * sc) << 16);
+  }
+  out[2 * i] = u32x4{o[0], o[1], o[2], o[3]};
+  out[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 // ---------------------------------------------------------------------------
 // Per-row (per-token) dynamic E4M3 quantization of a bf16 activation matrix,
 // the input side of an FP8 linear: scale_r = amax_r / 448 in fp32 (1 for an
@@ -281,6 +329,27 @@ hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scal
   const int64_t blocks = (n16 + 255) / 256;
   hipLaunchKernelGGL(dequant_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t *>(codes), scale, reinterpret_cast<u32x4 *>(out), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_int8(const int8_t *codes, int64_t rows, int64_t cols, const float *scales,
+                               uint16_t *out, hipStream_t s) {
+  if (cols % 16) return hipErrorInvalidValue;
+  const int64_t n16 = rows * cols / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_int8_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4 *>(codes), scales, cols / 16, reinterpret_cast<u32x4 *>(out),
+                     n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mxfp8(const uint8_t *codes, int64_t n, const uint8_t *scales, uint16_t *out,
+                                hipStream_t s) {
+  if (n % 32) return hipErrorInvalidValue;
+  const int64_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_mxfp8_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4 *>(codes), scales, reinterpret_cast<u32x4 *>(out), n16);
   return hipGetLastError();
 }
 

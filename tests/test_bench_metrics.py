@@ -86,7 +86,8 @@ def test_block_flops_and_kernel_work():
     assert total * 1e12 == pytest.approx(24 * 28800 * 5120 ** 2 + 4 * 28800 ** 2 * 5120, rel=1e-12)
     assert bench.kernel_work("attention", 5120, 28800)[2] == "mfma"
     assert bench.kernel_work("ln1_modulate", 5120, 28800)[2] == "hbm"
-    assert bench.kernel_work("dequant_fp8", 5120, 28800, fp8=False)[0] == 0
+    assert bench.kernel_work("dequant_weights", 5120, 28800, form="bf16")[0] == 0
+    assert bench.kernel_work("dequant_weights", 5120, 28800, form="int8")[0] == pytest.approx((54 * 5120 ** 2 + 60 * 5120) / 1e9)
 
 
 def test_counted_traffic_is_null_once_the_kernel_changed(monkeypatch):

@@ -410,9 +410,80 @@ def test_kernel_slot_names():
     quantisations just before the linears they feed; out of range gives NULL."""
     names = dlo.kernel_names()
     assert len(names) == dlo.KERNELS_PER_BLOCK == len(set(names))
-    order = ["dequant_fp8", "adaln_gemv", "ln1_modulate", "quant_h", "gemm_qk", "gemm_v_t", "attention",
+    order = ["dequant_weights", "adaln_gemv", "ln1_modulate", "quant_h", "gemm_qk", "gemm_v_t", "attention",
              "quant_attn", "gemm_out_residual", "ln2_modulate", "quant_h2", "gemm_fc1_gelu", "quant_u",
              "gemm_fc2_residual"]
     assert names == order
     assert dlo.lib().dlo_kernel_name(dlo.KERNELS_PER_BLOCK) is None
     assert dlo.lib().dlo_kernel_name(-1) is None
+
+
+# ---------------------------------------------------------------------------
+# INT8 and MXFP8 weight groups
+# ---------------------------------------------------------------------------
+
+def _quant_matrices():
+    rng = np.random.default_rng(11)
+    a = rng.normal(0, 0.02, (64, 256))
+    a[3] = 0.0                                     # zero row / zero blocks
+    a[5, 7] = 3.0                                  # outlier
+    a[9, 32:64] = 0.0
+    b = rng.normal(0, 1.0, (48, 96)) * np.exp(rng.uniform(-14, 14, (48, 96)))   # wide dynamic range
+    c = rng.normal(0, 0.5, (2048, 1024))           # the threaded path
+    d = (np.frombuffer(rng.bytes(2 * 40 * 64), dtype=np.uint16).reshape(40, 64) & 0x7F7F)  # any finite bits
+    e = np.zeros((3, 32))
+    return [_bf16(a), _bf16(b), _bf16(c), d.astype(np.uint16), _bf16(e), np.zeros((0, 32), np.uint16)]
+
+
+def test_int8_quantizer_matches_oracle_byte_for_byte():
+    from oracle import quant
+    for w in _quant_matrices():
+        codes, scales = dlo.quantize_int8(w)
+        rc, rs = quant.quantize_int8(w)
+        assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(codes, rc)
+
+
+def test_mxfp8_quantizer_matches_oracle_byte_for_byte():
+    from oracle import quant
+    for w in _quant_matrices():
+        codes, scales = dlo.quantize_mxfp8(w)
+        rc, rs = quant.quantize_mxfp8(w)
+        assert np.array_equal(scales, rs)
+        assert np.array_equal(codes, rc)
+    with pytest.raises(dlo.DLOError):
+        dlo.quantize_mxfp8(np.zeros((2, 48), np.uint16))          # columns not a multiple of 32
+
+
+@pytest.mark.parametrize("form", ["int8", "mxfp8"])
+def test_quantised_schema_plan_and_pack(form):
+    from oracle import quant
+    d, k = 256, 4
+    sch = dlo.block_schema(d, form=form)
+    q = quant.quantize_block(synth.block_params(1, 0, d), form)
+    assert [(n, dt, int(a.size)) for n, dt, a in q] == sch
+    # libdlo's own quantizer gives the same block, byte for byte
+    ql = dlo.quantize_block(synth.block_params(1, 0, d), form)
+    for (n1, d1, a1), (n2, d2, a2) in zip(q, ql):
+        assert (n1, d1) == (n2, d2) and np.asarray(a1).tobytes() == np.asarray(a2).tobytes()
+    p = dlo.Plan([(d, 4, q), (d, 4, synth.block_params(1, 1, d))], k)
+    info = p.block_info(0)
+    assert info["form"] == form and p.block_info(1)["form"] == "bf16"
+    want_dt = ["i8", "f32"] if form == "int8" else ["fp8", "e8m0", "f32"]
+    assert info["dtype"] == want_dt
+    bp = op.plan_block(op.specs_of(q), k)
+    assert info["extent"] == bp.extent and info["region"] == [g.region for g in bp.groups]
+    assert info["numel"] == [g.numel for g in bp.groups]
+    st = dlo.HostStore(p, pinned=False)
+    st.pack(0, [(d, 4, q), (d, 4, synth.block_params(1, 1, d))])
+    sh = op.pack_block(q, bp)
+    for g in range(len(bp.groups)):
+        for r in range(k):
+            assert st.shard(0, g, r).tobytes() == sh[g][r].tobytes()
+    # the workspace holds all five dequantised weights (18 d^2 bf16)
+    p_bf = dlo.Plan([(d, 4, synth.block_params(1, 1, d))], k)
+    al = lambda n: (n + 255) // 256 * 256
+    assert p.workspace_bytes(64) - p_bf.workspace_bytes(64) == al(36 * d * d)
+    if form == "mxfp8":
+        with pytest.raises(dlo.DLOError):
+            dlo.block_schema(48, form="mxfp8")
