@@ -419,9 +419,10 @@ int dlo_quantize_fp8(const uint16_t *w, int64_t n, uint8_t *codes, float *scale)
 int dlo_block_schema_int8(int32_t d, int32_t i, const char **name, int32_t *dtype, int64_t *numel);
 
 /* Parameter i (0 <= i < 21) of the MXFP8 form (same passage: online MXFP8 keeps
- * an fp8 weight plus an e8m0 block scale): X.weight [out, in] becomes X.weight
- * (DLO_FP8_E4M3, same shape) followed by X.weight_scale (DLO_E8M0, one per 32
- * consecutive elements of a row: out * in / 32 elements).  Groups: E4M3
+ * an fp8 weight plus an e8m0 block scale, possibly as a transposed view): X.weight
+ * [out, in] becomes X.weight (DLO_FP8_E4M3, same shape) followed by
+ * X.weight_scale (DLO_E8M0, one per 32 consecutive elements of a row, stored
+ * block-major [in / 32, out]: out * in / 32 elements).  Groups: E4M3
  * (18 d^2), E8M0 (18 d^2 / 32) and fp32.  Its forward dequantises each weight
  * to bf16(code_value * 2^(e - 127)) (exact), then runs the bf16 block forward.
  * DLO_E_ARG for i out of range or d % 32 != 0. */
@@ -435,10 +436,11 @@ int dlo_block_schema_mxfp8(int32_t d, int32_t i, const char **name, int32_t *dty
 int dlo_quantize_int8(const uint16_t *w, int64_t rows, int64_t cols, int8_t *codes, float *scales);
 
 /* The same for the MXFP8 block (OCP MX, E4M3 elements): for each 32-element
- * block of a row, X = floor(log2 amax) - 8 clamped to [-127, 127] (-127 for an
- * all-zero block), scales[r * cols / 32 + b] = X + 127, codes = the E4M3 code
- * nearest to float(w) / 2^X, ties to the even code, saturating at +-448.
- * cols % 32 == 0, else DLO_E_ARG. */
+ * block b of row r, X = floor(log2 amax) - 8 clamped to [-127, 127] (-127 for
+ * an all-zero block), scales[b * rows + r] = X + 127 (block-major: the
+ * transposed view of [rows, cols / 32]), codes = the E4M3 code nearest to
+ * float(w) / 2^X, ties to the even code, saturating at +-448.  cols % 32 == 0,
+ * else DLO_E_ARG. */
 int dlo_quantize_mxfp8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *codes, uint8_t *scales);
 
 /* The kernels the block forward is made of, callable one at a time (device
@@ -542,11 +544,13 @@ int dlo_op_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint
 int dlo_op_dequant_int8(const int8_t *codes, int64_t rows, int64_t cols, const float *scales, uint16_t *out,
                         void *stream);
 
-/* MXFP8 weight dequantisation: out[i] = bf16(value(codes[i]) * 2^(scales[i / 32]
- * - 127)), exact for scales whose products stay in bf16's normal range; E8M0
- * byte 255 gives NaN.  n % 32 == 0, codes 16-B and out 32-B aligned, else
- * DLO_E_UNSUPPORTED. */
-int dlo_op_dequant_mxfp8(const uint8_t *codes, int64_t n, const uint8_t *scales, uint16_t *out, void *stream);
+/* MXFP8 weight dequantisation: out[r, j] = bf16(value(codes[r, j]) *
+ * 2^(scales[(j / 32) * rows + r] - 127)) (scales block-major, as the MXFP8 block
+ * form stores them), exact for scales whose products stay in bf16's normal
+ * range; E8M0 byte 255 gives NaN.  cols % 32 == 0, codes 16-B and out 32-B
+ * aligned, else DLO_E_UNSUPPORTED. */
+int dlo_op_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols, const uint8_t *scales, uint16_t *out,
+                         void *stream);
 
 int dlo_op_digest(const void *base, const int64_t *offsets, const int64_t *lengths,
                   int32_t n_regions, uint64_t *out, void *stream);

@@ -168,8 +168,8 @@ _SIGS = {
                                           ctypes.c_void_p]),
     "dlo_op_dequant_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]),
-    "dlo_op_dequant_mxfp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                                            ctypes.c_void_p]),
+    "dlo_op_dequant_mxfp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]),
     "dlo_op_dequant_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]),
     "dlo_op_digest": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
@@ -244,12 +244,13 @@ def quantize_int8(w_bf16):
 
 
 def quantize_mxfp8(w_bf16):
-    """dlo_quantize_mxfp8 on a host matrix of bf16 bit patterns -> (E4M3 codes, E8M0 scales [rows, cols / 32])."""
+    """dlo_quantize_mxfp8 on a host matrix of bf16 bit patterns -> (E4M3 codes, E8M0 scales block-major
+    [cols / 32, rows])."""
     w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
     if w.ndim != 2:
         raise ValueError("quantize_mxfp8 takes a matrix")
     codes = np.empty(w.shape, dtype=np.uint8)
-    scales = np.empty((w.shape[0], w.shape[1] // 32), dtype=np.uint8)
+    scales = np.empty((w.shape[1] // 32, w.shape[0]), dtype=np.uint8)
     _check(lib().dlo_quantize_mxfp8(w.ctypes.data_as(ctypes.c_void_p), w.shape[0], w.shape[1],
                                     codes.ctypes.data_as(ctypes.c_void_p), scales.ctypes.data_as(ctypes.c_void_p)))
     return codes, scales
@@ -533,8 +534,8 @@ def op_dequant_int8(codes, rows, cols, scales, out, stream):
     _check(lib().dlo_op_dequant_int8(codes, rows, cols, scales, out, stream))
 
 
-def op_dequant_mxfp8(codes, n, scales, out, stream):
-    _check(lib().dlo_op_dequant_mxfp8(codes, n, scales, out, stream))
+def op_dequant_mxfp8(codes, rows, cols, scales, out, stream):
+    _check(lib().dlo_op_dequant_mxfp8(codes, rows, cols, scales, out, stream))
 
 
 def op_digest(base, offsets, lengths, out, stream):

@@ -550,7 +550,7 @@ int dlo_quantize_mxfp8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *c
         std::memcpy(&u, &amax, 4);
         X = std::max(-127, std::min(127, (int)((u >> 23) & 0xFF) - 127 - 8));
       }
-      scales[r * nb + b] = (uint8_t)(X + 127);
+      scales[b * rows + r] = (uint8_t)(X + 127);   // block-major [cols / 32, rows]
       for (int j = 0; j < 32; ++j) codes[r * cols + b * 32 + j] = e4m3_encode(std::ldexp(widen_bf16(wb[j]), -X));
     }
   });
@@ -1115,7 +1115,7 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
       e = bp.kind == KIND_DIT_INT8
               ? dlo::launch_dequant_int8(reinterpret_cast<const int8_t *>(P(kWeightP[i])), rows, cols,
                                          reinterpret_cast<const float *>(sc), dst, s)
-              : dlo::launch_dequant_mxfp8(reinterpret_cast<const uint8_t *>(P(kWeightP[i])), rows * cols,
+              : dlo::launch_dequant_mxfp8(reinterpret_cast<const uint8_t *>(P(kWeightP[i])), rows, cols,
                                           reinterpret_cast<const uint8_t *>(sc), dst, s);
       if (e != hipSuccess) return e;
       Wt[i] = dst;
@@ -1568,11 +1568,13 @@ int dlo_op_dequant_int8(const int8_t *codes, int64_t rows, int64_t cols, const f
   return rc ? rc : ok();
 }
 
-int dlo_op_dequant_mxfp8(const uint8_t *codes, int64_t n, const uint8_t *scales, uint16_t *out, void *stream) {
+int dlo_op_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols, const uint8_t *scales, uint16_t *out,
+                         void *stream) {
   if (!codes || !scales || !out) return fail(DLO_E_ARG, "NULL argument");
-  if (n < 0 || n % 32 || (uintptr_t)codes % 16 || (uintptr_t)out % 32)
-    return fail(DLO_E_UNSUPPORTED, "dequant_mxfp8: n %% 32 == 0, codes 16-B and out 32-B aligned required");
-  int rc = check_hip(dlo::launch_dequant_mxfp8(codes, n, scales, out, (hipStream_t)stream), "dequant_mxfp8");
+  if (rows < 0 || cols < 32 || cols % 32 || (uintptr_t)codes % 16 || (uintptr_t)out % 32)
+    return fail(DLO_E_UNSUPPORTED, "dequant_mxfp8: cols %% 32 == 0, codes 16-B and out 32-B aligned required");
+  int rc = check_hip(dlo::launch_dequant_mxfp8(codes, rows, cols, scales, out, (hipStream_t)stream),
+                     "dequant_mxfp8");
   return rc ? rc : ok();
 }
 

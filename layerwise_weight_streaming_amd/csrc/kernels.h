@@ -51,9 +51,9 @@ hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scal
 // INT8 weight [rows, cols] with one fp32 scale per row -> bf16; cols % 16 == 0
 hipError_t launch_dequant_int8(const int8_t *codes, int64_t rows, int64_t cols, const float *scales,
                                uint16_t *out, hipStream_t s);
-// MXFP8 weight: n E4M3 codes with one E8M0 scale per 32 -> bf16; n % 32 == 0
-hipError_t launch_dequant_mxfp8(const uint8_t *codes, int64_t n, const uint8_t *scales, uint16_t *out,
-                                hipStream_t s);
+// MXFP8 weight [rows, cols] with E8M0 scales block-major [cols / 32, rows] -> bf16; cols % 32 == 0
+hipError_t launch_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols, const uint8_t *scales,
+                                uint16_t *out, hipStream_t s);
 
 // per-row dynamic E4M3 of bf16 x [M, K] (row stride ldx): scale[r] = amax_r / 448
 // (1 for a zero row), q[r, k] = E4M3 code nearest to x / scale[r]; K, ldx, ldq

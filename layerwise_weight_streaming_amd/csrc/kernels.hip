@@ -226,16 +226,18 @@ __global__ __launch_bounds__(256) void dequant_int8_kernel(const u32x4 *__restri
 }
 
 // MXFP8 weights (same passage: an fp8 weight and an e8m0 block scale, here one
-// per 32 consecutive elements): code value * 2^(e - 127); the product is exact
-// in fp32 and fits bf16's 8-bit significand, so the rounding never changes it
-// for scales of normal range.  E8M0 byte 255 is NaN, 0 is 2^-127.  16 codes per
-// thread, all in one scale block.
+// per 32 consecutive elements of a row, stored block-major [cols / 32, rows]):
+// code value * 2^(e - 127); the product is exact in fp32 and fits bf16's 8-bit
+// significand, so the rounding never changes it for scales of normal range.
+// E8M0 byte 255 is NaN, 0 is 2^-127.  16 codes per thread, all in one block.
 __global__ __launch_bounds__(256) void dequant_mxfp8_kernel(const u32x4 *__restrict__ codes,
-                                                           const uint8_t *__restrict__ scales,
-                                                           u32x4 *__restrict__ out, int64_t n16) {
+                                                           const uint8_t *__restrict__ scales, int64_t rows,
+                                                           int64_t cols16, u32x4 *__restrict__ out,
+                                                           int64_t n16) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n16) return;
-  const uint32_t eb = scales[i >> 1];
+  const int64_t r = i / cols16, blk = (i - r * cols16) >> 1;
+  const uint32_t eb = scales[blk * rows + r];
   const float sc = eb == 255u ? __uint_as_float(0x7FC00000u)
                               : eb == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(eb << 23);
   const u32x4 w = codes[i];
@@ -343,13 +345,14 @@ hipError_t launch_dequant_int8(const int8_t *codes, int64_t rows, int64_t cols, 
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_mxfp8(const uint8_t *codes, int64_t n, const uint8_t *scales, uint16_t *out,
-                                hipStream_t s) {
-  if (n % 32) return hipErrorInvalidValue;
-  const int64_t n16 = n / 16;
+hipError_t launch_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols, const uint8_t *scales,
+                                uint16_t *out, hipStream_t s) {
+  if (cols % 32) return hipErrorInvalidValue;
+  const int64_t n16 = rows * cols / 16;
   if (n16 == 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_mxfp8_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<const u32x4 *>(codes), scales, reinterpret_cast<u32x4 *>(out), n16);
+                     reinterpret_cast<const u32x4 *>(codes), scales, rows, cols / 16,
+                     reinterpret_cast<u32x4 *>(out), n16);
   return hipGetLastError();
 }
 

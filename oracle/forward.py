@@ -83,9 +83,9 @@ def param_dict(params):
         elif dt == "i8" and sdt == "f32":
             scl = np.asarray(sc, np.float32).reshape(-1)
             out[name] = quant.dequantize_int8(np.asarray(c, np.int8).reshape(scl.size, -1), scl)
-        elif dt == "fp8" and sdt == "e8m0":
+        elif dt == "fp8" and sdt == "e8m0":   # scales block-major [in / 32, out]
             c2 = np.asarray(c, np.uint8)
-            out[name] = quant.dequantize_mxfp8(c2, np.asarray(sc, np.uint8).reshape(c2.shape[0], -1))
+            out[name] = quant.dequantize_mxfp8(c2, np.asarray(sc, np.uint8).reshape(-1, c2.shape[0]).T)
         else:
             raise ValueError(f"{name}: no dequantisation for {dt} codes with {sdt} scales")
     return out
@@ -139,7 +139,7 @@ def modulation(c, P, d):
     return [mod[i * d:(i + 1) * d] for i in range(6)]
 
 
-def dit_block(x, c, P, n_heads, act_fp8=False):
+def dit_block(x, c, P, n_heads, act_fp8=False, act_mx=False):
     """One block on residual x [T, D] (float64, updated copy returned).
 
     act_fp8: the four block linears take their input through per-token E4M3
@@ -147,11 +147,18 @@ def dit_block(x, c, P, n_heads, act_fp8=False):
     online FP8 linears; the adaLN linear keeps its float input.  The quantizer
     reads the input as the model stores it, rounded to bf16 (round_bf16): the
     pages fix no precision for this decision, so it is taken in the storage
-    precision of the activations it quantizes.
+    precision of the activations it quantizes.  act_mx: the same with MXFP8
+    inputs (oracle.quant.fake_quant_mx_rows: per row, blocks of 32 along the
+    input dimension), the W8A8 form of an MXFP8 block's linears.
     """
-    from . import fp8
+    from . import fp8, quant
 
-    lin_in = (lambda t: fp8.fake_quant_rows(round_bf16(t))) if act_fp8 else (lambda t: t)
+    if act_mx:
+        lin_in = quant.fake_quant_mx_rows
+    elif act_fp8:
+        lin_in = lambda t: fp8.fake_quant_rows(round_bf16(t))
+    else:
+        lin_in = lambda t: t
     d = P["norm1.weight"].shape[0]
     x = np.array(x, dtype=np.float64, copy=True)
     shift1, scale1, gate1, shift2, scale2, gate2 = modulation(c, P, d)
@@ -198,13 +205,15 @@ def forward_stack(x, c, blocks, heads, passes, act_fp8=False):
     """``passes`` chained passes over the blocks.
 
     blocks: list of [(name, dtype, array)] per block; heads: heads per block.
-    act_fp8: blocks with FP8 weights run their linears in the W8A8 form
-    (see dit_block); bf16 blocks are unaffected.
+    act_fp8: blocks with per-tensor FP8 or MXFP8 weights run their linears in
+    the W8A8 form (see dit_block: per-row E4M3 or MXFP8 inputs); bf16 and INT8
+    blocks are unaffected.
     """
     Ps = [param_dict(b) for b in blocks]
-    fp8_block = [any(dt == "fp8" for _, dt, _ in b) for b in blocks]
+    mx_block = [any(dt == "e8m0" for _, dt, _ in b) for b in blocks]
+    fp8_block = [any(dt == "fp8" for _, dt, _ in b) and not mx for b, mx in zip(blocks, mx_block)]
     y = np.asarray(x, dtype=np.float64)
     for _ in range(passes):
-        for P, H, f8 in zip(Ps, heads, fp8_block):
-            y = dit_block(y, c, P, H, act_fp8=act_fp8 and f8)
+        for P, H, f8, mx in zip(Ps, heads, fp8_block, mx_block):
+            y = dit_block(y, c, P, H, act_fp8=act_fp8 and f8, act_mx=act_fp8 and mx)
     return y

@@ -22,7 +22,12 @@ readings here (listed in the design doc as well):
   normal E4M3 value), clamped to [-127, 127]; an all-zero block takes
   X = -127; each element is the E4M3 code nearest to float32(w) / 2^X, ties to
   the even code, saturating at +-448; the E8M0 byte is X + 127 (255 is NaN).
-  The dequantised weight is code_value * 2^X, exactly.
+  The dequantised weight is code_value * 2^X, exactly.  The block form keeps
+  the scales block-major, [in / 32, out] (the transposed view the pages allow
+  for a finalised tensor): the scales of one input block for consecutive
+  output rows are adjacent, the order a block-scaled matrix product reads.
+* W8A8 with MXFP8 weights: each linear's input (as stored in bf16) is
+  quantised the same way, per row in blocks of 32 along the input dimension.
 """
 from __future__ import annotations
 
@@ -111,8 +116,8 @@ def quantize_block(params, form: str):
 
     Every bf16 matrix ``X.weight`` [out, in] becomes ``X.weight`` (int8 codes, or
     E4M3 codes as "fp8") followed by ``X.weight_scale`` (fp32 [out], or E8M0
-    [out * in / 32] as "e8m0"); fp32 parameters stay as they are, so each linear
-    registers weight, weight_scale, bias.
+    [in / 32, out] block-major as "e8m0"); fp32 parameters stay as they are, so
+    each linear registers weight, weight_scale, bias.
     """
     out = []
     for name, dt, arr in params:
@@ -125,7 +130,17 @@ def quantize_block(params, form: str):
             out += [(name, "i8", codes), (name + "_scale", "f32", scale)]
         elif form == "mxfp8":
             codes, scale = quantize_mxfp8(a)
-            out += [(name, "fp8", codes), (name + "_scale", "e8m0", scale.reshape(-1))]
+            out += [(name, "fp8", codes), (name + "_scale", "e8m0", np.ascontiguousarray(scale.T).reshape(-1))]
         else:
             raise ValueError(f"unknown form {form!r}")
     return out
+
+
+def fake_quant_mx_rows(x) -> np.ndarray:
+    """What a W8A8 MXFP8 linear multiplies: the input rounded to bf16 (as stored),
+    quantised per row in blocks of 32 (quantize_mxfp8), dequantised exactly."""
+    from .forward import round_bf16
+    r = round_bf16(x).astype(np.float32)                       # exact: bf16 values
+    bits = (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    codes, scales = quantize_mxfp8(bits)
+    return dequantize_mxfp8(codes, scales)

@@ -39,21 +39,24 @@ def test_dequant_int8_every_code():
 
 
 def test_dequant_mxfp8_every_code():
-    """Every E4M3 code against E8M0 scales from 2^-107 to 2^103: the product is exact in
-    bf16 (the code's 4 significant bits fit), NaN codes and the NaN scale give NaN."""
+    """Every E4M3 code against E8M0 scales from 2^-107 to 2^103 (block-major
+    [cols / 32, rows]): the product is exact in bf16 (the code's 4 significant bits
+    fit), NaN codes and the NaN scale give NaN."""
     torch = require_gpu()
-    n = 256 * 64
+    rows, cols = 64, 256
+    n = rows * cols
     rng = np.random.default_rng(8)
     codes = np.tile(np.arange(256, dtype=np.uint8), n // 256)
     rng.shuffle(codes)
-    scales = rng.integers(20, 231, n // 32).astype(np.uint8)
-    scales[5] = 255
+    scales = rng.integers(20, 231, (cols // 32, rows)).astype(np.uint8)
+    scales[1, 5] = 255
     dc, ds = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
     out = torch.empty(n, dtype=torch.int16, device="cuda")
-    dlo.op_dequant_mxfp8(dc.data_ptr(), n, ds.data_ptr(), out.data_ptr(), 0)
+    dlo.op_dequant_mxfp8(dc.data_ptr(), rows, cols, ds.data_ptr(), out.data_ptr(), 0)
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint16)
-    vals = fp8.DECODE[codes] * quant.e8m0_value(np.repeat(scales, 32))
+    vals = (fp8.DECODE[codes].reshape(rows, cols) *
+            np.repeat(quant.e8m0_value(scales).T, 32, axis=1)).reshape(-1)
     nan = np.isnan(vals)
     assert np.array_equal(got[~nan], _bf16_rne(vals[~nan].astype(np.float32)))
     assert np.array_equal(vals[~nan], ((got[~nan].astype(np.uint32) << 16).view(np.float32)).astype(np.float64))
@@ -68,7 +71,7 @@ def test_dequant_rejects_unsupported_shapes():
     with pytest.raises(dlo.DLOError):
         dlo.op_dequant_int8(c.data_ptr(), 2, 24, s_.data_ptr(), o.data_ptr(), 0)
     with pytest.raises(dlo.DLOError):
-        dlo.op_dequant_mxfp8(c.data_ptr(), 48, s_.data_ptr(), o.data_ptr(), 0)
+        dlo.op_dequant_mxfp8(c.data_ptr(), 1, 48, s_.data_ptr(), o.data_ptr(), 0)
 
 
 def _check_trace(tr, n, passes, regs):

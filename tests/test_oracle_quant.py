@@ -150,7 +150,7 @@ def test_quantised_block_form_is_the_bf16_block_with_dequantised_weights(form):
         if dt in ("i8", "fp8"):
             sc = dict((n, a) for n, _, a in q)[name + "_scale"]
             deq[name] = (quant.dequantize_int8(arr, sc) if form == "int8"
-                         else quant.dequantize_mxfp8(arr, sc.reshape(arr.shape[0], -1)))
+                         else quant.dequantize_mxfp8(arr, sc.reshape(-1, arr.shape[0]).T))
             assert np.array_equal(P[name], deq[name])
     rng = np.random.default_rng(6)
     x, c = rng.standard_normal((T, d)), rng.standard_normal(d)
@@ -160,3 +160,45 @@ def test_quantised_block_form_is_the_bf16_block_with_dequantised_weights(form):
     # the quantised block stays close to the bf16 one
     y, yb = of.dit_block(x, c, P, H), of.dit_block(x, c, of.param_dict(params), H)
     assert np.max(np.abs((y - x) - (yb - x))) < 0.1 * np.max(np.abs(yb - x))
+
+
+def test_mx_block_form_keeps_scales_block_major():
+    """X.weight_scale of the MXFP8 form lists, for each 32-wide input block, the scales
+    of all output rows: element (b, r) sits at b * out + r."""
+    d = 64
+    params = synth.block_params(7, 0, d)
+    q = dict((n, (dt, a)) for n, dt, a in quant.quantize_block(params, "mxfp8"))
+    w = dict((n, a) for n, _, a in params)["mlp.fc2.weight"]          # [d, 4d]
+    _, rs = quant.quantize_mxfp8(w)                                   # [d, 4d / 32]
+    dt, sc = q["mlp.fc2.weight_scale"]
+    assert dt == "e8m0" and sc.size == d * 4 * d // 32
+    for b in range(4 * d // 32):
+        for r in range(d):
+            assert sc[b * d + r] == rs[r, b]
+
+
+def test_mx_activation_fake_quant():
+    """W8A8 MXFP8 input: round to bf16, quantise per row in blocks of 32, dequantise;
+    against the block rule written out for one row."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((3, 64)) * np.exp2(rng.uniform(-8, 8, (3, 64)))
+    y = quant.fake_quant_mx_rows(x)
+    for r in range(3):
+        for b in range(2):
+            blk = of.round_bf16(x[r, 32 * b:32 * b + 32])
+            X = _shared_exp_by_doubling(np.max(np.abs(blk))) - 8
+            for j in range(32):
+                v = blk[j] / 2.0 ** X
+                d_ = np.abs(fp8.DECODE[:0x7F] - min(abs(v), 448.0))
+                d_[np.isnan(d_)] = np.inf
+                best = np.flatnonzero(d_ == d_.min())
+                code = best[0] if best.size == 1 else best[best % 2 == 0][0]
+                want = fp8.DECODE[code] * 2.0 ** X * (-1 if v < 0 else 1)
+                assert y[r, 32 * b + j] == want
+    # an MXFP8 block in the W8A8 form stays close to its W8A16 form
+    d, H, T = 64, 2, 12
+    P = of.param_dict(quant.quantize_block(synth.block_params(8, 0, d), "mxfp8"))
+    xx, c = rng.standard_normal((T, d)), rng.standard_normal(d)
+    y16, y8 = of.dit_block(xx, c, P, H), of.dit_block(xx, c, P, H, act_mx=True)
+    err = np.max(np.abs((y8 - xx) - (y16 - xx))) / np.max(np.abs(y16 - xx))
+    assert 0 < err < 0.1
