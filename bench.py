@@ -40,13 +40,17 @@ def kernel_work(name, d, T, form="bf16", w8a8=False):
     if name == "dequant_weights":   # codes (+ scales) in, bf16 weights out
         if fp8:     # the four linears, W8A16 only
             return (12 * d * d * 3 if not w8a8 else 0) / 1e9, "GB", "hbm"
+        if form == "mxfp8" and w8a8:   # the adaLN weight only
+            return (6 * d * d * 3 + 6 * d * d // 32) / 1e9, "GB", "hbm"
         if form == "int8":   # all five weights, fp32 scale per row (15 d rows)
             return (18 * d * d * 3 + 15 * d * 4) / 1e9, "GB", "hbm"
         if form == "mxfp8":  # all five weights, one E8M0 per 32 codes
             return (18 * d * d * 3 + 18 * d * d // 32) / 1e9, "GB", "hbm"
         return 0.0, "GB", "hbm"
-    if name.startswith("quant_"):   # bf16 rows in, E4M3 codes + fp32 row scales out
+    if name.startswith("quant_"):   # bf16 rows in, E4M3 codes + fp32 row / E8M0 block scales out
         K = 4 * d if name == "quant_u" else d
+        if form == "mxfp8" and w8a8:
+            return (T * K * 3 + T * K // 32) / 1e9, "GB", "hbm"
         return ((T * K * 3 + T * 4) if (fp8 and w8a8) else 0) / 1e9, "GB", "hbm"
     if name == "adaln_gemv":   # bf16 or E4M3 weight rows, silu(c), bias in, modulation out
         return (6 * d * d * (1 if fp8 else 2) + 6 * d * 4 * 2 + d * 4) / 1e9, "GB", "hbm"
@@ -284,8 +288,9 @@ def main():
                          "scales per row; mxfp8: E4M3 weights + E8M0 scales per 32 (quantized on the host before "
                          "packing), dequantised on the device after each copy")
     ap.add_argument("--compute", default="bf16", choices=["bf16", "fp8"],
-                    help="fp8 (needs --weights fp8): the four linears of each block as W8A8 "
-                         "FP8 products (per-row E4M3 inputs); attention stays bf16")
+                    help="fp8 (needs --weights fp8 or mxfp8): the four linears of each block as W8A8 "
+                         "FP8 products (per-row E4M3 inputs, or per-row MXFP8 inputs with hardware "
+                         "block scales); attention stays bf16")
     ap.add_argument("--resident-layers", type=int, default=0,
                     help="keep blocks 0 .. R-1 in device memory; stream the rest")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -296,8 +301,8 @@ def main():
                     help="skip the streamed == resident bit-exact check")
     args = ap.parse_args()
 
-    if args.compute == "fp8" and args.weights != "fp8":
-        print("--compute fp8 needs --weights fp8", file=sys.stderr)
+    if args.compute == "fp8" and args.weights not in ("fp8", "mxfp8"):
+        print("--compute fp8 needs --weights fp8 or mxfp8", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the stack is streamed from this host into this "
@@ -418,7 +423,7 @@ def main():
     _, unit, kbound = kernel_work(dname, w.width(0), T)
     avg_ms = per_kernel[jdom] / launches
     achieved = work[jdom] / launches / (avg_ms * 1e-3)
-    fp8_mfma = w8a8 and dname.startswith("gemm_") and any(i["fp8"] for i in infos)
+    fp8_mfma = w8a8 and dname.startswith("gemm_") and any(i["form"] in ("fp8", "mxfp8") for i in infos)
     peak = (PEAK_FP8_TFLOPS if fp8_mfma else PEAK_BF16_TFLOPS) if kbound == "mfma" else PEAK_HBM_GBS
     roofline = {"kernel": dname, "bound": kbound, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s" if kbound == "mfma" else "GB/s", "frac": achieved / peak,

@@ -277,16 +277,18 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 #define DLO_TRACE_TIMING 2u  /* timestamp copies, block computes and every kernel */
 #define DLO_RESIDENT 4u      /* no streaming: block b is read from resident_blocks[b] (same as
                                 n_resident = number of blocks) */
-#define DLO_FP8_COMPUTE 8u   /* Per-tensor FP8 blocks (dlo_block_schema_fp8) run their
-                                qkv, out, fc1 and fc2 linears as W8A8
-                                products ([Doc] "Request and loading constraints", online FP8
-                                linears): the input quantised per row to E4M3 as by
-                                dlo_op_quantize_rows_fp8, then dlo_op_gemm_fp8 with the
-                                weight's codes and scale read in place from the slot.
-                                Without it an FP8 block dequantises its four linears'
-                                weights to bf16 (W8A16).  Either way an FP8 block's adaLN
-                                GEMV reads its codes (dlo_op_adaln_fp8).  bf16, INT8 and
-                                MXFP8 blocks are unaffected. */
+#define DLO_FP8_COMPUTE 8u   /* FP8 and MXFP8 blocks run their qkv, out, fc1 and fc2
+                                linears as W8A8 products ([Doc] "Request and loading
+                                constraints", online FP8 and MXFP8 linears), the weight's
+                                codes and scales read in place from the slot: per-tensor
+                                FP8 quantises each input per row to E4M3
+                                (dlo_op_quantize_rows_fp8, dlo_op_gemm_fp8); MXFP8 per row
+                                in blocks of 32 (dlo_op_quantize_rows_mxfp8,
+                                dlo_op_gemm_mxfp8).  Without it their linears run on
+                                dequantised bf16 weights (W8A16).  An FP8 block's adaLN GEMV
+                                reads its codes (dlo_op_adaln_fp8); an MXFP8 block's runs on
+                                its dequantised weight.  bf16 and INT8 blocks are
+                                unaffected. */
 
 typedef struct {
   void *slot[2];            /* device, slot_bytes each, distinct (unused if nothing streams) */
@@ -506,6 +508,29 @@ int dlo_op_quantize_rows_fp8(const uint16_t *x, int64_t ldx, int32_t M, int32_t 
 int dlo_op_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B, int64_t ldb,
                     const float *b_scale, int32_t M, int32_t N, int32_t K, const float *bias,
                     const float *gate, void *C, int64_t ldc, int32_t epilogue, void *stream);
+
+/* Per-row MXFP8 quantization of an activation matrix, the input side of a W8A8
+ * MXFP8 linear (the MX rule of dlo_quantize_mxfp8 applied to each row of x bf16
+ * [M, K], row stride ldx): codes uint8 [M, ldq] (OCP E4M3), scales E8M0
+ * block-major [K / 32, lds] (row r of block b at b * lds + r); rows M .. lds - 1
+ * of scales are set to 127 (2^0).  All device, caller-owned.  K % 32 == 0, ldx
+ * and ldq multiples of 8 and >= K, lds >= M, x 16-B and codes 8-B aligned, else
+ * DLO_E_UNSUPPORTED. */
+int dlo_op_quantize_rows_mxfp8(const uint16_t *x, int64_t ldx, int32_t M, int32_t K, uint8_t *codes,
+                               int64_t ldq, uint8_t *scales, int64_t lds, void *stream);
+
+/* The MXFP8 form of dlo_op_gemm: C = sum over 32-blocks b of (A_b B_b^T) *
+ * 2^(sa[b, m] - 127) * 2^(sb[b, n] - 127) + bias, then the epilogue (0..3 as for
+ * dlo_op_gemm), with A [M, K] and B [N, K] OCP E4M3 codes (row strides lda, ldb
+ * in bytes), a_scales E8M0 block-major [K / 32, lds_a] and b_scales [K / 32,
+ * lds_b] (as dlo_op_quantize_rows_mxfp8 and the MXFP8 block form store them);
+ * the block scales are applied by v_mfma_scale_f32_32x32x64_f8f6f4 itself.  All
+ * device, caller-owned.  N % 256 == 0, K % 64 == 0, lds_a >= M and lds_b >= N
+ * multiples of 4, scales 4-B aligned, the rest as for dlo_op_gemm_fp8, else
+ * DLO_E_UNSUPPORTED. */
+int dlo_op_gemm_mxfp8(const uint8_t *A, int64_t lda, const uint8_t *a_scales, int64_t lds_a, const uint8_t *B,
+                      int64_t ldb, const uint8_t *b_scales, int64_t lds_b, int32_t M, int32_t N, int32_t K,
+                      const float *bias, const float *gate, void *C, int64_t ldc, int32_t epilogue, void *stream);
 
 /* Feature-major copy of the v part of a fused qkv buffer, the layout the
  * block's attention reads its values in:

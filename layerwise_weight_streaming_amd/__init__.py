@@ -140,6 +140,14 @@ _SIGS = {
     "dlo_op_adaln_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_void_p]),
+    "dlo_op_quantize_rows_mxfp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "dlo_op_gemm_mxfp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_void_p]),
     "dlo_op_quantize_rows_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                                 ctypes.c_void_p, ctypes.c_void_p]),
@@ -502,6 +510,15 @@ def op_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, stream):
 
 def op_adaln_fp8(W, w_scale, b, cond, rows, d, out, workspace, workspace_bytes, stream):
     _check(lib().dlo_op_adaln_fp8(W, w_scale, b, cond, rows, d, out, workspace, workspace_bytes, stream))
+
+
+def op_quantize_rows_mxfp8(x, ldx, M, K, codes, ldq, scales, lds, stream):
+    _check(lib().dlo_op_quantize_rows_mxfp8(x, ldx, M, K, codes, ldq, scales, lds, stream))
+
+
+def op_gemm_mxfp8(A, lda, a_scales, lds_a, B, ldb, b_scales, lds_b, M, N, K, bias, gate, C, ldc, epilogue, stream):
+    _check(lib().dlo_op_gemm_mxfp8(A, lda, a_scales, lds_a, B, ldb, b_scales, lds_b, M, N, K, bias, gate, C, ldc,
+                                   epilogue, stream))
 
 
 def op_quantize_rows_fp8(x, ldx, M, K, codes, ldq, scales, stream):

@@ -93,6 +93,14 @@ __device__ __forceinline__ void dl_load_so(i32x4 rsrc, uint32_t lds_base, int vo
                : "memory");
 }
 
+// 4 B per lane from rsrc + voff + soff into LDS at lds_base + 4 * lane
+__device__ __forceinline__ void dl_load_dw_so(i32x4 rsrc, uint32_t lds_base, int voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, %3 offen lds"
+               :
+               : "v"(voff), "s"(lds_base), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
 // s_waitcnt vmcnt(N) then s_barrier (N an immediate)
 template <int N>
 __device__ __forceinline__ void vmcnt_barrier() {

@@ -228,6 +228,7 @@ struct dlo_plan {
   int32_t max_d = 0;
   int32_t max_fp8_d = 0;   // widest per-tensor FP8 block (0: none)
   int32_t max_q_d = 0;     // widest INT8 or MXFP8 block (0: none)
+  int32_t max_mx_d = 0;    // widest MXFP8 block (0: none)
   uint64_t id = 0;
   mutable std::mutex mu;
   mutable std::vector<dlo_run *> detached;   // runs started without a handle
@@ -441,12 +442,20 @@ int64_t round_up64(int64_t T) { return (T + 63) / 64 * 64; }
 // weights (12 f^2 bf16), an INT8 or MXFP8 block's five (18 q^2 bf16)
 int64_t dequant_bytes(int64_t f, int64_t q) { return std::max(24 * f * f, 36 * q * q); }
 
-int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d) {
-  const int64_t d = max_d, f = fp8_d;
-  // quantised blocks: their dequantised weights; FP8 blocks also the E4M3 codes
-  // [T, 4f] and row scales [T] of a linear's input in the W8A8 form
+// bytes of a W8A8 linear input's scales: fp32 per row (FP8), or E8M0 per 32
+// elements block-major [4 mx / 32, T64] (MXFP8)
+int64_t act_scale_bytes(int64_t T, int64_t f, int64_t mx) {
+  return std::max(f > 0 ? 4 * T : 0, mx * round_up64(T) / 8);
+}
+
+int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, int32_t mx_d) {
+  const int64_t d = max_d, f = fp8_d, mx = mx_d;
+  // quantised blocks: their dequantised weights; FP8 and MXFP8 blocks also the
+  // E4M3 codes [T, 4d] and the scales of a linear's input in the W8A8 form
   const int64_t dq = align_up(dequant_bytes(f, q_d), DLO_ALIGN);
-  const int64_t w8a8 = f > 0 ? align_up(4 * T * f, DLO_ALIGN) + align_up(4 * T, DLO_ALIGN) : 0;
+  const int64_t w8a8 = (f > 0 || mx > 0) ? align_up(4 * T * std::max(f, mx), DLO_ALIGN) +
+                                             align_up(act_scale_bytes(T, f, mx), DLO_ALIGN)
+                                       : 0;
   return align_up(4 * d, DLO_ALIGN) + align_up(24 * d, DLO_ALIGN) + align_up(2 * T * d, DLO_ALIGN) +
          align_up(8 * round_up64(T) * d, DLO_ALIGN) + dq + w8a8;
 }
@@ -675,6 +684,7 @@ int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_pl
     pl->max_d = std::max(pl->max_d, bp.d);
     if (bp.kind == KIND_DIT_FP8) pl->max_fp8_d = std::max(pl->max_fp8_d, bp.d);
     if (bp.kind == KIND_DIT_INT8 || bp.kind == KIND_DIT_MX) pl->max_q_d = std::max(pl->max_q_d, bp.d);
+    if (bp.kind == KIND_DIT_MX) pl->max_mx_d = std::max(pl->max_mx_d, bp.d);
   }
   pl->id = g_plan_ids++;
   *out = pl;
@@ -731,7 +741,7 @@ int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens) {
     return -1;
   }
   g_err.clear();
-  return workspace_bytes_for(plan->max_d, tokens, plan->max_fp8_d, plan->max_q_d);
+  return workspace_bytes_for(plan->max_d, tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d);
 }
 
 int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, int64_t cap,
@@ -1055,7 +1065,7 @@ struct Workspace {
   uint8_t *act_codes;
 };
 
-Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d) {
+Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, int32_t mx_d) {
   char *p = static_cast<char *>(ws);
   Workspace w;
   w.silu_c = reinterpret_cast<float *>(p);
@@ -1069,8 +1079,8 @@ Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d) 
   w.dq = reinterpret_cast<uint16_t *>(p);   // a quantised block's weights, dequantised to bf16
   p += align_up(dequant_bytes(fp8_d, q_d), DLO_ALIGN);
   w.act_codes = reinterpret_cast<uint8_t *>(p);  // W8A8: a linear input's E4M3 codes [T, <= 4d]
-  p += fp8_d > 0 ? align_up(4 * T * fp8_d, DLO_ALIGN) : 0;
-  w.act_scale = reinterpret_cast<float *>(p);    // ... and its per-row scales [T]
+  p += (fp8_d > 0 || mx_d > 0) ? align_up(4 * T * std::max(fp8_d, mx_d), DLO_ALIGN) : 0;
+  w.act_scale = reinterpret_cast<float *>(p);    // ... and its scales (fp32 per row, or E8M0 block-major)
   return w;
 }
 
@@ -1086,14 +1096,15 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   const int d = bp.d, H = bp.heads, dh = d / H, T = a->tokens;
   auto P = [&](int lp) { return base + bp.logical_byte(lp); };
   auto F = [&](int lp) { return reinterpret_cast<const float *>(P(lp)); };
-  const bool fp8 = bp.kind == KIND_DIT_FP8;
-  const bool w8a8 = fp8 && (a->flags & DLO_FP8_COMPUTE);
+  const bool fp8 = bp.kind == KIND_DIT_FP8, mx = bp.kind == KIND_DIT_MX;
+  const bool w8a8 = (fp8 || mx) && (a->flags & DLO_FP8_COMPUTE);
   hipError_t e;
   // bf16 weights: in the slot, or (FP8 block) dequantised into the workspace;
   // FP8 codes and scales: in the slot
   const uint16_t *Wt[5] = {};
   const uint8_t *W8[5] = {};
   const float *S8[5] = {};
+  const uint8_t *SM[5] = {};   // MXFP8: E8M0 scales, block-major [in / 32, out]
   if (fp8) {
     uint16_t *dst = w.dq;
     for (int i = 0; i < 5; ++i) {
@@ -1112,6 +1123,9 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
     for (int i = 0; i < 5; ++i) {
       const int64_t rows = kWeightRows[i] * d, cols = kWeightCols[i] * d;
       const char *sc = base + bp.param_byte(kFp8Scale[i]);
+      W8[i] = reinterpret_cast<const uint8_t *>(P(kWeightP[i]));
+      SM[i] = reinterpret_cast<const uint8_t *>(sc);
+      if (w8a8 && i > 0) continue;   // W8A8 MXFP8: only the adaLN weight runs in bf16
       e = bp.kind == KIND_DIT_INT8
               ? dlo::launch_dequant_int8(reinterpret_cast<const int8_t *>(P(kWeightP[i])), rows, cols,
                                          reinterpret_cast<const float *>(sc), dst, s)
@@ -1137,16 +1151,23 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   uint16_t *u = w.big;
   uint8_t *q8 = w.act_codes;
   float *qs = w.act_scale;
+  uint8_t *mxs = reinterpret_cast<uint8_t *>(w.act_scale);   // MXFP8: [K / 32, T64] block-major
+  const int64_t T64 = round_up64(T);
   // a linear: A [T, K] bf16 (row stride K) times weight i's rows n0 .. n0 + N - 1
   auto linear = [&](const uint16_t *A, int K, int i, int64_t n0, int N, const float *bias,
                     const float *gate, void *C, int64_t ldc, int epi) {
+    if (w8a8 && mx)
+      return dlo::launch_gemm_mxfp8(q8, K, mxs, T64, W8[i] + n0 * K, K, SM[i] + n0, kWeightRows[i] * d, T, N,
+                                    K, bias, gate, C, ldc, epi, s);
     if (w8a8)
       return dlo::launch_gemm_fp8(q8, K, qs, W8[i] + n0 * K, K, S8[i], T, N, K, bias, gate, C, ldc, epi, s);
     return dlo::launch_gemm(A, K, Wt[i] + n0 * K, K, T, N, K, bias, gate, C, ldc, epi, s);
   };
   // W8A8: the per-row E4M3 codes of a linear's input; otherwise nothing
   auto quant = [&](const uint16_t *A, int K) {
-    return w8a8 ? dlo::launch_quant_rows_fp8(A, K, T, K, q8, K, qs, s) : hipSuccess;
+    if (!w8a8) return hipSuccess;
+    return mx ? dlo::launch_quant_rows_mx(A, K, T, K, q8, K, mxs, T64, s)
+              : dlo::launch_quant_rows_fp8(A, K, T, K, q8, K, qs, s);
   };
 #define DLO_STEP(call, j)                                                   \
   if ((e = (call)) != hipSuccess) return e;                                 \
@@ -1212,7 +1233,7 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
     return fail(DLO_E_UNSUPPORTED, "x_row_stride too large for 32-bit tile offsets");
   if (((int64_t)a->tokens + 64) * 3 * plan->max_d * 2 >= ((int64_t)1 << 31))
     return fail(DLO_E_UNSUPPORTED, "tokens x 3 d too large for 32-bit buffer offsets");
-  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d);
+  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d);
   if (a->workspace_bytes < need)
     return fail(DLO_E_WORKSPACE, "workspace %lld < %lld bytes", (long long)a->workspace_bytes, (long long)need);
   if (!resident) {
@@ -1290,7 +1311,7 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
     r.t_copy_begin = r.t_copy_end = r.t_compute_begin = r.t_compute_end = -1.f;
   }
 
-  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d);
+  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d);
   hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
   auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
   hipError_t e = hipSuccess;
@@ -1556,6 +1577,41 @@ int dlo_op_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint
   if (n < 0 || n % 16 || (uintptr_t)codes % 16 || (uintptr_t)out % 32)
     return fail(DLO_E_UNSUPPORTED, "dequant: n %% 16 == 0, codes 16-B and out 32-B aligned required");
   int rc = check_hip(dlo::launch_dequant_fp8(codes, n, scale, out, (hipStream_t)stream), "dequant_fp8");
+  return rc ? rc : ok();
+}
+
+int dlo_op_quantize_rows_mxfp8(const uint16_t *x, int64_t ldx, int32_t M, int32_t K, uint8_t *codes,
+                               int64_t ldq, uint8_t *scales, int64_t lds, void *stream) {
+  if (!x || !codes || !scales) return fail(DLO_E_ARG, "NULL argument");
+  if (M < 1 || K < 32 || K % 32 || ldx < K || ldq < K || ldx % 8 || ldq % 8 || lds < M)
+    return fail(DLO_E_UNSUPPORTED, "quantize_rows_mxfp8: K %% 32 == 0, ldx and ldq >= K and multiples of 8, lds >= M");
+  if ((uintptr_t)x % 16 || (uintptr_t)codes % 8)
+    return fail(DLO_E_UNSUPPORTED, "quantize_rows_mxfp8: x 16-B and codes 8-B aligned");
+  int rc = check_hip(dlo::launch_quant_rows_mx(x, ldx, M, K, codes, ldq, scales, lds, (hipStream_t)stream),
+                     "quantize_rows_mxfp8");
+  return rc ? rc : ok();
+}
+
+int dlo_op_gemm_mxfp8(const uint8_t *A, int64_t lda, const uint8_t *a_scales, int64_t lds_a, const uint8_t *B,
+                      int64_t ldb, const uint8_t *b_scales, int64_t lds_b, int32_t M, int32_t N, int32_t K,
+                      const float *bias, const float *gate, void *C, int64_t ldc, int32_t epilogue, void *stream) {
+  if (!A || !a_scales || !B || !b_scales || !bias || !C) return fail(DLO_E_ARG, "NULL argument");
+  if (epilogue < 0 || epilogue > 3) return fail(DLO_E_ARG, "unknown epilogue %d", epilogue);
+  if (epilogue == DLO_EPI_GATED_RESIDUAL && !gate) return fail(DLO_E_ARG, "gate is required");
+  const bool trans = epilogue == DLO_EPI_BIAS_T;
+  if (M < 1 || N < 256 || N % 256 || K < 64 || K % 64 || lda < K || ldb < K ||
+      ldc < (trans ? round_up64(M) : N) || lda % 16 || ldb % 16 || (trans && ldc % 8) || lds_a < M ||
+      lds_a % 4 || lds_b < N || lds_b % 4)
+    return fail(DLO_E_UNSUPPORTED, "gemm_mxfp8: N %% 256 == 0, K %% 64 == 0, ld >= extent, lda and ldb "
+                                   "multiples of 16, lds_a >= M and lds_b >= N multiples of 4");
+  if ((int64_t)256 * lda >= (int64_t)1 << 31 || (int64_t)256 * ldb >= (int64_t)1 << 31 ||
+      (int64_t)256 * ldc * 4 >= (int64_t)1 << 31 || (int64_t)(K / 32) * std::max(lds_a, lds_b) >= (int64_t)1 << 31)
+    return fail(DLO_E_UNSUPPORTED, "gemm_mxfp8: leading dimension too large for 32-bit offsets");
+  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 16 || (gate && (uintptr_t)gate % 16) ||
+      (uintptr_t)A % 16 || (uintptr_t)B % 16 || (uintptr_t)a_scales % 4 || (uintptr_t)b_scales % 4)
+    return fail(DLO_E_UNSUPPORTED, "gemm_mxfp8: A, B, C, bias and gate 16-B, scales 4-B aligned, ldc %% 4 == 0");
+  int rc = check_hip(dlo::launch_gemm_mxfp8(A, lda, a_scales, lds_a, B, ldb, b_scales, lds_b, M, N, K, bias, gate,
+                                            C, ldc, epilogue, (hipStream_t)stream), "gemm_mxfp8");
   return rc ? rc : ok();
 }
 

@@ -195,23 +195,33 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
 // 128 g .. +127 of every k-tile; the 4-deep ring gives each load six phases
 // to land.
 //
-// F8: A and B hold OCP E4M3 codes (1 byte per element) instead of bf16.  A
-// stage row is still 64 bytes, now 64 elements: one v_mfma_f32_32x32x64_f8f6f4
-// k-step per stage, whose operand (32 consecutive k-bytes of a row per lane)
-// is two 16-B chunks of the swizzled row; each phase issues 8 of these MFMAs,
-// the same MFMA time as 16 bf16 ones, over twice the K.  The fp32 result is
-// scaled by a_scale[row] * *b_scale before the epilogue.
-template <int EPI, bool F8>
+// Q = 1 (FP8) and Q = 2 (MXFP8): A and B hold OCP E4M3 codes (1 byte per
+// element) instead of bf16.  A stage row is still 64 bytes, now 64 elements:
+// one v_mfma_scale_f32_32x32x64_f8f6f4 k-step per stage; each phase issues 8
+// of these MFMAs, the same MFMA time as 16 bf16 ones, over twice the K.  The
+// instruction's k-blocks of 32 are bytes 0-15 of both lane halves and bytes
+// 16-31 of both (measured), so lane half h takes chunks h and 2 + h of the
+// swizzled row: k 16h .. 16h + 15 of each 32-block.  Q = 1: the fp32 result is
+// scaled by a_scale[row] * *b_scale before the epilogue.  Q = 2: a_scale and
+// b_scale are E8M0 bytes, block-major ([K / 32][lds_a] and [K / 32][lds_b],
+// rows from 0 and from n0 respectively); each stage's two 32-blocks of scales
+// for the tile's 256 A rows and 256 B rows (1 KB) travel with the tiles, by
+// DMA into LDS, and the instruction applies them (lane (row m, half h) holds
+// block h's scale of its row).
+template <int EPI, int Q>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     const void *__restrict__ A, int64_t lda, const void *__restrict__ B, int64_t ldb,
     int M, int N, int K, const float *__restrict__ bias, const float *__restrict__ gate,
-    void *__restrict__ Cv, int64_t ldc, const float *__restrict__ a_scale,
-    const float *__restrict__ b_scale) {
+    void *__restrict__ Cv, int64_t ldc, const void *__restrict__ a_scale,
+    const void *__restrict__ b_scale, int64_t lds_a, int64_t lds_b) {
+  constexpr bool F8 = Q > 0, MX = Q == 2;
   constexpr int ES = F8 ? 1 : 2;             // bytes per element
   constexpr int KSTAGE = 64 / ES;            // elements of k per stage
   constexpr int BN = 256, WN = 4, NJ = 2, STAGES = 4;
   constexpr int B_TILE = BN * DL_BK;
-  constexpr int STAGE = DL_TILE + B_TILE;
+  constexpr int SC_STAGE = MX ? 1024 : 0;    // MXFP8: two copies of 1 KB of scale bytes
+  constexpr int STAGE = DL_TILE + B_TILE + SC_STAGE;
+  constexpr int LPS = MX ? 5 : 4;            // loads per wave per stage
   constexpr int C_LD = BN + 8, X_LD = BN + 4;
   constexpr int RING = STAGES * STAGE;
   constexpr int CSTAGE = EPI == EPI_GATED_RESIDUAL ? 128 * X_LD * 2 : GBM * C_LD;
@@ -238,6 +248,15 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
                                (uint32_t)(a_rows * lda * ES));
   const i32x4 b_rsrc = dl_rsrc(static_cast<const char *>(B) + (int64_t)n0 * ldb * ES,
                                (uint32_t)(BN * ldb * ES));
+  // MXFP8: wave wq of each group loads one 256-B scale segment per stage into
+  // its group's copy: A block 2kt, A block 2kt + 1, B block 2kt, B block 2kt + 1
+  // (bytes past the scale arrays read 0; A rows past lds_a read the next block
+  // row's finite scales, multiplied by zero codes)
+  const int sc_h = wq & 1;
+  const i32x4 sc_rsrc = dl_rsrc(wq < 2 ? a_scale : b_scale,
+                                (uint32_t)((int64_t)(K / 32) * (wq < 2 ? lds_a : lds_b)));
+  const int sc_voff = (wq < 2 ? m0 : n0) + 4 * lane;
+  const int64_t sc_ld = wq < 2 ? lds_a : lds_b;
 
   // 16-row load blocks 8 g + 2 wq + i (i < 2) of A and of B
   int a_voff[2], b_voff[2];
@@ -263,6 +282,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
       dl_load_so(b_rsrc,
                  __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(DL_TILE * 2 + (grp * 8 + wq * 2 + i) * 1024)),
                  b_voff[i], koff);
+    if constexpr (MX)
+      dl_load_dw_so(sc_rsrc,
+                    __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((DL_TILE + B_TILE) * 2 + grp * 1024 + wq * 256)),
+                    sc_voff, __builtin_amdgcn_readfirstlane((uint32_t)((2 * kt + sc_h) * sc_ld)));
   };
 
   f32x16 acc[4][NJ];
@@ -283,6 +306,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   };
   struct Frags8 {
     u32x4 a[4][2], b[NJ][2];
+    int sa[4], sb[NJ];   // MXFP8: E8M0 scale bytes of the lane's rows, block fk
   };
   using Frags = std::conditional_t<F8, Frags8, FragsB>;
   // fragment byte offsets inside a stage: the XOR swizzle depends on row bits
@@ -294,13 +318,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     a_lane[kk] = dl_lds_off(wm * 128 + frow, kk * 2 + fk) * 2;
     b_lane[kk] = (DL_TILE + dl_lds_off(wn * 64 + frow, kk * 2 + fk)) * 2;
   }
-  // F8 operand of lane (row, fk): k-bytes 32 fk .. 32 fk + 31 = chunks 2 fk, 2 fk + 1
+  // F8 operand of lane (row, fk): bytes 0-15 = chunk fk (k 16 fk ..), bytes 16-31 =
+  // chunk 2 + fk (k 32 + 16 fk ..), so each instruction k-block of 32 is one
+  // 32-element block of the rows
   int a8_lane[2], b8_lane[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    a8_lane[h] = dl_lds_off(wm * 128 + frow, 2 * fk + h) * 2;
-    b8_lane[h] = (DL_TILE + dl_lds_off(wn * 64 + frow, 2 * fk + h)) * 2;
+    a8_lane[h] = dl_lds_off(wm * 128 + frow, 2 * h + fk) * 2;
+    b8_lane[h] = (DL_TILE + dl_lds_off(wn * 64 + frow, 2 * h + fk)) * 2;
   }
+  // MXFP8 scale bytes in a stage: this group's copy, A segment fk then B segment fk
+  const int sa_lane = (DL_TILE + B_TILE) * 2 + grp * 1024 + fk * 256 + wm * 128 + frow;
+  const int sb_lane = (DL_TILE + B_TILE) * 2 + grp * 1024 + 512 + fk * 256 + wn * 64 + frow;
   auto read_tile = [&](auto st_c, Frags &f) {
     constexpr int S = decltype(st_c)::value;
     const char *base = lds_bytes + S * STAGE * 2;
@@ -311,6 +340,12 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
         for (int i = 0; i < 4; ++i) f.a[i][h] = *reinterpret_cast<const u32x4 *>(base + a8_lane[h] + i * 32 * 64);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) f.b[j][h] = *reinterpret_cast<const u32x4 *>(base + b8_lane[h] + j * 32 * 64);
+      }
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.sa[i] = *reinterpret_cast<const uint8_t *>(base + sa_lane + i * 32);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) f.sb[j] = *reinterpret_cast<const uint8_t *>(base + sb_lane + j * 32);
       }
     } else {
 #pragma unroll
@@ -331,6 +366,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
         asm volatile("" ::"v"(f.a[0][h]), "v"(f.a[1][h]), "v"(f.a[2][h]), "v"(f.a[3][h]));
         asm volatile("" ::"v"(f.b[0][h]), "v"(f.b[1][h]));
       }
+      if constexpr (MX) {
+        asm volatile("" ::"v"(f.sa[0]), "v"(f.sa[1]), "v"(f.sa[2]), "v"(f.sa[3]));
+        asm volatile("" ::"v"(f.sb[0]), "v"(f.sb[1]));
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -350,10 +389,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
           const i32x8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                             (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-          // format 0 (E4M3) for both operands, no block scales
-          acc[i][j] = EPI == EPI_BIAS_T
-                          ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, 0, 0, 0)
-                          : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
+          // format 0 (E4M3) for both operands; MXFP8: each operand's block scale
+          // (byte 0 of the scale register), else none
+          if constexpr (MX)
+            acc[i][j] = EPI == EPI_BIAS_T
+                            ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, f.sa[i],
+                                                                              0, f.sb[j])
+                            : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, f.sb[j],
+                                                                              0, f.sa[i]);
+          else
+            acc[i][j] = EPI == EPI_BIAS_T
+                            ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, 0, 0, 0)
+                            : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
         }
     } else {
 #pragma unroll
@@ -377,11 +424,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     younger = min(younger, nk - 1 - s);
     __builtin_amdgcn_sched_barrier(0);
     if (younger >= 3)
-      vmcnt_barrier<12>();
+      vmcnt_barrier<3 * LPS>();
     else if (younger == 2)
-      vmcnt_barrier<8>();
+      vmcnt_barrier<2 * LPS>();
     else if (younger == 1)
-      vmcnt_barrier<4>();
+      vmcnt_barrier<LPS>();
     else
       vmcnt_barrier<0>();
     __builtin_amdgcn_sched_barrier(0);
@@ -416,22 +463,23 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   }
   if (grp == 0) phase_barrier(2 * nk);
 
-  if constexpr (F8) {
+  if constexpr (Q == 1) {
     // A's per-row scale times B's scale (rows past M read no scale)
-    const float sb = *b_scale;
+    const float *a_sc = static_cast<const float *>(a_scale);
+    const float sb = *static_cast<const float *>(b_scale);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (EPI == EPI_BIAS_T) {  // lane holds rows 8 (r / 4) + 4 fk + r % 4 of row block i
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fk * 4 + (r & 3);
-          const float f = (row < M ? a_scale[row] : 0.f) * sb;
+          const float f = (row < M ? a_sc[row] : 0.f) * sb;
 #pragma unroll
           for (int j = 0; j < NJ; ++j) acc[i][j][r] *= f;
         }
       } else {  // lane holds row frow of row block i
         const int row = m0 + wm * 128 + i * 32 + frow;
-        const float f = (row < M ? a_scale[row] : 0.f) * sb;
+        const float f = (row < M ? a_sc[row] : 0.f) * sb;
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -442,16 +490,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   gemm_epilogue<EPI, BN, WN>(acc, smem, tid, wm, wn, lane, m0, n0, M, bias, gate, Cv, ldc);
 }
 
-template <bool F8>
+template <int Q>
 hipError_t launch_gemm_t(const void *A, int64_t lda, const void *B, int64_t ldb, int M, int N, int K,
                          const float *bias, const float *gate, void *C, int64_t ldc, int epilogue,
-                         const float *a_scale, const float *b_scale, hipStream_t s) {
+                         const void *a_scale, const void *b_scale, int64_t lds_a, int64_t lds_b, hipStream_t s) {
   const int tiles = ((M + GBM - 1) / GBM) * (N / 256);
   switch (epilogue) {
 #define DLO_GEMM_CASE(E)                                                                            \
   case E:                                                                                           \
-    hipLaunchKernelGGL((gemm_pp_kernel<E, F8>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb, M, N, K, \
-                       bias, gate, C, ldc, a_scale, b_scale);                                       \
+    hipLaunchKernelGGL((gemm_pp_kernel<E, Q>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb, M, N, K, \
+                       bias, gate, C, ldc, a_scale, b_scale, lds_a, lds_b);                        \
     break;
     DLO_GEMM_CASE(EPI_BIAS)
     DLO_GEMM_CASE(EPI_BIAS_GELU)
@@ -469,13 +517,22 @@ hipError_t launch_gemm_t(const void *A, int64_t lda, const void *B, int64_t ldb,
 hipError_t launch_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int M,
                        int N, int K, const float *bias, const float *gate, void *C, int64_t ldc,
                        int epilogue, hipStream_t s) {
-  return launch_gemm_t<false>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, nullptr, nullptr, s);
+  return launch_gemm_t<0>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, nullptr, nullptr, 0, 0, s);
 }
 
 hipError_t launch_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B,
                            int64_t ldb, const float *b_scale, int M, int N, int K, const float *bias,
                            const float *gate, void *C, int64_t ldc, int epilogue, hipStream_t s) {
-  return launch_gemm_t<true>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, a_scale, b_scale, s);
+  return launch_gemm_t<1>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, a_scale, b_scale, 0, 0, s);
+}
+
+hipError_t launch_gemm_mxfp8(const uint8_t *A, int64_t lda, const uint8_t *a_scale, int64_t lds_a,
+                             const uint8_t *B, int64_t ldb, const uint8_t *b_scale, int64_t lds_b, int M, int N,
+                             int K, const float *bias, const float *gate, void *C, int64_t ldc, int epilogue,
+                             hipStream_t s) {
+  if (lds_a < M || lds_a % 4 || lds_b % 4 || K % 64) return hipErrorInvalidValue;
+  return launch_gemm_t<2>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, a_scale, b_scale, lds_a, lds_b,
+                          s);
 }
 
 }  // namespace dlo

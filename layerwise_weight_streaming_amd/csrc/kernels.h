@@ -38,6 +38,13 @@ hipError_t launch_v_transpose(const uint16_t *v, int64_t ldv, int T, int d, uint
 hipError_t launch_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B,
                            int64_t ldb, const float *b_scale, int M, int N, int K, const float *bias,
                            const float *gate, void *C, int64_t ldc, int epilogue, hipStream_t s);
+// MXFP8 GEMM: A [M, K] and B [N, K] E4M3 codes with E8M0 block scales block-major,
+// a_scale [K / 32][lds_a] (row m at column m), b_scale [K / 32][lds_b] (row n at
+// column n); lds_a >= M, lds_a and lds_b multiples of 4, K % 64 == 0
+hipError_t launch_gemm_mxfp8(const uint8_t *A, int64_t lda, const uint8_t *a_scale, int64_t lds_a,
+                             const uint8_t *B, int64_t ldb, const uint8_t *b_scale, int64_t lds_b, int M, int N,
+                             int K, const float *bias, const float *gate, void *C, int64_t ldc, int epilogue,
+                             hipStream_t s);
 
 // per-head softmax(q k^T / sqrt(dh)) v: q, k from a fused qkv buffer, v from
 // its feature-major copy vt (launch_v_transpose); dh in {64, 128}
@@ -60,6 +67,10 @@ hipError_t launch_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols
 // multiples of 8, x 16-B and q 8-B aligned
 hipError_t launch_quant_rows_fp8(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,
                                  float *scale, hipStream_t s);
+// per-row MXFP8 of a bf16 matrix [M, K]: codes [M, ldq], E8M0 scales block-major
+// [K / 32, lds] (rows M .. lds - 1: 127); K % 32 == 0, lds >= M
+hipError_t launch_quant_rows_mx(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,
+                               uint8_t *scale, int64_t lds, hipStream_t s);
 
 // *out = digest of the regions (base + offsets[i], lengths[i]); offsets multiples of 8
 hipError_t launch_digest(const void *base, const int64_t *offsets, const int64_t *lengths,

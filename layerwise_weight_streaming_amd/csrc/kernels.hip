@@ -322,6 +322,52 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t *__r
   }
 }
 
+// Per-row MXFP8 quantization of a bf16 activation matrix, the input side of a
+// W8A8 MXFP8 linear: each block of 32 consecutive elements of a row gets
+// X = floor(log2 amax) - 8 clamped to [-127, 127] (-127 for an all-zero block),
+// its E8M0 byte X + 127 written block-major (scale[b * lds + row]), and codes
+// e4m3(x * 2^-X) (the scaling is exact).  One 256-thread workgroup per row, four
+// lanes per block (8 elements each).  Rows M .. lds - 1 only get scale bytes
+// 127 (2^0), so a block-scaled product reading whole 4-row groups sees finite
+// scales there.
+__global__ __launch_bounds__(256) void quant_rows_mx_kernel(const uint16_t *__restrict__ x, int64_t ldx, int M,
+                                                            int K, uint8_t *__restrict__ q, int64_t ldq,
+                                                            uint8_t *__restrict__ scale, int64_t lds) {
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int nblk = K / 32;
+  if (row >= M) {
+    for (int b = tid; b < nblk; b += 256) scale[b * lds + row] = 127;
+    return;
+  }
+  const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + row * ldx);
+  uint2 *qr = reinterpret_cast<uint2 *>(q + row * ldq);
+  for (int c = tid; c < K / 8; c += 256) {   // 8 elements per thread; 4 consecutive threads = one block
+    const u32x4 v = xr[c];
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __uint_as_float(v[e] << 16);
+      f[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    // floor(log2 amax) from the exponent field (bf16 values: normal, subnormal or 0)
+    const int X = amax > 0.f ? max(-127, min(127, (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 8)) : -127;
+    const float p2 = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X, 127 - X in [8, 254]
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      w[h] = e4m3_code(f[4 * h] * p2) | (e4m3_code(f[4 * h + 1] * p2) << 8) |
+             (e4m3_code(f[4 * h + 2] * p2) << 16) | (e4m3_code(f[4 * h + 3] * p2) << 24);
+    qr[c] = make_uint2(w[0], w[1]);
+    if ((c & 3) == 0) scale[(int64_t)(c >> 2) * lds + row] = (uint8_t)(X + 127);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
@@ -360,6 +406,13 @@ hipError_t launch_quant_rows_fp8(const uint16_t *x, int64_t ldx, int M, int K, u
                                  float *scale, hipStream_t s) {
   if (M < 1 || K < 8 || K % 8 || ldx % 8 || ldq % 8) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3(M), dim3(256), 0, s, x, ldx, K, q, ldq, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_mx(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,
+                               uint8_t *scale, int64_t lds, hipStream_t s) {
+  if (M < 1 || K < 32 || K % 32 || ldx % 8 || ldq % 8 || lds < M) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_mx_kernel, dim3((unsigned)lds), dim3(256), 0, s, x, ldx, M, K, q, ldq, scale, lds);
   return hipGetLastError();
 }
 

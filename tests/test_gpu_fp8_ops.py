@@ -234,3 +234,151 @@ def test_gemm_fp8_rejects_unsupported_shapes():
         with pytest.raises(dlo.DLOError):
             dlo.op_gemm_fp8(a.data_ptr(), lda, s.data_ptr(), b.data_ptr(), 128, s.data_ptr(), M, N, K,
                             bias.data_ptr(), 0, c.data_ptr(), 256, epi, 0)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (W8A8 with E8M0 block scales applied by the matrix instruction)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,ldx_extra,lds_extra", [(7, 64, 0, 1), (300, 5120, 8, 20), (33, 20480, 0, 3),
+                                                     (1, 32, 0, 0), (129, 1056, 24, 63)])
+def test_quantize_rows_mxfp8_bit_exact(M, K, ldx_extra, lds_extra):
+    torch = require_gpu()
+    from oracle import quant
+    say("quantize rows mxfp8", M, K, ldx_extra, lds_extra)
+    x = _quant_inputs(M, K, M * 17 + K)
+    ldx, lds = K + ldx_extra, M + lds_extra
+    xp = np.full((M, ldx), 0x7F7F, np.uint16)
+    xp[:, :K] = x
+    dx = _dev(torch, xp.view(np.int16))
+    dq = torch.full((M, K), 0xA5, dtype=torch.uint8, device="cuda")
+    ds = torch.full((K // 32, lds), 0xEE, dtype=torch.uint8, device="cuda")
+    dlo.op_quantize_rows_mxfp8(dx.data_ptr(), ldx, M, K, dq.data_ptr(), K, ds.data_ptr(), lds,
+                               torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    q, s = dq.cpu().numpy(), ds.cpu().numpy()
+    codes, scales = quant.quantize_mxfp8(x)
+    assert np.array_equal(s[:, :M], scales.T)
+    assert np.all(s[:, M:] == 127)
+    bad = np.argwhere(q != codes)
+    assert bad.size == 0, (len(bad), bad[:5])
+
+
+def _mx_operand(seed, rows, K, std, lds):
+    """bf16 normals quantised by the oracle: codes [rows, K], scales block-major [K / 32, lds]
+    (padding rows 127, as the quantizer op leaves them)."""
+    from oracle import quant
+    codes, sc = quant.quantize_mxfp8(_bf16_rand(seed, (rows, K), std))
+    blk = np.full((K // 32, lds), 127, np.uint8)
+    blk[:, :rows] = sc.T
+    return codes, blk
+
+
+def _mx_ref(a_codes, a_blk, b_codes, b_blk, bias):
+    from oracle import quant
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    a = quant.dequantize_mxfp8(a_codes, a_blk[:, :M].T)
+    b = quant.dequantize_mxfp8(b_codes, b_blk[:, :N].T)
+    return of.linear(a, b, bias.astype(np.float64)), np.abs(a) @ np.abs(b).T
+
+
+@pytest.mark.parametrize("M,N,K,b_pad", [(300, 512, 128, 0), (64, 768, 256, 256), (1000, 256, 320, 0),
+                                         (1, 256, 64, 4), (129, 512, 64, 0)])
+@pytest.mark.parametrize("epi", [dlo.EPI_BIAS, dlo.EPI_BIAS_GELU, dlo.EPI_GATED_RESIDUAL, dlo.EPI_BIAS_T])
+def test_gemm_mxfp8_small(M, N, K, b_pad, epi):
+    """b_pad > 0: B's scales sit at a column offset inside a wider block-major array
+    (lds_b = N + 2 b_pad, base + b_pad), as a slice of the fused qkv weight does."""
+    torch = require_gpu()
+    say("gemm mxfp8", M, N, K, "epi", epi, "b_pad", b_pad)
+    lds_a = (M + 3) // 4 * 4
+    a_codes, a_blk = _mx_operand(M * 7 + N + K, M, K, 1.0, lds_a)
+    b_codes, b_blk = _mx_operand(M * 7 + N + K + 1, N, K, 0.05, N)
+    lds_b = N + 2 * b_pad
+    b_wide = np.full((K // 32, lds_b), 0xFF, np.uint8)      # NaN scales outside the slice
+    b_wide[:, b_pad:b_pad + N] = b_blk
+    bias = synth.normal_f32(3, 11, 1, 0, (N,), 0.0, 0.1)
+    gate = synth.normal_f32(4, 11, 2, 0, (N,), 0.0, 1.0)
+    ref, mag = _mx_ref(a_codes, a_blk, b_codes, b_blk, bias)
+    dA, dsa, dB, dsb = _dev(torch, a_codes), _dev(torch, a_blk), _dev(torch, b_codes), _dev(torch, b_wide)
+    db, dg = _dev(torch, bias), _dev(torch, gate)
+    s = torch.cuda.current_stream().cuda_stream
+
+    def run(C, ldc, e, g=0):
+        dlo.op_gemm_mxfp8(dA.data_ptr(), K, dsa.data_ptr(), lds_a, dB.data_ptr(), K, dsb.data_ptr() + b_pad, lds_b,
+                          M, N, K, db.data_ptr(), g, C.data_ptr(), ldc, e, s)
+        torch.cuda.synchronize()
+
+    if epi == dlo.EPI_GATED_RESIDUAL:
+        X0 = synth.normal_f32(5, 11, 3, 0, (M, N))
+        dX = _dev(torch, X0)
+        run(dX, N, epi, dg.data_ptr())
+        got = dX.cpu().numpy().astype(np.float64)
+        want = X0.astype(np.float64) + gate.astype(np.float64) * ref
+        bound = 2.0 ** -10 * np.abs(gate.astype(np.float64)) * mag + 2.0 ** -22 * (np.abs(want) + np.abs(X0))
+        bad = np.abs(got - want) > bound
+        assert not bad.any(), (int(bad.sum()), float(np.max(np.abs(got - want) / bound)))
+    elif epi == dlo.EPI_BIAS_T:
+        M64 = (M + 63) // 64 * 64
+        ldc = M64 + 8
+        dCt = torch.full((N, ldc), 0x7FC0, dtype=torch.int16, device="cuda")
+        run(dCt, ldc, epi)
+        dC = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+        run(dC, N, dlo.EPI_BIAS)
+        ct = dCt.cpu().numpy().view(np.uint16)
+        nbad, worst = _close_bf16(bf16_to_f64(ct[:, :M].T), ref)
+        assert nbad == 0, (nbad, worst)
+        assert np.all(ct[:, M:M64] == 0) and np.all(ct[:, M64:] == 0x7FC0)
+        assert np.array_equal(ct[:, :M].T, dC.cpu().numpy().view(np.uint16))
+    else:
+        dC = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+        run(dC, N, epi)
+        got = bf16_to_f64(dC.cpu().numpy().view(np.uint16))
+        want = of.gelu_erf(ref) if epi == dlo.EPI_BIAS_GELU else ref
+        nbad, worst = _close_bf16(got, want)
+        assert nbad == 0, (nbad, worst)
+
+
+def test_gemm_mxfp8_full_size_sampled():
+    """FFN-up product of the Super workload in MXFP8 (M=28800, N=20480, K=5120): codes over
+    the whole E4M3 range and block scales from 2^-17 to 2^3, sampled rows and columns."""
+    torch = require_gpu()
+    from oracle import quant
+    M, N, K = 28800, 20480, 5120
+    say("gemm mxfp8 full size", M, N, K)
+    A = _uniform_codes(31, (M, K))
+    B = _uniform_codes(32, (N, K))
+    rng = np.random.default_rng(33)
+    sa = rng.integers(110, 131, (K // 32, M)).astype(np.uint8)
+    sb = rng.integers(110, 131, (K // 32, N)).astype(np.uint8)
+    bias = synth.normal_f32(34, 11, 1, 0, (N,), 0.0, 0.02)
+    dA, dsa, dB, dsb, db = _dev(torch, A), _dev(torch, sa), _dev(torch, B), _dev(torch, sb), _dev(torch, bias)
+    dC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    dlo.op_gemm_mxfp8(dA.data_ptr(), K, dsa.data_ptr(), M, dB.data_ptr(), K, dsb.data_ptr(), N, M, N, K,
+                      db.data_ptr(), 0, dC.data_ptr(), N, dlo.EPI_BIAS, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rows = np.concatenate([rng.integers(0, M, 48), [0, M - 1, 28671, 28672]])
+    cols = np.concatenate([rng.integers(0, N, 48), [0, N - 1, 255, 256]])
+    C = dC[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16)[:, cols]
+    a = quant.dequantize_mxfp8(A[rows], sa[:, rows].T)
+    b = quant.dequantize_mxfp8(B[cols], sb[:, cols].T)
+    ref = of.linear(a, b, bias[cols].astype(np.float64))
+    nbad, worst = _close_bf16(bf16_to_f64(C), ref)
+    assert nbad == 0, (nbad, worst)
+
+
+def test_mxfp8_ops_reject_unsupported_shapes():
+    torch = require_gpu()
+    a = torch.zeros((64, 128), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((256, 128), dtype=torch.uint8, device="cuda")
+    s = torch.ones(4096, dtype=torch.uint8, device="cuda")
+    bias = torch.zeros(256, dtype=torch.float32, device="cuda")
+    c = torch.zeros((64, 256), dtype=torch.int16, device="cuda")
+    for M, N, K, lds_a, lds_b in [(64, 256, 96, 64, 256), (64, 256, 128, 62, 256), (64, 256, 128, 66, 256),
+                                  (64, 256, 128, 64, 254), (64, 200, 128, 64, 200)]:
+        with pytest.raises(dlo.DLOError):
+            dlo.op_gemm_mxfp8(a.data_ptr(), 128, s.data_ptr(), lds_a, b.data_ptr(), 128, s.data_ptr(), lds_b, M, N, K,
+                              bias.data_ptr(), 0, c.data_ptr(), 256, 0, 0)
+    x = torch.zeros((4, 64), dtype=torch.int16, device="cuda")
+    for M, K, lds in [(4, 48, 4), (4, 64, 3)]:
+        with pytest.raises(dlo.DLOError):
+            dlo.op_quantize_rows_mxfp8(x.data_ptr(), 64, M, K, a.data_ptr(), 64, s.data_ptr(), lds, 0)

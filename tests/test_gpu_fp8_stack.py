@@ -32,6 +32,7 @@ import synth
 import layerwise_weight_streaming_amd as dlo
 from oracle import forward as of
 from oracle import plan as op
+from oracle import quant
 from oracle import schedule as sc
 from tests.gpu_util import TOL, fp8_blocks, make_runner_params, rel_err, require_gpu, say
 
@@ -52,12 +53,22 @@ def _check_trace(tr, n, passes, regs):
         assert got["digest_pre"] == want and got["digest_post"] == want, e.step
 
 
-def test_w8a8_single_block_matches_the_w8a8_oracle():
-    """One FP8 block (d = 256, 4 heads, 64 tokens), one pass."""
+def _blocks(w, stack, form, which=None):
+    """The stack's blocks in the per-tensor FP8 form (libdlo's quantizer, checked equal to
+    the oracle's) or the MXFP8 form (the oracle's quantizer)."""
+    if form == "fp8":
+        return fp8_blocks(w, stack, which)
+    return [quant.quantize_block(ps, "mxfp8") if which is None or b in which else ps
+            for b, ps in enumerate(stack.blocks)]
+
+
+@pytest.mark.parametrize("form", ["fp8", "mxfp8"])
+def test_w8a8_single_block_matches_the_w8a8_oracle(form):
+    """One FP8 or MXFP8 block (d = 256, 4 heads, 64 tokens), one pass."""
     require_gpu()
     w = synth.WORKLOADS["tiny"]
     stack = synth.make_stack(w, 21, 1)
-    blocks = fp8_blocks(w, stack)
+    blocks = _blocks(w, stack, form)
     r = make_runner_params(w, blocks)
     r.set_inputs(stack.x, stack.c)
     r.forward(1, flags=dlo.FP8_COMPUTE, want_run=False)
@@ -69,22 +80,25 @@ def test_w8a8_single_block_matches_the_w8a8_oracle():
     ref16 = of.forward_stack(x0, stack.c, blocks, heads, 1)
     e_max = rel_err(x_gpu - x0, ref8 - x0)
     e8, e16 = _rms_rel(x_gpu - x0, ref8 - x0), _rms_rel(x_gpu - x0, ref16 - x0)
-    say(f"W8A8 block: update max {e_max:.3e}; rms vs W8A8 oracle {e8:.3e}, vs W8A16 oracle {e16:.3e}")
+    say(f"W8A8 {form} block: update max {e_max:.3e}; rms vs W8A8 oracle {e8:.3e}, vs W8A16 oracle {e16:.3e}")
     assert e8 <= 1e-2 and e_max <= 2 * TOL
     assert e8 < 0.25 * e16
 
 
-def test_w8a8_block_is_the_op_sequence():
+@pytest.mark.parametrize("form", ["fp8", "mxfp8"])
+def test_w8a8_block_is_the_op_sequence(form):
     """The streamed W8A8 block computes, bit for bit, what the C-ABI ops compute when
     called one by one in the block's order (each op is checked against the oracle in
-    test_gpu_fp8_ops.py and test_gpu_ops.py): adaLN on the E4M3 W_ada, LN1 +
-    modulate, per-row E4M3 of h, the q/k and V^T FP8 products, attention, E4M3 of a,
-    the gated out product, LN2 + modulate, E4M3 of h2, the fc1 product with GELU, E4M3
-    of u, the gated fc2 product."""
+    test_gpu_fp8_ops.py, test_gpu_quant_weights.py and test_gpu_ops.py): adaLN (FP8:
+    on the E4M3 W_ada; MXFP8: on its dequantised bf16 copy), LN1 + modulate, the input
+    quantisation of h (per-row E4M3, or MXFP8 blocks), the q/k and V^T products (the
+    v part's MXFP8 scales a column slice of the fused weight's), attention, the input
+    quantisation of a, the gated out product, LN2 + modulate, that of h2, the fc1
+    product with GELU, that of u, the gated fc2 product."""
     torch = require_gpu()
     w = synth.WORKLOADS["tiny"]
     stack = synth.make_stack(w, 23, 1)
-    blocks = fp8_blocks(w, stack)
+    blocks = _blocks(w, stack, form)
     r = make_runner_params(w, blocks)
     r.set_inputs(stack.x, stack.c)
     r.forward(1, flags=dlo.FP8_COMPUTE, want_run=False)
@@ -100,12 +114,21 @@ def test_w8a8_block_is_the_op_sequence():
     c = torch.from_numpy(np.ascontiguousarray(stack.c, dtype=np.float32)).cuda()
     mod = torch.empty(6 * d, dtype=torch.float32, device="cuda")
     ws = torch.empty(4 * d, dtype=torch.uint8, device="cuda")
-    dlo.op_adaln_fp8(ptr("adaln.weight"), ptr("adaln.weight_scale"), ptr("adaln.bias"), c.data_ptr(), 6 * d, d,
-                     mod.data_ptr(), ws.data_ptr(), ws.numel(), s)
+    if form == "fp8":
+        dlo.op_adaln_fp8(ptr("adaln.weight"), ptr("adaln.weight_scale"), ptr("adaln.bias"), c.data_ptr(), 6 * d, d,
+                         mod.data_ptr(), ws.data_ptr(), ws.numel(), s)
+    else:
+        w_ada = torch.empty(6 * d * d, dtype=torch.int16, device="cuda")
+        dlo.op_dequant_mxfp8(ptr("adaln.weight"), 6 * d, d, ptr("adaln.weight_scale"), w_ada.data_ptr(), s)
+        dlo.op_adaln(w_ada.data_ptr(), ptr("adaln.bias"), c.data_ptr(), 6 * d, d, mod.data_ptr(), ws.data_ptr(),
+                     ws.numel(), s)
     m = lambda i: mod.data_ptr() + 4 * i * d
     h = torch.empty((T, d), dtype=torch.int16, device="cuda")
     codes = torch.empty((T, 4 * d), dtype=torch.uint8, device="cuda")
     scales = torch.empty(T, dtype=torch.float32, device="cuda")
+    T64 = (T + 63) // 64 * 64
+    mx_scales = torch.empty((4 * d // 32) * T64, dtype=torch.uint8, device="cuda")
+    rows_of = {"attn.qkv.weight": 3 * d, "attn.out.weight": d, "mlp.fc1.weight": 4 * d, "mlp.fc2.weight": d}
     ldvt = dlo.v_t_stride(T)
     qk = torch.empty((T, 2 * d), dtype=torch.int16, device="cuda")
     vt = torch.empty((d, ldvt), dtype=torch.int16, device="cuda")
@@ -113,11 +136,18 @@ def test_w8a8_block_is_the_op_sequence():
     u = torch.empty((T, 4 * d), dtype=torch.int16, device="cuda")
 
     def quant(src, K):
-        dlo.op_quantize_rows_fp8(src.data_ptr(), K, T, K, codes.data_ptr(), K, scales.data_ptr(), s)
+        if form == "fp8":
+            dlo.op_quantize_rows_fp8(src.data_ptr(), K, T, K, codes.data_ptr(), K, scales.data_ptr(), s)
+        else:
+            dlo.op_quantize_rows_mxfp8(src.data_ptr(), K, T, K, codes.data_ptr(), K, mx_scales.data_ptr(), T64, s)
 
     def lin(wname, K, row0, N, bias, gate, C, ldc, epi):
-        dlo.op_gemm_fp8(codes.data_ptr(), K, scales.data_ptr(), ptr(wname) + row0 * K, K, ptr(wname + "_scale"),
-                        T, N, K, bias, gate, C, ldc, epi, s)
+        if form == "fp8":
+            dlo.op_gemm_fp8(codes.data_ptr(), K, scales.data_ptr(), ptr(wname) + row0 * K, K,
+                            ptr(wname + "_scale"), T, N, K, bias, gate, C, ldc, epi, s)
+        else:
+            dlo.op_gemm_mxfp8(codes.data_ptr(), K, mx_scales.data_ptr(), T64, ptr(wname) + row0 * K, K,
+                              ptr(wname + "_scale") + row0, rows_of[wname], T, N, K, bias, gate, C, ldc, epi, s)
 
     dlo.op_ln_modulate(x.data_ptr(), D, T, d, ptr("norm1.weight"), ptr("norm1.bias"), ptr("norm1.eps"),
                        m(0), m(1), h.data_ptr(), s)
@@ -139,20 +169,21 @@ def test_w8a8_block_is_the_op_sequence():
     assert np.array_equal(x_ops.view(np.uint32), x_fwd.view(np.uint32))
 
 
+@pytest.mark.parametrize("form", ["fp8", "mxfp8"])
 @pytest.mark.parametrize("name,n_blocks,tokens,which", [
-    ("tiny", None, None, None),                 # every block FP8, 2 passes, odd count
-    ("8blk", None, None, {0, 2, 3, 5}),         # FP8 and bf16 blocks mixed
+    ("tiny", None, None, None),                 # every block quantised, 2 passes, odd count
+    ("8blk", None, None, {0, 2, 3, 5}),         # quantised and bf16 blocks mixed
     ("irregular", 3, 256, None),                # widths 2048/3072/4096, k = 4
 ])
-def test_w8a8_stack_streamed(name, n_blocks, tokens, which):
+def test_w8a8_stack_streamed(form, name, n_blocks, tokens, which):
     require_gpu()
     w = synth.WORKLOADS[name]
     if tokens is not None:
         w = w.with_(tokens=tokens)
     n = w.n_blocks if n_blocks is None else n_blocks
-    say(f"W8A8 stack {name} n={n} T={w.tokens} which={which}")
+    say(f"W8A8 {form} stack {name} n={n} T={w.tokens} which={which}")
     stack = synth.make_stack(w, 21, n)
-    blocks = fp8_blocks(w, stack, which)
+    blocks = _blocks(w, stack, form, which)
     r = make_runner_params(w, blocks)
     r.set_inputs(stack.x, stack.c)
     run = r.forward(w.passes, flags=dlo.TRACE_DIGEST | dlo.FP8_COMPUTE)
