@@ -226,3 +226,30 @@ def test_w8a8_leaves_bf16_blocks_alone():
     r.forward(w.passes, flags=dlo.FP8_COMPUTE, want_run=False)
     assert np.array_equal(r.x_host().view(np.uint32), a.view(np.uint32))
     r.close()
+
+
+@pytest.mark.parametrize("form", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("tokens", [77, 200])
+def test_w8a8_ragged_token_counts(form, tokens):
+    """Token counts off the 64-row grid: the quantizers' rows, the V^T padding and the
+    GEMMs' partial row tiles in the W8A8 forward; streamed == resident, and the update
+    within the stacks' gross-error bound of the W8A8 oracle."""
+    require_gpu()
+    w = synth.WORKLOADS["tiny"].with_(tokens=tokens)
+    say(f"W8A8 {form} ragged T={tokens}")
+    stack = synth.make_stack(w, 25)
+    blocks = _blocks(w, stack, form)
+    r = make_runner_params(w, blocks)
+    r.set_inputs(stack.x, stack.c)
+    r.forward(w.passes, flags=dlo.FP8_COMPUTE, want_run=False)
+    x_gpu = r.x_host()
+    r.set_inputs(stack.x, stack.c)
+    r.forward(w.passes, flags=dlo.FP8_COMPUTE, resident=True, want_run=False)
+    assert np.array_equal(r.x_host().view(np.uint32), x_gpu.view(np.uint32))
+    r.close()
+    assert np.isfinite(x_gpu).all()
+    x0 = np.asarray(stack.x, np.float64)
+    ref = of.forward_stack(x0, stack.c, blocks, [w.heads(b) for b in range(w.n_blocks)], w.passes, act_fp8=True)
+    e = _rms_rel(x_gpu - x0, ref - x0)
+    say(f"update rms rel err vs the W8A8 oracle {e:.3e}")
+    assert e < 0.1
