@@ -1,4 +1,5 @@
-// gfx950 GEMM of the DiT block linears: C = A B^T with bf16 operands, fp32
+// gfx950 GEMM of the DiT block linears: C = A B^T with bf16, FP8 (E4M3, per-row
+// and per-tensor scales) or MXFP8 (E4M3 with E8M0 block scales) operands, fp32
 // accumulation and fused epilogues (bias, bias + GELU, gated residual, and bias
 // with the result stored transposed).
 #include <hip/hip_runtime.h>
@@ -19,11 +20,12 @@ namespace {
 constexpr int GBM = 256;
 
 // ---------------------------------------------------------------------------
-// GEMM: C[M, N] = A[M, K] B[N, K]^T, bf16 in, fp32 accumulate (direct-to-LDS).
-// Workgroup tile 256 x 256 x 32 with 8 waves of 128 x 64 (MFMA 32x32 tiles).
-// Operand tiles travel HBM/L2 -> LDS with buffer_load ... lds (no register
-// staging) into a ring of 4 LDS stages.  One LDS stage = A and B tiles of 256
-// rows x 64 B; a row holds 4 chunks of 16 B whose order is XOR-swizzled
+// GEMM: C[M, N] = A[M, K] B[N, K]^T, fp32 accumulate (direct-to-LDS).
+// Workgroup tile 256 x 256 x (64 bytes of K: 32 bf16 or 64 E4M3 elements) with
+// 8 waves of 128 x 64 (MFMA 32x32 tiles).  Operand tiles travel HBM/L2 -> LDS
+// with buffer_load ... lds (no register staging) into a ring of 4 LDS stages.
+// One LDS stage = A and B tiles of 256 rows x 64 B (plus, for MXFP8, their
+// scale bytes); a row holds 4 chunks of 16 B whose order is XOR-swizzled
 // (dl_swz) so that the MFMA operand reads are free of bank conflicts.  A load
 // instruction fills 1 KB of LDS: 64 lanes x 16 B at M0 + 16 * lane, i.e. 16
 // rows.  The tile order is XCD-aware and grouped by 4 row tiles: each XCD's
