@@ -47,6 +47,8 @@ def kernel_work(name, d, T, form="bf16", w8a8=False):
         if form == "mxfp8":  # all five weights, one E8M0 per 32 codes
             return (18 * d * d * 3 + 18 * d * d // 32) / 1e9, "GB", "hbm"
         return 0.0, "GB", "hbm"
+    if name in ("quant_h", "quant_h2") and w8a8:   # written by the fused LayerNorm
+        return 0.0, "GB", "hbm"
     if name.startswith("quant_"):   # bf16 rows in, E4M3 codes + fp32 row / E8M0 block scales out
         K = 4 * d if name == "quant_u" else d
         if form == "mxfp8" and w8a8:
@@ -55,6 +57,8 @@ def kernel_work(name, d, T, form="bf16", w8a8=False):
     if name == "adaln_gemv":   # bf16 or E4M3 weight rows, silu(c), bias in, modulation out
         return (6 * d * d * (1 if fp8 else 2) + 6 * d * 4 * 2 + d * 4) / 1e9, "GB", "hbm"
     if name in ("ln1_modulate", "ln2_modulate"):
+        if w8a8 and form in ("fp8", "mxfp8"):   # fp32 rows in, E4M3 codes + scales out
+            return (T * d * 5 + (T * d // 32 if form == "mxfp8" else T * 4)) / 1e9, "GB", "hbm"
         return (T * d * 4 + T * d * 2) / 1e9, "GB", "hbm"
     flops = {"gemm_qk": 2 * T * d * 2 * d, "gemm_v_t": 2 * T * d * d, "attention": 4 * T * T * d,
              "gemm_out_residual": 2 * T * d * d, "gemm_fc1_gelu": 8 * T * d * d,

@@ -364,8 +364,10 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
  * block and for W8A8), adaln_gemv, ln1_modulate, quant_h,
  * gemm_qk, gemm_v_t, attention, quant_attn, gemm_out_residual, ln2_modulate,
  * quant_h2, gemm_fc1_gelu, quant_u, gemm_fc2_residual (dlo_kernel_name).  The
- * quant_* entries are the W8A8 input quantisations, 0 unless an FP8 block runs
- * with DLO_FP8_COMPUTE. */
+ * quant_* entries are the W8A8 input quantisations, 0 unless an FP8 or MXFP8
+ * block runs with DLO_FP8_COMPUTE; there LayerNorm + modulate writes the
+ * quantised h and h2 itself (counted in ln1_modulate / ln2_modulate), so
+ * quant_h and quant_h2 stay 0. */
 #define DLO_KERNELS_PER_BLOCK 14
 int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
 /* name of kernel j (0 <= j < DLO_KERNELS_PER_BLOCK) of a block forward */

@@ -1174,17 +1174,23 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   if (kernel_end && (e = hipEventRecord(kernel_end[j], s)) != hipSuccess) return e;
   DLO_STEP(fp8 ? dlo::launch_adaln_gemv_fp8(W8[0], S8[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s)
                : dlo::launch_adaln_gemv(Wt[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 1)
-  DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N1_W), F(P_N1_B), F(P_N1_EPS), mod + 0 * d,
-                                   mod + 1 * d, w.h, s), 2)
-  DLO_STEP(quant(w.h, d), 3)
+  // W8A8: LayerNorm + modulate writes the next linear's E4M3 input directly
+  // (quant_h and quant_h2 then record nothing)
+  auto ln = [&](int pw, int pb, int pe, const float *shift_, const float *scale_) {
+    if (w8a8)
+      return dlo::launch_ln_modulate_quant(x, ldx, T, d, F(pw), F(pb), F(pe), shift_, scale_, q8, d,
+                                           mx ? static_cast<void *>(mxs) : static_cast<void *>(qs), T64, mx, s);
+    return dlo::launch_ln_modulate(x, ldx, T, d, F(pw), F(pb), F(pe), shift_, scale_, w.h, s);
+  };
+  DLO_STEP(ln(P_N1_W, P_N1_B, P_N1_EPS, mod + 0 * d, mod + 1 * d), 2)
+  DLO_STEP(hipSuccess, 3)
   DLO_STEP(linear(w.h, d, 1, 0, 2 * d, F(P_QKV_B), nullptr, qk, 2 * d, dlo::EPI_BIAS), 4)
   DLO_STEP(linear(w.h, d, 1, 2 * d, d, F(P_QKV_B) + 2 * d, nullptr, vt, ldvt, dlo::EPI_BIAS_T), 5)
   DLO_STEP(dlo::launch_attention(qk, 2 * d, vt, ldvt, T, H, dh, attn, d, s), 6)
   DLO_STEP(quant(attn, d), 7)
   DLO_STEP(linear(attn, d, 2, 0, d, F(P_OUT_B), mod + 2 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 8)
-  DLO_STEP(dlo::launch_ln_modulate(x, ldx, T, d, F(P_N2_W), F(P_N2_B), F(P_N2_EPS), mod + 3 * d,
-                                   mod + 4 * d, w.h, s), 9)
-  DLO_STEP(quant(w.h, d), 10)
+  DLO_STEP(ln(P_N2_W, P_N2_B, P_N2_EPS, mod + 3 * d, mod + 4 * d), 9)
+  DLO_STEP(hipSuccess, 10)
   DLO_STEP(linear(w.h, d, 3, 0, 4 * d, F(P_FC1_B), nullptr, u, 4 * d, dlo::EPI_BIAS_GELU), 11)
   DLO_STEP(quant(u, 4 * d), 12)
   DLO_STEP(linear(u, 4 * d, 4, 0, d, F(P_FC2_B), mod + 5 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 13)

@@ -19,6 +19,12 @@ hipError_t launch_adaln_gemv_fp8(const uint8_t *W, const float *wscale, const fl
 hipError_t launch_ln_modulate(const float *x, int64_t ldx, int T, int d, const float *gamma,
                               const float *beta, const float *eps, const float *shift,
                               const float *scale, uint16_t *out, hipStream_t s);
+// the same fused with a W8A8 linear's input quantisation (no bf16 output): codes [T, ldq];
+// mx = false: fp32 row scales qscale[T]; mx = true: E8M0 scales block-major [d / 32, lds],
+// rows T .. lds - 1 set to 127 (lds >= T)
+hipError_t launch_ln_modulate_quant(const float *x, int64_t ldx, int T, int d, const float *gamma,
+                                    const float *beta, const float *eps, const float *shift, const float *scale,
+                                    uint8_t *q, int64_t ldq, void *qscale, int64_t lds, bool mx, hipStream_t s);
 
 enum GemmEpilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_GATED_RESIDUAL = 2, EPI_BIAS_T = 3 };
 

@@ -368,7 +368,116 @@ __global__ __launch_bounds__(256) void quant_rows_mx_kernel(const uint16_t *__re
   }
 }
 
+// LayerNorm + modulate fused with the input quantisation of a W8A8 linear:
+// the modulated row is computed and rounded to bf16 exactly as
+// ln_modulate_kernel does, then quantised from registers as the stand-alone
+// quantizers do (MX = false: per-row E4M3 with an fp32 scale; MX = true: E8M0
+// per 32 columns, block-major [d / 32, lds], rows T .. lds - 1 set to 127), so
+// codes and scales are bit-identical to LN followed by the quantizer, without
+// the bf16 row's round trip through memory.  Thread tid holds columns
+// i * 256 + tid: a 32-column block is one half of a wave.
+template <int VPT, bool MX>
+__global__ __launch_bounds__(256) void ln_modulate_quant_kernel(
+    const float *__restrict__ x, int64_t ldx, int T, int d, const float *__restrict__ gamma,
+    const float *__restrict__ beta, const float *__restrict__ eps_p, const float *__restrict__ shift,
+    const float *__restrict__ scale, uint8_t *__restrict__ q, int64_t ldq, void *__restrict__ qscale,
+    int64_t lds) {
+  __shared__ float red[3][4];
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int64_t row = blockIdx.x;
+  if (row >= T) {   // MX padding rows of the block-major scales
+    if constexpr (MX)
+      for (int b = tid; b < d / 32; b += 256) static_cast<uint8_t *>(qscale)[b * lds + row] = 127;
+    return;
+  }
+  const float *xr = x + row * ldx;
+  float v[VPT];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    v[i] = xr[i * 256 + tid];
+    s += v[i];
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[0][wv] = s;
+  __syncthreads();
+  const float mean = (red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)d;
+  float qv = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    float dv = v[i] - mean;
+    qv += dv * dv;
+  }
+  qv = wave_sum(qv);
+  if (lane == 0) red[1][wv] = qv;
+  __syncthreads();
+  const float var = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) / (float)d;
+  const float rstd = 1.0f / sqrtf(var + eps_p[0]);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int col = i * 256 + tid;
+    float y = (v[i] - mean) * rstd * gamma[col] + beta[col];
+    y = y * (1.0f + scale[col]) + shift[col];
+    v[i] = __uint_as_float((uint32_t)f32_to_bf16(y) << 16);   // the bf16 value the linear reads
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  uint8_t *qr = q + row * ldq;
+  if constexpr (MX) {
+    uint8_t *sc = static_cast<uint8_t *>(qscale);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      float a = fabsf(v[i]);
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, WAVE));
+      const int X = a > 0.f ? max(-127, min(127, (int)((__float_as_uint(a) >> 23) & 0xFF) - 127 - 8)) : -127;
+      const float p2 = __uint_as_float((uint32_t)(127 - X) << 23);
+      qr[i * 256 + tid] = (uint8_t)e4m3_code(v[i] * p2);
+      if ((lane & 31) == 0) sc[(int64_t)(i * 8 + tid / 32) * lds + row] = (uint8_t)(X + 127);
+    }
+  } else {
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+    if (lane == 0) red[2][wv] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
+    const float sq = amax == 0.f ? 1.0f : amax / 448.0f;
+    if (tid == 0) static_cast<float *>(qscale)[row] = sq;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) qr[i * 256 + tid] = (uint8_t)e4m3_code(v[i] / sq);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_ln_modulate_quant(const float *x, int64_t ldx, int T, int d, const float *gamma,
+                                    const float *beta, const float *eps, const float *shift, const float *scale,
+                                    uint8_t *q, int64_t ldq, void *qscale, int64_t lds, bool mx, hipStream_t s) {
+  if (d % 256 || d > 8192 || (mx && lds < T)) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(mx ? lds : T);
+  switch (d / 256) {
+#define DLO_LNQ_CASE(V)                                                                                   \
+  case V:                                                                                                 \
+    if (mx)                                                                                               \
+      hipLaunchKernelGGL((ln_modulate_quant_kernel<V, true>), dim3(grid), dim3(256), 0, s, x, ldx, T, d,   \
+                         gamma, beta, eps, shift, scale, q, ldq, qscale, lds);                            \
+    else                                                                                                  \
+      hipLaunchKernelGGL((ln_modulate_quant_kernel<V, false>), dim3(grid), dim3(256), 0, s, x, ldx, T, d,  \
+                         gamma, beta, eps, shift, scale, q, ldq, qscale, lds);                            \
+    break;
+    DLO_LNQ_CASE(1) DLO_LNQ_CASE(2) DLO_LNQ_CASE(3) DLO_LNQ_CASE(4) DLO_LNQ_CASE(5) DLO_LNQ_CASE(6)
+    DLO_LNQ_CASE(7) DLO_LNQ_CASE(8) DLO_LNQ_CASE(9) DLO_LNQ_CASE(10) DLO_LNQ_CASE(11)
+    DLO_LNQ_CASE(12) DLO_LNQ_CASE(13) DLO_LNQ_CASE(14) DLO_LNQ_CASE(15) DLO_LNQ_CASE(16)
+    DLO_LNQ_CASE(17) DLO_LNQ_CASE(18) DLO_LNQ_CASE(19) DLO_LNQ_CASE(20) DLO_LNQ_CASE(21)
+    DLO_LNQ_CASE(22) DLO_LNQ_CASE(23) DLO_LNQ_CASE(24) DLO_LNQ_CASE(25) DLO_LNQ_CASE(26)
+    DLO_LNQ_CASE(27) DLO_LNQ_CASE(28) DLO_LNQ_CASE(29) DLO_LNQ_CASE(30) DLO_LNQ_CASE(31)
+    DLO_LNQ_CASE(32)
+#undef DLO_LNQ_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant_fp8(const uint8_t *codes, int64_t n, const float *scale, uint16_t *out,
                               hipStream_t s) {
