@@ -49,6 +49,8 @@ def kernel_work(name, d, T, form="bf16", w8a8=False):
         return 0.0, "GB", "hbm"
     if name in ("quant_h", "quant_h2") and w8a8:   # written by the fused LayerNorm
         return 0.0, "GB", "hbm"
+    if name == "quant_u" and w8a8 and form == "mxfp8":   # written by the fc1 epilogue
+        return 0.0, "GB", "hbm"
     if name.startswith("quant_"):   # bf16 rows in, E4M3 codes + fp32 row / E8M0 block scales out
         K = 4 * d if name == "quant_u" else d
         if form == "mxfp8" and w8a8:

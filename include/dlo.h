@@ -367,7 +367,8 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
  * quant_* entries are the W8A8 input quantisations, 0 unless an FP8 or MXFP8
  * block runs with DLO_FP8_COMPUTE; there LayerNorm + modulate writes the
  * quantised h and h2 itself (counted in ln1_modulate / ln2_modulate), so
- * quant_h and quant_h2 stay 0. */
+ * quant_h and quant_h2 stay 0, and for MXFP8 the fc1 GEMM's epilogue writes the
+ * quantised u (quant_u stays 0). */
 #define DLO_KERNELS_PER_BLOCK 14
 int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
 /* name of kernel j (0 <= j < DLO_KERNELS_PER_BLOCK) of a block forward */

@@ -63,6 +63,28 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
 
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
+// The OCP E4M3 code nearest to x: ties to the even code, magnitudes of 448 and
+// above saturate to 448, NaN -> 0x7F.  The encoder works on the fp32 exponent
+// and a 3-bit mantissa rounded by v_rndne (every scaling by a power of two is
+// exact).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  if (x != x) return 0x7Fu;
+  const float a = fabsf(x);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f)  // below 2^-6: subnormal steps of 2^-9 (8 steps = the smallest normal)
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  int E = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;                      // a in [2^E, 2^(E+1))
+  const float f = __uint_as_float((__float_as_uint(a) & 0x7FFFFFu) | 0x3F800000u);  // a / 2^E in [1, 2)
+  int m = (int)__builtin_rintf(f * 8.0f) - 8;
+  if (m == 8) {
+    m = 0;
+    ++E;
+  }
+  return sign | (uint32_t)(((E + 7) << 3) | m);
+}
+
 // raw buffer descriptor: base, no stride, num_records bytes (reads past it return 0)
 __device__ __forceinline__ i32x4 dl_rsrc(const void *base, uint32_t bytes) {
   const uint64_t b = (uint64_t)base;

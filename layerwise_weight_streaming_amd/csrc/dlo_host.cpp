@@ -1191,9 +1191,21 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   DLO_STEP(linear(attn, d, 2, 0, d, F(P_OUT_B), mod + 2 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 8)
   DLO_STEP(ln(P_N2_W, P_N2_B, P_N2_EPS, mod + 3 * d, mod + 4 * d), 9)
   DLO_STEP(hipSuccess, 10)
-  DLO_STEP(linear(w.h, d, 3, 0, 4 * d, F(P_FC1_B), nullptr, u, 4 * d, dlo::EPI_BIAS_GELU), 11)
-  DLO_STEP(quant(u, 4 * d), 12)
-  DLO_STEP(linear(u, 4 * d, 4, 0, d, F(P_FC2_B), mod + 5 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 13)
+  if (w8a8 && mx) {
+    // MXFP8: the fc1 epilogue quantises u itself (32-column blocks never leave
+    // its column tile); u's codes and scales take the place of the bf16 u
+    uint8_t *uq = reinterpret_cast<uint8_t *>(w.big);
+    uint8_t *us = uq + align_up((int64_t)T * 4 * d, DLO_ALIGN);
+    DLO_STEP(dlo::launch_gemm_mxfp8(q8, d, mxs, T64, W8[3], d, SM[3], kWeightRows[3] * d, T, 4 * d, d,
+                                    F(P_FC1_B), nullptr, uq, 4 * d, dlo::EPI_GELU_MX, s, us, T64), 11)
+    DLO_STEP(hipSuccess, 12)
+    DLO_STEP(dlo::launch_gemm_mxfp8(uq, 4 * d, us, T64, W8[4], 4 * d, SM[4], kWeightRows[4] * d, T, d, 4 * d,
+                                    F(P_FC2_B), mod + 5 * d, x, ldx, dlo::EPI_GATED_RESIDUAL, s), 13)
+  } else {
+    DLO_STEP(linear(w.h, d, 3, 0, 4 * d, F(P_FC1_B), nullptr, u, 4 * d, dlo::EPI_BIAS_GELU), 11)
+    DLO_STEP(quant(u, 4 * d), 12)
+    DLO_STEP(linear(u, 4 * d, 4, 0, d, F(P_FC2_B), mod + 5 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 13)
+  }
 #undef DLO_STEP
   return hipSuccess;
 }

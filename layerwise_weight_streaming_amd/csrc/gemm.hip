@@ -54,7 +54,8 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
                                               int tid, int wm, int wn, int lane, int m0, int n0,
                                               int M, const float *__restrict__ bias,
                                               const float *__restrict__ gate, void *__restrict__ Cv,
-                                              int64_t ldc) {
+                                              int64_t ldc, uint8_t *__restrict__ out_scale = nullptr,
+                                              int64_t lds_out = 0) {
   // Epilogue, staged through LDS so that global accesses are whole rows.
   // acc[i][j] holds the transposed 32x32 sub-tile (the MFMA took B as its first
   // operand): lane l has row i*32 + l%32 of the wave's rows and, for g = 0..3,
@@ -111,7 +112,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
         for (int i = 0; i < 4; ++i) {
           float v0 = acc[i][j][g * 4 + 0] + bv.x, v1 = acc[i][j][g * 4 + 1] + bv.y;
           float v2 = acc[i][j][g * 4 + 2] + bv.z, v3 = acc[i][j][g * 4 + 3] + bv.w;
-          if (EPI == EPI_BIAS_GELU) {
+          if (EPI == EPI_BIAS_GELU || EPI == EPI_GELU_MX) {
             v0 = gelu_erf(v0);
             v1 = gelu_erf(v1);
             v2 = gelu_erf(v2);
@@ -127,12 +128,49 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
       }
     __syncthreads();
     constexpr int SEG = BN / 8;               // 16-B segments per row
-    uint16_t *C = reinterpret_cast<uint16_t *>(Cv) + (int64_t)m0 * ldc + n0;
+    if constexpr (EPI == EPI_GELU_MX) {
+      // four consecutive threads hold one 32-column block of a row (SEG % 4 == 0):
+      // its maximum by two shuffles, then the MX rule of quant_rows_mx_kernel
+      uint8_t *Q = static_cast<uint8_t *>(Cv) + (int64_t)m0 * ldc + n0;
 #pragma unroll
-    for (int it = 0; it < GBM * SEG / NT; ++it) {
-      const int e = it * NT + tid, row = e / SEG, c8 = (e % SEG) * 8;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(&smem[row * C_LD + c8]);
-      if (full || m0 + row < M) *reinterpret_cast<u32x4 *>(&C[row * ldc32 + c8]) = v;
+      for (int it = 0; it < GBM * SEG / NT; ++it) {
+        const int e = it * NT + tid, row = e / SEG, c8 = (e % SEG) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(&smem[row * C_LD + c8]);
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f[2 * q] = __uint_as_float(v[q] << 16);
+          f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        const int X = amax > 0.f ? max(-127, min(127, (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 8))
+                                 : -127;
+        const float p2 = __uint_as_float((uint32_t)(127 - X) << 23);
+        const int64_t srow = (int64_t)((n0 + c8) >> 5) * lds_out + m0 + row;
+        if (full || m0 + row < M) {
+          uint32_t w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            w[h] = e4m3_code(f[4 * h] * p2) | (e4m3_code(f[4 * h + 1] * p2) << 8) |
+                   (e4m3_code(f[4 * h + 2] * p2) << 16) | (e4m3_code(f[4 * h + 3] * p2) << 24);
+          *reinterpret_cast<uint2 *>(&Q[row * ldc32 + c8]) = make_uint2(w[0], w[1]);
+          if ((tid & 3) == 0) out_scale[srow] = (uint8_t)(X + 127);
+        } else if ((tid & 3) == 0 && m0 + row < lds_out) {
+          out_scale[srow] = 127;
+        }
+      }
+    } else {
+      uint16_t *C = reinterpret_cast<uint16_t *>(Cv) + (int64_t)m0 * ldc + n0;
+#pragma unroll
+      for (int it = 0; it < GBM * SEG / NT; ++it) {
+        const int e = it * NT + tid, row = e / SEG, c8 = (e % SEG) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(&smem[row * C_LD + c8]);
+        if (full || m0 + row < M) *reinterpret_cast<u32x4 *>(&C[row * ldc32 + c8]) = v;
+      }
     }
   } else {
     float *xs = reinterpret_cast<float *>(smem);
@@ -215,7 +253,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     const void *__restrict__ A, int64_t lda, const void *__restrict__ B, int64_t ldb,
     int M, int N, int K, const float *__restrict__ bias, const float *__restrict__ gate,
     void *__restrict__ Cv, int64_t ldc, const void *__restrict__ a_scale,
-    const void *__restrict__ b_scale, int64_t lds_a, int64_t lds_b) {
+    const void *__restrict__ b_scale, int64_t lds_a, int64_t lds_b, uint8_t *__restrict__ out_scale,
+    int64_t lds_out) {
   constexpr bool F8 = Q > 0, MX = Q == 2;
   constexpr int ES = F8 ? 1 : 2;             // bytes per element
   constexpr int KSTAGE = 64 / ES;            // elements of k per stage
@@ -489,24 +528,32 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
       }
     }
   }
-  gemm_epilogue<EPI, BN, WN>(acc, smem, tid, wm, wn, lane, m0, n0, M, bias, gate, Cv, ldc);
+  gemm_epilogue<EPI, BN, WN>(acc, smem, tid, wm, wn, lane, m0, n0, M, bias, gate, Cv, ldc, out_scale, lds_out);
 }
 
 template <int Q>
 hipError_t launch_gemm_t(const void *A, int64_t lda, const void *B, int64_t ldb, int M, int N, int K,
                          const float *bias, const float *gate, void *C, int64_t ldc, int epilogue,
-                         const void *a_scale, const void *b_scale, int64_t lds_a, int64_t lds_b, hipStream_t s) {
+                         const void *a_scale, const void *b_scale, int64_t lds_a, int64_t lds_b, hipStream_t s,
+                         uint8_t *out_scale = nullptr, int64_t lds_out = 0) {
   const int tiles = ((M + GBM - 1) / GBM) * (N / 256);
   switch (epilogue) {
 #define DLO_GEMM_CASE(E)                                                                            \
   case E:                                                                                           \
     hipLaunchKernelGGL((gemm_pp_kernel<E, Q>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb, M, N, K, \
-                       bias, gate, C, ldc, a_scale, b_scale, lds_a, lds_b);                        \
+                       bias, gate, C, ldc, a_scale, b_scale, lds_a, lds_b, out_scale, lds_out);    \
     break;
     DLO_GEMM_CASE(EPI_BIAS)
     DLO_GEMM_CASE(EPI_BIAS_GELU)
     DLO_GEMM_CASE(EPI_GATED_RESIDUAL)
     DLO_GEMM_CASE(EPI_BIAS_T)
+    case EPI_GELU_MX:
+      if constexpr (Q == 2) {
+        hipLaunchKernelGGL((gemm_pp_kernel<EPI_GELU_MX, 2>), dim3(tiles), dim3(512), 0, s, A, lda, B, ldb, M, N, K,
+                           bias, gate, C, ldc, a_scale, b_scale, lds_a, lds_b, out_scale, lds_out);
+        break;
+      }
+      return hipErrorInvalidValue;
 #undef DLO_GEMM_CASE
     default:
       return hipErrorInvalidValue;
@@ -531,10 +578,11 @@ hipError_t launch_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, 
 hipError_t launch_gemm_mxfp8(const uint8_t *A, int64_t lda, const uint8_t *a_scale, int64_t lds_a,
                              const uint8_t *B, int64_t ldb, const uint8_t *b_scale, int64_t lds_b, int M, int N,
                              int K, const float *bias, const float *gate, void *C, int64_t ldc, int epilogue,
-                             hipStream_t s) {
+                             hipStream_t s, uint8_t *out_scale, int64_t lds_out) {
   if (lds_a < M || lds_a % 4 || lds_b % 4 || K % 64) return hipErrorInvalidValue;
+  if (epilogue == EPI_GELU_MX && (!out_scale || lds_out < M || ldc % 8)) return hipErrorInvalidValue;
   return launch_gemm_t<2>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, a_scale, b_scale, lds_a, lds_b,
-                          s);
+                          s, out_scale, lds_out);
 }
 
 }  // namespace dlo

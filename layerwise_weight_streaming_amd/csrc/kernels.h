@@ -26,7 +26,10 @@ hipError_t launch_ln_modulate_quant(const float *x, int64_t ldx, int T, int d, c
                                     const float *beta, const float *eps, const float *shift, const float *scale,
                                     uint8_t *q, int64_t ldq, void *qscale, int64_t lds, bool mx, hipStream_t s);
 
-enum GemmEpilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_GATED_RESIDUAL = 2, EPI_BIAS_T = 3 };
+// EPI_GELU_MX (MXFP8 GEMM only): bias + GELU, the bf16-rounded result quantised
+// per 32 columns to E4M3 codes [M, ldc] and E8M0 scales block-major
+// [N / 32, lds_out] (rows M .. lds_out - 1 inside the last row tile: 127)
+enum GemmEpilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_GATED_RESIDUAL = 2, EPI_BIAS_T = 3, EPI_GELU_MX = 4 };
 
 // C = A B^T + bias (see dlo_op_gemm); N % 256 == 0, K % 64 == 0.  EPI_BIAS_T
 // stores C^T [N, ldc]: rows m in [M, M rounded up to 64) as 0, nothing beyond
@@ -50,7 +53,7 @@ hipError_t launch_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, 
 hipError_t launch_gemm_mxfp8(const uint8_t *A, int64_t lda, const uint8_t *a_scale, int64_t lds_a,
                              const uint8_t *B, int64_t ldb, const uint8_t *b_scale, int64_t lds_b, int M, int N,
                              int K, const float *bias, const float *gate, void *C, int64_t ldc, int epilogue,
-                             hipStream_t s);
+                             hipStream_t s, uint8_t *out_scale = nullptr, int64_t lds_out = 0);
 
 // per-head softmax(q k^T / sqrt(dh)) v: q, k from a fused qkv buffer, v from
 // its feature-major copy vt (launch_v_transpose); dh in {64, 128}

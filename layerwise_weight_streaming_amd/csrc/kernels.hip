@@ -259,28 +259,9 @@ __global__ __launch_bounds__(256) void dequant_mxfp8_kernel(const u32x4 *__restr
 // all-zero row; NaN entries ignored), code = the E4M3 value nearest to
 // x / scale_r (IEEE fp32 division), ties to the even code, saturating at 448,
 // NaN -> 0x7F.  One workgroup per row: an amax pass, then a quantize pass over
-// the (cache-hot) row; 16-B loads of 8 bf16, 8-B stores of 8 codes.
+// the (cache-hot) row; 16-B loads of 8 bf16, 8-B stores of 8 codes; the
+// encoder (e4m3_code) is shared with the GEMM's MXFP8 epilogue.
 // ---------------------------------------------------------------------------
-
-// The encoder works on the fp32 exponent and a 3-bit mantissa rounded by
-// v_rndne (every scaling by a power of two is exact).
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  const uint32_t bits = __float_as_uint(x);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  if (x != x) return 0x7Fu;
-  const float a = fabsf(x);
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f)  // below 2^-6: subnormal steps of 2^-9 (8 steps = the smallest normal)
-    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  int E = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;                      // a in [2^E, 2^(E+1))
-  const float f = __uint_as_float((__float_as_uint(a) & 0x7FFFFFu) | 0x3F800000u);  // a / 2^E in [1, 2)
-  int m = (int)__builtin_rintf(f * 8.0f) - 8;
-  if (m == 8) {
-    m = 0;
-    ++E;
-  }
-  return sign | (uint32_t)(((E + 7) << 3) | m);
-}
 
 __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t *__restrict__ x, int64_t ldx,
                                                              int K, uint8_t *__restrict__ q, int64_t ldq,
