@@ -106,3 +106,32 @@ def test_counted_traffic_is_null_once_the_kernel_changed(monkeypatch):
     # counted on the Super shape only
     monkeypatch.setattr(bench, "kernel_source_sha", lambda f: recorded[f])
     assert bench.counted_traffic("attention", "nano") is None
+
+
+def test_kernel_work_of_the_quantised_forms():
+    """Algorithmic bytes per slot for each weight form and compute mode (Super shape)."""
+    d, T = 5120, 28800
+    kw = lambda n, f, w8=False: bench.kernel_work(n, d, T, f, w8)[0] * 1e9
+    # W8A16 dequantisation: FP8 the four linears (12 d^2 codes in, 24 d^2 bytes out),
+    # INT8 / MXFP8 all five weights plus their scales
+    assert kw("dequant_weights", "fp8") == 36 * d * d
+    assert kw("dequant_weights", "int8") == 54 * d * d + 60 * d
+    assert kw("dequant_weights", "mxfp8") == 54 * d * d + 18 * d * d // 32
+    # W8A8: nothing dequantised for FP8, the adaLN weight for MXFP8
+    assert kw("dequant_weights", "fp8", True) == 0
+    assert kw("dequant_weights", "mxfp8", True) == 18 * d * d + 6 * d * d // 32
+    # the adaLN GEMV reads E4M3 codes only for per-tensor FP8
+    assert kw("adaln_gemv", "fp8") < kw("adaln_gemv", "mxfp8") == kw("adaln_gemv", "bf16")
+    # W8A8: LayerNorm writes codes (+ scales), quant_h / quant_h2 do nothing
+    assert kw("ln1_modulate", "fp8", True) == T * d * 5 + T * 4
+    assert kw("ln2_modulate", "mxfp8", True) == T * d * 5 + T * d // 32
+    for f in ("fp8", "mxfp8"):
+        assert kw("quant_h", f, True) == kw("quant_h2", f, True) == 0
+        assert kw("quant_attn", f, True) > 0
+    # u: quantised by its own pass for FP8, by the fc1 epilogue for MXFP8
+    assert kw("quant_u", "fp8", True) == T * 4 * d * 3 + T * 4
+    assert kw("quant_u", "mxfp8", True) == 0
+    # no quantisation without W8A8, nor for bf16 and INT8 blocks
+    for f in ("bf16", "int8", "fp8", "mxfp8"):
+        assert kw("quant_attn", f) == kw("quant_u", f) == 0
+    assert kw("quant_attn", "int8", True) == 0
