@@ -491,3 +491,27 @@ def test_quantised_schema_plan_and_pack(form):
     if form == "mxfp8":
         with pytest.raises(dlo.DLOError):
             dlo.block_schema(48, form="mxfp8")
+
+
+@pytest.mark.parametrize("mutate", ["per-row scale on FP8 codes", "int8 codes with E8M0 scales",
+                                    "E8M0 scales per 16", "scale before weight"])
+def test_forward_fails_closed_on_unvalidated_quantised_layouts(mutate):
+    """Only the three quantised block forms are streamed: a quantised layout that is
+    not one of them (a scale of another granularity or type, another order) plans and
+    packs as plain byte groups, but the forward refuses it (DLO_E_UNSUPPORTED)."""
+    from oracle import quant
+    d = 256
+    q = quant.quantize_block(synth.block_params(3, 0, d), "mxfp8" if mutate != "per-row scale on FP8 codes" else "int8")
+    if mutate == "per-row scale on FP8 codes":      # INT8's fp32 row scales under E4M3 codes
+        q = [(n, "fp8" if dt == "i8" else dt, np.asarray(a).view(np.uint8) if dt == "i8" else a) for n, dt, a in q]
+    elif mutate == "int8 codes with E8M0 scales":
+        q = [(n, "i8" if dt == "fp8" else dt, np.asarray(a).view(np.int8) if dt == "fp8" else a) for n, dt, a in q]
+    elif mutate == "E8M0 scales per 16":
+        q = [(n, dt, np.concatenate([a, a]) if dt == "e8m0" else a) for n, dt, a in q]
+    else:                                            # weight_scale registered before its weight
+        q = [q[1], q[0]] + q[2:]
+    p = dlo.Plan([(d, 4, q)], 2)
+    assert p.block_info(0)["form"] is None
+    st = dlo.HostStore(p, pinned=False)
+    st.pack(0, [(d, 4, q)])
+    assert _status(lambda: dlo.forward_stack(p, st, **_args(p))) == "DLO_E_UNSUPPORTED"
