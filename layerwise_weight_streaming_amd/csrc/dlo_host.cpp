@@ -1099,8 +1099,8 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   const bool fp8 = bp.kind == KIND_DIT_FP8, mx = bp.kind == KIND_DIT_MX;
   const bool w8a8 = (fp8 || mx) && (a->flags & DLO_FP8_COMPUTE);
   hipError_t e;
-  // bf16 weights: in the slot, or (FP8 block) dequantised into the workspace;
-  // FP8 codes and scales: in the slot
+  // bf16 weights: in the slot, or (quantised block, W8A16) dequantised into the
+  // workspace; codes and scales of a quantised block: in the slot
   const uint16_t *Wt[5] = {};
   const uint8_t *W8[5] = {};
   const float *S8[5] = {};
@@ -1163,7 +1163,7 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
       return dlo::launch_gemm_fp8(q8, K, qs, W8[i] + n0 * K, K, S8[i], T, N, K, bias, gate, C, ldc, epi, s);
     return dlo::launch_gemm(A, K, Wt[i] + n0 * K, K, T, N, K, bias, gate, C, ldc, epi, s);
   };
-  // W8A8: the per-row E4M3 codes of a linear's input; otherwise nothing
+  // W8A8: a linear input's codes (per-row E4M3, or MXFP8 per 32 columns); otherwise nothing
   auto quant = [&](const uint16_t *A, int K) {
     if (!w8a8) return hipSuccess;
     return mx ? dlo::launch_quant_rows_mx(A, K, T, K, q8, K, mxs, T64, s)
