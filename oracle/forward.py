@@ -139,7 +139,7 @@ def modulation(c, P, d):
     return [mod[i * d:(i + 1) * d] for i in range(6)]
 
 
-def dit_block(x, c, P, n_heads, act_fp8=False, act_mx=False):
+def dit_block(x, c, P, n_heads, act_fp8=False, act_mx=False, act_int8=False):
     """One block on residual x [T, D] (float64, updated copy returned).
 
     act_fp8: the four block linears take their input through per-token E4M3
@@ -149,11 +149,15 @@ def dit_block(x, c, P, n_heads, act_fp8=False, act_mx=False):
     pages fix no precision for this decision, so it is taken in the storage
     precision of the activations it quantizes.  act_mx: the same with MXFP8
     inputs (oracle.quant.fake_quant_mx_rows: per row, blocks of 32 along the
-    input dimension), the W8A8 form of an MXFP8 block's linears.
+    input dimension), the W8A8 form of an MXFP8 block's linears.  act_int8:
+    the same with per-row int8 inputs (oracle.quant.fake_quant_int8_rows), the
+    W8A8 form of an INT8 block's linears.
     """
     from . import fp8, quant
 
-    if act_mx:
+    if act_int8:
+        lin_in = quant.fake_quant_int8_rows
+    elif act_mx:
         lin_in = quant.fake_quant_mx_rows
     elif act_fp8:
         lin_in = lambda t: fp8.fake_quant_rows(round_bf16(t))
@@ -205,15 +209,16 @@ def forward_stack(x, c, blocks, heads, passes, act_fp8=False):
     """``passes`` chained passes over the blocks.
 
     blocks: list of [(name, dtype, array)] per block; heads: heads per block.
-    act_fp8: blocks with per-tensor FP8 or MXFP8 weights run their linears in
-    the W8A8 form (see dit_block: per-row E4M3 or MXFP8 inputs); bf16 and INT8
-    blocks are unaffected.
+    act_fp8: blocks with per-tensor FP8, MXFP8 or INT8 weights run their
+    linears in the W8A8 form (see dit_block: per-row E4M3, MXFP8 or int8
+    inputs); bf16 blocks are unaffected.
     """
     Ps = [param_dict(b) for b in blocks]
     mx_block = [any(dt == "e8m0" for _, dt, _ in b) for b in blocks]
+    i8_block = [any(dt == "i8" for _, dt, _ in b) for b in blocks]
     fp8_block = [any(dt == "fp8" for _, dt, _ in b) and not mx for b, mx in zip(blocks, mx_block)]
     y = np.asarray(x, dtype=np.float64)
     for _ in range(passes):
-        for P, H, f8, mx in zip(Ps, heads, fp8_block, mx_block):
-            y = dit_block(y, c, P, H, act_fp8=act_fp8 and f8, act_mx=act_fp8 and mx)
+        for P, H, f8, mx, i8 in zip(Ps, heads, fp8_block, mx_block, i8_block):
+            y = dit_block(y, c, P, H, act_fp8=act_fp8 and f8, act_mx=act_fp8 and mx, act_int8=act_fp8 and i8)
     return y

@@ -28,6 +28,9 @@ readings here (listed in the design doc as well):
   output rows are adjacent, the order a block-scaled matrix product reads.
 * W8A8 with MXFP8 weights: each linear's input (as stored in bf16) is
   quantised the same way, per row in blocks of 32 along the input dimension.
+* W8A8 with INT8 weights: each linear's input (as stored in bf16) is
+  quantised by the INT8 rule per row (symmetric, amax / 127); the product is
+  the exact integer dot product of the codes times both scales.
 """
 from __future__ import annotations
 
@@ -144,3 +147,13 @@ def fake_quant_mx_rows(x) -> np.ndarray:
     bits = (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     codes, scales = quantize_mxfp8(bits)
     return dequantize_mxfp8(codes, scales)
+
+
+def fake_quant_int8_rows(x) -> np.ndarray:
+    """What a W8A8 INT8 linear multiplies: the input rounded to bf16 (as stored),
+    quantised per row by the INT8 rule (quantize_int8), dequantised exactly."""
+    from .forward import round_bf16
+    r = round_bf16(x).astype(np.float32)                       # exact: bf16 values
+    bits = (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    codes, scales = quantize_int8(bits)
+    return dequantize_int8(codes, scales)

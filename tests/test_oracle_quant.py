@@ -202,3 +202,31 @@ def test_mx_activation_fake_quant():
     y16, y8 = of.dit_block(xx, c, P, H), of.dit_block(xx, c, P, H, act_mx=True)
     err = np.max(np.abs((y8 - xx) - (y16 - xx))) / np.max(np.abs(y16 - xx))
     assert 0 < err < 0.1
+
+
+def test_int8_activation_fake_quant():
+    """W8A8 INT8 input: round to bf16, quantise per row by the INT8 rule, dequantise;
+    against the rule written out (nearest integer by search, amax / 127 in float32)."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((4, 48)) * np.exp2(rng.uniform(-6, 6, (4, 1)))
+    x[2] = 0.0
+    y = quant.fake_quant_int8_rows(x)
+    cand = np.arange(-127, 128, dtype=np.float64)
+    for r in range(4):
+        xb = of.round_bf16(x[r]).astype(np.float32)
+        amax = np.float32(np.max(np.abs(xb)))
+        s = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(127))
+        for j in range(48):
+            v = float(np.float32(xb[j] / s))
+            d_ = np.abs(cand - v)
+            best = cand[d_ == d_.min()]
+            q = best[0] if best.size == 1 else best[best % 2 == 0][0]
+            assert y[r, j] == q * float(s)
+    assert np.all(y[2] == 0)
+    # an INT8 block in the W8A8 form stays close to its W8A16 form
+    d, H, T = 64, 2, 12
+    P = of.param_dict(quant.quantize_block(synth.block_params(9, 0, d), "int8"))
+    xx, c = rng.standard_normal((T, d)), rng.standard_normal(d)
+    y16, y8 = of.dit_block(xx, c, P, H), of.dit_block(xx, c, P, H, act_int8=True)
+    err = np.max(np.abs((y8 - xx) - (y16 - xx))) / np.max(np.abs(y16 - xx))
+    assert 0 < err < 0.1
