@@ -28,34 +28,38 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA (TOP/s), published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 LINK_PEAK_GBS = 32.0 * 16 * 128 / 130 / 8   # PCIe 5.0 x16, one direction: 63.0 GB/s
 
 
 def kernel_work(name, d, T, form="bf16", w8a8=False):
     """Algorithmic work of one launch: (amount, unit, bound).  form: the block's
-    weight form ("bf16", "fp8", "int8", "mxfp8"); w8a8: FP8 blocks run with FP8
-    compute (the linears' inputs quantised, no weight dequantised)."""
+    weight form ("bf16", "fp8", "int8", "mxfp8"); w8a8: quantised blocks run W8A8
+    (the linears' inputs quantised, only the adaLN weight dequantised, and for
+    per-tensor FP8 not even that)."""
     fp8 = form == "fp8"
     if name == "dequant_weights":   # codes (+ scales) in, bf16 weights out
         if fp8:     # the four linears, W8A16 only
             return (12 * d * d * 3 if not w8a8 else 0) / 1e9, "GB", "hbm"
         if form == "mxfp8" and w8a8:   # the adaLN weight only
             return (6 * d * d * 3 + 6 * d * d // 32) / 1e9, "GB", "hbm"
+        if form == "int8" and w8a8:
+            return (6 * d * d * 3 + 6 * d * 4) / 1e9, "GB", "hbm"
         if form == "int8":   # all five weights, fp32 scale per row (15 d rows)
             return (18 * d * d * 3 + 15 * d * 4) / 1e9, "GB", "hbm"
         if form == "mxfp8":  # all five weights, one E8M0 per 32 codes
             return (18 * d * d * 3 + 18 * d * d // 32) / 1e9, "GB", "hbm"
         return 0.0, "GB", "hbm"
-    if name in ("quant_h", "quant_h2") and w8a8:   # written by the fused LayerNorm
+    if name in ("quant_h", "quant_h2") and w8a8 and form != "int8":   # written by the fused LayerNorm
         return 0.0, "GB", "hbm"
     if name == "quant_u" and w8a8 and form == "mxfp8":   # written by the fc1 epilogue
         return 0.0, "GB", "hbm"
-    if name.startswith("quant_"):   # bf16 rows in, E4M3 codes + fp32 row / E8M0 block scales out
+    if name.startswith("quant_"):   # bf16 rows in, 1-byte codes + fp32 row / E8M0 block scales out
         K = 4 * d if name == "quant_u" else d
         if form == "mxfp8" and w8a8:
             return (T * K * 3 + T * K // 32) / 1e9, "GB", "hbm"
-        return ((T * K * 3 + T * 4) if (fp8 and w8a8) else 0) / 1e9, "GB", "hbm"
+        return ((T * K * 3 + T * 4) if (form in ("fp8", "int8") and w8a8) else 0) / 1e9, "GB", "hbm"
     if name == "adaln_gemv":   # bf16 or E4M3 weight rows, silu(c), bias in, modulation out
         return (6 * d * d * (1 if fp8 else 2) + 6 * d * 4 * 2 + d * 4) / 1e9, "GB", "hbm"
     if name in ("ln1_modulate", "ln2_modulate"):
@@ -307,8 +311,8 @@ def main():
                     help="skip the streamed == resident bit-exact check")
     args = ap.parse_args()
 
-    if args.compute == "fp8" and args.weights not in ("fp8", "mxfp8"):
-        print("--compute fp8 needs --weights fp8 or mxfp8", file=sys.stderr)
+    if args.compute == "fp8" and args.weights not in ("fp8", "mxfp8", "int8"):
+        print("--compute fp8 needs --weights fp8, mxfp8 or int8", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the stack is streamed from this host into this "
@@ -430,9 +434,12 @@ def main():
     avg_ms = per_kernel[jdom] / launches
     achieved = work[jdom] / launches / (avg_ms * 1e-3)
     fp8_mfma = w8a8 and dname.startswith("gemm_") and any(i["form"] in ("fp8", "mxfp8") for i in infos)
-    peak = (PEAK_FP8_TFLOPS if fp8_mfma else PEAK_BF16_TFLOPS) if kbound == "mfma" else PEAK_HBM_GBS
+    i8_mfma = w8a8 and dname.startswith("gemm_") and any(i["form"] == "int8" for i in infos)
+    peak = ((PEAK_INT8_TOPS if i8_mfma else PEAK_FP8_TFLOPS if fp8_mfma else PEAK_BF16_TFLOPS)
+            if kbound == "mfma" else PEAK_HBM_GBS)
     roofline = {"kernel": dname, "bound": kbound, "achieved": achieved, "peak": peak,
-                "unit": "TFLOP/s" if kbound == "mfma" else "GB/s", "frac": achieved / peak,
+                "unit": ("TOP/s" if i8_mfma else "TFLOP/s") if kbound == "mfma" else "GB/s",
+                "frac": achieved / peak,
                 "traffic": counted_traffic(dname, w.name),
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "avg_launch_ms": avg_ms,
@@ -447,7 +454,8 @@ def main():
         "ms_per_step": wall / args.steps * 1e3,
         "step_ms": {"per_step": step_ms, "median": float(np.median(step_ms))},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8e4m3+bf16" if w8a8 else "bf16", "data": "synthetic",
+        "dtype": ("int8+bf16" if args.weights == "int8" else "fp8e4m3+bf16") if w8a8 else "bf16",
+        "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "n_blocks": n,
                    "widths": list(w.widths), "head_dim": w.head_dim, "tokens": T, "batch": 1,
                    "k": w.k, "passes": P, "slot_bytes": r.plan.slot_bytes,

@@ -145,11 +145,12 @@ int dlo_plan_block_info(const dlo_plan *plan, int32_t b, dlo_block_info *out);
 int dlo_plan_param_offset(const dlo_plan *plan, int32_t b, int32_t p, int64_t *byte_offset);
 
 /* Device workspace needed by dlo_forward_stack for `tokens` rows (batch 1):
- * activations of one block at the widest d, plus, when the plan holds FP8
- * blocks, the bf16 weights of the widest FP8 block's four linears (12 d^2
- * elements) that its forward dequantises into and the E4M3 codes (tokens x 4 d
- * bytes) and row scales of a W8A8 linear's input (DLO_FP8_COMPUTE); -1 on
- * error. */
+ * activations of one block at the widest d, plus, when the plan holds quantised
+ * blocks, the bf16 weights their forward dequantises into (an FP8 block's four
+ * linears, 12 d^2 elements; an INT8 or MXFP8 block's five, 18 d^2) and the
+ * 1-byte codes (tokens x 4 d) and scales of a W8A8 linear's input
+ * (DLO_FP8_COMPUTE: fp32 per row for FP8 and INT8, E8M0 [4 d / 32, tokens
+ * rounded up to 64] for MXFP8); -1 on error. */
 int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens);
 
 /* ---------------------------------------------------------------------------
@@ -277,18 +278,19 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 #define DLO_TRACE_TIMING 2u  /* timestamp copies, block computes and every kernel */
 #define DLO_RESIDENT 4u      /* no streaming: block b is read from resident_blocks[b] (same as
                                 n_resident = number of blocks) */
-#define DLO_FP8_COMPUTE 8u   /* FP8 and MXFP8 blocks run their qkv, out, fc1 and fc2
-                                linears as W8A8 products ([Doc] "Request and loading
-                                constraints", online FP8 and MXFP8 linears), the weight's
-                                codes and scales read in place from the slot: per-tensor
-                                FP8 quantises each input per row to E4M3
+#define DLO_FP8_COMPUTE 8u   /* FP8, MXFP8 and INT8 blocks run their qkv, out, fc1 and
+                                fc2 linears as W8A8 products ([Doc] "Request and loading
+                                constraints", online FP8, INT8 and MXFP8 linears), the
+                                weight's codes and scales read in place from the slot:
+                                per-tensor FP8 quantises each input per row to E4M3
                                 (dlo_op_quantize_rows_fp8, dlo_op_gemm_fp8); MXFP8 per row
                                 in blocks of 32 (dlo_op_quantize_rows_mxfp8,
-                                dlo_op_gemm_mxfp8).  Without it their linears run on
-                                dequantised bf16 weights (W8A16).  An FP8 block's adaLN GEMV
-                                reads its codes (dlo_op_adaln_fp8); an MXFP8 block's runs on
-                                its dequantised weight.  bf16 and INT8 blocks are
-                                unaffected. */
+                                dlo_op_gemm_mxfp8); INT8 per row to int8
+                                (dlo_op_quantize_rows_int8, dlo_op_gemm_int8).  Without it
+                                their linears run on dequantised bf16 weights (W8A16).  An
+                                FP8 block's adaLN GEMV reads its codes (dlo_op_adaln_fp8);
+                                MXFP8 and INT8 blocks' run on the dequantised weight.  bf16
+                                blocks are unaffected. */
 
 typedef struct {
   void *slot[2];            /* device, slot_bytes each, distinct (unused if nothing streams) */
@@ -364,11 +366,12 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
  * block and for W8A8), adaln_gemv, ln1_modulate, quant_h,
  * gemm_qk, gemm_v_t, attention, quant_attn, gemm_out_residual, ln2_modulate,
  * quant_h2, gemm_fc1_gelu, quant_u, gemm_fc2_residual (dlo_kernel_name).  The
- * quant_* entries are the W8A8 input quantisations, 0 unless an FP8 or MXFP8
- * block runs with DLO_FP8_COMPUTE; there LayerNorm + modulate writes the
+ * quant_* entries are the W8A8 input quantisations, 0 unless a quantised block
+ * runs with DLO_FP8_COMPUTE; for FP8 and MXFP8 LayerNorm + modulate writes the
  * quantised h and h2 itself (counted in ln1_modulate / ln2_modulate), so
  * quant_h and quant_h2 stay 0, and for MXFP8 the fc1 GEMM's epilogue writes the
- * quantised u (quant_u stays 0). */
+ * quantised u (quant_u stays 0); INT8 quantises all four inputs in their own
+ * passes. */
 #define DLO_KERNELS_PER_BLOCK 14
 int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
 /* name of kernel j (0 <= j < DLO_KERNELS_PER_BLOCK) of a block forward */
@@ -511,6 +514,30 @@ int dlo_op_quantize_rows_fp8(const uint16_t *x, int64_t ldx, int32_t M, int32_t 
 int dlo_op_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B, int64_t ldb,
                     const float *b_scale, int32_t M, int32_t N, int32_t K, const float *bias,
                     const float *gate, void *C, int64_t ldc, int32_t epilogue, void *stream);
+
+/* Per-row INT8 quantization of an activation matrix, the input side of a W8A8
+ * INT8 linear ([Doc] "Request and loading constraints", online INT8 linears;
+ * the symmetric rule of dlo_quantize_int8 applied to each row of x bf16 [M, K],
+ * row stride ldx): scales fp32 [M] = amax / 127 (1 for a row of zeros), codes
+ * int8 [M, ldq] = x / scale (fp32 division) rounded to nearest-even, clamped to
+ * +-127.  All device, caller-owned.  K % 8 == 0, ldx and ldq multiples of 8 and
+ * >= K, x 16-B and codes 8-B aligned, else DLO_E_UNSUPPORTED. */
+int dlo_op_quantize_rows_int8(const uint16_t *x, int64_t ldx, int32_t M, int32_t K, int8_t *codes,
+                              int64_t ldq, float *scales, void *stream);
+
+/* The INT8 form of dlo_op_gemm (W8A8 INT8, same passage): C = float(A B^T) *
+ * a_scale[m] * b_scale[n] + bias, then the epilogue (0..3 as for dlo_op_gemm),
+ * with A [M, K] and B [N, K] int8 codes (row strides lda, ldb in bytes), a_scale
+ * fp32 [M] (as dlo_op_quantize_rows_int8 writes it) and b_scale fp32 [N] (the
+ * weight's per-output-row scales, as dlo_quantize_int8 writes them, 4-B
+ * aligned); the sums are exact int32 on v_mfma_i32_32x32x32_i8 (|sum| <= K *
+ * 127^2 < 2^31 for K < 133 000), converted to fp32 once.  All device,
+ * caller-owned.  N % 256 == 0, K % 64 == 0, lda and ldb multiples of 16, A, B,
+ * C, bias and gate 16-B aligned, ldc as for dlo_op_gemm, else
+ * DLO_E_UNSUPPORTED. */
+int dlo_op_gemm_int8(const int8_t *A, int64_t lda, const float *a_scale, const int8_t *B, int64_t ldb,
+                     const float *b_scale, int32_t M, int32_t N, int32_t K, const float *bias,
+                     const float *gate, void *C, int64_t ldc, int32_t epilogue, void *stream);
 
 /* Per-row MXFP8 quantization of an activation matrix, the input side of a W8A8
  * MXFP8 linear (the MX rule of dlo_quantize_mxfp8 applied to each row of x bf16

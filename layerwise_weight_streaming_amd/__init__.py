@@ -155,6 +155,13 @@ _SIGS = {
                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]),
+    "dlo_op_quantize_rows_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                                 ctypes.c_void_p, ctypes.c_void_p]),
+    "dlo_op_gemm_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]),
     "dlo_op_v_transpose": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                           ctypes.c_void_p]),
@@ -528,6 +535,15 @@ def op_quantize_rows_fp8(x, ldx, M, K, codes, ldq, scales, stream):
 def op_gemm_fp8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc, epilogue, stream):
     _check(lib().dlo_op_gemm_fp8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc, epilogue,
                                  stream))
+
+
+def op_quantize_rows_int8(x, ldx, M, K, codes, ldq, scales, stream):
+    _check(lib().dlo_op_quantize_rows_int8(x, ldx, M, K, codes, ldq, scales, stream))
+
+
+def op_gemm_int8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc, epilogue, stream):
+    _check(lib().dlo_op_gemm_int8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc, epilogue,
+                                  stream))
 
 
 def v_t_stride(T):

@@ -229,6 +229,7 @@ struct dlo_plan {
   int32_t max_fp8_d = 0;   // widest per-tensor FP8 block (0: none)
   int32_t max_q_d = 0;     // widest INT8 or MXFP8 block (0: none)
   int32_t max_mx_d = 0;    // widest MXFP8 block (0: none)
+  int32_t max_i8_d = 0;    // widest INT8 block (0: none)
   uint64_t id = 0;
   mutable std::mutex mu;
   mutable std::vector<dlo_run *> detached;   // runs started without a handle
@@ -442,17 +443,17 @@ int64_t round_up64(int64_t T) { return (T + 63) / 64 * 64; }
 // weights (12 f^2 bf16), an INT8 or MXFP8 block's five (18 q^2 bf16)
 int64_t dequant_bytes(int64_t f, int64_t q) { return std::max(24 * f * f, 36 * q * q); }
 
-// bytes of a W8A8 linear input's scales: fp32 per row (FP8), or E8M0 per 32
-// elements block-major [4 mx / 32, T64] (MXFP8)
+// bytes of a W8A8 linear input's scales: fp32 per row (FP8 and INT8, widest
+// such block f), or E8M0 per 32 elements block-major [4 mx / 32, T64] (MXFP8)
 int64_t act_scale_bytes(int64_t T, int64_t f, int64_t mx) {
   return std::max(f > 0 ? 4 * T : 0, mx * round_up64(T) / 8);
 }
 
-int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, int32_t mx_d) {
-  const int64_t d = max_d, f = fp8_d, mx = mx_d;
-  // quantised blocks: their dequantised weights; FP8 and MXFP8 blocks also the
-  // E4M3 codes [T, 4d] and the scales of a linear's input in the W8A8 form
-  const int64_t dq = align_up(dequant_bytes(f, q_d), DLO_ALIGN);
+int64_t workspace_bytes_for(int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, int32_t mx_d, int32_t i8_d) {
+  const int64_t d = max_d, f = std::max(fp8_d, i8_d), mx = mx_d;
+  // quantised blocks: their dequantised weights; all of them also the 1-byte
+  // codes [T, 4d] and the scales of a linear's input in the W8A8 form
+  const int64_t dq = align_up(dequant_bytes(fp8_d, q_d), DLO_ALIGN);
   const int64_t w8a8 = (f > 0 || mx > 0) ? align_up(4 * T * std::max(f, mx), DLO_ALIGN) +
                                              align_up(act_scale_bytes(T, f, mx), DLO_ALIGN)
                                        : 0;
@@ -685,6 +686,7 @@ int dlo_plan_blocks(const dlo_block *blocks, int32_t n_blocks, int32_t k, dlo_pl
     if (bp.kind == KIND_DIT_FP8) pl->max_fp8_d = std::max(pl->max_fp8_d, bp.d);
     if (bp.kind == KIND_DIT_INT8 || bp.kind == KIND_DIT_MX) pl->max_q_d = std::max(pl->max_q_d, bp.d);
     if (bp.kind == KIND_DIT_MX) pl->max_mx_d = std::max(pl->max_mx_d, bp.d);
+    if (bp.kind == KIND_DIT_INT8) pl->max_i8_d = std::max(pl->max_i8_d, bp.d);
   }
   pl->id = g_plan_ids++;
   *out = pl;
@@ -741,7 +743,7 @@ int64_t dlo_plan_workspace_bytes(const dlo_plan *plan, int32_t tokens) {
     return -1;
   }
   g_err.clear();
-  return workspace_bytes_for(plan->max_d, tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d);
+  return workspace_bytes_for(plan->max_d, tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d, plan->max_i8_d);
 }
 
 int dlo_plan_schedule(const dlo_plan *plan, int32_t passes, dlo_sched_op *ops, int64_t cap,
@@ -1065,7 +1067,7 @@ struct Workspace {
   uint8_t *act_codes;
 };
 
-Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, int32_t mx_d) {
+Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, int32_t mx_d, int32_t i8_d) {
   char *p = static_cast<char *>(ws);
   Workspace w;
   w.silu_c = reinterpret_cast<float *>(p);
@@ -1078,8 +1080,9 @@ Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, 
   p += align_up(8 * round_up64(T) * max_d, DLO_ALIGN);
   w.dq = reinterpret_cast<uint16_t *>(p);   // a quantised block's weights, dequantised to bf16
   p += align_up(dequant_bytes(fp8_d, q_d), DLO_ALIGN);
-  w.act_codes = reinterpret_cast<uint8_t *>(p);  // W8A8: a linear input's E4M3 codes [T, <= 4d]
-  p += (fp8_d > 0 || mx_d > 0) ? align_up(4 * T * std::max(fp8_d, mx_d), DLO_ALIGN) : 0;
+  w.act_codes = reinterpret_cast<uint8_t *>(p);  // W8A8: a linear input's 1-byte codes [T, <= 4d]
+  const int32_t wq = std::max(std::max(fp8_d, i8_d), mx_d);
+  p += wq > 0 ? align_up(4 * T * wq, DLO_ALIGN) : 0;
   w.act_scale = reinterpret_cast<float *>(p);    // ... and its scales (fp32 per row, or E8M0 block-major)
   return w;
 }
@@ -1096,8 +1099,8 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   const int d = bp.d, H = bp.heads, dh = d / H, T = a->tokens;
   auto P = [&](int lp) { return base + bp.logical_byte(lp); };
   auto F = [&](int lp) { return reinterpret_cast<const float *>(P(lp)); };
-  const bool fp8 = bp.kind == KIND_DIT_FP8, mx = bp.kind == KIND_DIT_MX;
-  const bool w8a8 = (fp8 || mx) && (a->flags & DLO_FP8_COMPUTE);
+  const bool fp8 = bp.kind == KIND_DIT_FP8, mx = bp.kind == KIND_DIT_MX, i8 = bp.kind == KIND_DIT_INT8;
+  const bool w8a8 = (fp8 || mx || i8) && (a->flags & DLO_FP8_COMPUTE);
   hipError_t e;
   // bf16 weights: in the slot, or (quantised block, W8A16) dequantised into the
   // workspace; codes and scales of a quantised block: in the slot
@@ -1125,7 +1128,7 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
       const char *sc = base + bp.param_byte(kFp8Scale[i]);
       W8[i] = reinterpret_cast<const uint8_t *>(P(kWeightP[i]));
       SM[i] = reinterpret_cast<const uint8_t *>(sc);
-      if (w8a8 && i > 0) continue;   // W8A8 MXFP8: only the adaLN weight runs in bf16
+      if (w8a8 && i > 0) continue;   // W8A8: only the adaLN weight runs in bf16
       e = bp.kind == KIND_DIT_INT8
               ? dlo::launch_dequant_int8(reinterpret_cast<const int8_t *>(P(kWeightP[i])), rows, cols,
                                          reinterpret_cast<const float *>(sc), dst, s)
@@ -1159,13 +1162,18 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
     if (w8a8 && mx)
       return dlo::launch_gemm_mxfp8(q8, K, mxs, T64, W8[i] + n0 * K, K, SM[i] + n0, kWeightRows[i] * d, T, N,
                                     K, bias, gate, C, ldc, epi, s);
+    if (w8a8 && i8)
+      return dlo::launch_gemm_int8(reinterpret_cast<const int8_t *>(q8), K, qs,
+                                   reinterpret_cast<const int8_t *>(W8[i]) + n0 * K, K,
+                                   reinterpret_cast<const float *>(SM[i]) + n0, T, N, K, bias, gate, C, ldc, epi, s);
     if (w8a8)
       return dlo::launch_gemm_fp8(q8, K, qs, W8[i] + n0 * K, K, S8[i], T, N, K, bias, gate, C, ldc, epi, s);
     return dlo::launch_gemm(A, K, Wt[i] + n0 * K, K, T, N, K, bias, gate, C, ldc, epi, s);
   };
-  // W8A8: a linear input's codes (per-row E4M3, or MXFP8 per 32 columns); otherwise nothing
+  // W8A8: a linear input's codes (per-row E4M3 or int8, or MXFP8 per 32 columns); otherwise nothing
   auto quant = [&](const uint16_t *A, int K) {
     if (!w8a8) return hipSuccess;
+    if (i8) return dlo::launch_quant_rows_int8(A, K, T, K, reinterpret_cast<int8_t *>(q8), K, qs, s);
     return mx ? dlo::launch_quant_rows_mx(A, K, T, K, q8, K, mxs, T64, s)
               : dlo::launch_quant_rows_fp8(A, K, T, K, q8, K, qs, s);
   };
@@ -1174,23 +1182,24 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   if (kernel_end && (e = hipEventRecord(kernel_end[j], s)) != hipSuccess) return e;
   DLO_STEP(fp8 ? dlo::launch_adaln_gemv_fp8(W8[0], S8[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s)
                : dlo::launch_adaln_gemv(Wt[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 1)
-  // W8A8: LayerNorm + modulate writes the next linear's E4M3 input directly
-  // (quant_h and quant_h2 then record nothing)
+  // W8A8 FP8 / MXFP8: LayerNorm + modulate writes the next linear's codes
+  // directly (quant_h and quant_h2 then record nothing); INT8 quantises h in
+  // its own pass
   auto ln = [&](int pw, int pb, int pe, const float *shift_, const float *scale_) {
-    if (w8a8)
+    if (w8a8 && !i8)
       return dlo::launch_ln_modulate_quant(x, ldx, T, d, F(pw), F(pb), F(pe), shift_, scale_, q8, d,
                                            mx ? static_cast<void *>(mxs) : static_cast<void *>(qs), T64, mx, s);
     return dlo::launch_ln_modulate(x, ldx, T, d, F(pw), F(pb), F(pe), shift_, scale_, w.h, s);
   };
   DLO_STEP(ln(P_N1_W, P_N1_B, P_N1_EPS, mod + 0 * d, mod + 1 * d), 2)
-  DLO_STEP(hipSuccess, 3)
+  DLO_STEP(i8 ? quant(w.h, d) : hipSuccess, 3)
   DLO_STEP(linear(w.h, d, 1, 0, 2 * d, F(P_QKV_B), nullptr, qk, 2 * d, dlo::EPI_BIAS), 4)
   DLO_STEP(linear(w.h, d, 1, 2 * d, d, F(P_QKV_B) + 2 * d, nullptr, vt, ldvt, dlo::EPI_BIAS_T), 5)
   DLO_STEP(dlo::launch_attention(qk, 2 * d, vt, ldvt, T, H, dh, attn, d, s), 6)
   DLO_STEP(quant(attn, d), 7)
   DLO_STEP(linear(attn, d, 2, 0, d, F(P_OUT_B), mod + 2 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 8)
   DLO_STEP(ln(P_N2_W, P_N2_B, P_N2_EPS, mod + 3 * d, mod + 4 * d), 9)
-  DLO_STEP(hipSuccess, 10)
+  DLO_STEP(i8 ? quant(w.h, d) : hipSuccess, 10)
   if (w8a8 && mx) {
     // MXFP8: the fc1 epilogue quantises u itself (32-column blocks never leave
     // its column tile); u's codes and scales take the place of the bf16 u
@@ -1251,7 +1260,7 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
     return fail(DLO_E_UNSUPPORTED, "x_row_stride too large for 32-bit tile offsets");
   if (((int64_t)a->tokens + 64) * 3 * plan->max_d * 2 >= ((int64_t)1 << 31))
     return fail(DLO_E_UNSUPPORTED, "tokens x 3 d too large for 32-bit buffer offsets");
-  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d);
+  const int64_t need = workspace_bytes_for(plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d, plan->max_i8_d);
   if (a->workspace_bytes < need)
     return fail(DLO_E_WORKSPACE, "workspace %lld < %lld bytes", (long long)a->workspace_bytes, (long long)need);
   if (!resident) {
@@ -1329,7 +1338,7 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
     r.t_copy_begin = r.t_copy_end = r.t_compute_begin = r.t_compute_end = -1.f;
   }
 
-  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d);
+  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d, plan->max_i8_d);
   hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
   auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
   hipError_t e = hipSuccess;
@@ -1557,6 +1566,40 @@ int dlo_op_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const u
     return fail(DLO_E_UNSUPPORTED, "gemm_fp8: A, B, C, bias and gate must be 16-B aligned and ldc %% 4 == 0");
   int rc = check_hip(dlo::launch_gemm_fp8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc,
                                           epilogue, (hipStream_t)stream), "gemm_fp8");
+  return rc ? rc : ok();
+}
+
+int dlo_op_quantize_rows_int8(const uint16_t *x, int64_t ldx, int32_t M, int32_t K, int8_t *codes,
+                              int64_t ldq, float *scales, void *stream) {
+  if (!x || !codes || !scales) return fail(DLO_E_ARG, "NULL argument");
+  if (M < 1 || K < 8 || K % 8 || ldx < K || ldq < K || ldx % 8 || ldq % 8)
+    return fail(DLO_E_UNSUPPORTED, "quantize_rows_int8: K %% 8 == 0, ldx and ldq >= K and multiples of 8");
+  if ((uintptr_t)x % 16 || (uintptr_t)codes % 8 || (uintptr_t)scales % 4)
+    return fail(DLO_E_UNSUPPORTED, "quantize_rows_int8: x 16-B, codes 8-B and scales 4-B aligned");
+  int rc = check_hip(dlo::launch_quant_rows_int8(x, ldx, M, K, codes, ldq, scales, (hipStream_t)stream),
+                     "quantize_rows_int8");
+  return rc ? rc : ok();
+}
+
+int dlo_op_gemm_int8(const int8_t *A, int64_t lda, const float *a_scale, const int8_t *B, int64_t ldb,
+                     const float *b_scale, int32_t M, int32_t N, int32_t K, const float *bias,
+                     const float *gate, void *C, int64_t ldc, int32_t epilogue, void *stream) {
+  if (!A || !a_scale || !B || !b_scale || !bias || !C) return fail(DLO_E_ARG, "NULL argument");
+  if (epilogue < 0 || epilogue > 3) return fail(DLO_E_ARG, "unknown epilogue %d", epilogue);
+  if (epilogue == DLO_EPI_GATED_RESIDUAL && !gate) return fail(DLO_E_ARG, "gate is required");
+  const bool trans = epilogue == DLO_EPI_BIAS_T;
+  if (M < 1 || N < 256 || N % 256 || K < 64 || K % 64 || lda < K || ldb < K ||
+      ldc < (trans ? round_up64(M) : N) || lda % 16 || ldb % 16 || (trans && ldc % 8))
+    return fail(DLO_E_UNSUPPORTED,
+                "gemm_int8: N %% 256 == 0, K %% 64 == 0, ld >= extent, lda and ldb multiples of 16");
+  if ((int64_t)256 * lda >= (int64_t)1 << 31 || (int64_t)256 * ldb >= (int64_t)1 << 31 ||
+      (int64_t)256 * ldc * 4 >= (int64_t)1 << 31)
+    return fail(DLO_E_UNSUPPORTED, "gemm_int8: leading dimension too large for 32-bit tile offsets");
+  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 16 || (gate && (uintptr_t)gate % 16) ||
+      (uintptr_t)A % 16 || (uintptr_t)B % 16 || (uintptr_t)a_scale % 4 || (uintptr_t)b_scale % 4)
+    return fail(DLO_E_UNSUPPORTED, "gemm_int8: A, B, C, bias and gate must be 16-B aligned and ldc %% 4 == 0");
+  int rc = check_hip(dlo::launch_gemm_int8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc,
+                                           epilogue, (hipStream_t)stream), "gemm_int8");
   return rc ? rc : ok();
 }
 

@@ -248,6 +248,10 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
 // for the tile's 256 A rows and 256 B rows (1 KB) travel with the tiles, by
 // DMA into LDS, and the instruction applies them (lane (row m, half h) holds
 // block h's scale of its row).
+// Q = 3 (INT8): A and B hold int8 codes; a stage row of 64 bytes is two
+// v_mfma_i32_32x32x32_i8 k-steps of 32, each lane's 16 k-bytes read exactly as
+// the bf16 fragments are; the int32 sums are exact, then converted to fp32 and
+// scaled by a_scale[row] * b_scale[column] (fp32, per row of A and of B).
 template <int EPI, int Q>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     const void *__restrict__ A, int64_t lda, const void *__restrict__ B, int64_t ldb,
@@ -255,8 +259,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     void *__restrict__ Cv, int64_t ldc, const void *__restrict__ a_scale,
     const void *__restrict__ b_scale, int64_t lds_a, int64_t lds_b, uint8_t *__restrict__ out_scale,
     int64_t lds_out) {
-  constexpr bool F8 = Q > 0, MX = Q == 2;
-  constexpr int ES = F8 ? 1 : 2;             // bytes per element
+  constexpr bool F8 = Q == 1 || Q == 2, MX = Q == 2, I8 = Q == 3;
+  constexpr int ES = Q > 0 ? 1 : 2;          // bytes per element
   constexpr int KSTAGE = 64 / ES;            // elements of k per stage
   constexpr int BN = 256, WN = 4, NJ = 2, STAGES = 4;
   constexpr int B_TILE = BN * DL_BK;
@@ -443,6 +447,20 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
                             ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, 0, 0, 0)
                             : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
         }
+    } else if constexpr (I8) {
+      // int32 sums in the fp32 accumulator registers, bit for bit
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const i32x4v av = __builtin_bit_cast(i32x4v, f.a[kk][i]), bv = __builtin_bit_cast(i32x4v, f.b[kk][j]);
+            const i32x16 c = __builtin_bit_cast(i32x16, acc[i][j]);
+            acc[i][j] = __builtin_bit_cast(f32x16, EPI == EPI_BIAS_T
+                                                       ? __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0)
+                                                       : __builtin_amdgcn_mfma_i32_32x32x32_i8(bv, av, c, 0, 0, 0));
+          }
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -528,6 +546,32 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
       }
     }
   }
+  if constexpr (Q == 3) {
+    // the exact int32 sums to fp32 (whole-vector conversion), times A's row
+    // scale and B's row (output column) scale
+    const float *a_sc = static_cast<const float *>(a_scale), *b_sc = static_cast<const float *>(b_scale);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        f32x16 sc;
+        if (EPI == EPI_BIAS_T) {  // lane: column j*32 + frow; rows 8 (r / 4) + 4 fk + r % 4 of row block i
+          const float sbv = b_sc[n0 + wn * 64 + j * 32 + frow];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + fk * 4 + (r & 3);
+            sc[r] = (row < M ? a_sc[row] : 0.f) * sbv;
+          }
+        } else {  // lane: row frow of row block i; columns j*32 + 8 g + 4 fk + 0..3
+          const int row = m0 + wm * 128 + i * 32 + frow;
+          const float fa = row < M ? a_sc[row] : 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)  // scalar loads: a packed block's scales are only 4-B aligned
+            sc[r] = fa * b_sc[n0 + wn * 64 + j * 32 + (r >> 2) * 8 + fk * 4 + (r & 3)];
+        }
+        acc[i][j] = __builtin_convertvector(__builtin_bit_cast(i32x16, acc[i][j]), f32x16) * sc;
+      }
+  }
   gemm_epilogue<EPI, BN, WN>(acc, smem, tid, wm, wn, lane, m0, n0, M, bias, gate, Cv, ldc, out_scale, lds_out);
 }
 
@@ -573,6 +617,13 @@ hipError_t launch_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, 
                            int64_t ldb, const float *b_scale, int M, int N, int K, const float *bias,
                            const float *gate, void *C, int64_t ldc, int epilogue, hipStream_t s) {
   return launch_gemm_t<1>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, a_scale, b_scale, 0, 0, s);
+}
+
+hipError_t launch_gemm_int8(const int8_t *A, int64_t lda, const float *a_scale, const int8_t *B, int64_t ldb,
+                            const float *b_scale, int M, int N, int K, const float *bias, const float *gate, void *C,
+                            int64_t ldc, int epilogue, hipStream_t s) {
+  if (K % 64) return hipErrorInvalidValue;
+  return launch_gemm_t<3>(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue, a_scale, b_scale, 0, 0, s);
 }
 
 hipError_t launch_gemm_mxfp8(const uint8_t *A, int64_t lda, const uint8_t *a_scale, int64_t lds_a,

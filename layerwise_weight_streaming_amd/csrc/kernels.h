@@ -47,6 +47,11 @@ hipError_t launch_v_transpose(const uint16_t *v, int64_t ldv, int T, int d, uint
 hipError_t launch_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B,
                            int64_t ldb, const float *b_scale, int M, int N, int K, const float *bias,
                            const float *gate, void *C, int64_t ldc, int epilogue, hipStream_t s);
+// INT8 GEMM: A [M, K] and B [N, K] int8 codes, exact int32 sums times a_scale[m] *
+// b_scale[n] (fp32, b_scale 16-B aligned); the epilogues and constraints of launch_gemm
+hipError_t launch_gemm_int8(const int8_t *A, int64_t lda, const float *a_scale, const int8_t *B, int64_t ldb,
+                            const float *b_scale, int M, int N, int K, const float *bias, const float *gate, void *C,
+                            int64_t ldc, int epilogue, hipStream_t s);
 // MXFP8 GEMM: A [M, K] and B [N, K] E4M3 codes with E8M0 block scales block-major,
 // a_scale [K / 32][lds_a] (row m at column m), b_scale [K / 32][lds_b] (row n at
 // column n); lds_a >= M, lds_a and lds_b multiples of 4, K % 64 == 0
@@ -76,6 +81,10 @@ hipError_t launch_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols
 // multiples of 8, x 16-B and q 8-B aligned
 hipError_t launch_quant_rows_fp8(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,
                                  float *scale, hipStream_t s);
+// per-row int8 of bf16 x [M, K]: scale[r] = amax_r / 127 (1 for a zero row), q[r, k] =
+// x / scale[r] rounded to nearest-even, clamped to +-127; constraints as above
+hipError_t launch_quant_rows_int8(const uint16_t *x, int64_t ldx, int M, int K, int8_t *q, int64_t ldq,
+                                  float *scale, hipStream_t s);
 // per-row MXFP8 of a bf16 matrix [M, K]: codes [M, ldq], E8M0 scales block-major
 // [K / 32, lds] (rows M .. lds - 1: 127); K % 32 == 0, lds >= M
 hipError_t launch_quant_rows_mx(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,

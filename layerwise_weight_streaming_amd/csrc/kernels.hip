@@ -263,6 +263,9 @@ __global__ __launch_bounds__(256) void dequant_mxfp8_kernel(const u32x4 *__restr
 // encoder (e4m3_code) is shared with the GEMM's MXFP8 epilogue.
 // ---------------------------------------------------------------------------
 
+// I8: the INT8 rule instead (scale = amax / 127, code = the fp32 quotient
+// rounded to nearest-even, clamped to +-127).
+template <bool I8>
 __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t *__restrict__ x, int64_t ldx,
                                                              int K, uint8_t *__restrict__ q, int64_t ldq,
                                                              float *__restrict__ scale) {
@@ -285,18 +288,26 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t *__r
   if (lane == 0) red[wv] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = amax == 0.f ? 1.0f : amax / 448.0f;
+  const float s = amax == 0.f ? 1.0f : amax / (I8 ? 127.0f : 448.0f);
   if (tid == 0) scale[row] = s;
   uint2 *qr = reinterpret_cast<uint2 *>(q + row * ldq);
+  auto code = [&](float v) -> uint32_t {
+    if constexpr (I8) {
+      const float t = __builtin_rintf(v / s);
+      return t != t ? 0u : (uint32_t)(uint8_t)(int8_t)fmaxf(-127.f, fminf(127.f, t));
+    } else {
+      return e4m3_code(v / s);
+    }
+  };
   for (int c = tid; c < nch; c += 256) {
     const u32x4 v = xr[c];
     uint32_t w[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t c0 = e4m3_code(__uint_as_float(v[2 * h] << 16) / s);
-      const uint32_t c1 = e4m3_code(__uint_as_float(v[2 * h] & 0xffff0000u) / s);
-      const uint32_t c2 = e4m3_code(__uint_as_float(v[2 * h + 1] << 16) / s);
-      const uint32_t c3 = e4m3_code(__uint_as_float(v[2 * h + 1] & 0xffff0000u) / s);
+      const uint32_t c0 = code(__uint_as_float(v[2 * h] << 16));
+      const uint32_t c1 = code(__uint_as_float(v[2 * h] & 0xffff0000u));
+      const uint32_t c2 = code(__uint_as_float(v[2 * h + 1] << 16));
+      const uint32_t c3 = code(__uint_as_float(v[2 * h + 1] & 0xffff0000u));
       w[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
     }
     qr[c] = make_uint2(w[0], w[1]);
@@ -495,7 +506,15 @@ hipError_t launch_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols
 hipError_t launch_quant_rows_fp8(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,
                                  float *scale, hipStream_t s) {
   if (M < 1 || K < 8 || K % 8 || ldx % 8 || ldq % 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3(M), dim3(256), 0, s, x, ldx, K, q, ldq, scale);
+  hipLaunchKernelGGL(quant_rows_fp8_kernel<false>, dim3(M), dim3(256), 0, s, x, ldx, K, q, ldq, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_int8(const uint16_t *x, int64_t ldx, int M, int K, int8_t *q, int64_t ldq,
+                                  float *scale, hipStream_t s) {
+  if (M < 1 || K < 8 || K % 8 || ldx % 8 || ldq % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel<true>, dim3(M), dim3(256), 0, s, x, ldx, K,
+                     reinterpret_cast<uint8_t *>(q), ldq, scale);
   return hipGetLastError();
 }
 

@@ -134,4 +134,9 @@ def test_kernel_work_of_the_quantised_forms():
     # no quantisation without W8A8, nor for bf16 and INT8 blocks
     for f in ("bf16", "int8", "fp8", "mxfp8"):
         assert kw("quant_attn", f) == kw("quant_u", f) == 0
-    assert kw("quant_attn", "int8", True) == 0
+    # W8A8 INT8: the adaLN weight dequantised; h, h2, attn and u quantised in their own passes
+    assert kw("dequant_weights", "int8", True) == 18 * d * d + 24 * d
+    assert kw("ln1_modulate", "int8", True) == T * d * 6
+    for n in ("quant_h", "quant_h2", "quant_attn"):
+        assert kw(n, "int8", True) == T * d * 3 + T * 4
+    assert kw("quant_u", "int8", True) == T * 4 * d * 3 + T * 4

@@ -55,16 +55,16 @@ def _check_trace(tr, n, passes, regs):
 
 def _blocks(w, stack, form, which=None):
     """The stack's blocks in the per-tensor FP8 form (libdlo's quantizer, checked equal to
-    the oracle's) or the MXFP8 form (the oracle's quantizer)."""
+    the oracle's) or the MXFP8 or INT8 form (the oracle's quantizer)."""
     if form == "fp8":
         return fp8_blocks(w, stack, which)
-    return [quant.quantize_block(ps, "mxfp8") if which is None or b in which else ps
+    return [quant.quantize_block(ps, form) if which is None or b in which else ps
             for b, ps in enumerate(stack.blocks)]
 
 
-@pytest.mark.parametrize("form", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("form", ["fp8", "mxfp8", "int8"])
 def test_w8a8_single_block_matches_the_w8a8_oracle(form):
-    """One FP8 or MXFP8 block (d = 256, 4 heads, 64 tokens), one pass."""
+    """One FP8, MXFP8 or INT8 block (d = 256, 4 heads, 64 tokens), one pass."""
     require_gpu()
     w = synth.WORKLOADS["tiny"]
     stack = synth.make_stack(w, 21, 1)
@@ -81,17 +81,26 @@ def test_w8a8_single_block_matches_the_w8a8_oracle(form):
     e_max = rel_err(x_gpu - x0, ref8 - x0)
     e8, e16 = _rms_rel(x_gpu - x0, ref8 - x0), _rms_rel(x_gpu - x0, ref16 - x0)
     say(f"W8A8 {form} block: update max {e_max:.3e}; rms vs W8A8 oracle {e8:.3e}, vs W8A16 oracle {e16:.3e}")
-    assert e8 <= 1e-2 and e_max <= 2 * TOL
-    assert e8 < 0.25 * e16
+    if form == "int8":
+        # int8 activations (step amax / 127) move a block's output only ~1.4 % (rms) from the
+        # W8A16 result, while the int8 decisions taken on the GPU's bf16 inputs (which differ
+        # from the oracle's by bf16 rounding upstream, the bf16 copy of the adaLN weight
+        # included) already account for ~1 %: closer to its own oracle, not 4x closer
+        assert e8 <= 1.5e-2 and e_max <= 2 * TOL
+        assert e8 < 0.85 * e16
+    else:
+        assert e8 <= 1e-2 and e_max <= 2 * TOL
+        assert e8 < 0.25 * e16
 
 
-@pytest.mark.parametrize("form", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("form", ["fp8", "mxfp8", "int8"])
 def test_w8a8_block_is_the_op_sequence(form):
     """The streamed W8A8 block computes, bit for bit, what the C-ABI ops compute when
     called one by one in the block's order (each op is checked against the oracle in
     test_gpu_fp8_ops.py, test_gpu_quant_weights.py and test_gpu_ops.py): adaLN (FP8:
-    on the E4M3 W_ada; MXFP8: on its dequantised bf16 copy), LN1 + modulate, the input
-    quantisation of h (per-row E4M3, or MXFP8 blocks), the q/k and V^T products (the
+    on the E4M3 W_ada; MXFP8, INT8: on its dequantised bf16 copy), LN1 + modulate, the
+    input quantisation of h (per-row E4M3 or int8, or MXFP8 blocks), the q/k and V^T
+    products (the
     v part's MXFP8 scales a column slice of the fused weight's), attention, the input
     quantisation of a, the gated out product, LN2 + modulate, that of h2, the fc1
     product with GELU, that of u, the gated fc2 product."""
@@ -119,7 +128,8 @@ def test_w8a8_block_is_the_op_sequence(form):
                          mod.data_ptr(), ws.data_ptr(), ws.numel(), s)
     else:
         w_ada = torch.empty(6 * d * d, dtype=torch.int16, device="cuda")
-        dlo.op_dequant_mxfp8(ptr("adaln.weight"), 6 * d, d, ptr("adaln.weight_scale"), w_ada.data_ptr(), s)
+        deq = dlo.op_dequant_mxfp8 if form == "mxfp8" else dlo.op_dequant_int8
+        deq(ptr("adaln.weight"), 6 * d, d, ptr("adaln.weight_scale"), w_ada.data_ptr(), s)
         dlo.op_adaln(w_ada.data_ptr(), ptr("adaln.bias"), c.data_ptr(), 6 * d, d, mod.data_ptr(), ws.data_ptr(),
                      ws.numel(), s)
     m = lambda i: mod.data_ptr() + 4 * i * d
@@ -138,6 +148,8 @@ def test_w8a8_block_is_the_op_sequence(form):
     def quant(src, K):
         if form == "fp8":
             dlo.op_quantize_rows_fp8(src.data_ptr(), K, T, K, codes.data_ptr(), K, scales.data_ptr(), s)
+        elif form == "int8":
+            dlo.op_quantize_rows_int8(src.data_ptr(), K, T, K, codes.data_ptr(), K, scales.data_ptr(), s)
         else:
             dlo.op_quantize_rows_mxfp8(src.data_ptr(), K, T, K, codes.data_ptr(), K, mx_scales.data_ptr(), T64, s)
 
@@ -145,6 +157,9 @@ def test_w8a8_block_is_the_op_sequence(form):
         if form == "fp8":
             dlo.op_gemm_fp8(codes.data_ptr(), K, scales.data_ptr(), ptr(wname) + row0 * K, K,
                             ptr(wname + "_scale"), T, N, K, bias, gate, C, ldc, epi, s)
+        elif form == "int8":   # per-output-row fp32 scales: the slice's rows
+            dlo.op_gemm_int8(codes.data_ptr(), K, scales.data_ptr(), ptr(wname) + row0 * K, K,
+                             ptr(wname + "_scale") + 4 * row0, T, N, K, bias, gate, C, ldc, epi, s)
         else:
             dlo.op_gemm_mxfp8(codes.data_ptr(), K, mx_scales.data_ptr(), T64, ptr(wname) + row0 * K, K,
                               ptr(wname + "_scale") + row0, rows_of[wname], T, N, K, bias, gate, C, ldc, epi, s)
@@ -169,7 +184,7 @@ def test_w8a8_block_is_the_op_sequence(form):
     assert np.array_equal(x_ops.view(np.uint32), x_fwd.view(np.uint32))
 
 
-@pytest.mark.parametrize("form", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("form", ["fp8", "mxfp8", "int8"])
 @pytest.mark.parametrize("name,n_blocks,tokens,which", [
     ("tiny", None, None, None),                 # every block quantised, 2 passes, odd count
     ("8blk", None, None, {0, 2, 3, 5}),         # quantised and bf16 blocks mixed
@@ -228,7 +243,7 @@ def test_w8a8_leaves_bf16_blocks_alone():
     r.close()
 
 
-@pytest.mark.parametrize("form", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("form", ["fp8", "mxfp8", "int8"])
 @pytest.mark.parametrize("tokens", [77, 200])
 def test_w8a8_ragged_token_counts(form, tokens):
     """Token counts off the 64-row grid: the quantizers' rows, the V^T padding and the

@@ -480,13 +480,13 @@ def test_quantised_schema_plan_and_pack(form):
     for g in range(len(bp.groups)):
         for r in range(k):
             assert st.shard(0, g, r).tobytes() == sh[g][r].tobytes()
-    # the workspace holds all five dequantised weights (18 d^2 bf16); for MXFP8 also
-    # the W8A8 input's E4M3 codes [T, 4d] and E8M0 scales [4d / 32, T64]
+    # the workspace holds all five dequantised weights (18 d^2 bf16) and the W8A8
+    # input's codes [T, 4d] with its scales (INT8 fp32 [T], MXFP8 E8M0 [4d / 32, T64])
     p_bf = dlo.Plan([(d, 4, synth.block_params(1, 1, d))], k)
     al = lambda n: (n + 255) // 256 * 256
     for T in (64, 1000):
         T64 = (T + 63) // 64 * 64
-        extra = al(4 * T * d) + al(4 * d // 32 * T64) if form == "mxfp8" else 0
+        extra = al(4 * T * d) + (al(4 * d // 32 * T64) if form == "mxfp8" else al(4 * T))
         assert p.workspace_bytes(T) - p_bf.workspace_bytes(T) == al(36 * d * d) + extra
     if form == "mxfp8":
         with pytest.raises(dlo.DLOError):
