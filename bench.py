@@ -241,20 +241,76 @@ def measure_link(torch, dev, gib=1, reps=4):
     return reps * n / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(w, seed, n_blocks, rows=128):
+def cpu_facts():
+    """Host CPU model (lscpu, /proc/cpuinfo), usable cores, and the BLAS library numpy runs on."""
+    import subprocess
+    facts = {"nproc": len(os.sched_getaffinity(0))}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            k, _, v = ln.partition(":")
+            if k.strip() in ("Model name", "Vendor ID", "Socket(s)", "Core(s) per socket", "Thread(s) per core"):
+                facts["lscpu_" + k.strip().lower().replace(" ", "_").replace("(s)", "s")] = v.strip()
+    except Exception:
+        pass
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                facts["cpuinfo_model"] = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        facts["blas"] = [{"api": i.get("internal_api"), "version": i.get("version"),
+                          "threads": i.get("num_threads"), "arch": i.get("architecture"),
+                          "lib": os.path.basename(i.get("filepath", ""))} for i in threadpool_info()]
+    except Exception:
+        facts["blas"] = None
+    return facts
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count()
+
+
+def cpu_tiny_stack(seed, threads):
+    """The oracle's full tiny stack (3 blocks, d = 256, 64 tokens, 2 passes) with the
+    BLAS pool limited to ``threads``: blocks/s over repetitions totalling >= 1 s."""
+    import synth
+    from oracle import forward as of
+    from threadpoolctl import threadpool_limits
+    w = synth.WORKLOADS["tiny"]
+    st = synth.make_stack(w, seed)
+    heads = [w.heads(b) for b in range(w.n_blocks)]
+    with threadpool_limits(limits=threads):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            of.forward_stack(st.x, st.c, st.blocks, heads, w.passes)
+            reps += 1
+            if time.perf_counter() - t0 >= 1.0:
+                break
+        dt = (time.perf_counter() - t0) / reps
+    return {"threads": threads, "blocks_per_s": w.n_blocks * w.passes / dt,
+            "tokens_per_s": w.tokens * w.passes / dt, "s_per_stack": dt}
+
+
+def cpu_baseline(w, seed, n_blocks, rows=640, full_block=False):
     """The oracle, untouched, on a bounded sample: sampled output rows of the first block.
 
     dit_block_rows computes LN1 and the k/v projections for every token and the
     rest of the block for ``rows`` query rows; its FLOPs are counted and the
-    rate is scaled to whole blocks by the ratio of FLOPs.
+    rate is scaled to whole blocks by the ratio of FLOPs.  full_block: also time
+    the oracle's whole first block (dit_block at the workload's full shape) and
+    extrapolate it to the stack, labelled as such.
     """
     import synth
     from oracle import forward as of
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count()
+    cores = blas_threads()
     d, T, H = w.width(0), w.tokens, w.heads(0)
     params = synth.block_params(seed, 0, d)
     x = synth.activations(seed, T, w.D)
@@ -272,13 +328,25 @@ def cpu_baseline(w, seed, n_blocks, rows=128):
     f_sample = 2 * T * d * 2 * d + rows * (2 * d * d + 4 * T * d + 2 * d * d + 16 * d * d) + 12 * d * d
     frac = f_sample / block_flops(d, T)
     blocks_per_s = frac / dt
-    return {"value": blocks_per_s, "unit": "blocks/s", "cores": cores, "kind": "oracle",
-            # a pass of the n-block stack moves T tokens
-            "tokens_per_s": blocks_per_s * T / n_blocks,
-            "sample": (f"float64 oracle, first block of the {w.name} stack (d={d}, T={T}): "
-                       f"k/v for all tokens + {rows} sampled query rows, {dt:.3g} s per sample "
-                       f"(mean of {reps}) for {frac * 100:.2f}% of a block's FLOPs, scaled by that "
-                       f"FLOP fraction")}
+    out = {"value": blocks_per_s, "unit": "blocks/s", "cores": cores, "kind": "oracle",
+           # a pass of the n-block stack moves T tokens
+           "tokens_per_s": blocks_per_s * T / n_blocks,
+           "sample": (f"float64 oracle, first block of the {w.name} stack (d={d}, T={T}): "
+                      f"k/v for all tokens + {rows} sampled query rows, {dt:.3g} s per sample "
+                      f"(mean of {reps}) for {frac * 100:.2f}% of a block's FLOPs, scaled by that "
+                      f"FLOP fraction"),
+           "host": cpu_facts(),
+           "tiny_full_stack": [cpu_tiny_stack(seed, 1), cpu_tiny_stack(seed, cores)]}
+    if full_block:
+        t0 = time.perf_counter()
+        of.dit_block(x, c, P, H)
+        tb = time.perf_counter() - t0
+        out["full_block"] = {"s_per_block": tb, "blocks_per_s": 1.0 / tb,
+                             "extrapolated_stack_s": tb * n_blocks * w.passes,
+                             "note": (f"one whole block of the {w.name} stack by the float64 oracle at full "
+                                      f"shape (d={d}, T={T}); the stack time is extrapolated "
+                                      f"({n_blocks} blocks x {w.passes} passes), not run")}
+    return out
 
 
 def main():
@@ -307,6 +375,10 @@ def main():
                     help="first run one plain device-to-device copy of this many MiB "
                          "(a known-size kernel to scale HBM counters by)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full-block", action="store_true",
+                    help="also time the oracle's whole first block at full shape (minutes for Super)")
+    ap.add_argument("--resident-steps", type=int, default=None,
+                    help="timed all-resident steps for the run-based cross-check (default min(steps, 5))")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the streamed == resident bit-exact check")
     args = ap.parse_args()
@@ -469,7 +541,10 @@ def main():
                 "link_peak_GBps": LINK_PEAK_GBS, "measured_link_GBps": link,
                 "frac_of_link_peak": (avg.get("h2d_busy_GBps") or 0) / LINK_PEAK_GBS},
         "mfma_util": {"busy": avg.get("mfma_util_busy"), "wall": avg.get("mfma_util_wall"),
-                      "peak_TFLOPs": PEAK_BF16_TFLOPS},
+                      "peak_TFLOPs": PEAK_BF16_TFLOPS,
+                      "basis": ("bf16-equivalent: every block FLOP against the bf16 dense peak, although "
+                                "the linears run on 8-bit MFMA" if w8a8 else
+                                "every block FLOP against the bf16 dense peak")},
         "overlap_eff": avg.get("overlap_eff"), "wall_eff": avg.get("wall_eff"),
         "bound_resource": bound,
         "steady_window": {k: avg.get(k) for k in ("window_ms", "compute_busy_ms", "copy_busy_ms")},
@@ -490,33 +565,39 @@ def main():
         r.set_inputs(x0, c0)
         r.make_resident()
         r.synchronize()
-        torch.cuda.synchronize(dev)
-        t0 = time.perf_counter()
         r.forward(P, flags=cflags, resident=True, want_run=False)
-        r.synchronize()
-        torch.cuda.synchronize(dev)
-        t_res = time.perf_counter() - t0
         xr = r.x_host()
-        r.free_resident()
         result["streamed_equals_resident"] = bool(np.array_equal(xs.view(np.uint32), xr.view(np.uint32)))
         result["finite"] = bool(np.isfinite(xs).all())
-        # run-based cross-check of the overlap: a resident step is the compute
-        # alone; the copy stream's busy time per streamed step is the copy alone
-        t_str = wall / args.steps
+        # run-based cross-check of the overlap: an all-resident step is the compute
+        # alone; the copy stream's busy time per streamed step is the copy alone.
+        # Both step times are GPU times from the same HIP events (first event to the
+        # last block's end), medians over timed steps after a warm step each.
+        n_res = args.resident_steps if args.resident_steps is not None else min(args.steps, 5)
+        res_ms = []
+        for _ in range(max(n_res, 1)):
+            run = r.forward(P, flags=dlo.TRACE_TIMING | cflags, resident=True)
+            res_ms.append(max(e["t_compute_end"] for e in run.trace()))
+            run.close()
+        r.free_resident()
+        t_res = float(np.median(res_ms)) * 1e-3
+        t_str = float(np.median(step_ms)) * 1e-3
         t_copy = avg.get("copy_busy_step_ms", 0.0) * 1e-3
         result["cross_check"] = {
             "streamed_step_ms": t_str * 1e3, "resident_step_ms": t_res * 1e3,
+            "resident_steps": len(res_ms), "streamed_steps": len(step_ms),
             "copy_busy_step_ms": t_copy * 1e3,
             "run_overlap": (t_copy + t_res - t_str) / max(min(t_copy, t_res), 1e-9),
             "streaming_cost": t_str / t_res - 1.0,
+            "basis": "medians of per-step GPU times (HIP events) over the timed streamed and resident steps",
         }
         log(f"verify: equal={result['streamed_equals_resident']}; resident step {t_res * 1e3:.0f} ms "
-            f"vs streamed {t_str * 1e3:.0f} ms")
+            f"vs streamed {t_str * 1e3:.0f} ms (medians of {len(res_ms)} and {len(step_ms)} steps)")
 
     r.close()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
-        result["cpu_baseline"] = cpu_baseline(w, args.seed, n)
+        result["cpu_baseline"] = cpu_baseline(w, args.seed, n, full_block=args.cpu_full_block)
     print(json.dumps(result), flush=True)
 
 

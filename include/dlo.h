@@ -188,7 +188,9 @@ int dlo_host_store_info(const dlo_host_store *store, int32_t *pinned_blocks,
                         int64_t *pinned_bytes, int32_t *staged_blocks);
 
 /* Destroys the store.  Copies that read it must have completed: the caller
- * synchronises the copy stream of every run that used it first. */
+ * synchronises the copy stream of every run that used it first.  The store's
+ * staging stream (host fills of the staging buffers) is drained here before any
+ * memory is freed. */
 void dlo_host_store_destroy(dlo_host_store *store);
 
 /* Packs blocks [b_begin, b_end): blocks[i] describes block b_begin + i and must
@@ -323,9 +325,11 @@ typedef struct {
  * everything the caller enqueued on the compute stream before the call happens
  * before the run, and the copy stream waits for it too.  Each call starts afresh
  * at block 0 in slot 0.  Caller memory must stay valid until the compute stream
- * has drained.  With a fully pinned store the call returns without waiting; when
- * blocks are staged, the host fills each staging buffer in step order, so the
- * call returns once the last staged block has been handed to the copy stream.
+ * has drained.  The call returns once everything is enqueued, without waiting
+ * for any copy or kernel, also when blocks are staged: a staged block's fill of
+ * its pinned staging buffer is a host function on the store's own staging
+ * stream (ordered after the buffer's previous DMA), and the block's DMA on the
+ * copy stream waits for that fill.
  * If run_out is non-NULL it receives a handle for dlo_slot_trace (free with
  * dlo_run_destroy); otherwise the library releases the run's resources once it
  * has completed. */
@@ -482,8 +486,9 @@ int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const 
  *               [M, M64) (M rounded up to 64) are 0, columns from M64 on are
  *               not written; ldc >= M64 and ldc % 8 == 0.  The block computes
  *               its v part this way, in the layout dlo_op_attention reads.
- * N % 256 == 0, K % 64 == 0, M >= 1; lda, ldb multiples of 8; C, bias and gate
- * 16-B aligned and ldc % 4 == 0 (else DLO_E_UNSUPPORTED). */
+ * N % 256 == 0, K % 64 == 0, M >= 1; lda, ldb multiples of 8; C 16-B aligned,
+ * bias and gate 4-B aligned (as the fp32 parameters packed back to back in a slot
+ * are) and ldc % 4 == 0 (else DLO_E_UNSUPPORTED). */
 enum { DLO_EPI_BIAS = 0, DLO_EPI_BIAS_GELU = 1, DLO_EPI_GATED_RESIDUAL = 2, DLO_EPI_BIAS_T = 3 };
 int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int32_t M,
                 int32_t N, int32_t K, const float *bias, const float *gate, void *C, int64_t ldc,
@@ -509,7 +514,7 @@ int dlo_op_quantize_rows_fp8(const uint16_t *x, int64_t ldx, int32_t M, int32_t 
  * per-tensor scale, [Doc] "Request and loading constraints"); every product is
  * exact and accumulates in fp32 on v_mfma_f32_32x32x64_f8f6f4.  All device,
  * caller-owned.  N % 256 == 0, K % 64 == 0, lda and ldb multiples of 16, A, B,
- * C, bias and gate 16-B aligned, ldc as for dlo_op_gemm, else
+ * C 16-B aligned, bias and gate 4-B aligned, ldc as for dlo_op_gemm, else
  * DLO_E_UNSUPPORTED. */
 int dlo_op_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const uint8_t *B, int64_t ldb,
                     const float *b_scale, int32_t M, int32_t N, int32_t K, const float *bias,
@@ -533,7 +538,7 @@ int dlo_op_quantize_rows_int8(const uint16_t *x, int64_t ldx, int32_t M, int32_t
  * aligned); the sums are exact int32 on v_mfma_i32_32x32x32_i8 (|sum| <= K *
  * 127^2 < 2^31 for K < 133 000), converted to fp32 once.  All device,
  * caller-owned.  N % 256 == 0, K % 64 == 0, lda and ldb multiples of 16, A, B,
- * C, bias and gate 16-B aligned, ldc as for dlo_op_gemm, else
+ * C 16-B aligned, bias and gate 4-B aligned, ldc as for dlo_op_gemm, else
  * DLO_E_UNSUPPORTED. */
 int dlo_op_gemm_int8(const int8_t *A, int64_t lda, const float *a_scale, const int8_t *B, int64_t ldb,
                      const float *b_scale, int32_t M, int32_t N, int32_t K, const float *bias,

@@ -243,9 +243,12 @@ struct dlo_host_store {
   std::vector<uint8_t> pinned;                 // per block: shards in pinned memory
   std::vector<std::vector<int64_t>> shard_at;  // per block: byte offset of (g * k + r)
   std::vector<uint8_t> packed;                 // per block flag
-  // two bounded pinned staging buffers (one slot each) for pageable blocks
+  // two bounded pinned staging buffers (one slot each) for pageable blocks, and
+  // the library's own stream on which host functions fill them
   char *staging[2] = {nullptr, nullptr};
-  hipEvent_t staging_free[2] = {nullptr, nullptr};
+  hipEvent_t staging_free[2] = {nullptr, nullptr};    // DMA out of buffer j done
+  hipEvent_t staging_filled[2] = {nullptr, nullptr};  // host fill of buffer j done
+  hipStream_t stage_stream = nullptr;
   int64_t staging_bytes = 0;
   int64_t staged_uses = 0;
   const void *shard(int b, int g, int r) const {
@@ -308,15 +311,15 @@ struct Step {
   int64_t next_step;                                  // step that reads the prefetch, -1 if none
 };
 
-// [Jul] "Slot Tracking: i%2 + Dynamic Correction": each hook starts at i % 2 and
-// takes the slot its predecessor (circularly) prefetched into, once there is one.
-// With n_res resident blocks ([Doc] "Validation coverage": resident-layer
-// requests), blocks 0 .. n_res-1 read no slot; the hooks of the streamed blocks
-// are linked circularly among themselves and follow the same rule.
+// [Jul] "Slot Tracking: i%2 + Dynamic Correction": the hooks form a ring; a step
+// reads the slot its ring predecessor last prefetched into, or its own parity
+// h % 2 while the predecessor has prefetched nothing, and prefetches the next
+// block of the ring into the other slot.  With n_res resident blocks ([Doc]
+// "Validation coverage": resident-layer requests), blocks 0 .. n_res-1 read no
+// slot and the ring holds only the streamed blocks.
 std::vector<Step> hook_steps(int n, int passes, int n_res) {
   const int m = n - n_res;
-  std::vector<int> cur((size_t)std::max(m, 1)), pref((size_t)std::max(m, 1), -1);
-  for (int h = 0; h < m; ++h) cur[h] = h % 2;
+  std::vector<int> pref((size_t)std::max(m, 1), -1);   // hook -> slot of its latest prefetch
   const int64_t total = (int64_t)n * passes, streamed_total = (int64_t)m * passes;
   std::vector<Step> out;
   out.reserve((size_t)total);
@@ -326,11 +329,10 @@ std::vector<Step> hook_steps(int n, int passes, int n_res) {
     Step s{t, p, i, -1, -1, -1, -1};
     if (i >= n_res) {
       const int h = i - n_res, prev = (h + m - 1) % m;
-      if (pref[prev] >= 0) cur[h] = pref[prev];
-      s.slot = cur[h];
+      s.slot = pref[prev] >= 0 ? pref[prev] : h % 2;
       if (u + 1 < streamed_total) {
         s.next_block = n_res + (h + 1) % m;
-        s.next_slot = 1 - cur[h];
+        s.next_slot = 1 - s.slot;
         pref[h] = s.next_slot;
       }
       ++u;
@@ -770,13 +772,18 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 
 void dlo_host_store_destroy(dlo_host_store *store) {
   if (!store) return;
+  // drain first: host fills still queued on the staging stream, then the DMAs
+  // that read the staging buffers
+  if (store->stage_stream) (void)hipStreamSynchronize(store->stage_stream);
   for (int j = 0; j < 2; ++j) {
     if (store->staging_free[j]) {
       (void)hipEventSynchronize(store->staging_free[j]);
       (void)hipEventDestroy(store->staging_free[j]);
     }
+    if (store->staging_filled[j]) (void)hipEventDestroy(store->staging_filled[j]);
     if (store->staging[j]) (void)hipHostFree(store->staging[j]);
   }
+  if (store->stage_stream) (void)hipStreamDestroy(store->stage_stream);
   for (size_t b = 0; b < store->mem.size(); ++b) {
     char *m = store->mem[b];
     if (!m) continue;
@@ -800,8 +807,12 @@ int ensure_staging(dlo_host_store *st) {
                   hipGetErrorString(e));
     st->staging[j] = static_cast<char *>(m);
     e = hipEventCreateWithFlags(&st->staging_free[j], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st->staging_filled[j], hipEventDisableTiming);
     if (e != hipSuccess) return fail(DLO_E_HIP, "hipEventCreate: %s", hipGetErrorString(e));
   }
+  // default priority, not synchronising with the null stream
+  hipError_t e = hipStreamCreateWithFlags(&st->stage_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) return fail(DLO_E_HIP, "hipStreamCreate (staging): %s", hipGetErrorString(e));
   st->staging_bytes = bytes;
   return DLO_OK;
 }
@@ -1004,11 +1015,27 @@ const void *from_staging(const dlo_host_store *, const char *staging, int, int, 
   return staging + off;
 }
 
-// One block into `dst` on stream s.  A pinned block is copied directly; a pageable
-// block first goes (host memcpy, several threads) into the staging buffer whose
-// previous DMA has completed, laid out as the slot image, then is DMA'd from there.
-// Returns a dlo status (host-side waits can fail too).
-// `begin` (optional) is recorded on s just before the DMAs are enqueued.
+// Host function run in stream order on the store's staging stream: copies one
+// block's shards (pageable memory) into a pinned staging buffer, laid out as the
+// slot image.  It makes no HIP call.
+struct StageJob {
+  std::vector<CopyTask> tasks;
+};
+
+void stage_fill(void *p) {
+  StageJob *job = static_cast<StageJob *>(p);
+  run_copies(job->tasks);
+  delete job;
+}
+
+// One block into `dst` on stream s, enqueued without waiting on the host.  A
+// pinned block is copied directly.  A pageable block goes through staging
+// buffer j = (use count) mod 2 ([Doc] "Rank-local path without DLO AllGather":
+// two bounded pinned staging slots): on the staging stream, wait until the
+// buffer's previous DMA has drained, fill it on the host (a host function,
+// several threads), record FILLED[j]; on s, wait for FILLED[j], DMA the image
+// into dst, record FREE[j].  The fill of one buffer overlaps the DMA out of the
+// other.  `begin` (optional) is recorded on s just before the DMAs.
 int place(const dlo_plan *plan, dlo_host_store *st, int b, char *dst, hipStream_t s,
           hipEvent_t begin = nullptr) {
   if (st->pinned[b]) {
@@ -1021,18 +1048,28 @@ int place(const dlo_plan *plan, dlo_host_store *st, int b, char *dst, hipStream_
   int rc = ensure_staging(st);
   if (rc) return rc;
   const int j = (int)(st->staged_uses++ & 1);
-  // wait on the host until the staging buffer's previous DMA has drained
-  rc = check_hip(hipEventSynchronize(st->staging_free[j]), "hipEventSynchronize(staging)");
-  if (rc) return rc;
   const BlockPlan &bp = plan->blocks[b];
-  std::vector<CopyTask> tasks;
+  StageJob *job = new (std::nothrow) StageJob;
+  if (!job) return fail(DLO_E_HOSTMEM, "out of host memory");
   for (int g = 0; g < bp.n_groups; ++g) {
     const int64_t sb = bp.gshard[g] * elt_bytes(bp.gdtype[g]);
     for (int r = 0; r < plan->k && sb > 0; ++r)
-      tasks.push_back({st->staging[j] + bp.gregion[g] + r * sb,
-                       static_cast<const char *>(st->shard(b, g, r)), sb});
+      job->tasks.push_back({st->staging[j] + bp.gregion[g] + r * sb,
+                            static_cast<const char *>(st->shard(b, g, r)), sb});
   }
-  run_copies(tasks);
+  rc = check_hip(hipStreamWaitEvent(st->stage_stream, st->staging_free[j], 0), "hipStreamWaitEvent(staging)");
+  if (rc) {
+    delete job;
+    return rc;
+  }
+  rc = check_hip(hipLaunchHostFunc(st->stage_stream, stage_fill, job), "hipLaunchHostFunc(staging)");
+  if (rc) {
+    delete job;
+    return rc;
+  }
+  rc = check_hip(hipEventRecord(st->staging_filled[j], st->stage_stream), "hipEventRecord(staging)");
+  if (!rc) rc = check_hip(hipStreamWaitEvent(s, st->staging_filled[j], 0), "hipStreamWaitEvent(staging)");
+  if (rc) return rc;
   if (begin) {
     rc = check_hip(hipEventRecord(begin, s), "hipEventRecord");
     if (rc) return rc;
@@ -1528,8 +1565,8 @@ int dlo_op_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, 
   if ((int64_t)256 * lda * 2 >= (int64_t)1 << 31 || (int64_t)256 * ldb * 2 >= (int64_t)1 << 31 ||
       (int64_t)256 * ldc * 4 >= (int64_t)1 << 31)
     return fail(DLO_E_UNSUPPORTED, "gemm: leading dimension too large for 32-bit tile offsets");
-  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 16 || (gate && (uintptr_t)gate % 16))
-    return fail(DLO_E_UNSUPPORTED, "gemm: C, bias and gate must be 16-B aligned and ldc %% 4 == 0");
+  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 4 || (gate && (uintptr_t)gate % 4))
+    return fail(DLO_E_UNSUPPORTED, "gemm: C 16-B, bias and gate 4-B aligned, ldc %% 4 == 0");
   int rc = check_hip(dlo::launch_gemm(A, lda, B, ldb, M, N, K, bias, gate, C, ldc, epilogue,
                                       (hipStream_t)stream), "gemm");
   return rc ? rc : ok();
@@ -1561,9 +1598,9 @@ int dlo_op_gemm_fp8(const uint8_t *A, int64_t lda, const float *a_scale, const u
   if ((int64_t)256 * lda >= (int64_t)1 << 31 || (int64_t)256 * ldb >= (int64_t)1 << 31 ||
       (int64_t)256 * ldc * 4 >= (int64_t)1 << 31)
     return fail(DLO_E_UNSUPPORTED, "gemm_fp8: leading dimension too large for 32-bit tile offsets");
-  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 16 || (gate && (uintptr_t)gate % 16) ||
+  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 4 || (gate && (uintptr_t)gate % 4) ||
       (uintptr_t)A % 16 || (uintptr_t)B % 16)
-    return fail(DLO_E_UNSUPPORTED, "gemm_fp8: A, B, C, bias and gate must be 16-B aligned and ldc %% 4 == 0");
+    return fail(DLO_E_UNSUPPORTED, "gemm_fp8: A, B and C 16-B, bias and gate 4-B aligned, ldc %% 4 == 0");
   int rc = check_hip(dlo::launch_gemm_fp8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc,
                                           epilogue, (hipStream_t)stream), "gemm_fp8");
   return rc ? rc : ok();
@@ -1595,9 +1632,9 @@ int dlo_op_gemm_int8(const int8_t *A, int64_t lda, const float *a_scale, const i
   if ((int64_t)256 * lda >= (int64_t)1 << 31 || (int64_t)256 * ldb >= (int64_t)1 << 31 ||
       (int64_t)256 * ldc * 4 >= (int64_t)1 << 31)
     return fail(DLO_E_UNSUPPORTED, "gemm_int8: leading dimension too large for 32-bit tile offsets");
-  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 16 || (gate && (uintptr_t)gate % 16) ||
+  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 4 || (gate && (uintptr_t)gate % 4) ||
       (uintptr_t)A % 16 || (uintptr_t)B % 16 || (uintptr_t)a_scale % 4 || (uintptr_t)b_scale % 4)
-    return fail(DLO_E_UNSUPPORTED, "gemm_int8: A, B, C, bias and gate must be 16-B aligned and ldc %% 4 == 0");
+    return fail(DLO_E_UNSUPPORTED, "gemm_int8: A, B and C 16-B, bias, gate and scales 4-B aligned, ldc %% 4 == 0");
   int rc = check_hip(dlo::launch_gemm_int8(A, lda, a_scale, B, ldb, b_scale, M, N, K, bias, gate, C, ldc,
                                            epilogue, (hipStream_t)stream), "gemm_int8");
   return rc ? rc : ok();
@@ -1668,9 +1705,9 @@ int dlo_op_gemm_mxfp8(const uint8_t *A, int64_t lda, const uint8_t *a_scales, in
   if ((int64_t)256 * lda >= (int64_t)1 << 31 || (int64_t)256 * ldb >= (int64_t)1 << 31 ||
       (int64_t)256 * ldc * 4 >= (int64_t)1 << 31 || (int64_t)(K / 32) * std::max(lds_a, lds_b) >= (int64_t)1 << 31)
     return fail(DLO_E_UNSUPPORTED, "gemm_mxfp8: leading dimension too large for 32-bit offsets");
-  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 16 || (gate && (uintptr_t)gate % 16) ||
+  if (ldc % 4 || (uintptr_t)C % 16 || (uintptr_t)bias % 4 || (gate && (uintptr_t)gate % 4) ||
       (uintptr_t)A % 16 || (uintptr_t)B % 16 || (uintptr_t)a_scales % 4 || (uintptr_t)b_scales % 4)
-    return fail(DLO_E_UNSUPPORTED, "gemm_mxfp8: A, B, C, bias and gate 16-B, scales 4-B aligned, ldc %% 4 == 0");
+    return fail(DLO_E_UNSUPPORTED, "gemm_mxfp8: A, B and C 16-B, bias, gate and scales 4-B aligned, ldc %% 4 == 0");
   int rc = check_hip(dlo::launch_gemm_mxfp8(A, lda, a_scales, lds_a, B, ldb, b_scales, lds_b, M, N, K, bias, gate,
                                             C, ldc, epilogue, (hipStream_t)stream), "gemm_mxfp8");
   return rc ? rc : ok();

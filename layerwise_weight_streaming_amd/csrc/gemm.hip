@@ -45,6 +45,11 @@ __device__ __forceinline__ int dl_lds_off(int row, int chunk) {  // element offs
   return row * DL_BK + ((chunk ^ dl_swz(row)) << 3);
 }
 
+// Four consecutive fp32 values from an address that is only 4-B aligned: the
+// block's fp32 parameters sit back to back in a slot, so a bias or a gate
+// vector may start at any multiple of 4 bytes.
+__device__ __forceinline__ float4 load4(const float *p) { return make_float4(p[0], p[1], p[2], p[3]); }
+
 // Epilogue of a 256 x BN tile held by 2 x WN waves (acc: the wave's 128 x BN/WN
 // sub-tile in 32x32 MFMA tiles, transposed except for EPI_BIAS_T).  smem: at
 // least 256 x (BN + 8) bf16 (bias epilogues; BN x (256 + 8) for EPI_BIAS_T) or
@@ -107,7 +112,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = wn * (BN / WN) + j * 32 + g * 8 + fk * 4;
-        const float4 bv = *reinterpret_cast<const float4 *>(&bias[n0 + col]);
+        const float4 bv = load4(&bias[n0 + col]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v0 = acc[i][j][g * 4 + 0] + bv.x, v1 = acc[i][j][g * 4 + 1] + bv.y;
@@ -184,8 +189,8 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int col = wn * (BN / WN) + j * 32 + g * 8 + fk * 4;
-            const float4 bv = *reinterpret_cast<const float4 *>(&bias[n0 + col]);
-            const float4 gv = *reinterpret_cast<const float4 *>(&gate[n0 + col]);
+            const float4 bv = load4(&bias[n0 + col]);
+            const float4 gv = load4(&gate[n0 + col]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               float4 v;

@@ -10,8 +10,8 @@ Contents, each function citing the passage it follows:
 * ``oracle.plan``     -- flatten-by-dtype, ceil-div sharding with zero padding,
                          reassembly at all-gather offsets, slot sizing, slot
                          digests (the race-detector definition).
-* ``oracle.schedule`` -- the two-slot hook rule (``i % 2`` plus the
-                         ``_prefetched_slot`` correction), a static-rule
+* ``oracle.schedule`` -- the two-slot hook rule (parity, corrected by the
+                         ring predecessor's prefetch), a static-rule
                          negative control, and a happens-before checker for
                          programs of copy / compute / event operations.
 * ``oracle.forward``  -- the DiT stack with every weight resident, in float64

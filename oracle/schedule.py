@@ -1,10 +1,14 @@
 """Oracle: two-slot schedule of the streamed stack, and a hazard checker.
 
-Hook rule, from [Jul] "Slot Tracking: i%2 + Dynamic Correction": hook i starts
-with ``current_slot = i % 2``; whenever the previous hook (circularly, block
-i-1 mod n) has a ``_prefetched_slot``, hook i takes that as its current slot.
-Each hook prefetches the next block (circularly) into the other slot while its
-own block computes ([Jul] "How It Works", last paragraph; [Aug] section 3).
+Slot rule ([Jul] "Slot Tracking: i%2 + Dynamic Correction"): every block has a
+hook, and the hooks form a ring (block i follows block i-1 mod n).  A step of
+block h reads the slot into which the hook before it in the ring last
+prefetched; while that hook has prefetched nothing yet, it reads slot h mod 2.
+Each step prefetches the next block of the ring into the other slot while its
+own block computes ([Jul] "How It Works"; [Aug] section 3).  For an odd
+block count the plain parity h mod 2 would send the head back into the slot the
+tail is reading; following the predecessor's prefetch is what keeps the two
+slots alternating across the pass boundary.
 
 Readings where the pages are silent:
 
@@ -42,8 +46,7 @@ def simulate_hooks(n: int, passes: int, n_resident: int = 0):
     if n < 1 or passes < 1 or not 0 <= n_resident <= n:
         raise ValueError("n, passes >= 1 and 0 <= n_resident <= n required")
     m = n - n_resident
-    current = [h % 2 for h in range(m)]
-    prefetched = [None] * m
+    last_prefetch = {}          # hook -> slot of its latest prefetch
     streamed_total = m * passes
     u = 0
     trace = []
@@ -53,15 +56,13 @@ def simulate_hooks(n: int, passes: int, n_resident: int = 0):
             trace.append(SlotEvent(t, p, i, -1, -1, -1))
             continue
         h = i - n_resident
-        prev = (h - 1) % m
-        if prefetched[prev] is not None:
-            current[h] = prefetched[prev]
+        read = last_prefetch.get((h - 1) % m, h % 2)
         if u + 1 < streamed_total:
-            nxt, ps = n_resident + (h + 1) % m, 1 - current[h]
-            prefetched[h] = ps
+            nxt, ps = n_resident + (h + 1) % m, 1 - read
+            last_prefetch[h] = ps
         else:
             nxt, ps = -1, -1
-        trace.append(SlotEvent(t, p, i, current[h], nxt, ps))
+        trace.append(SlotEvent(t, p, i, read, nxt, ps))
         u += 1
     return trace
 

@@ -66,6 +66,58 @@ def test_gemm_small(M, N, K, epi):
         assert nbad == 0, (nbad, worst)
 
 
+@pytest.mark.parametrize("offset_floats", [1, 2, 3])
+@pytest.mark.parametrize("epi", [dlo.EPI_BIAS, dlo.EPI_BIAS_GELU, dlo.EPI_GATED_RESIDUAL, dlo.EPI_BIAS_T])
+def test_gemm_bias_and_gate_at_slot_offsets(offset_floats, epi):
+    """bias and gate 4-B aligned only (4, 8 and 12 bytes past a 16-B boundary), the
+    way the fp32 parameters of a block sit back to back in a slot: the same result
+    as with 16-B aligned copies of the same values, bit for bit, and the oracle's."""
+    torch = require_gpu()
+    M, N, K = 300, 512, 128
+    say("gemm bias/gate offset", offset_floats, "epi", epi)
+    A = _bf16_rand(41, (M, K))
+    B = _bf16_rand(42, (N, K), 0.05)
+    bias = synth.normal_f32(43, 9, 1, 0, (N,), 0.0, 0.1)
+    gate = synth.normal_f32(44, 9, 2, 0, (N,), 0.0, 1.0)
+    X0 = synth.normal_f32(45, 9, 3, 0, (M, N))
+    # one fp32 buffer holding bias then gate, each starting offset_floats past 16 B
+    packed = np.zeros(2 * N + 16, np.float32)
+    packed[offset_floats:offset_floats + N] = bias
+    packed[N + 4 + offset_floats:2 * N + 4 + offset_floats] = gate
+    dP = _dev(torch, packed)
+    p_bias = dP.data_ptr() + 4 * offset_floats
+    p_gate = dP.data_ptr() + 4 * (N + 4 + offset_floats)
+    assert p_bias % 16 != 0 and p_gate % 16 != 0
+    da_bias, da_gate = _dev(torch, bias), _dev(torch, gate)
+    dA, dB = _dev(torch, A), _dev(torch, B)
+    s = torch.cuda.current_stream().cuda_stream
+    ref = of.linear(bf16_to_f64(A), bf16_to_f64(B), bias.astype(np.float64))
+    outs = []
+    for pb, pg in ((p_bias, p_gate), (da_bias.data_ptr(), da_gate.data_ptr())):
+        if epi == dlo.EPI_GATED_RESIDUAL:
+            dX = _dev(torch, X0)
+            dlo.op_gemm(dA.data_ptr(), K, dB.data_ptr(), K, M, N, K, pb, pg, dX.data_ptr(), N, epi, s)
+            torch.cuda.synchronize()
+            outs.append(dX.cpu().numpy())
+        else:
+            ldc = (M + 63) // 64 * 64 if epi == dlo.EPI_BIAS_T else N
+            rows = N if epi == dlo.EPI_BIAS_T else M
+            dC = torch.zeros((rows, ldc), dtype=torch.int16, device="cuda")
+            dlo.op_gemm(dA.data_ptr(), K, dB.data_ptr(), K, M, N, K, pb, 0, dC.data_ptr(), ldc, epi, s)
+            torch.cuda.synchronize()
+            outs.append(dC.cpu().numpy().view(np.uint16))
+    assert np.array_equal(outs[0].view(np.uint32 if outs[0].dtype == np.float32 else np.uint16),
+                          outs[1].view(np.uint32 if outs[1].dtype == np.float32 else np.uint16))
+    if epi == dlo.EPI_GATED_RESIDUAL:
+        got = outs[0].astype(np.float64)
+        assert rel_err(got - X0, gate.astype(np.float64) * ref) < 1e-5
+    else:
+        got = bf16_to_f64(outs[0][:, :M].T if epi == dlo.EPI_BIAS_T else outs[0])
+        want = of.gelu_erf(ref) if epi == dlo.EPI_BIAS_GELU else ref
+        nbad, worst = _close_bf16(got, want)
+        assert nbad == 0, (nbad, worst)
+
+
 def test_gemm_full_size_sampled():
     """QKV-shaped product of the Super workload (M=28800, N=15360, K=5120), sampled."""
     torch = require_gpu()

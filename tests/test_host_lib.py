@@ -308,10 +308,12 @@ def test_op_validation_errors():
     assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 100, 64, 1, 0, 1, 100, 0, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 256, 60, 1, 0, 1, 256, 0, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_gemm, 1, 64, 1, 64, 10, 256, 64, 1, 0, 1, 256, 2, 0) == "DLO_E_ARG"  # no gate
-    # epilogue stores are 8/16-B vectors: C, bias, gate 16-B aligned, ldc % 4 == 0
+    # epilogue stores are 8/16-B vectors: C 16-B aligned, ldc % 4 == 0; bias and gate
+    # are read as fp32 scalars, 4-B aligned (as packed in a slot)
     assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 16, 16, 0x1008, 256, 2, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 16, 16, 0x1000, 258, 2, 0) == "DLO_E_UNSUPPORTED"
-    assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 0x1004, 16, 0x1000, 256, 0, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 0x1002, 16, 0x1000, 256, 0, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_gemm, 16, 64, 16, 64, 10, 256, 64, 16, 0x1006, 0x1000, 256, 2, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_attention, 16, 3 * 4 * 32, 16, 64, 10, 4, 32, 16, 128, 0) == "DLO_E_UNSUPPORTED"
     # V^T row stride below T rounded up to 64, and misaligned V^T
     assert _status(dlo.op_attention, 16, 3 * 4 * 64, 16, 56, 10, 4, 64, 16, 256, 0) == "DLO_E_UNSUPPORTED"
