@@ -463,6 +463,21 @@ int dlo_quantize_mxfp8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *c
 int dlo_op_adaln(const uint16_t *W, const float *b, const float *cond, int32_t rows, int32_t d,
                  float *out, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* dlo_op_adaln without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): SiLU(cond[:d]) is staged in a static device array of
+ * DLO_NOALLOC_MAX_D floats inside the library instead of a caller workspace.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the array's device address is looked up once per device, on the
+ * first call with that device current.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (different streams, or other threads)
+ * race and give undefined results; calls ordered on one stream are safe (each
+ * call writes all d entries it reads).  Same arguments and results as
+ * dlo_op_adaln, bit for bit; d > DLO_NOALLOC_MAX_D is DLO_E_UNSUPPORTED. */
+#define DLO_NOALLOC_MAX_D 8192
+int dlo_op_adaln_noalloc(const uint16_t *W, const float *b, const float *cond, int32_t rows, int32_t d,
+                         float *out, void *stream);
+
 /* The same on an FP8 block's adaLN weight ([Doc] "Request and loading
  * constraints": a 1-byte weight plus an fp32 scale): out[r] = w_scale[0] *
  * sum_j value(W[r, j]) * silu(c[j]) + b[r], W OCP E4M3 codes [rows, d] (16-B

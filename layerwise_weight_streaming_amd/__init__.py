@@ -131,6 +131,8 @@ _SIGS = {
     "dlo_run_destroy": (None, [ctypes.c_void_p]),
     "dlo_op_adaln": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "dlo_op_adaln_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p]),
     "dlo_op_ln_modulate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                           ctypes.c_int32] + [ctypes.c_void_p] * 7),
     "dlo_op_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
@@ -505,6 +507,13 @@ def place_block(plan, store, b, dst, dst_bytes, stream):
 
 def op_adaln(W, b, cond, rows, d, out, workspace, workspace_bytes, stream):
     _check(lib().dlo_op_adaln(W, b, cond, rows, d, out, workspace, workspace_bytes, stream))
+
+
+def op_adaln_noalloc(W, b, cond, rows, d, out, stream):
+    _check(lib().dlo_op_adaln_noalloc(W, b, cond, rows, d, out, stream))
+
+
+NOALLOC_MAX_D = 8192
 
 
 def op_ln_modulate(x, ldx, T, d, gamma, beta, eps, shift, scale, out, stream):

@@ -22,6 +22,8 @@
 #include "../../include/dlo.h"
 #include "kernels.h"
 
+static_assert(DLO_NOALLOC_MAX_D == dlo::NOALLOC_MAX_D, "the header's scratch limit is the kernel's");
+
 namespace {
 
 thread_local std::string g_err;
@@ -1524,6 +1526,17 @@ int dlo_op_adaln(const uint16_t *W, const float *b, const float *cond, int32_t r
   float *sc = static_cast<float *>(workspace);
   int rc = check_hip(dlo::launch_silu(cond, sc, d, s), "silu");
   if (!rc) rc = check_hip(dlo::launch_adaln_gemv(W, sc, b, out, rows, d, s), "adaln_gemv");
+  return rc ? rc : ok();
+}
+
+int dlo_op_adaln_noalloc(const uint16_t *W, const float *b, const float *cond, int32_t rows, int32_t d,
+                         float *out, void *stream) {
+  if (!W || !b || !cond || !out) return fail(DLO_E_ARG, "NULL argument");
+  if (rows < 1 || d < 8 || d % 8) return fail(DLO_E_UNSUPPORTED, "adaln_noalloc: rows >= 1, d %% 8 == 0 required");
+  if (d > DLO_NOALLOC_MAX_D)
+    return fail(DLO_E_UNSUPPORTED, "adaln_noalloc: d = %d exceeds the static scratch (%d floats)", d,
+                DLO_NOALLOC_MAX_D);
+  int rc = check_hip(dlo::launch_adaln_noalloc(W, b, cond, rows, d, out, (hipStream_t)stream), "adaln_noalloc");
   return rc ? rc : ok();
 }
 

@@ -11,6 +11,11 @@ hipError_t launch_silu(const float *c, float *out, int n, hipStream_t s);
 // out[r] = sum_j W[r, j] * sc[j] + b[r]   (W bf16 [rows, d], d % 8 == 0)
 hipError_t launch_adaln_gemv(const uint16_t *W, const float *sc, const float *b, float *out,
                              int rows, int d, hipStream_t s);
+// the adaLN GEMV with SiLU(c) staged in the library's static device scratch instead
+// of a workspace: no allocation; d % 8 == 0, d <= NOALLOC_MAX_D
+constexpr int NOALLOC_MAX_D = 8192;
+hipError_t launch_adaln_noalloc(const uint16_t *W, const float *b, const float *cond, int rows, int d,
+                                float *out, hipStream_t s);
 // the adaLN GEMV on E4M3 codes W [rows, d] with per-tensor scale *wscale; d % 16 == 0
 hipError_t launch_adaln_gemv_fp8(const uint8_t *W, const float *wscale, const float *sc, const float *b,
                                  float *out, int rows, int d, hipStream_t s);

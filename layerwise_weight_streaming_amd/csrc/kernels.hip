@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -535,6 +537,47 @@ hipError_t launch_adaln_gemv(const uint16_t *W, const float *sc, const float *b,
   hipLaunchKernelGGL(adaln_gemv_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, W, sc, b, out,
                      rows, d);
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free adaLN entry point (dlo_op_adaln_noalloc): the
+// SiLU of the conditioning vector, NOALLOC_MAX_D floats.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, looked up once per device and kept in noalloc_ptr.
+static __device__ __align__(256) float scratch[NOALLOC_MAX_D];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+float *noalloc_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(float **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    noalloc_ptr[dev] = static_cast<float *>(p);
+  }
+  *ptr = noalloc_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_adaln_noalloc(const uint16_t *W, const float *b, const float *cond, int rows, int d,
+                                float *out, hipStream_t s) {
+  if (d < 8 || d % 8 || d > NOALLOC_MAX_D || rows < 1) return hipErrorInvalidValue;
+  float *sc = nullptr;
+  hipError_t e = noalloc_scratch(&sc);
+  if (e != hipSuccess) return e;
+  // silu writes all d entries of the scratch before the GEMV reads them: nothing
+  // carried over from an earlier call is read
+  if ((e = launch_silu(cond, sc, d, s)) != hipSuccess) return e;
+  return launch_adaln_gemv(W, sc, b, out, rows, d, s);
 }
 
 hipError_t launch_adaln_gemv_fp8(const uint8_t *W, const float *wscale, const float *sc, const float *b,
