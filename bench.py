@@ -241,6 +241,35 @@ def measure_link(torch, dev, gib=1, reps=4):
     return reps * n / (ms * 1e-3) / 1e9
 
 
+def mfma_sustained(torch, dev, iters=2000, reps=3):
+    """Dense bf16 MFMA rate with register operands and no memory traffic (libdlo's
+    dlo_op_mfma_rate), both instruction shapes, median of reps each: the rate the
+    chip holds under its power limit, beside the published 2.5 PFLOP/s."""
+    import layerwise_weight_streaming_amd as dlo
+    g = torch.Generator(device="cpu").manual_seed(7)
+    vals = (torch.rand(4096 * 8, generator=g) * 2 - 1).to(torch.bfloat16).to(dev)
+    out = torch.empty(dlo.MFMA_RATE_THREADS, dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream(device=dev)
+    res = {}
+    with torch.cuda.stream(s):
+        for form in (0, 1):
+            dlo.op_mfma_rate(form, vals.data_ptr(), out.data_ptr(), 200, s.cuda_stream)   # warm
+    for rep in range(reps):
+        for form in (0, 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(s):
+                e0.record(s)
+                fl = dlo.op_mfma_rate(form, vals.data_ptr(), out.data_ptr(), iters, s.cuda_stream)
+                e1.record(s)
+            s.synchronize()
+            res.setdefault(form, []).append(fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    med = {f: float(np.median(v)) for f, v in res.items()}
+    return {"mfma_32x32x16_TFLOPs": med[0], "mfma_16x16x32_TFLOPs": med[1],
+            "frac_of_published_peak": {"32x32x16": med[0] / PEAK_BF16_TFLOPS, "16x16x32": med[1] / PEAK_BF16_TFLOPS},
+            "note": "dense bf16 MFMA chains on register operands, no memory traffic, median of "
+                    f"{reps} runs each, taken right after the timed steps"}
+
+
 def cpu_facts():
     """Host CPU model (lscpu, /proc/cpuinfo), usable cores, and the BLAS library numpy runs on."""
     import subprocess
@@ -517,6 +546,10 @@ def main():
                 "avg_launch_ms": avg_ms,
                 "per_launch": f"{work[jdom] / launches:.4g} {unit}"}
 
+    mfma_ceiling = mfma_sustained(torch, dev)
+    log(f"sustained MFMA rate: {mfma_ceiling['mfma_32x32x16_TFLOPs']:.0f} / "
+        f"{mfma_ceiling['mfma_16x16x32_TFLOPs']:.0f} TFLOP/s (32x32x16 / 16x16x32)")
+
     blocks_done = n * P * args.steps
     result = {
         "metric": "DiT blocks/s with streaming",
@@ -550,6 +583,7 @@ def main():
         "steady_window": {k: avg.get(k) for k in ("window_ms", "compute_busy_ms", "copy_busy_ms")},
         "per_kernel_ms_per_block": {nm: per_kernel[j] / launches for j, nm in enumerate(names)},
         "roofline": roofline,
+        "mfma_sustained": mfma_ceiling,
         # device weight memory of the streamed path: exactly two slots of the largest block
         "weight_hbm": {"two_slots_bytes": 2 * r.plan.slot_bytes, "allocated_bytes": r.slot_alloc_bytes},
         "setup_s": {"pin_alloc": t_alloc, "generate": t_gen, "pack": t_pack},

@@ -188,9 +188,7 @@ int dlo_host_store_info(const dlo_host_store *store, int32_t *pinned_blocks,
                         int64_t *pinned_bytes, int32_t *staged_blocks);
 
 /* Destroys the store.  Copies that read it must have completed: the caller
- * synchronises the copy stream of every run that used it first.  The store's
- * staging stream (host fills of the staging buffers) is drained here before any
- * memory is freed. */
+ * synchronises the copy stream of every run that used it first. */
 void dlo_host_store_destroy(dlo_host_store *store);
 
 /* Packs blocks [b_begin, b_end): blocks[i] describes block b_begin + i and must
@@ -325,11 +323,10 @@ typedef struct {
  * everything the caller enqueued on the compute stream before the call happens
  * before the run, and the copy stream waits for it too.  Each call starts afresh
  * at block 0 in slot 0.  Caller memory must stay valid until the compute stream
- * has drained.  The call returns once everything is enqueued, without waiting
- * for any copy or kernel, also when blocks are staged: a staged block's fill of
- * its pinned staging buffer is a host function on the store's own staging
- * stream (ordered after the buffer's previous DMA), and the block's DMA on the
- * copy stream waits for that fill.
+ * has drained.  With a fully pinned store the call returns without waiting;
+ * when blocks are staged, the calling thread fills each staging buffer in step
+ * order (waiting for the buffer's previous DMA first), so the call returns once
+ * the last staged block has been handed to the copy stream.
  * If run_out is non-NULL it receives a handle for dlo_slot_trace (free with
  * dlo_run_destroy); otherwise the library releases the run's resources once it
  * has completed. */
@@ -629,6 +626,18 @@ int dlo_op_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols, const
 
 int dlo_op_digest(const void *base, const int64_t *offsets, const int64_t *lengths,
                   int32_t n_regions, uint64_t *out, void *stream);
+
+/* Measurement: the sustained dense bf16 MFMA rate of the GPU with operands in
+ * registers and no memory traffic in the loop -- the practical roofline of the
+ * block's MFMA kernels under the chip's power limit, which the published dense
+ * peak (256 CUs at 2.4 GHz) assumes away.  form 0: v_mfma_f32_32x32x16_bf16,
+ * form 1: v_mfma_f32_16x16x32_bf16 (the same FLOPs per iteration).  Launches
+ * one pass of `iters` iterations on `stream`; *flops (host, optional) receives
+ * the FLOPs it performs.  in: device, 4096 x 8 bf16 operand values (16-B
+ * aligned); out: device fp32 [DLO_MFMA_RATE_THREADS] checksums (caller-owned).
+ * DLO_E_ARG for a NULL pointer, another form or iters < 1. */
+#define DLO_MFMA_RATE_THREADS (256 * 512)
+int dlo_op_mfma_rate(int32_t form, const uint16_t *in, float *out, int32_t iters, double *flops, void *stream);
 
 #ifdef __cplusplus
 }

@@ -131,6 +131,8 @@ _SIGS = {
     "dlo_run_destroy": (None, [ctypes.c_void_p]),
     "dlo_op_adaln": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "dlo_op_mfma_rate": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]),
     "dlo_op_adaln_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_void_p, ctypes.c_void_p]),
     "dlo_op_ln_modulate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
@@ -514,6 +516,14 @@ def op_adaln_noalloc(W, b, cond, rows, d, out, stream):
 
 
 NOALLOC_MAX_D = 8192
+MFMA_RATE_THREADS = 256 * 512
+
+
+def op_mfma_rate(form, in_ptr, out_ptr, iters, stream):
+    """Enqueues the sustained-MFMA-rate probe; returns the FLOPs it performs."""
+    fl = ctypes.c_double(0.0)
+    _check(lib().dlo_op_mfma_rate(form, in_ptr, out_ptr, iters, ctypes.byref(fl), stream))
+    return fl.value
 
 
 def op_ln_modulate(x, ldx, T, d, gamma, beta, eps, shift, scale, out, stream):

@@ -1,9 +1,14 @@
 // Device-side helpers shared by the gfx950 kernels of the DiT block forward.
 //
-// Wave size 64.  MFMA: v_mfma_f32_32x32x16_bf16.  For that instruction lane l
-// supplies row (l % 32) of A and column (l % 32) of B, each as eight bf16 at
-// k = 8 * (l / 32) .. +7, and receives column (l % 32) of the 32x32 fp32
-// result at rows (r / 4) * 8 + (l / 32) * 4 + r % 4, r = 0..15.
+// Wave size 64.  MFMA v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) of
+// A and column (l % 32) of B, each as eight bf16 at k = 8 * (l / 32) .. +7, and
+// receives column (l % 32) of the 32x32 fp32 result at rows
+// (r / 4) * 8 + (l / 32) * 4 + r % 4, r = 0..15.  v_mfma_f32_16x16x32_bf16:
+// lane l supplies row (l % 16) of A and column (l % 16) of B, eight bf16 each at
+// k = 8 * (l / 16) .. +7, and receives column (l % 16) of the 16x16 result at
+// rows 4 * (l / 16) + r, r = 0..3.  On this chip the 16x16x32 form sustains a
+// higher clock under the power cap (measured: 2.09 against 1.76 GHz with dense
+// register operands), so the bf16 GEMMs use it.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -15,6 +20,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));

@@ -23,6 +23,7 @@
 #include "kernels.h"
 
 static_assert(DLO_NOALLOC_MAX_D == dlo::NOALLOC_MAX_D, "the header's scratch limit is the kernel's");
+static_assert(DLO_MFMA_RATE_THREADS == dlo::MFMA_RATE_GRID * 512, "the header's probe size is the kernel's");
 
 namespace {
 
@@ -245,12 +246,9 @@ struct dlo_host_store {
   std::vector<uint8_t> pinned;                 // per block: shards in pinned memory
   std::vector<std::vector<int64_t>> shard_at;  // per block: byte offset of (g * k + r)
   std::vector<uint8_t> packed;                 // per block flag
-  // two bounded pinned staging buffers (one slot each) for pageable blocks, and
-  // the library's own stream on which host functions fill them
+  // two bounded pinned staging buffers (one slot each) for pageable blocks
   char *staging[2] = {nullptr, nullptr};
   hipEvent_t staging_free[2] = {nullptr, nullptr};    // DMA out of buffer j done
-  hipEvent_t staging_filled[2] = {nullptr, nullptr};  // host fill of buffer j done
-  hipStream_t stage_stream = nullptr;
   int64_t staging_bytes = 0;
   int64_t staged_uses = 0;
   const void *shard(int b, int g, int r) const {
@@ -774,18 +772,13 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 
 void dlo_host_store_destroy(dlo_host_store *store) {
   if (!store) return;
-  // drain first: host fills still queued on the staging stream, then the DMAs
-  // that read the staging buffers
-  if (store->stage_stream) (void)hipStreamSynchronize(store->stage_stream);
   for (int j = 0; j < 2; ++j) {
     if (store->staging_free[j]) {
       (void)hipEventSynchronize(store->staging_free[j]);
       (void)hipEventDestroy(store->staging_free[j]);
     }
-    if (store->staging_filled[j]) (void)hipEventDestroy(store->staging_filled[j]);
     if (store->staging[j]) (void)hipHostFree(store->staging[j]);
   }
-  if (store->stage_stream) (void)hipStreamDestroy(store->stage_stream);
   for (size_t b = 0; b < store->mem.size(); ++b) {
     char *m = store->mem[b];
     if (!m) continue;
@@ -809,12 +802,8 @@ int ensure_staging(dlo_host_store *st) {
                   hipGetErrorString(e));
     st->staging[j] = static_cast<char *>(m);
     e = hipEventCreateWithFlags(&st->staging_free[j], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&st->staging_filled[j], hipEventDisableTiming);
     if (e != hipSuccess) return fail(DLO_E_HIP, "hipEventCreate: %s", hipGetErrorString(e));
   }
-  // default priority, not synchronising with the null stream
-  hipError_t e = hipStreamCreateWithFlags(&st->stage_stream, hipStreamNonBlocking);
-  if (e != hipSuccess) return fail(DLO_E_HIP, "hipStreamCreate (staging): %s", hipGetErrorString(e));
   st->staging_bytes = bytes;
   return DLO_OK;
 }
@@ -1017,27 +1006,16 @@ const void *from_staging(const dlo_host_store *, const char *staging, int, int, 
   return staging + off;
 }
 
-// Host function run in stream order on the store's staging stream: copies one
-// block's shards (pageable memory) into a pinned staging buffer, laid out as the
-// slot image.  It makes no HIP call.
-struct StageJob {
-  std::vector<CopyTask> tasks;
-};
-
-void stage_fill(void *p) {
-  StageJob *job = static_cast<StageJob *>(p);
-  run_copies(job->tasks);
-  delete job;
-}
-
-// One block into `dst` on stream s, enqueued without waiting on the host.  A
-// pinned block is copied directly.  A pageable block goes through staging
-// buffer j = (use count) mod 2 ([Doc] "Rank-local path without DLO AllGather":
-// two bounded pinned staging slots): on the staging stream, wait until the
-// buffer's previous DMA has drained, fill it on the host (a host function,
-// several threads), record FILLED[j]; on s, wait for FILLED[j], DMA the image
-// into dst, record FREE[j].  The fill of one buffer overlaps the DMA out of the
-// other.  `begin` (optional) is recorded on s just before the DMAs.
+// One block into `dst` on stream s.  A pinned block is copied directly.  A
+// pageable block goes through staging buffer j = (use count) mod 2 ([Doc]
+// "Rank-local path without DLO AllGather": two bounded pinned staging slots):
+// the calling thread waits until the buffer's previous DMA has drained, copies
+// the block's shards into it (several threads) laid out as the slot image, and
+// enqueues the DMA into dst; the fill of one buffer overlaps the DMA out of the
+// other.  (A fill run as a host function on a stream of its own, so that the
+// call would not wait, made the runtime serialise the copy and compute streams
+// of the whole run: measured overlap 0 on the Super stack.)  `begin`
+// (optional) is recorded on s just before the DMAs.  Returns a dlo status.
 int place(const dlo_plan *plan, dlo_host_store *st, int b, char *dst, hipStream_t s,
           hipEvent_t begin = nullptr) {
   if (st->pinned[b]) {
@@ -1050,28 +1028,17 @@ int place(const dlo_plan *plan, dlo_host_store *st, int b, char *dst, hipStream_
   int rc = ensure_staging(st);
   if (rc) return rc;
   const int j = (int)(st->staged_uses++ & 1);
+  rc = check_hip(hipEventSynchronize(st->staging_free[j]), "hipEventSynchronize(staging)");
+  if (rc) return rc;
   const BlockPlan &bp = plan->blocks[b];
-  StageJob *job = new (std::nothrow) StageJob;
-  if (!job) return fail(DLO_E_HOSTMEM, "out of host memory");
+  std::vector<CopyTask> tasks;
   for (int g = 0; g < bp.n_groups; ++g) {
     const int64_t sb = bp.gshard[g] * elt_bytes(bp.gdtype[g]);
     for (int r = 0; r < plan->k && sb > 0; ++r)
-      job->tasks.push_back({st->staging[j] + bp.gregion[g] + r * sb,
-                            static_cast<const char *>(st->shard(b, g, r)), sb});
+      tasks.push_back({st->staging[j] + bp.gregion[g] + r * sb,
+                       static_cast<const char *>(st->shard(b, g, r)), sb});
   }
-  rc = check_hip(hipStreamWaitEvent(st->stage_stream, st->staging_free[j], 0), "hipStreamWaitEvent(staging)");
-  if (rc) {
-    delete job;
-    return rc;
-  }
-  rc = check_hip(hipLaunchHostFunc(st->stage_stream, stage_fill, job), "hipLaunchHostFunc(staging)");
-  if (rc) {
-    delete job;
-    return rc;
-  }
-  rc = check_hip(hipEventRecord(st->staging_filled[j], st->stage_stream), "hipEventRecord(staging)");
-  if (!rc) rc = check_hip(hipStreamWaitEvent(s, st->staging_filled[j], 0), "hipStreamWaitEvent(staging)");
-  if (rc) return rc;
+  run_copies(tasks);
   if (begin) {
     rc = check_hip(hipEventRecord(begin, s), "hipEventRecord");
     if (rc) return rc;
@@ -1742,6 +1709,15 @@ int dlo_op_dequant_mxfp8(const uint8_t *codes, int64_t rows, int64_t cols, const
     return fail(DLO_E_UNSUPPORTED, "dequant_mxfp8: cols %% 32 == 0, codes 16-B and out 32-B aligned required");
   int rc = check_hip(dlo::launch_dequant_mxfp8(codes, rows, cols, scales, out, (hipStream_t)stream),
                      "dequant_mxfp8");
+  return rc ? rc : ok();
+}
+
+int dlo_op_mfma_rate(int32_t form, const uint16_t *in, float *out, int32_t iters, double *flops, void *stream) {
+  if (!in || !out) return fail(DLO_E_ARG, "NULL argument");
+  if ((form != 0 && form != 1) || iters < 1) return fail(DLO_E_ARG, "mfma_rate: form 0 or 1, iters >= 1");
+  if ((uintptr_t)in % 16 || (uintptr_t)out % 4) return fail(DLO_E_UNSUPPORTED, "mfma_rate: in 16-B, out 4-B aligned");
+  if (flops) *flops = (double)dlo::MFMA_RATE_GRID * 8 * iters * 262144.0;
+  int rc = check_hip(dlo::launch_mfma_rate(form, in, out, iters, (hipStream_t)stream), "mfma_rate");
   return rc ? rc : ok();
 }
 

@@ -22,7 +22,8 @@ constexpr int GBM = 256;
 // ---------------------------------------------------------------------------
 // GEMM: C[M, N] = A[M, K] B[N, K]^T, fp32 accumulate (direct-to-LDS).
 // Workgroup tile 256 x 256 x (64 bytes of K: 32 bf16 or 64 E4M3 elements) with
-// 8 waves of 128 x 64 (MFMA 32x32 tiles).  Operand tiles travel HBM/L2 -> LDS
+// 8 waves of 128 x 64 (bf16: 16x16x32 MFMA tiles, one k-step per stage; 8-bit
+// operands: 32x32 tiles).  Operand tiles travel HBM/L2 -> LDS
 // with buffer_load ... lds (no register staging) into a ring of 4 LDS stages.
 // One LDS stage = A and B tiles of 256 rows x 64 B (plus, for MXFP8, their
 // scale bytes); a row holds 4 chunks of 16 B whose order is XOR-swizzled
@@ -227,11 +228,137 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][BN / WN / 3
   }
 }
 
+// Epilogue of a 256 x BN tile held by 2 x WN waves in 16 x 16 MFMA tiles:
+// acc[i][j] is the wave's 16 x 16 sub-tile (i < 8 row tiles, j < BN / WN / 16
+// column tiles).  With B as the MFMA's first operand, lane l holds row
+// i*16 + l%16 and the four consecutive columns j*16 + 4(l/16) + 0..3; for
+// EPI_BIAS_T (A first) column j*16 + l%16 and the four consecutive rows
+// i*16 + 4(l/16) + 0..3.  Staged through LDS like gemm_epilogue, whose
+// copy-out it shares.
+template <int EPI, int BN, int WN>
+__device__ __forceinline__ void gemm_epilogue16(const f32x4 (&acc)[8][BN / WN / 16], uint16_t *smem, int tid,
+                                                int wm, int wn, int lane, int m0, int n0, int M,
+                                                const float *__restrict__ bias, const float *__restrict__ gate,
+                                                void *__restrict__ Cv, int64_t ldc) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // ring no longer read
+  const bool full = m0 + GBM <= M;
+  const int ldc32 = (int)ldc;
+  constexpr int NT = 128 * WN;
+  constexpr int NJ = BN / WN / 16;
+  constexpr int C_LD = BN + 8, X_LD = BN + 4;
+  const int fr = lane & 15, fq = lane >> 4;
+  if (EPI == EPI_BIAS_T) {
+    const int M64 = (M + 63) & ~63;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = wn * (BN / WN) + j * 16 + fr;
+      const float bv = bias[n0 + col];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = wm * 128 + i * 16 + fq * 4;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = (full || m0 + row + e < M) ? (__bf16)(acc[i][j][e] + bv) : (__bf16)0.0f;
+        *reinterpret_cast<bf16x4 *>(&smem[col * (GBM + 8) + row]) = o;
+      }
+    }
+    __syncthreads();
+    constexpr int SEG = GBM / 8;
+    uint16_t *C = reinterpret_cast<uint16_t *>(Cv) + (int64_t)n0 * ldc + m0;
+#pragma unroll
+    for (int it = 0; it < BN * SEG / NT; ++it) {
+      const int e = it * NT + tid, row = e / SEG, c8 = (e % SEG) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&smem[row * (GBM + 8) + c8]);
+      if (full || m0 + c8 < M64) *reinterpret_cast<u32x4 *>(&C[row * ldc32 + c8]) = v;
+    }
+  } else if (EPI != EPI_GATED_RESIDUAL) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = wn * (BN / WN) + j * 16 + fq * 4;
+      const float4 bv = load4(&bias[n0 + col]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v0 = acc[i][j][0] + bv.x, v1 = acc[i][j][1] + bv.y;
+        float v2 = acc[i][j][2] + bv.z, v3 = acc[i][j][3] + bv.w;
+        if (EPI == EPI_BIAS_GELU) {
+          v0 = gelu_erf(v0);
+          v1 = gelu_erf(v1);
+          v2 = gelu_erf(v2);
+          v3 = gelu_erf(v3);
+        }
+        bf16x4 o;
+        o[0] = (__bf16)v0;
+        o[1] = (__bf16)v1;
+        o[2] = (__bf16)v2;
+        o[3] = (__bf16)v3;
+        *reinterpret_cast<bf16x4 *>(&smem[(wm * 128 + i * 16 + fr) * C_LD + col]) = o;
+      }
+    }
+    __syncthreads();
+    constexpr int SEG = BN / 8;
+    uint16_t *C = reinterpret_cast<uint16_t *>(Cv) + (int64_t)m0 * ldc + n0;
+#pragma unroll
+    for (int it = 0; it < GBM * SEG / NT; ++it) {
+      const int e = it * NT + tid, row = e / SEG, c8 = (e % SEG) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&smem[row * C_LD + c8]);
+      if (full || m0 + row < M) *reinterpret_cast<u32x4 *>(&C[row * ldc32 + c8]) = v;
+    }
+  } else {
+    float *xs = reinterpret_cast<float *>(smem);
+    constexpr int SEG = BN / 4;
+    float *X = reinterpret_cast<float *>(Cv) + (int64_t)m0 * ldc + n0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int col = wn * (BN / WN) + j * 16 + fq * 4;
+          const float4 bv = load4(&bias[n0 + col]);
+          const float4 gv = load4(&gate[n0 + col]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float4 v;
+            v.x = gv.x * (acc[i][j][0] + bv.x);
+            v.y = gv.y * (acc[i][j][1] + bv.y);
+            v.z = gv.z * (acc[i][j][2] + bv.z);
+            v.w = gv.w * (acc[i][j][3] + bv.w);
+            *reinterpret_cast<float4 *>(&xs[(i * 16 + fr) * X_LD + col]) = v;
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int PER = 128 * SEG / NT;
+      float4 xv[PER];
+#pragma unroll
+      for (int it = 0; it < PER; ++it) {
+        const int e = it * NT + tid, row = half * 128 + e / SEG, c4 = (e % SEG) * 4;
+        xv[it] = (full || m0 + row < M) ? *reinterpret_cast<const float4 *>(&X[row * ldc32 + c4])
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int it = 0; it < PER; ++it) {
+        const int e = it * NT + tid, row = half * 128 + e / SEG, c4 = (e % SEG) * 4;
+        const float4 u = *reinterpret_cast<const float4 *>(&xs[(e / SEG) * X_LD + c4]);
+        float4 v = xv[it];
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+        if (full || m0 + row < M) *reinterpret_cast<float4 *>(&X[row * ldc32 + c4]) = v;
+      }
+      if (half == 0) __syncthreads();
+    }
+  }
+}
+
 // Ping-pong schedule.  Wave w owns rows 128 (w / 4) .. +127 and columns
 // 64 (w % 4) .. +63 of the tile; group g = w / 4 holds one wave on every SIMD.
 // Each wave alternates a memory phase (issue its share of the loads of k-tile
-// s + 3, read all fragments of k-tile s from LDS) and a compute phase (16
-// MFMAs on those fragments).  Group 1 runs one phase behind group 0 and a
+// s + 3, read all fragments of k-tile s from LDS) and a compute phase (the
+// MFMAs on those fragments: bf16 32 of 16x16x32, the same products in the same
+// k order per output element as 16 of 32x32x16, with bit-identical results,
+// measured).  Group 1 runs one phase behind group 0 and a
 // workgroup barrier separates phases, so on every SIMD one wave multiplies
 // while the other one feeds: the MFMA pipe sees a dense run of MFMAs instead
 // of MFMAs interleaved with the waits of LDS reads (5-6 % faster on the DiT
@@ -338,13 +465,25 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
                     sc_voff, __builtin_amdgcn_readfirstlane((uint32_t)((2 * kt + sc_h) * sc_ld)));
   };
 
-  f32x16 acc[4][NJ];
+  constexpr bool M16 = Q == 0;   // bf16: 16 x 16 x 32 MFMA tiles
+  // 32 x 32 tiles (acc) or, M16, 16 x 16 tiles (acc16; acc unused)
+  f32x16 acc[M16 ? 1 : 4][M16 ? 1 : NJ];
+  f32x4 acc16[M16 ? 8 : 1][M16 ? 4 : 1];
+  if constexpr (M16) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 4; ++r) acc16[i][j][r] = 0.f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
 
   const int nk = K / KSTAGE;
   const int frow = lane & 31, fk = lane >> 5;
@@ -358,7 +497,15 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     u32x4 a[4][2], b[NJ][2];
     int sa[4], sb[NJ];   // MXFP8: E8M0 scale bytes of the lane's rows, block fk
   };
-  using Frags = std::conditional_t<F8, Frags8, FragsB>;
+  // M16: one k-step of 32 per stage: 8 row tiles of A, 4 column tiles of B (16 rows each)
+  struct Frags16 {
+    bf16x8 a[8], b[4];
+  };
+  using Frags = std::conditional_t<F8, Frags8, std::conditional_t<M16, Frags16, FragsB>>;
+  // M16 operand of lane l: row l % 16 of a 16-row tile, k chunk l / 16 (k 8 (l / 16) ..);
+  // the swizzle depends on row bits 1..3 only, so tiles 16 rows apart are immediate offsets
+  const int a16_lane = dl_lds_off(wm * 128 + (lane & 15), lane >> 4) * 2;
+  const int b16_lane = (DL_TILE + dl_lds_off(wn * 64 + (lane & 15), lane >> 4)) * 2;
   // fragment byte offsets inside a stage: the XOR swizzle depends on row bits
   // 1..3 only, so rows 32 apart share it and the 32-row steps are immediates
   const char *lds_bytes = reinterpret_cast<const char *>(&smem[0]);
@@ -397,6 +544,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) f.sb[j] = *reinterpret_cast<const uint8_t *>(base + sb_lane + j * 32);
       }
+    } else if constexpr (M16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(base + a16_lane + i * 16 * DL_BK * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(base + b16_lane + j * 16 * DL_BK * 2);
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -420,6 +572,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
         asm volatile("" ::"v"(f.sa[0]), "v"(f.sa[1]), "v"(f.sa[2]), "v"(f.sa[3]));
         asm volatile("" ::"v"(f.sb[0]), "v"(f.sb[1]));
       }
+    } else if constexpr (M16) {
+      asm volatile("" ::"v"(f.a[0]), "v"(f.a[1]), "v"(f.a[2]), "v"(f.a[3]));
+      asm volatile("" ::"v"(f.a[4]), "v"(f.a[5]), "v"(f.a[6]), "v"(f.a[7]));
+      asm volatile("" ::"v"(f.b[0]), "v"(f.b[1]), "v"(f.b[2]), "v"(f.b[3]));
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -466,6 +622,14 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
                                                        ? __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0)
                                                        : __builtin_amdgcn_mfma_i32_32x32x32_i8(bv, av, c, 0, 0, 0));
           }
+    } else if constexpr (M16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc16[i][j] = EPI == EPI_BIAS_T
+                            ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc16[i][j], 0, 0, 0)
+                            : __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc16[i][j], 0, 0, 0);
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -577,7 +741,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
         acc[i][j] = __builtin_convertvector(__builtin_bit_cast(i32x16, acc[i][j]), f32x16) * sc;
       }
   }
-  gemm_epilogue<EPI, BN, WN>(acc, smem, tid, wm, wn, lane, m0, n0, M, bias, gate, Cv, ldc, out_scale, lds_out);
+  if constexpr (M16)
+    gemm_epilogue16<EPI, BN, WN>(acc16, smem, tid, wm, wn, lane, m0, n0, M, bias, gate, Cv, ldc);
+  else
+    gemm_epilogue<EPI, BN, WN>(acc, smem, tid, wm, wn, lane, m0, n0, M, bias, gate, Cv, ldc, out_scale, lds_out);
 }
 
 template <int Q>

@@ -95,6 +95,12 @@ hipError_t launch_quant_rows_int8(const uint16_t *x, int64_t ldx, int M, int K, 
 hipError_t launch_quant_rows_mx(const uint16_t *x, int64_t ldx, int M, int K, uint8_t *q, int64_t ldq,
                                uint8_t *scale, int64_t lds, hipStream_t s);
 
+// sustained MFMA rate probe: MFMA_RATE_GRID workgroups of 512 threads, each wave
+// iters x 262144 FLOP (form 0: 32x32x16 bf16, form 1: 16x16x32 bf16); in: 4096 x 8
+// bf16 operand values; out: fp32 [MFMA_RATE_GRID * 512] checksums
+constexpr int MFMA_RATE_GRID = 256;
+hipError_t launch_mfma_rate(int form, const uint16_t *in, float *out, int iters, hipStream_t s);
+
 // *out = digest of the regions (base + offsets[i], lengths[i]); offsets multiples of 8
 hipError_t launch_digest(const void *base, const int64_t *offsets, const int64_t *lengths,
                          int n, uint64_t *out, hipStream_t s);

@@ -127,6 +127,50 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Sustained MFMA rate (measurement): every wave keeps independent accumulator
+// chains busy with dense bf16 products of register operands (the values of
+// `in`, random-looking bits, so the datapath toggles as in real work), no
+// memory traffic in the loop.  The time per FLOP of this kernel is the chip's
+// practical bf16 roofline under its power limit, for either MFMA shape.
+// ---------------------------------------------------------------------------
+
+template <int FORM>
+__global__ __launch_bounds__(512, 1) void mfma_rate_kernel(const bf16x8 *__restrict__ in, float *__restrict__ out,
+                                                           int iters) {
+  const int t = blockIdx.x * 512 + threadIdx.x;
+  const bf16x8 a = in[t % 4096], b = in[(t + 1234) % 4096];
+  float sum = 0.f;
+  if constexpr (FORM == 0) {   // 8 chains of v_mfma_f32_32x32x16_bf16
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[i][r];
+  } else {   // 16 chains of v_mfma_f32_16x16x32_bf16: the same FLOPs per iteration
+    f32x4 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum += acc[i][r];
+  }
+  out[t] = sum;
+}
+
+// ---------------------------------------------------------------------------
 // slot digest
 // ---------------------------------------------------------------------------
 
@@ -524,6 +568,17 @@ hipError_t launch_quant_rows_mx(const uint16_t *x, int64_t ldx, int M, int K, ui
                                uint8_t *scale, int64_t lds, hipStream_t s) {
   if (M < 1 || K < 32 || K % 32 || ldx % 8 || ldq % 8 || lds < M) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quant_rows_mx_kernel, dim3((unsigned)lds), dim3(256), 0, s, x, ldx, M, K, q, ldq, scale, lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_rate(int form, const uint16_t *in, float *out, int iters, hipStream_t s) {
+  const bf16x8 *v = reinterpret_cast<const bf16x8 *>(in);
+  if (form == 0)
+    hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(MFMA_RATE_GRID), dim3(512), 0, s, v, out, iters);
+  else if (form == 1)
+    hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(MFMA_RATE_GRID), dim3(512), 0, s, v, out, iters);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

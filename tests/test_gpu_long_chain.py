@@ -63,6 +63,15 @@ def _runner(w, seed, n, digests=False):
     return r, dig
 
 
+def _same_inputs(x0, g):
+    """The seeded inputs here are the ones the goldens were written from.  The
+    generator's Box-Muller runs through the C library's vector logf/cosf, whose
+    last bits can differ between CPU models (measured: 2 ulp of fp32), so the
+    check allows 1e-5; a wrong seed or shape is off by O(1)."""
+    assert x0[g["rows"]].shape == g["x0"].shape
+    assert np.max(np.abs(x0[g["rows"]].astype(np.float64) - g["x0"])) <= 1e-5
+
+
 def _compare(tag, x_gpu, g, i):
     rows, x0 = g["rows"], g["x0"]
     ref = g["ref"][i]
@@ -92,7 +101,7 @@ def test_nano_full_stack_two_passes():
     assert (n, passes, T, D) == (w.n_blocks, w.passes, w.tokens, w.D)
     x0 = synth.activations(seed, T, D)
     c = synth.conditioning(seed, D)
-    assert np.array_equal(x0[g["rows"]].astype(np.float64), g["x0"])
+    _same_inputs(x0, g)
     errs = []
     # checkpoint 0: a 24-block plan, one pass
     n24 = int(g["steps"][0])
@@ -124,7 +133,7 @@ def test_irregular_prefix_full_tokens():
     assert (T, D) == (w.tokens, w.D)
     x0 = synth.activations(seed, T, D)
     c = synth.conditioning(seed, D)
-    assert np.array_equal(x0[g["rows"]].astype(np.float64), g["x0"])
+    _same_inputs(x0, g)
     r, dig = _runner(w, seed, n, digests=True)
     errs = []
     for p in range(1, passes + 1):

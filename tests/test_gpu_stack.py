@@ -230,39 +230,6 @@ def test_staged_store_matches_pinned(mode, limit_blocks):
     r.close()
 
 
-def test_staged_forward_returns_before_copies():
-    """dlo_forward_stack on a fully staged store returns as soon as everything is
-    enqueued: the host fills of the staging buffers run later, on the store's
-    staging stream, so the call takes a small part of the run's time and the
-    copy stream still has work when it returns; the result equals the pinned
-    store's bit for bit."""
-    import time
-    torch = require_gpu()
-    from layerwise_weight_streaming_amd.runner import StackRunner
-    w = synth.WORKLOADS["8blk"]
-    stack = synth.make_stack(w, 6)
-    blocks = [(w.width(b), w.heads(b), ps) for b, ps in enumerate(stack.blocks)]
-    ref = make_runner(w, stack)
-    ref.forward(w.passes, want_run=False)
-    x_ref = ref.x_host()
-    ref.close()
-    r = StackRunner(spec_blocks(w, w.n_blocks), w.k, w.tokens, w.D, store_mode="pageable")
-    r.pack(0, blocks)
-    for it in range(3):   # the first call also allocates the staging buffers
-        r.set_inputs(stack.x, stack.c)
-        t0 = time.perf_counter()
-        r.forward(w.passes, want_run=False)
-        t_call = time.perf_counter() - t0
-        pending = not r.copy.query()
-        r.synchronize()
-        t_total = time.perf_counter() - t0
-        say(f"call {it}: returned after {1e3 * t_call:.2f} ms of {1e3 * t_total:.2f} ms, copies pending {pending}")
-        assert np.array_equal(r.x_host().view(np.uint32), x_ref.view(np.uint32))
-    # 32 staged blocks of 37.8 MB: their host fills alone take well over 10 ms
-    assert pending and t_call < 0.25 * t_total
-    r.close()
-
-
 @pytest.mark.parametrize("n_resident", [1, 3, 7, 8])
 def test_resident_layers_match_full_streaming(n_resident):
     """Blocks 0 .. R-1 resident, the rest streamed: the slot trace and digests follow
