@@ -485,7 +485,8 @@ int dlo_op_adaln_fp8(const uint8_t *W, const float *w_scale, const float *b, con
                      int32_t d, float *out, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* out[t, :] = bf16( LN(x[t, :d]; gamma, beta, *eps) * (1 + scale) + shift ), t < T;
- * x fp32 with row stride ldx; out bf16 [T, d]. */
+ * x fp32 with row stride ldx (x 16-B aligned, ldx % 4 == 0); out bf16 [T, d]
+ * (8-B aligned); d % 256 == 0, d <= 8192.  Else DLO_E_UNSUPPORTED. */
 int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const float *gamma,
                        const float *beta, const float *eps, const float *shift,
                        const float *scale, uint16_t *out, void *stream);

@@ -1527,6 +1527,8 @@ int dlo_op_ln_modulate(const float *x, int64_t ldx, int32_t T, int32_t d, const 
   if (!x || !gamma || !beta || !eps || !shift || !scale || !out) return fail(DLO_E_ARG, "NULL argument");
   if (T < 1 || d < 256 || d % 256 || d > 8192 || ldx < d)
     return fail(DLO_E_UNSUPPORTED, "ln_modulate: d %% 256 == 0, d <= 8192, ldx >= d required");
+  if ((uintptr_t)x % 16 || ldx % 4 || (uintptr_t)out % 8)
+    return fail(DLO_E_UNSUPPORTED, "ln_modulate: x 16-B aligned with ldx %% 4 == 0, out 8-B aligned required");
   int rc = check_hip(dlo::launch_ln_modulate(x, ldx, T, d, gamma, beta, eps, shift, scale, out,
                                              (hipStream_t)stream), "ln_modulate");
   return rc ? rc : ok();

@@ -85,46 +85,113 @@ __global__ __launch_bounds__(256) void adaln_gemv_fp8_kernel(const uint8_t *__re
   if (lane == 0) out[row] = acc * *wscale + b[row];
 }
 
-template <int VPT>  // values per thread: d / 256
-__global__ __launch_bounds__(256) void ln_modulate_kernel(
-    const float *__restrict__ x, int64_t ldx, int d, const float *__restrict__ gamma,
-    const float *__restrict__ beta, const float *__restrict__ eps_p,
-    const float *__restrict__ shift, const float *__restrict__ scale, uint16_t *__restrict__ out) {
-  __shared__ float red[2][4];
+// The LayerNorm row statistics of both LN kernels (one order of summation, so
+// that the two round alike): each thread sums its float4 chunks, then the wave,
+// then the four waves' partials in order; the variance in a second pass over
+// the registers (chunks at or past d4 hold zeros and are skipped there).
+// Two barriers; red is reused by the next row only after the second.
+template <int NC>
+__device__ __forceinline__ void ln_stats(const float4 (&v)[NC], int d4, float inv_d, float eps,
+                                         float (&red)[2][4], float &mean, float &rstd) {
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-  const int64_t row = blockIdx.x;
-  const float *xr = x + row * ldx;
-  float v[VPT];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    v[i] = xr[i * 256 + tid];
-    s += v[i];
-  }
+  for (int i = 0; i < NC; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   s = wave_sum(s);
   if (lane == 0) red[0][wv] = s;
   __syncthreads();
-  const float mean = (red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)d;
+  mean = (red[0][0] + red[0][1] + red[0][2] + red[0][3]) * inv_d;
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    float dv = v[i] - mean;
-    q += dv * dv;
+  for (int i = 0; i < NC; ++i) {
+    if (tid + 256 * i < d4) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
+      q += (a * a + b * b) + (c * c + e * e);
+    }
   }
   q = wave_sum(q);
   if (lane == 0) red[1][wv] = q;
   __syncthreads();
-  const float var = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) / (float)d;
-  const float rstd = 1.0f / sqrtf(var + eps_p[0]);
-  uint16_t *orow = out + row * d;
+  const float var = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) * inv_d;
+  rstd = 1.0f / sqrtf(var + eps);
+}
+
+// (LN(x) * gamma + beta) * (1 + scale) + shift on four columns; sc holds 1 + scale
+__device__ __forceinline__ float4 ln_mod4(float4 v, float mean, float rstd, float4 g, float4 b, float4 sc,
+                                          float4 sh) {
+  float4 y;
+  y.x = ((v.x - mean) * rstd * g.x + b.x) * sc.x + sh.x;
+  y.y = ((v.y - mean) * rstd * g.y + b.y) * sc.y + sh.y;
+  y.z = ((v.z - mean) * rstd * g.z + b.z) * sc.z + sh.z;
+  y.w = ((v.w - mean) * rstd * g.w + b.w) * sc.w + sh.w;
+  return y;
+}
+
+// the fp32 value of bf16(f), round to nearest even
+__device__ __forceinline__ float bf16_round(float f) { return __uint_as_float((uint32_t)f32_to_bf16(f) << 16); }
+
+// LayerNorm + modulate, h = bf16(LN(x[t, :d]) * (1 + scale) + shift), with
+// several rows per workgroup: thread t owns the float4 column chunks t + 256 i
+// (i < NC); the four per-column vectors (gamma, beta, 1 + scale, shift) are
+// loaded once into registers and reused for every row the workgroup takes
+// (rows blockIdx.x, + gridDim.x, ...), so the parameters cost one read per
+// workgroup instead of one per row; the next row's x is loaded before the
+// current row's reductions; 16-B loads, 8-B bf16x4 stores.
+template <int NC>
+__global__ __launch_bounds__(256) void ln_rows_kernel(const float *__restrict__ x, int64_t ldx, int T, int d,
+                                                      const float *__restrict__ gamma, const float *__restrict__ beta,
+                                                      const float *__restrict__ eps_p, const float *__restrict__ shift,
+                                                      const float *__restrict__ scale, uint16_t *__restrict__ out) {
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x;
+  const int d4 = d / 4;
+  float4 g[NC], b[NC], sc[NC], sh[NC];
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int col = i * 256 + tid;
-    float y = (v[i] - mean) * rstd * gamma[col] + beta[col];
-    y = y * (1.0f + scale[col]) + shift[col];
-    orow[col] = f32_to_bf16(y);
+  for (int i = 0; i < NC; ++i) {
+    const int c = 4 * (tid + 256 * i);
+    if (c < d) {   // 4-B aligned parameters: four scalar loads
+      g[i] = make_float4(gamma[c], gamma[c + 1], gamma[c + 2], gamma[c + 3]);
+      b[i] = make_float4(beta[c], beta[c + 1], beta[c + 2], beta[c + 3]);
+      sc[i] = make_float4(1.0f + scale[c], 1.0f + scale[c + 1], 1.0f + scale[c + 2], 1.0f + scale[c + 3]);
+      sh[i] = make_float4(shift[c], shift[c + 1], shift[c + 2], shift[c + 3]);
+    }
+  }
+  const float eps = eps_p[0];
+  const float inv_d = 1.0f / (float)d;
+  int row = blockIdx.x;
+  float4 v[NC];
+  auto load = [&](int r, float4 (&dst)[NC]) {
+    const float4 *xr = reinterpret_cast<const float4 *>(x + (int64_t)r * ldx);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = tid + 256 * i;
+      dst[i] = (r < T && c4 < d4) ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load(row, v);
+  for (; row < T; row += gridDim.x) {
+    float4 vn[NC];
+    load(row + gridDim.x, vn);
+    float mean, rstd;
+    ln_stats<NC>(v, d4, inv_d, eps, red, mean, rstd);
+    uint16_t *orow = out + (int64_t)row * d;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = tid + 256 * i;
+      if (c4 < d4) {
+        const float4 y = ln_mod4(v[i], mean, rstd, g[i], b[i], sc[i], sh[i]);
+        bf16x4 o;
+        o[0] = (__bf16)y.x;
+        o[1] = (__bf16)y.y;
+        o[2] = (__bf16)y.z;
+        o[3] = (__bf16)y.w;
+        *reinterpret_cast<bf16x4 *>(orow + 4 * c4) = o;
+      }
+      v[i] = vn[i];
+    }
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // Sustained MFMA rate (measurement): every wave keeps independent accumulator
@@ -170,6 +237,7 @@ __global__ __launch_bounds__(512, 1) void mfma_rate_kernel(const bf16x8 *__restr
   out[t] = sum;
 }
 
+
 // ---------------------------------------------------------------------------
 // slot digest
 // ---------------------------------------------------------------------------
@@ -214,14 +282,6 @@ __global__ __launch_bounds__(256) void digest_kernel(const uint8_t *__restrict__
   if ((threadIdx.x % WAVE) == 0) atomicAdd((unsigned long long *)out, (unsigned long long)acc);
 }
 
-template <int VPT>
-hipError_t ln_launch(const float *x, int64_t ldx, int T, int d, const float *gamma,
-                     const float *beta, const float *eps, const float *shift, const float *scale,
-                     uint16_t *out, hipStream_t s) {
-  hipLaunchKernelGGL(ln_modulate_kernel<VPT>, dim3(T), dim3(256), 0, s, x, ldx, d, gamma, beta,
-                     eps, shift, scale, out);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // FP8 weights: E4M3 codes -> bf16(code value * scale).  gfx950's
@@ -407,20 +467,22 @@ __global__ __launch_bounds__(256) void quant_rows_mx_kernel(const uint16_t *__re
 }
 
 // LayerNorm + modulate fused with the input quantisation of a W8A8 linear:
-// the modulated row is computed and rounded to bf16 exactly as
-// ln_modulate_kernel does, then quantised from registers as the stand-alone
-// quantizers do (MX = false: per-row E4M3 with an fp32 scale; MX = true: E8M0
-// per 32 columns, block-major [d / 32, lds], rows T .. lds - 1 set to 127), so
-// codes and scales are bit-identical to LN followed by the quantizer, without
-// the bf16 row's round trip through memory.  Thread tid holds columns
-// i * 256 + tid: a 32-column block is one half of a wave.
-template <int VPT, bool MX>
+// the modulated row is computed with ln_rows_kernel's layout and arithmetic
+// (ln_stats, ln_mod4) and rounded to bf16 as it does, then quantised from
+// registers as the stand-alone quantizers do (MX = false: per-row E4M3 with an
+// fp32 scale; MX = true: E8M0 per 32 columns, block-major [d / 32, lds], rows
+// T .. lds - 1 set to 127), so codes and scales are bit-identical to LN followed
+// by the quantizer, without the bf16 row's round trip through memory.  One row
+// per workgroup; thread tid holds the float4 chunks tid + 256 i, so a 32-column
+// block is eight neighbouring lanes.
+template <int NC, bool MX>
 __global__ __launch_bounds__(256) void ln_modulate_quant_kernel(
     const float *__restrict__ x, int64_t ldx, int T, int d, const float *__restrict__ gamma,
     const float *__restrict__ beta, const float *__restrict__ eps_p, const float *__restrict__ shift,
     const float *__restrict__ scale, uint8_t *__restrict__ q, int64_t ldq, void *__restrict__ qscale,
     int64_t lds) {
-  __shared__ float red[3][4];
+  __shared__ float red[2][4];
+  __shared__ float redm[4];
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int64_t row = blockIdx.x;
   if (row >= T) {   // MX padding rows of the block-major scales
@@ -428,61 +490,65 @@ __global__ __launch_bounds__(256) void ln_modulate_quant_kernel(
       for (int b = tid; b < d / 32; b += 256) static_cast<uint8_t *>(qscale)[b * lds + row] = 127;
     return;
   }
-  const float *xr = x + row * ldx;
-  float v[VPT];
-  float s = 0.f;
+  const int d4 = d / 4;
+  const float4 *xr = reinterpret_cast<const float4 *>(x + row * ldx);
+  float4 v[NC];
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    v[i] = xr[i * 256 + tid];
-    s += v[i];
+  for (int i = 0; i < NC; ++i) {
+    const int c4 = tid + 256 * i;
+    v[i] = c4 < d4 ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  s = wave_sum(s);
-  if (lane == 0) red[0][wv] = s;
-  __syncthreads();
-  const float mean = (red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)d;
-  float qv = 0.f;
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    float dv = v[i] - mean;
-    qv += dv * dv;
-  }
-  qv = wave_sum(qv);
-  if (lane == 0) red[1][wv] = qv;
-  __syncthreads();
-  const float var = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) / (float)d;
-  const float rstd = 1.0f / sqrtf(var + eps_p[0]);
+  float mean, rstd;
+  ln_stats<NC>(v, d4, 1.0f / (float)d, eps_p[0], red, mean, rstd);
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int col = i * 256 + tid;
-    float y = (v[i] - mean) * rstd * gamma[col] + beta[col];
-    y = y * (1.0f + scale[col]) + shift[col];
-    v[i] = __uint_as_float((uint32_t)f32_to_bf16(y) << 16);   // the bf16 value the linear reads
-    amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < NC; ++i) {
+    const int c4 = tid + 256 * i, c = 4 * c4;
+    if (c4 < d4) {
+      const float4 g = make_float4(gamma[c], gamma[c + 1], gamma[c + 2], gamma[c + 3]);
+      const float4 b = make_float4(beta[c], beta[c + 1], beta[c + 2], beta[c + 3]);
+      const float4 sc = make_float4(1.0f + scale[c], 1.0f + scale[c + 1], 1.0f + scale[c + 2], 1.0f + scale[c + 3]);
+      const float4 sh = make_float4(shift[c], shift[c + 1], shift[c + 2], shift[c + 3]);
+      const float4 y = ln_mod4(v[i], mean, rstd, g, b, sc, sh);
+      // the bf16 values the linear reads
+      v[i] = make_float4(bf16_round(y.x), bf16_round(y.y), bf16_round(y.z), bf16_round(y.w));
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    } else {
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
-  uint8_t *qr = q + row * ldq;
+  uint32_t *qr = reinterpret_cast<uint32_t *>(q + row * ldq);
   if constexpr (MX) {
     uint8_t *sc = static_cast<uint8_t *>(qscale);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      float a = fabsf(v[i]);
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = tid + 256 * i;
+      float a = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, WAVE));
+      for (int o = 1; o < 8; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, WAVE));
       const int X = a > 0.f ? max(-127, min(127, (int)((__float_as_uint(a) >> 23) & 0xFF) - 127 - 8)) : -127;
       const float p2 = __uint_as_float((uint32_t)(127 - X) << 23);
-      qr[i * 256 + tid] = (uint8_t)e4m3_code(v[i] * p2);
-      if ((lane & 31) == 0) sc[(int64_t)(i * 8 + tid / 32) * lds + row] = (uint8_t)(X + 127);
+      if (c4 < d4) {
+        qr[c4] = e4m3_code(v[i].x * p2) | (e4m3_code(v[i].y * p2) << 8) | (e4m3_code(v[i].z * p2) << 16) |
+                 (e4m3_code(v[i].w * p2) << 24);
+        if ((lane & 7) == 0) sc[(int64_t)(c4 / 8) * lds + row] = (uint8_t)(X + 127);
+      }
     }
   } else {
 #pragma unroll
     for (int o = WAVE / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
-    if (lane == 0) red[2][wv] = amax;
+    if (lane == 0) redm[wv] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
+    amax = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
     const float sq = amax == 0.f ? 1.0f : amax / 448.0f;
     if (tid == 0) static_cast<float *>(qscale)[row] = sq;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) qr[i * 256 + tid] = (uint8_t)e4m3_code(v[i] / sq);
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = tid + 256 * i;
+      if (c4 < d4)
+        qr[c4] = e4m3_code(v[i].x / sq) | (e4m3_code(v[i].y / sq) << 8) | (e4m3_code(v[i].z / sq) << 16) |
+                 (e4m3_code(v[i].w / sq) << 24);
+    }
   }
 }
 
@@ -491,25 +557,20 @@ __global__ __launch_bounds__(256) void ln_modulate_quant_kernel(
 hipError_t launch_ln_modulate_quant(const float *x, int64_t ldx, int T, int d, const float *gamma,
                                     const float *beta, const float *eps, const float *shift, const float *scale,
                                     uint8_t *q, int64_t ldq, void *qscale, int64_t lds, bool mx, hipStream_t s) {
-  if (d % 256 || d > 8192 || (mx && lds < T)) return hipErrorInvalidValue;
+  if (T < 1 || d % 256 || d > 8192 || ldx % 4 || ldq % 4 || (mx && lds < T)) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(mx ? lds : T);
-  switch (d / 256) {
-#define DLO_LNQ_CASE(V)                                                                                   \
-  case V:                                                                                                 \
+  switch ((d + 1023) / 1024) {
+#define DLO_LNQ_CASE(NC)                                                                                  \
+  case NC:                                                                                                \
     if (mx)                                                                                               \
-      hipLaunchKernelGGL((ln_modulate_quant_kernel<V, true>), dim3(grid), dim3(256), 0, s, x, ldx, T, d,   \
+      hipLaunchKernelGGL((ln_modulate_quant_kernel<NC, true>), dim3(grid), dim3(256), 0, s, x, ldx, T, d,  \
                          gamma, beta, eps, shift, scale, q, ldq, qscale, lds);                            \
     else                                                                                                  \
-      hipLaunchKernelGGL((ln_modulate_quant_kernel<V, false>), dim3(grid), dim3(256), 0, s, x, ldx, T, d,  \
+      hipLaunchKernelGGL((ln_modulate_quant_kernel<NC, false>), dim3(grid), dim3(256), 0, s, x, ldx, T, d, \
                          gamma, beta, eps, shift, scale, q, ldq, qscale, lds);                            \
     break;
-    DLO_LNQ_CASE(1) DLO_LNQ_CASE(2) DLO_LNQ_CASE(3) DLO_LNQ_CASE(4) DLO_LNQ_CASE(5) DLO_LNQ_CASE(6)
-    DLO_LNQ_CASE(7) DLO_LNQ_CASE(8) DLO_LNQ_CASE(9) DLO_LNQ_CASE(10) DLO_LNQ_CASE(11)
-    DLO_LNQ_CASE(12) DLO_LNQ_CASE(13) DLO_LNQ_CASE(14) DLO_LNQ_CASE(15) DLO_LNQ_CASE(16)
-    DLO_LNQ_CASE(17) DLO_LNQ_CASE(18) DLO_LNQ_CASE(19) DLO_LNQ_CASE(20) DLO_LNQ_CASE(21)
-    DLO_LNQ_CASE(22) DLO_LNQ_CASE(23) DLO_LNQ_CASE(24) DLO_LNQ_CASE(25) DLO_LNQ_CASE(26)
-    DLO_LNQ_CASE(27) DLO_LNQ_CASE(28) DLO_LNQ_CASE(29) DLO_LNQ_CASE(30) DLO_LNQ_CASE(31)
-    DLO_LNQ_CASE(32)
+    DLO_LNQ_CASE(1) DLO_LNQ_CASE(2) DLO_LNQ_CASE(3) DLO_LNQ_CASE(4)
+    DLO_LNQ_CASE(5) DLO_LNQ_CASE(6) DLO_LNQ_CASE(7) DLO_LNQ_CASE(8)
 #undef DLO_LNQ_CASE
     default:
       return hipErrorInvalidValue;
@@ -646,21 +707,25 @@ hipError_t launch_adaln_gemv_fp8(const uint8_t *W, const float *wscale, const fl
 hipError_t launch_ln_modulate(const float *x, int64_t ldx, int T, int d, const float *gamma,
                               const float *beta, const float *eps, const float *shift,
                               const float *scale, uint16_t *out, hipStream_t s) {
-  switch (d / 256) {
-#define DLO_LN_CASE(V) \
-  case V:              \
-    return ln_launch<V>(x, ldx, T, d, gamma, beta, eps, shift, scale, out, s);
-    DLO_LN_CASE(1) DLO_LN_CASE(2) DLO_LN_CASE(3) DLO_LN_CASE(4) DLO_LN_CASE(5) DLO_LN_CASE(6)
-    DLO_LN_CASE(7) DLO_LN_CASE(8) DLO_LN_CASE(9) DLO_LN_CASE(10) DLO_LN_CASE(11)
-    DLO_LN_CASE(12) DLO_LN_CASE(13) DLO_LN_CASE(14) DLO_LN_CASE(15) DLO_LN_CASE(16)
-    DLO_LN_CASE(17) DLO_LN_CASE(18) DLO_LN_CASE(19) DLO_LN_CASE(20) DLO_LN_CASE(21)
-    DLO_LN_CASE(22) DLO_LN_CASE(23) DLO_LN_CASE(24) DLO_LN_CASE(25) DLO_LN_CASE(26)
-    DLO_LN_CASE(27) DLO_LN_CASE(28) DLO_LN_CASE(29) DLO_LN_CASE(30) DLO_LN_CASE(31)
-    DLO_LN_CASE(32)
+  if (T < 1 || d < 4 || d % 4 || d > 8192 || ldx % 4) return hipErrorInvalidValue;
+  // one workgroup per row up to the cap; past it each workgroup takes several
+  // rows (the cap keeps two workgroups per CU resident at 8 chunks per thread)
+  const int nc = (d + 1023) / 1024;
+  const int cap = nc >= 5 ? 512 : 768;
+  const dim3 grid(T < cap ? T : cap);
+  switch (nc) {
+#define DLO_LN_CASE(NC)                                                                                      \
+  case NC:                                                                                                   \
+    hipLaunchKernelGGL(ln_rows_kernel<NC>, grid, dim3(256), 0, s, x, ldx, T, d, gamma, beta, eps, shift,     \
+                       scale, out);                                                                          \
+    break;
+    DLO_LN_CASE(1) DLO_LN_CASE(2) DLO_LN_CASE(3) DLO_LN_CASE(4)
+    DLO_LN_CASE(5) DLO_LN_CASE(6) DLO_LN_CASE(7) DLO_LN_CASE(8)
 #undef DLO_LN_CASE
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 hipError_t launch_digest(const void *base, const int64_t *offsets, const int64_t *lengths, int n,

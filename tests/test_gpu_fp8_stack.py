@@ -23,8 +23,29 @@ reproduce the single-block figures), as much as that separation.  So:
   closer to it than to the W8A16 oracle;
 * stacks check the streaming (slot bytes and digests = oracle, hook schedule),
   streamed == resident bit for bit, that the flag changes FP8 blocks and leaves
-  bf16 blocks alone, and a gross-error bound of 0.1 (rms of the update).
+  bf16 blocks alone, and the rms error of the update against a bound derived
+  from the single-block one, eps1 (1 % FP8 and MXFP8, 1.5 % INT8): with N_q
+  quantised block steps, eps <= 2 eps1 sqrt(N_q).  Model: each quantised step
+  adds a divergence of at most eps1 of an update; its code decisions are taken
+  on inputs that already differ from the oracle's, so the steps' contributions
+  are uncorrelated and add in quadrature; the factor 2 covers the propagation of
+  earlier divergence through later blocks (LayerNorm inputs, weights of std
+  0.02) with the accumulated update taken as no smaller than one step's.  The
+  stack figures were known when this model was written; it is checked by its
+  margins (the nine cases sit at 0.17-0.7 of it), not tuned to them.
+
+What the comparison with the oracle can establish: that each op computes its
+definition (exactly, for codes, scales and integer products), that the block
+is the composition of those ops, that streaming changes no bit, and that one
+block lands where the W8A8 method puts it and not where W8A16 does.  What it
+cannot: code-for-code agreement of a multi-block W8A8 stack, because after the
+first block the two sides quantise inputs that differ by rounding; there the
+oracle bounds the size of the divergence, and a mistake confined to a later
+block is ruled out by the op and composition checks, which hold for every block
+of every stack (the forward runs one code path per form and width).
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -37,6 +58,10 @@ from oracle import schedule as sc
 from tests.gpu_util import TOL, fp8_blocks, make_runner_params, rel_err, require_gpu, say
 
 pytestmark = pytest.mark.gpu
+
+
+# the single-block rms bound of the update against the W8A8 oracle
+EPS1 = {"fp8": 1e-2, "mxfp8": 1e-2, "int8": 1.5e-2}
 
 
 def _rms_rel(got, ref):
@@ -86,10 +111,10 @@ def test_w8a8_single_block_matches_the_w8a8_oracle(form):
         # W8A16 result, while the int8 decisions taken on the GPU's bf16 inputs (which differ
         # from the oracle's by bf16 rounding upstream, the bf16 copy of the adaLN weight
         # included) already account for ~1 %: closer to its own oracle, not 4x closer
-        assert e8 <= 1.5e-2 and e_max <= 2 * TOL
+        assert e8 <= EPS1[form] and e_max <= 2 * TOL
         assert e8 < 0.85 * e16
     else:
-        assert e8 <= 1e-2 and e_max <= 2 * TOL
+        assert e8 <= EPS1[form] and e_max <= 2 * TOL
         assert e8 < 0.25 * e16
 
 
@@ -224,8 +249,10 @@ def test_w8a8_stack_streamed(form, name, n_blocks, tokens, which):
     heads = [w.heads(b) for b in range(n)]
     ref = of.forward_stack(x0, stack.c, blocks, heads, w.passes, act_fp8=True)
     e = _rms_rel(x_gpu - x0, ref - x0)
-    say(f"update rms rel err vs the W8A8 oracle {e:.3e}")
-    assert e < 0.1
+    n_q = (n if which is None else len(which)) * w.passes
+    bound = 2 * EPS1[form] * math.sqrt(n_q)
+    say(f"update rms rel err vs the W8A8 oracle {e:.3e} (bound {bound:.3e}, {n_q} quantised block steps)")
+    assert e < bound
 
 
 def test_w8a8_leaves_bf16_blocks_alone():
@@ -248,7 +275,7 @@ def test_w8a8_leaves_bf16_blocks_alone():
 def test_w8a8_ragged_token_counts(form, tokens):
     """Token counts off the 64-row grid: the quantizers' rows, the V^T padding and the
     GEMMs' partial row tiles in the W8A8 forward; streamed == resident, and the update
-    within the stacks' gross-error bound of the W8A8 oracle."""
+    within the stacks' derived bound of the W8A8 oracle."""
     require_gpu()
     w = synth.WORKLOADS["tiny"].with_(tokens=tokens)
     say(f"W8A8 {form} ragged T={tokens}")
@@ -266,5 +293,7 @@ def test_w8a8_ragged_token_counts(form, tokens):
     x0 = np.asarray(stack.x, np.float64)
     ref = of.forward_stack(x0, stack.c, blocks, [w.heads(b) for b in range(w.n_blocks)], w.passes, act_fp8=True)
     e = _rms_rel(x_gpu - x0, ref - x0)
-    say(f"update rms rel err vs the W8A8 oracle {e:.3e}")
-    assert e < 0.1
+    n_q = w.n_blocks * w.passes
+    bound = 2 * EPS1[form] * math.sqrt(n_q)
+    say(f"update rms rel err vs the W8A8 oracle {e:.3e} (bound {bound:.3e}, {n_q} quantised block steps)")
+    assert e < bound

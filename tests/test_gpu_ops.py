@@ -277,8 +277,11 @@ def test_attention_full_size_sampled():
 # at 4-B offsets as in a slot's fp32 region (goff = 1), the per-element path for
 # other widths and for ldx % 4 != 0
 @pytest.mark.parametrize("T,d,ldx,goff", [(1, 256, 256, 0), (33, 1024, 1024, 0), (17, 5120, 5120, 1),
-                                          (9, 2048, 4096, 0), (5, 3072, 3076, 1), (7, 1024, 1030, 0),
-                                          (3, 768, 768, 1)])
+                                          (9, 2048, 4096, 0), (5, 3072, 3076, 1), (7, 1024, 1032, 0),
+                                          (3, 768, 768, 1),
+                                          # more rows than workgroups: each takes several rows
+                                          (2000, 3072, 3072, 0), (1537, 5120, 5124, 1), (1030, 8192, 8192, 0),
+                                          (800, 2304, 2304, 1)])
 def test_ln_modulate(T, d, ldx, goff):
     torch = require_gpu()
     say("ln_modulate", T, d, ldx, goff)

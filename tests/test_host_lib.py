@@ -324,6 +324,10 @@ def test_op_validation_errors():
     assert _status(dlo.op_v_transpose, 16, 3 * 128, 10, 128, 0x1008, 64, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_v_transpose, 16, 3 * 128 - 8, 10, 128, 16, 64, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_ln_modulate, 1, 300, 4, 300, 1, 1, 1, 1, 1, 1, 0) == "DLO_E_UNSUPPORTED"
+    # x rows are read as float4 (16-B aligned x, ldx % 4 == 0), out written as 4 bf16
+    assert _status(dlo.op_ln_modulate, 16, 258, 4, 256, 16, 16, 16, 16, 16, 16, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_ln_modulate, 0x1004, 256, 4, 256, 16, 16, 16, 16, 16, 16, 0) == "DLO_E_UNSUPPORTED"
+    assert _status(dlo.op_ln_modulate, 16, 256, 4, 256, 16, 16, 16, 16, 16, 0x1002, 0) == "DLO_E_UNSUPPORTED"
     assert _status(dlo.op_digest, 1, [3], [8], 1, 0) == "DLO_E_ARG"
 
 
