@@ -270,6 +270,34 @@ def mfma_sustained(torch, dev, iters=2000, reps=3):
                     f"{reps} runs each, taken right after the timed steps"}
 
 
+def library_gemm(torch, dev, T, d, reps=5):
+    """hipBLASLt (torch.matmul on bf16) on the block's five GEMM shapes, for context
+    only (the path never calls it): A [T, K] times B^T with B [N, K] row-major, as
+    libdlo's GEMMs take them, no bias or epilogue; median of reps after a warm call."""
+    shapes = {"gemm_qk": (2 * d, d), "gemm_v_t": (d, d), "gemm_out_residual": (d, d),
+              "gemm_fc1_gelu": (4 * d, d), "gemm_fc2_residual": (d, 4 * d)}
+    g = torch.Generator(device="cpu").manual_seed(11)
+    out = {}
+    for name, (N, K) in shapes.items():
+        A = (torch.randn(T, K, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+        B = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+        torch.matmul(A, B.t())
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            C = torch.matmul(A, B.t())
+            e1.record()
+            torch.cuda.synchronize(dev)
+            ts.append(e0.elapsed_time(e1))
+            del C
+        ms = float(np.median(ts))
+        out[name] = {"M": T, "N": N, "K": K, "ms": ms, "TFLOPs": 2 * T * N * K / (ms * 1e-3) / 1e12}
+        del A, B
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_facts():
     """Host CPU model (lscpu, /proc/cpuinfo), usable cores, and the BLAS library numpy runs on."""
     import subprocess
@@ -408,6 +436,8 @@ def main():
                     help="also time the oracle's whole first block at full shape (minutes for Super)")
     ap.add_argument("--resident-steps", type=int, default=None,
                     help="timed all-resident steps for the run-based cross-check (default min(steps, 5))")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time hipBLASLt (torch.matmul) on the block's GEMM shapes, for context")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the streamed == resident bit-exact check")
     args = ap.parse_args()
@@ -550,6 +580,11 @@ def main():
     log(f"sustained MFMA rate: {mfma_ceiling['mfma_32x32x16_TFLOPs']:.0f} / "
         f"{mfma_ceiling['mfma_16x16x32_TFLOPs']:.0f} TFLOP/s (32x32x16 / 16x16x32)")
 
+    if args.library_gemm:
+        lib_gemm = library_gemm(torch, dev, T, w.width(0))
+        log("hipBLASLt on the block's GEMM shapes: " +
+            ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in lib_gemm.items()))
+
     blocks_done = n * P * args.steps
     result = {
         "metric": "DiT blocks/s with streaming",
@@ -589,6 +624,9 @@ def main():
         "setup_s": {"pin_alloc": t_alloc, "generate": t_gen, "pack": t_pack},
         "env": environment(torch, dev),
     }
+    if args.library_gemm:
+        result["library_gemm"] = {"note": "hipBLASLt via torch.matmul, bf16, no epilogue; context only",
+                                  **lib_gemm}
 
     if not args.no_verify:
         # the pages' own correctness criterion at full scale: streamed == resident, bit-exact

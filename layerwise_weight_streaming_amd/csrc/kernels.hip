@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "device_common.h"
@@ -55,6 +56,46 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(const uint16_t *__restr
   }
   acc = wave_sum(acc);
   if (lane == 0) out[row] = acc + b[row];
+}
+
+// The same GEMV for d % 512 == 0 (NCH = d / 512 16-B chunks per lane): each
+// wave keeps its lanes' share of silu(c) in registers and takes rows row,
+// row + (waves in the grid), ..., issuing all NCH loads of a row before its
+// sums, with a grid of as many workgroups as are resident at once.  The
+// per-lane order of summation is adaln_gemv_kernel's (bit-identical results);
+// the row loop saves the re-reads of silu(c) and puts NCH loads in flight per
+// wave (Super shape, 315 MB: 58 -> 50 us, 6.3 TB/s).
+template <int NCH>
+__global__ __launch_bounds__(256) void adaln_gemv_rows_kernel(const uint16_t *__restrict__ W,
+                                                              const float *__restrict__ sc,
+                                                              const float *__restrict__ b,
+                                                              float *__restrict__ out, int rows, int d) {
+  const int lane = threadIdx.x % WAVE;
+  const int nw = gridDim.x * 4;
+  float4 s[2 * NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (lane + WAVE * j) * 8;
+    s[2 * j] = *reinterpret_cast<const float4 *>(sc + c);
+    s[2 * j + 1] = *reinterpret_cast<const float4 *>(sc + c + 4);
+  }
+  for (int row = blockIdx.x * 4 + threadIdx.x / WAVE; row < rows; row += nw) {
+    const uint16_t *w = W + (int64_t)row * d;
+    u32x4 q[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) q[j] = *reinterpret_cast<const u32x4 *>(w + (lane + WAVE * j) * 8);
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const float4 s0 = s[2 * j], s1 = s[2 * j + 1];
+      acc += __uint_as_float(q[j][0] << 16) * s0.x + __uint_as_float(q[j][0] & 0xffff0000u) * s0.y;
+      acc += __uint_as_float(q[j][1] << 16) * s0.z + __uint_as_float(q[j][1] & 0xffff0000u) * s0.w;
+      acc += __uint_as_float(q[j][2] << 16) * s1.x + __uint_as_float(q[j][2] & 0xffff0000u) * s1.y;
+      acc += __uint_as_float(q[j][3] << 16) * s1.z + __uint_as_float(q[j][3] & 0xffff0000u) * s1.w;
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) out[row] = acc + b[row];
+  }
 }
 
 // The same GEMV on an FP8 block's E4M3 codes: each lane decodes 16 codes per
@@ -648,8 +689,50 @@ hipError_t launch_silu(const float *c, float *out, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+template <int NCH>
+hipError_t gemv_rows_launch(const uint16_t *W, const float *sc, const float *b, float *out, int rows, int d,
+                            hipStream_t s) {
+  // workgroups resident at once on the whole chip (the grid loops over rows, so
+  // this sets only the speed); the same for every MI355X in the process
+  static std::atomic<int> cap{0};
+  int c = cap.load(std::memory_order_relaxed);
+  if (c == 0) {
+    int occ = 0, ncu = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, adaln_gemv_rows_kernel<NCH>, 256, 0) != hipSuccess ||
+        occ < 1 || ncu < 1) {
+      occ = 2;
+      ncu = 256;
+    }
+    c = occ * ncu;
+    cap.store(c, std::memory_order_relaxed);
+  }
+  const int need = (rows + 3) / 4;
+  hipLaunchKernelGGL(adaln_gemv_rows_kernel<NCH>, dim3(need < c ? need : c), dim3(256), 0, s, W, sc, b, out,
+                     rows, d);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_adaln_gemv(const uint16_t *W, const float *sc, const float *b, float *out,
                              int rows, int d, hipStream_t s) {
+  // the row-looping form pays from d = 2048 on (at d = 1024 the one-row-per-wave
+  // grid is 8 % faster); the two give the same bits
+  if (d % 512 == 0 && d >= 2048 && d <= 8192) {
+    switch (d / 512) {
+#define DLO_GEMV_CASE(N) \
+  case N:                \
+    return gemv_rows_launch<N>(W, sc, b, out, rows, d, s);
+      DLO_GEMV_CASE(4) DLO_GEMV_CASE(5) DLO_GEMV_CASE(6) DLO_GEMV_CASE(7) DLO_GEMV_CASE(8) DLO_GEMV_CASE(9)
+      DLO_GEMV_CASE(10) DLO_GEMV_CASE(11) DLO_GEMV_CASE(12) DLO_GEMV_CASE(13) DLO_GEMV_CASE(14)
+      DLO_GEMV_CASE(15) DLO_GEMV_CASE(16)
+#undef DLO_GEMV_CASE
+      default:
+        break;
+    }
+  }
   hipLaunchKernelGGL(adaln_gemv_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, W, sc, b, out,
                      rows, d);
   return hipGetLastError();

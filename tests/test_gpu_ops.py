@@ -304,17 +304,21 @@ def test_ln_modulate(T, d, ldx, goff):
     assert nbad == 0, (nbad, worst)
 
 
-@pytest.mark.parametrize("d", [256, 1024, 5120])
-def test_adaln(d):
+@pytest.mark.parametrize("rows,d", [(6 * 256, 256), (6 * 1024, 1024), (6 * 2048, 2048), (6 * 5120, 5120),
+                                    (6 * 8192, 8192),
+                                    # the row-looping form (d % 512 == 0, d >= 2048): fewer rows than
+                                    # waves, and several rows per wave
+                                    (37, 4096), (13001, 2048)])
+def test_adaln(rows, d):
     torch = require_gpu()
-    say("adaln", d)
-    W = _bf16_rand(30 + d, (6 * d, d), 0.02)
-    b = synth.normal_f32(31, 9, 0, 0, (6 * d,), 0.0, 0.02)
+    say("adaln", rows, d)
+    W = _bf16_rand(30 + d, (rows, d), 0.02)
+    b = synth.normal_f32(31, 9, 0, 0, (rows,), 0.0, 0.02)
     c = synth.normal_f32(32, 9, 0, 0, (d,))
     dW, db, dc = _dev(torch, W), _dev(torch, b), _dev(torch, c)
-    out = torch.zeros(6 * d, dtype=torch.float32, device="cuda")
+    out = torch.zeros(rows, dtype=torch.float32, device="cuda")
     ws = torch.empty(4 * d, dtype=torch.uint8, device="cuda")
-    dlo.op_adaln(dW.data_ptr(), db.data_ptr(), dc.data_ptr(), 6 * d, d, out.data_ptr(),
+    dlo.op_adaln(dW.data_ptr(), db.data_ptr(), dc.data_ptr(), rows, d, out.data_ptr(),
                  ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     ref = of.linear(of.silu(c.astype(np.float64))[None, :], bf16_to_f64(W), b.astype(np.float64))[0]
