@@ -396,7 +396,8 @@ def cpu_baseline(w, seed, n_blocks, rows=640, full_block=False):
            "tiny_full_stack": [cpu_tiny_stack(seed, 1), cpu_tiny_stack(seed, cores)]}
     if full_block:
         t0 = time.perf_counter()
-        of.dit_block(x, c, P, H)
+        of.dit_block(x, c, P, H, progress=lambda msg: print(
+            f"[bench] cpu full block: {msg} ({time.perf_counter() - t0:.0f} s)", file=sys.stderr, flush=True))
         tb = time.perf_counter() - t0
         out["full_block"] = {"s_per_block": tb, "blocks_per_s": 1.0 / tb,
                              "extrapolated_stack_s": tb * n_blocks * w.passes,

@@ -111,11 +111,13 @@ def linear(a, w, b):
     return a @ w.T + b
 
 
-def attention(q, k, v, n_heads, chunk=1024):
+def attention(q, k, v, n_heads, chunk=1024, progress=None):
     """Per head: softmax(q_j k_j^T / sqrt(dh)) v_j over all keys; heads concatenated.
 
     q: [Tq, d], k and v: [Tk, d]; computed in query chunks of at most ``chunk``
-    rows (a memory bound only: each query row is independent).
+    rows (a memory bound only: each query row is independent).  progress, if
+    given, is called with a short message after each head (no effect on the
+    result).
     """
     tq, d = q.shape
     dh = d // n_heads
@@ -130,6 +132,8 @@ def attention(q, k, v, n_heads, chunk=1024):
             p = np.exp(s)
             p /= p.sum(axis=1, keepdims=True)
             out[r0:r0 + chunk, cols] = p @ vj
+        if progress is not None:
+            progress(f"attention head {j + 1}/{n_heads}")
     return out
 
 
@@ -139,7 +143,7 @@ def modulation(c, P, d):
     return [mod[i * d:(i + 1) * d] for i in range(6)]
 
 
-def dit_block(x, c, P, n_heads, act_fp8=False, act_mx=False, act_int8=False):
+def dit_block(x, c, P, n_heads, act_fp8=False, act_mx=False, act_int8=False, progress=None):
     """One block on residual x [T, D] (float64, updated copy returned).
 
     act_fp8: the four block linears take their input through per-token E4M3
@@ -151,7 +155,8 @@ def dit_block(x, c, P, n_heads, act_fp8=False, act_mx=False, act_int8=False):
     inputs (oracle.quant.fake_quant_mx_rows: per row, blocks of 32 along the
     input dimension), the W8A8 form of an MXFP8 block's linears.  act_int8:
     the same with per-row int8 inputs (oracle.quant.fake_quant_int8_rows), the
-    W8A8 form of an INT8 block's linears.
+    W8A8 form of an INT8 block's linears.  progress, if given, is called with a
+    short message after each stage (no effect on the result).
     """
     from . import fp8, quant
 
@@ -168,13 +173,18 @@ def dit_block(x, c, P, n_heads, act_fp8=False, act_mx=False, act_int8=False):
     shift1, scale1, gate1, shift2, scale2, gate2 = modulation(c, P, d)
     xb = x[:, :d]
     h = layer_norm(xb, P["norm1.weight"], P["norm1.bias"], P["norm1.eps"][0]) * (1.0 + scale1) + shift1
+    say = progress if progress is not None else (lambda msg: None)
     qkv = linear(lin_in(h), P["attn.qkv.weight"], P["attn.qkv.bias"])
+    say("qkv")
     q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
-    a = attention(q, k, v, n_heads)
+    a = attention(q, k, v, n_heads, progress=progress)
     xb += gate1 * linear(lin_in(a), P["attn.out.weight"], P["attn.out.bias"])
+    say("out")
     h2 = layer_norm(xb, P["norm2.weight"], P["norm2.bias"], P["norm2.eps"][0]) * (1.0 + scale2) + shift2
     u = gelu_erf(linear(lin_in(h2), P["mlp.fc1.weight"], P["mlp.fc1.bias"]))
+    say("fc1")
     xb += gate2 * linear(lin_in(u), P["mlp.fc2.weight"], P["mlp.fc2.bias"])
+    say("fc2")
     return x
 
 
