@@ -18,21 +18,29 @@ reproduce the single-block figures), as much as that separation.  So:
   GEMM and the FP8 adaLN GEMV element by element) in test_gpu_fp8_ops.py;
 * the streamed W8A8 block is checked bit for bit against those ops called one
   by one;
-* one tiny block is compared with the W8A8 oracle (rms of the update within
-  1 %, max-norm within 2 x the stack tolerance) and must sit at least four times
-  closer to it than to the W8A16 oracle;
+* one tiny block is compared with the W8A8 oracle against a prediction: a CPU
+  model of the GPU's rounding points (tests/w8a8_standin.py: the oracle's
+  steps with the GPU's bf16 storage and fp32 arithmetic; with the rounding off
+  it is the oracle, test_w8a8_model.py) lands 0.60 % (FP8), 0.39 % (MXFP8) and
+  1.00 % (INT8) from the oracle, and the GPU must land within half of that
+  prediction of it, nearer the model than the model is to the oracle, within
+  eps1 = 1.5 x the prediction rounded up to 0.5 % (1 %, 1 %, 2 %), within 2 x
+  the stack tolerance in max-norm, and nearer the W8A8 oracle than the W8A16
+  one (4x for FP8 and MXFP8);
 * stacks check the streaming (slot bytes and digests = oracle, hook schedule),
   streamed == resident bit for bit, that the flag changes FP8 blocks and leaves
   bf16 blocks alone, and the rms error of the update against a bound derived
-  from the single-block one, eps1 (1 % FP8 and MXFP8, 1.5 % INT8): with N_q
-  quantised block steps, eps <= 2 eps1 sqrt(N_q).  Model: each quantised step
-  adds a divergence of at most eps1 of an update; its code decisions are taken
-  on inputs that already differ from the oracle's, so the steps' contributions
-  are uncorrelated and add in quadrature; the factor 2 covers the propagation of
+  from eps1: with N_q quantised block steps, eps <= 2 eps1 sqrt(N_q).  Model:
+  each quantised step adds a divergence of at most eps1 of an update; its code
+  decisions are taken on inputs that already differ from the oracle's, so the
+  steps' contributions are uncorrelated and add in quadrature (the CPU model
+  shows it: another fp32 summation order alone moves a 6-step FP8 stack by
+  64 % of its distance to the oracle); the factor 2 covers the propagation of
   earlier divergence through later blocks (LayerNorm inputs, weights of std
   0.02) with the accumulated update taken as no smaller than one step's.  The
   stack figures were known when this model was written; it is checked by its
-  margins (the nine cases sit at 0.17-0.7 of it), not tuned to them.
+  margins (the nine cases sit at 0.1-0.7 of it), not tuned to them.  On the
+  tiny stack the CPU model's prediction is checked as for one block.
 
 What the comparison with the oracle can establish: that each op computes its
 definition (exactly, for codes, scales and integer products), that the block
@@ -55,13 +63,15 @@ from oracle import forward as of
 from oracle import plan as op
 from oracle import quant
 from oracle import schedule as sc
+from tests import w8a8_standin as ws
 from tests.gpu_util import TOL, fp8_blocks, make_runner_params, rel_err, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
 
-# the single-block rms bound of the update against the W8A8 oracle
-EPS1 = {"fp8": 1e-2, "mxfp8": 1e-2, "int8": 1.5e-2}
+# the single-block rms bound of the update against the W8A8 oracle: the CPU model's
+# prediction (tests/w8a8_standin.py) times 1.5, rounded up to a multiple of 0.5 %
+EPS1 = {"fp8": 1e-2, "mxfp8": 1e-2, "int8": 2e-2}
 
 
 def _rms_rel(got, ref):
@@ -89,33 +99,40 @@ def _blocks(w, stack, form, which=None):
 
 @pytest.mark.parametrize("form", ["fp8", "mxfp8", "int8"])
 def test_w8a8_single_block_matches_the_w8a8_oracle(form):
-    """One FP8, MXFP8 or INT8 block (d = 256, 4 heads, 64 tokens), one pass."""
+    """One FP8, MXFP8 or INT8 block (d = 256, 4 heads, 64 tokens), one pass.
+
+    Bounds from the CPU model of the GPU's rounding points (tests/w8a8_standin.py),
+    computed here on the same inputs before the GPU result is looked at: its rms
+    distance e_pred to the W8A8 oracle predicts the GPU's (the GPU must land within
+    half of e_pred of it, and nearer the model than the model is to the oracle);
+    EPS1 is 1.5 e_pred rounded up to 0.5 % (test_w8a8_model.py), so e8 <= EPS1
+    follows; and the block must sit nearer the W8A8 oracle than the W8A16 one (FP8,
+    MXFP8: 4x nearer, as the model does by 6x and 11x; INT8: nearer, the model's
+    ratio being 0.72, since int8 inputs move a block only ~1.4 % from W8A16)."""
     require_gpu()
     w = synth.WORKLOADS["tiny"]
     stack = synth.make_stack(w, 21, 1)
     blocks = _blocks(w, stack, form)
+    x0 = np.asarray(stack.x, np.float64)
+    heads = [w.heads(0)]
+    ref8 = of.forward_stack(x0, stack.c, blocks, heads, 1, act_fp8=True)
+    ref16 = of.forward_stack(x0, stack.c, blocks, heads, 1)
+    model = ws.stack(x0, stack.c, blocks, heads, 1, form)
+    e_pred = _rms_rel(model - x0, ref8 - x0)
     r = make_runner_params(w, blocks)
     r.set_inputs(stack.x, stack.c)
     r.forward(1, flags=dlo.FP8_COMPUTE, want_run=False)
     x_gpu = r.x_host().astype(np.float64)
     r.close()
-    x0 = np.asarray(stack.x, np.float64)
-    heads = [w.heads(0)]
-    ref8 = of.forward_stack(x0, stack.c, blocks, heads, 1, act_fp8=True)
-    ref16 = of.forward_stack(x0, stack.c, blocks, heads, 1)
     e_max = rel_err(x_gpu - x0, ref8 - x0)
     e8, e16 = _rms_rel(x_gpu - x0, ref8 - x0), _rms_rel(x_gpu - x0, ref16 - x0)
-    say(f"W8A8 {form} block: update max {e_max:.3e}; rms vs W8A8 oracle {e8:.3e}, vs W8A16 oracle {e16:.3e}")
-    if form == "int8":
-        # int8 activations (step amax / 127) move a block's output only ~1.4 % (rms) from the
-        # W8A16 result, while the int8 decisions taken on the GPU's bf16 inputs (which differ
-        # from the oracle's by bf16 rounding upstream, the bf16 copy of the adaLN weight
-        # included) already account for ~1 %: closer to its own oracle, not 4x closer
-        assert e8 <= EPS1[form] and e_max <= 2 * TOL
-        assert e8 < 0.85 * e16
-    else:
-        assert e8 <= EPS1[form] and e_max <= 2 * TOL
-        assert e8 < 0.25 * e16
+    e_model = _rms_rel(x_gpu - x0, model - x0)
+    say(f"W8A8 {form} block: update max {e_max:.3e}; rms vs W8A8 oracle {e8:.3e} (model predicts "
+        f"{e_pred:.3e}), vs W8A16 oracle {e16:.3e}, vs the model {e_model:.3e}")
+    assert abs(e8 - e_pred) <= 0.5 * e_pred
+    assert e_model < e_pred
+    assert e8 <= EPS1[form] and e_max <= 2 * TOL
+    assert e8 < (1.0 if form == "int8" else 0.25) * e16
 
 
 @pytest.mark.parametrize("form", ["fp8", "mxfp8", "int8"])
@@ -253,6 +270,11 @@ def test_w8a8_stack_streamed(form, name, n_blocks, tokens, which):
     bound = 2 * EPS1[form] * math.sqrt(n_q)
     say(f"update rms rel err vs the W8A8 oracle {e:.3e} (bound {bound:.3e}, {n_q} quantised block steps)")
     assert e < bound
+    if name == "tiny":   # every block quantised, small enough for the CPU model
+        model = ws.stack(x0, stack.c, blocks, heads, w.passes, form)
+        e_pred = _rms_rel(model - x0, ref - x0)
+        say(f"the CPU model of the GPU's rounding points predicts {e_pred:.3e}")
+        assert abs(e - e_pred) <= 0.5 * e_pred
 
 
 def test_w8a8_leaves_bf16_blocks_alone():
