@@ -232,6 +232,20 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
 #pragma unroll
     for (int r = 0; r < 16; ++r) sa[kb][r] -= m_run;
 
+  // Scheduling of the 2 DT PV MFMAs of two 16-key chunks: their V^T operand
+  // reads three ahead, NV VALU instructions after each MFMA.
+  auto pv_schedule = [&](auto nv_c) {
+    constexpr int NV = decltype(nv_c)::value;
+    constexpr int RV = 3;
+    __builtin_amdgcn_sched_group_barrier(0x100, RV, 0);  // LDS read
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i < 2 * DT - RV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+    }
+  };
+
   // block j (parity P = j & 1): scores sc (computed one iteration earlier),
   // next block's scores into sn; K_{j+1} in K slot 1 - P, V_j in V slot P
   auto iter = [&](int j, auto par_c, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
@@ -289,6 +303,10 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
         const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vb + t * 32 * AK * 2 + v_lane[c]);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
       }
+    // V^T reads three MFMAs ahead, four VALU instructions of the second half's
+    // P under each MFMA (left to itself the compiler issues each read just
+    // before its MFMA and waits on it: 1.5-1.9 % slower on the Super shape)
+    pv_schedule(std::integral_constant<int, 4>{});
     if (__any(!(ls1 < P_LIMIT)))
       raise(sc[1], pf[2], pf[3], ls1, [&](float delta) {
 #pragma unroll
@@ -305,6 +323,7 @@ __global__ __launch_bounds__(A_WAVES * 64, A_WAVES == 4 ? 2 : 1) void attention_
         const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vb + t * 32 * AK * 2 + v_lane[c]);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
       }
+    pv_schedule(std::integral_constant<int, 0>{});
   };
   int j = 0;
   for (; j + 1 < nkb; j += 2) {
