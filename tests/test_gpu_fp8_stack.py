@@ -136,7 +136,9 @@ def test_w8a8_single_block_matches_the_w8a8_oracle(form):
 
 
 @pytest.mark.parametrize("form", ["fp8", "mxfp8", "int8"])
-def test_w8a8_block_is_the_op_sequence(form):
+@pytest.mark.parametrize("shape", [None, dict(widths=(1280,), D=1280, tokens=100)],
+                         ids=["tiny", "d1280_T100"])
+def test_w8a8_block_is_the_op_sequence(form, shape):
     """The streamed W8A8 block computes, bit for bit, what the C-ABI ops compute when
     called one by one in the block's order (each op is checked against the oracle in
     test_gpu_fp8_ops.py, test_gpu_quant_weights.py and test_gpu_ops.py): adaLN (FP8:
@@ -145,9 +147,13 @@ def test_w8a8_block_is_the_op_sequence(form):
     products (the
     v part's MXFP8 scales a column slice of the fused weight's), attention, the input
     quantisation of a, the gated out product, LN2 + modulate, that of h2, the fc1
-    product with GELU, that of u, the gated fc2 product."""
+    product with GELU, that of u, the gated fc2 product.  The second shape (d = 1280:
+    320 float4 column chunks per row, the second 256-chunk pass of the LayerNorm
+    kernels partly idle; 100 tokens, off the 64-row grid) covers the fused
+    LayerNorm + quantisation's partial chunk pass and ragged rows."""
     torch = require_gpu()
-    w = synth.WORKLOADS["tiny"]
+    w = synth.WORKLOADS["tiny"] if shape is None else synth.WORKLOADS["tiny"].with_(**shape)
+    say(f"W8A8 {form} op sequence d={w.width(0)} T={w.tokens}")
     stack = synth.make_stack(w, 23, 1)
     blocks = _blocks(w, stack, form)
     r = make_runner_params(w, blocks)
