@@ -437,6 +437,8 @@ def main():
                     help="also time the oracle's whole first block at full shape (minutes for Super)")
     ap.add_argument("--resident-steps", type=int, default=None,
                     help="timed all-resident steps for the run-based cross-check (default min(steps, 5))")
+    ap.add_argument("--async-enqueue", action="store_true",
+                    help="timed steps with DLO_ASYNC_ENQUEUE (a library thread enqueues each step)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time hipBLASLt (torch.matmul) on the block's GEMM shapes, for context")
     ap.add_argument("--no-verify", action="store_true",
@@ -519,6 +521,7 @@ def main():
     R = args.resident_layers
     w8a8 = args.compute == "fp8"
     cflags = dlo.FP8_COMPUTE if w8a8 else 0
+    aflags = dlo.ASYNC_ENQUEUE if args.async_enqueue else 0
     if R:
         r.make_resident(R)
         log(f"{R} resident layers placed")
@@ -529,7 +532,12 @@ def main():
 
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    runs = [r.forward(P, flags=dlo.TRACE_TIMING | cflags, n_resident=R) for _ in range(args.steps)]
+    runs = []
+    for _ in range(args.steps):
+        if runs:
+            runs[-1].enqueued()   # ASYNC_ENQUEUE: the previous step's program is fully enqueued
+        runs.append(r.forward(P, flags=dlo.TRACE_TIMING | cflags | aflags, n_resident=R))
+    runs[-1].enqueued()
     r.synchronize()
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
@@ -602,7 +610,7 @@ def main():
                    "k": w.k, "passes": P, "slot_bytes": r.plan.slot_bytes,
                    "block_copy_bytes": max(copy_bytes), "host_store_bytes": sum(copy_bytes),
                    "parallelism": "single GPU", "store": args.store, "resident_layers": R,
-                   "weights": args.weights, "compute": args.compute,
+                   "weights": args.weights, "compute": args.compute, "async_enqueue": args.async_enqueue,
                    "pinned_blocks": store_info["pinned_blocks"],
                    "staged_blocks": store_info["staged_blocks"]},
         "tokens_per_s": T * P * args.steps / wall,

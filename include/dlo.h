@@ -291,6 +291,16 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
                                 FP8 block's adaLN GEMV reads its codes (dlo_op_adaln_fp8);
                                 MXFP8 and INT8 blocks' run on the dequantised weight.  bf16
                                 blocks are unaffected. */
+#define DLO_ASYNC_ENQUEUE 16u /* the call returns once the run is validated and its
+                                 resources exist; a library thread enqueues the program on
+                                 the two streams (filling the staging buffers of pageable
+                                 blocks, [Doc] "Rank-local path without DLO AllGather": the
+                                 staging slots as a pipeline stage of their own) while the
+                                 caller goes on.  Needs run_out.  Until dlo_run_enqueued
+                                 returns, the caller enqueues nothing on either stream (their
+                                 order is enqueue order), starts no other run on the plan
+                                 (DLO_E_STATE) and keeps the plan, the store and the args'
+                                 device buffers alive; the args struct itself is copied. */
 
 typedef struct {
   void *slot[2];            /* device, slot_bytes each, distinct (unused if nothing streams) */
@@ -307,7 +317,7 @@ typedef struct {
   int32_t tokens;           /* rows of x (batch 1), >= 1; (tokens + 64) * 3 * widest d * 2
                                < 2^31, else DLO_E_UNSUPPORTED */
   int32_t passes;           /* chained passes over the stack, >= 1 */
-  uint32_t flags;           /* DLO_TRACE_* | DLO_RESIDENT | DLO_FP8_COMPUTE */
+  uint32_t flags;           /* DLO_TRACE_* | DLO_RESIDENT | DLO_FP8_COMPUTE | DLO_ASYNC_ENQUEUE */
   int32_t n_resident;       /* resident layers R in [0, n] ([Doc] "Validation coverage":
                                resident-layer requests): blocks 0 .. R-1 are read from
                                resident_blocks[b] and never copied; blocks R .. n-1 stream
@@ -326,7 +336,8 @@ typedef struct {
  * has drained.  With a fully pinned store the call returns without waiting;
  * when blocks are staged, the calling thread fills each staging buffer in step
  * order (waiting for the buffer's previous DMA first), so the call returns once
- * the last staged block has been handed to the copy stream.
+ * the last staged block has been handed to the copy stream -- unless
+ * DLO_ASYNC_ENQUEUE hands all of that to a library thread.
  * If run_out is non-NULL it receives a handle for dlo_slot_trace (free with
  * dlo_run_destroy); otherwise the library releases the run's resources once it
  * has completed. */
@@ -379,6 +390,13 @@ int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
 const char *dlo_kernel_name(int32_t j);
 
 void dlo_run_destroy(dlo_run *run);   /* waits for the run first */
+
+/* DLO_ASYNC_ENQUEUE: waits until the run's program is fully enqueued and returns
+ * the status of that enqueue (the error a synchronous call would have returned;
+ * DLO_OK at once for a run started without the flag).  After it the streams and
+ * the plan are the caller's again.  dlo_slot_trace, dlo_run_kernel_times and
+ * dlo_run_destroy call it first. */
+int dlo_run_enqueued(dlo_run *run);
 
 /* Message for the last failure on this thread (valid until the next call). */
 const char *dlo_last_error(void);

@@ -24,7 +24,7 @@ STATUS = {0: "DLO_OK", -1: "DLO_E_ARG", -2: "DLO_E_HOSTMEM", -3: "DLO_E_PIN",
 DTYPES = {"bf16": 0, "f32": 1, "fp8": 2, "i8": 3, "e8m0": 4}   # fp8: OCP E4M3; e8m0: MX block scale
 DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
 STORE_PINNED, STORE_PAGEABLE, STORE_AUTO = 0, 1, 2
-TRACE_DIGEST, TRACE_TIMING, RESIDENT, FP8_COMPUTE = 1, 2, 4, 8
+TRACE_DIGEST, TRACE_TIMING, RESIDENT, FP8_COMPUTE, ASYNC_ENQUEUE = 1, 2, 4, 8, 16
 EPI_BIAS, EPI_BIAS_GELU, EPI_GATED_RESIDUAL, EPI_BIAS_T = 0, 1, 2, 3
 KERNELS_PER_BLOCK = 14
 MAX_GROUPS = 3
@@ -129,6 +129,7 @@ _SIGS = {
     "dlo_run_kernel_times": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
                                             ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "dlo_run_destroy": (None, [ctypes.c_void_p]),
+    "dlo_run_enqueued": (ctypes.c_int, [ctypes.c_void_p]),
     "dlo_op_adaln": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
     "dlo_op_mfma_rate": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
@@ -464,6 +465,10 @@ class Run:
             self.close()
         except Exception:
             pass
+
+    def enqueued(self):
+        """dlo_run_enqueued: joins an ASYNC_ENQUEUE run's enqueue (returns at once otherwise)."""
+        _check(lib().dlo_run_enqueued(self.h))
 
     def trace(self):
         n = ctypes.c_int64()

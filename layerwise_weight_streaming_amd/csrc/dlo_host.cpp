@@ -237,6 +237,7 @@ struct dlo_plan {
   mutable std::mutex mu;
   mutable std::vector<dlo_run *> detached;   // runs started without a handle
   mutable hipEvent_t last_done = nullptr;    // end of the previous run (any stream)
+  mutable dlo_run *enqueuing = nullptr;      // DLO_ASYNC_ENQUEUE run still being enqueued
 };
 
 struct dlo_host_store {
@@ -267,7 +268,24 @@ struct dlo_run {
   uint64_t *d_digest = nullptr;
   bool finished = false;
   std::vector<float> kernel_ms;
+  // DLO_ASYNC_ENQUEUE: the thread enqueuing the program, its status and message,
+  // and its own copy of the caller's arguments
+  const dlo_plan *plan = nullptr;
+  std::thread worker;
+  int enqueue_rc = 0;
+  std::string enqueue_msg;
+  dlo_forward_args args{};
+  std::vector<const void *> res_blocks;
 };
+
+// Joins a DLO_ASYNC_ENQUEUE run's enqueue thread (no-op otherwise) and lets the
+// plan start runs again.
+void finish_enqueue(dlo_run *r) {
+  if (!r || !r->worker.joinable()) return;
+  r->worker.join();
+  std::lock_guard<std::mutex> lk(r->plan->mu);
+  if (r->plan->enqueuing == r) r->plan->enqueuing = nullptr;
+}
 
 namespace {
 
@@ -280,6 +298,7 @@ int check_hip(hipError_t e, const char *what) {
 
 void run_free(dlo_run *r) {
   if (!r) return;
+  finish_enqueue(r);
   if (r->final_ev) (void)hipEventSynchronize(r->final_ev);
   for (auto &e : r->ev)
     if (e) (void)hipEventDestroy(e);
@@ -699,6 +718,10 @@ void dlo_plan_destroy(dlo_plan *plan) {
   if (!plan) return;
   {
     std::lock_guard<std::mutex> lk(plan->mu);
+    if (plan->enqueuing) {   // a run still being enqueued: let it finish enqueuing
+      if (plan->enqueuing->worker.joinable()) plan->enqueuing->worker.join();
+      plan->enqueuing = nullptr;
+    }
     reap_detached(plan, true);
     if (plan->last_done) (void)hipEventDestroy(plan->last_done);
   }
@@ -1228,7 +1251,7 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
 
 int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dlo_forward_args *a) {
   if (!plan || !a) return fail(DLO_E_ARG, "NULL plan or args");
-  if (a->flags & ~(DLO_TRACE_DIGEST | DLO_TRACE_TIMING | DLO_RESIDENT | DLO_FP8_COMPUTE))
+  if (a->flags & ~(DLO_TRACE_DIGEST | DLO_TRACE_TIMING | DLO_RESIDENT | DLO_FP8_COMPUTE | DLO_ASYNC_ENQUEUE))
     return fail(DLO_E_ARG, "unknown flags 0x%x", a->flags);
   const int n = (int)plan->blocks.size();
   if (!(a->flags & DLO_RESIDENT) && (a->n_resident < 0 || a->n_resident > n))
@@ -1288,12 +1311,94 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
 
 }  // namespace
 
+namespace {
+// Enqueues a validated run's program on its two streams; the calling thread
+// fills the staging buffers of pageable blocks.  Returns a dlo status.
+int enqueue_program(const dlo_plan *plan, dlo_host_store *store, const dlo_forward_args *a, dlo_run *run,
+                    const std::vector<dlo_sched_op> &prog, bool resident) {
+  constexpr int TEV = 3 + DLO_KERNELS_PER_BLOCK;  // copy begin, copy end, compute begin, kernels
+  hipStream_t cs = (hipStream_t)a->compute_stream, ps = (hipStream_t)a->copy_stream;
+  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d, plan->max_i8_d);
+  hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
+  auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
+  hipError_t e = hipSuccess;
+  int place_rc = DLO_OK;
+  auto HIP = [&](hipError_t x) {
+    if (e == hipSuccess && x != hipSuccess) e = x;
+    return e == hipSuccess;
+  };
+
+  // order after the previous run (even one on other streams) and after the caller's
+  // work on the compute stream
+  HIP(hipStreamWaitEvent(cs, plan->last_done, 0));
+  if (!resident) HIP(hipStreamWaitEvent(ps, plan->last_done, 0));
+  if (t0) HIP(hipEventRecord(t0, cs));
+  HIP(dlo::launch_silu(a->cond, w.silu_c, plan->max_d, cs));
+
+  for (const dlo_sched_op &op : prog) {
+    if (e != hipSuccess) break;
+    hipStream_t s = op.stream == DLO_STREAM_COMPUTE ? cs : ps;
+    switch (op.kind) {
+      case DLO_OP_RECORD:
+        HIP(hipEventRecord(run->ev[op.event], s));
+        break;
+      case DLO_OP_WAIT:
+        HIP(hipStreamWaitEvent(s, run->ev[op.event], 0));
+        break;
+      case DLO_OP_COPY: {
+        if (e == hipSuccess) {
+          int prc = place(plan, store, op.block,
+                          static_cast<char *>(a->slot[op.slot]), ps,
+                          run->timing ? tev(op.step, 0) : nullptr);
+          if (prc) {
+            place_rc = prc;
+            e = hipErrorUnknown;
+          }
+        }
+        if (run->timing) HIP(hipEventRecord(tev(op.step, 1), ps));
+        break;
+      }
+      case DLO_OP_COMPUTE: {
+        const BlockPlan &bp = plan->blocks[op.block];
+        const char *base = op.slot < 0 ? static_cast<const char *>(a->resident_blocks[op.block])
+                                       : static_cast<const char *>(a->slot[op.slot]);
+        int64_t offs[DLO_MAX_GROUPS], lens[DLO_MAX_GROUPS];
+        for (int g = 0; g < bp.n_groups; ++g) {
+          offs[g] = bp.gregion[g];
+          lens[g] = (int64_t)plan->k * bp.gshard[g] * elt_bytes(bp.gdtype[g]);
+        }
+        if (run->digest)
+          HIP(dlo::launch_digest(base, offs, lens, bp.n_groups, run->d_digest + 2 * op.step, cs));
+        if (run->timing) HIP(hipEventRecord(tev(op.step, 2), cs));
+        if (e == hipSuccess)
+          HIP(block_forward(bp, base, a, w, cs, run->timing ? &run->tev[(size_t)(op.step * TEV + 3)] : nullptr));
+        if (run->digest)
+          HIP(dlo::launch_digest(base, offs, lens, bp.n_groups, run->d_digest + 2 * op.step + 1, cs));
+        break;
+      }
+    }
+  }
+  HIP(hipEventRecord(run->final_ev, cs));
+  HIP(hipEventRecord(plan->last_done, cs));
+  if (e != hipSuccess) {
+    if (place_rc) return place_rc;
+    return fail(DLO_E_HIP, "enqueue failed: %s (synchronise both streams; x is undefined)",
+                hipGetErrorString(e));
+  }
+  return DLO_OK;
+}
+}  // namespace
+
 int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
                       const dlo_forward_args *a, dlo_run **run_out) {
   if (run_out) *run_out = nullptr;
   int rc = validate_forward(plan, store, a);
   if (rc) return rc;
+  if ((a->flags & DLO_ASYNC_ENQUEUE) && !run_out)
+    return fail(DLO_E_ARG, "DLO_ASYNC_ENQUEUE needs run_out (the run must be joined by dlo_run_enqueued)");
   std::lock_guard<std::mutex> lk(plan->mu);
+  if (plan->enqueuing)
+    return fail(DLO_E_STATE, "a DLO_ASYNC_ENQUEUE run of this plan is still being enqueued (dlo_run_enqueued first)");
   reap_detached(plan, false);
 
   const int n = (int)plan->blocks.size();
@@ -1301,7 +1406,6 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
   const bool resident = n_res == n;  // nothing streams
   const std::vector<Step> steps = hook_steps(n, a->passes, n_res);
   const std::vector<dlo_sched_op> prog = build_program(steps, resident);
-  hipStream_t cs = (hipStream_t)a->compute_stream, ps = (hipStream_t)a->copy_stream;
 
   dlo_run *run = new (std::nothrow) dlo_run;
   if (!run) return fail(DLO_E_HOSTMEM, "out of host memory");
@@ -1344,74 +1448,37 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
     r.t_copy_begin = r.t_copy_end = r.t_compute_begin = r.t_compute_end = -1.f;
   }
 
-  const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d, plan->max_i8_d);
-  hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
-  auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
-  hipError_t e = hipSuccess;
-  int place_rc = DLO_OK;
-  auto HIP = [&](hipError_t x) {
-    if (e == hipSuccess && x != hipSuccess) e = x;
-    return e == hipSuccess;
-  };
-
-  // order after the previous run (even one on other streams) and after the caller's
-  // work on the compute stream
-  HIP(hipStreamWaitEvent(cs, plan->last_done, 0));
-  if (!resident) HIP(hipStreamWaitEvent(ps, plan->last_done, 0));
-  if (t0) HIP(hipEventRecord(t0, cs));
-  HIP(dlo::launch_silu(a->cond, w.silu_c, plan->max_d, cs));
-
-  for (const dlo_sched_op &op : prog) {
-    if (e != hipSuccess) break;
-    hipStream_t s = op.stream == DLO_STREAM_COMPUTE ? cs : ps;
-    switch (op.kind) {
-      case DLO_OP_RECORD:
-        HIP(hipEventRecord(run->ev[op.event], s));
-        break;
-      case DLO_OP_WAIT:
-        HIP(hipStreamWaitEvent(s, run->ev[op.event], 0));
-        break;
-      case DLO_OP_COPY: {
-        if (e == hipSuccess) {
-          int prc = place(plan, const_cast<dlo_host_store *>(store), op.block,
-                          static_cast<char *>(a->slot[op.slot]), ps,
-                          run->timing ? tev(op.step, 0) : nullptr);
-          if (prc) {
-            place_rc = prc;
-            e = hipErrorUnknown;
-          }
-        }
-        if (run->timing) HIP(hipEventRecord(tev(op.step, 1), ps));
-        break;
-      }
-      case DLO_OP_COMPUTE: {
-        const BlockPlan &bp = plan->blocks[op.block];
-        const char *base = op.slot < 0 ? static_cast<const char *>(a->resident_blocks[op.block])
-                                       : static_cast<const char *>(a->slot[op.slot]);
-        int64_t offs[DLO_MAX_GROUPS], lens[DLO_MAX_GROUPS];
-        for (int g = 0; g < bp.n_groups; ++g) {
-          offs[g] = bp.gregion[g];
-          lens[g] = (int64_t)plan->k * bp.gshard[g] * elt_bytes(bp.gdtype[g]);
-        }
-        if (run->digest)
-          HIP(dlo::launch_digest(base, offs, lens, bp.n_groups, run->d_digest + 2 * op.step, cs));
-        if (run->timing) HIP(hipEventRecord(tev(op.step, 2), cs));
-        if (e == hipSuccess)
-          HIP(block_forward(bp, base, a, w, cs, run->timing ? &run->tev[(size_t)(op.step * TEV + 3)] : nullptr));
-        if (run->digest)
-          HIP(dlo::launch_digest(base, offs, lens, bp.n_groups, run->d_digest + 2 * op.step + 1, cs));
-        break;
-      }
+  if (a->flags & DLO_ASYNC_ENQUEUE) {
+    // the caller's arguments outlive the call in the run; the thread takes the
+    // calling thread's device and releases the plan when it has enqueued all
+    run->args = *a;
+    if (n_res > 0 && a->resident_blocks) {
+      run->res_blocks.assign(a->resident_blocks, a->resident_blocks + n_res);
+      run->args.resident_blocks = run->res_blocks.data();
     }
+    run->plan = plan;
+    plan->enqueuing = run;
+    dlo_host_store *st = const_cast<dlo_host_store *>(store);
+    try {
+      run->worker = std::thread([plan, st, run, prog, resident]() {
+        int rc = check_hip(hipSetDevice(run->device), "hipSetDevice");
+        if (!rc) rc = enqueue_program(plan, st, &run->args, run, prog, resident);
+        if (rc) run->enqueue_msg = dlo_last_error();
+        run->enqueue_rc = rc;
+      });
+    } catch (...) {
+      plan->enqueuing = nullptr;
+      run_free(run);
+      return fail(DLO_E_HOSTMEM, "could not start the enqueue thread");
+    }
+    *run_out = run;
+    return ok();
   }
-  HIP(hipEventRecord(run->final_ev, cs));
-  HIP(hipEventRecord(plan->last_done, cs));
-  if (e != hipSuccess) {
+  rc = enqueue_program(plan, const_cast<dlo_host_store *>(store), a, run, prog, resident);
+  if (rc) {
     // work may already be enqueued: keep the run until it drains
     plan->detached.push_back(run);
-    if (place_rc) return place_rc;
-    return fail(DLO_E_HIP, "enqueue failed: %s (synchronise both streams; x is undefined)",
-                hipGetErrorString(e));
+    return rc;
   }
   if (run_out)
     *run_out = run;
@@ -1420,8 +1487,17 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
   return ok();
 }
 
+int dlo_run_enqueued(dlo_run *run) {
+  if (!run) return fail(DLO_E_ARG, "NULL run");
+  finish_enqueue(run);
+  if (run->enqueue_rc) return fail(run->enqueue_rc, "%s", run->enqueue_msg.c_str());
+  return ok();
+}
+
 int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_out) {
   if (!run || !n_out) return fail(DLO_E_ARG, "NULL argument");
+  finish_enqueue(run);
+  if (run->enqueue_rc) return fail(run->enqueue_rc, "%s", run->enqueue_msg.c_str());
   const int64_t total = (int64_t)run->recs.size();
   *n_out = total;
   if (!run->finished) {

@@ -230,6 +230,55 @@ def test_staged_store_matches_pinned(mode, limit_blocks):
     r.close()
 
 
+@pytest.mark.parametrize("mode,limit_blocks", [("pageable", 0), ("auto", 3)])
+def test_async_enqueue_staged_store(mode, limit_blocks):
+    """DLO_ASYNC_ENQUEUE ([Doc] "Rank-local path without DLO AllGather": the staging slots
+    as a pipeline stage of their own): the call returns before its program is enqueued
+    (a synchronous call with staged blocks returns only once the last staged block is
+    handed to the copy stream), another run of the plan is refused until
+    dlo_run_enqueued, and the run computes the synchronous call's bits with the same
+    slot trace and digests."""
+    import time
+    require_gpu()
+    from layerwise_weight_streaming_amd.runner import StackRunner
+    w = synth.WORKLOADS["8blk"]
+    say(f"async enqueue, staged store {mode}")
+    stack = synth.make_stack(w, 6)
+    blocks = [(w.width(b), w.heads(b), ps) for b, ps in enumerate(stack.blocks)]
+    limit = 0
+    if limit_blocks:
+        limit = limit_blocks * (op.plan_block(op.specs_of(stack.blocks[0]), w.k).extent + 16 * 4096)
+    r = StackRunner(spec_blocks(w, w.n_blocks), w.k, w.tokens, w.D, store_mode=mode, pinned_limit=limit)
+    r.pack(0, blocks)
+    r.set_inputs(stack.x, stack.c)
+    r.forward(w.passes, want_run=False)   # staging buffers allocated, code loaded
+    r.synchronize()
+    r.set_inputs(stack.x, stack.c)
+    t0 = time.perf_counter()
+    run = r.forward(w.passes, flags=dlo.TRACE_DIGEST)
+    t_sync = time.perf_counter() - t0
+    tr_sync = run.trace()
+    x_sync = r.x_host()
+    run.close()
+
+    r.set_inputs(stack.x, stack.c)
+    t0 = time.perf_counter()
+    run = r.forward(w.passes, flags=dlo.TRACE_DIGEST | dlo.ASYNC_ENQUEUE)
+    t_async = time.perf_counter() - t0
+    with pytest.raises(dlo.DLOError) as ei:
+        r.forward(1, want_run=False)
+    assert ei.value.code == -7   # DLO_E_STATE: the plan is still being enqueued
+    run.enqueued()
+    tr = run.trace()
+    say(f"the call returned after {t_async * 1e3:.2f} ms (synchronous call: {t_sync * 1e3:.2f} ms)")
+    _check_trace(tr, w.n_blocks, w.passes, _expected_regions(w, stack, w.k))
+    assert tr == tr_sync
+    assert np.array_equal(r.x_host().view(np.uint32), x_sync.view(np.uint32))
+    assert t_async < 0.5 * t_sync
+    run.close()
+    r.close()
+
+
 @pytest.mark.parametrize("n_resident", [1, 3, 7, 8])
 def test_resident_layers_match_full_streaming(n_resident):
     """Blocks 0 .. R-1 resident, the rest streamed: the slot trace and digests follow

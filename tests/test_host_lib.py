@@ -272,7 +272,9 @@ def test_forward_validation_errors():
     assert _status(F, slots=(0x100000, 0x100000 + 256)) == "DLO_E_ARG"   # overlapping slots
     assert _status(F, slots=(0, 0x100000)) == "DLO_E_ARG"
     assert _status(F, flags=64) == "DLO_E_ARG"
-    assert _status(F, flags=16) == "DLO_E_ARG"
+    assert _status(F, flags=32) == "DLO_E_ARG"
+    # DLO_ASYNC_ENQUEUE hands the run to a thread that dlo_run_enqueued joins: a handle is required
+    assert _status(F, flags=dlo.ASYNC_ENQUEUE, want_run=False) == "DLO_E_ARG"
     assert _status(F, flags=dlo.RESIDENT) == "DLO_E_ARG"        # no resident pointers
     assert _status(F, n_resident=-1) == "DLO_E_ARG"
     assert _status(F, n_resident=4) == "DLO_E_ARG"              # more than the 3 blocks
