@@ -249,6 +249,8 @@ struct dlo_host_store {
   std::vector<uint8_t> packed;                 // per block flag
   // two bounded pinned staging buffers (one slot each) for pageable blocks
   char *staging[2] = {nullptr, nullptr};
+  std::mutex mu;                        // guards enqueuing
+  dlo_run *enqueuing = nullptr;         // DLO_ASYNC_ENQUEUE run still being enqueued
   hipEvent_t staging_free[2] = {nullptr, nullptr};    // DMA out of buffer j done
   int64_t staging_bytes = 0;
   int64_t staged_uses = 0;
@@ -271,6 +273,7 @@ struct dlo_run {
   // DLO_ASYNC_ENQUEUE: the thread enqueuing the program, its status and message,
   // and its own copy of the caller's arguments
   const dlo_plan *plan = nullptr;
+  dlo_host_store *store = nullptr;
   std::thread worker;
   int enqueue_rc = 0;
   std::string enqueue_msg;
@@ -281,10 +284,18 @@ struct dlo_run {
 // Joins a DLO_ASYNC_ENQUEUE run's enqueue thread (no-op otherwise) and lets the
 // plan start runs again.
 void finish_enqueue(dlo_run *r) {
-  if (!r || !r->worker.joinable()) return;
-  r->worker.join();
-  std::lock_guard<std::mutex> lk(r->plan->mu);
-  if (r->plan->enqueuing == r) r->plan->enqueuing = nullptr;
+  if (!r) return;
+  if (r->worker.joinable()) r->worker.join();
+  if (r->plan) {
+    std::lock_guard<std::mutex> lk(r->plan->mu);
+    if (r->plan->enqueuing == r) r->plan->enqueuing = nullptr;
+    r->plan = nullptr;
+  }
+  if (r->store) {
+    std::lock_guard<std::mutex> lk(r->store->mu);
+    if (r->store->enqueuing == r) r->store->enqueuing = nullptr;
+    r->store = nullptr;
+  }
 }
 
 namespace {
@@ -720,6 +731,7 @@ void dlo_plan_destroy(dlo_plan *plan) {
     std::lock_guard<std::mutex> lk(plan->mu);
     if (plan->enqueuing) {   // a run still being enqueued: let it finish enqueuing
       if (plan->enqueuing->worker.joinable()) plan->enqueuing->worker.join();
+      plan->enqueuing->plan = nullptr;
       plan->enqueuing = nullptr;
     }
     reap_detached(plan, true);
@@ -795,6 +807,14 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 
 void dlo_host_store_destroy(dlo_host_store *store) {
   if (!store) return;
+  {   // a run still being enqueued reads the store: let it finish enqueuing
+    std::lock_guard<std::mutex> lk(store->mu);
+    if (store->enqueuing) {
+      if (store->enqueuing->worker.joinable()) store->enqueuing->worker.join();
+      store->enqueuing->store = nullptr;
+      store->enqueuing = nullptr;
+    }
+  }
   for (int j = 0; j < 2; ++j) {
     if (store->staging_free[j]) {
       (void)hipEventSynchronize(store->staging_free[j]);
@@ -1456,8 +1476,6 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
       run->res_blocks.assign(a->resident_blocks, a->resident_blocks + n_res);
       run->args.resident_blocks = run->res_blocks.data();
     }
-    run->plan = plan;
-    plan->enqueuing = run;
     dlo_host_store *st = const_cast<dlo_host_store *>(store);
     try {
       run->worker = std::thread([plan, st, run, prog, resident]() {
@@ -1467,9 +1485,15 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
         run->enqueue_rc = rc;
       });
     } catch (...) {
-      plan->enqueuing = nullptr;
-      run_free(run);
+      run_free(run);   // nothing enqueued
       return fail(DLO_E_HOSTMEM, "could not start the enqueue thread");
+    }
+    run->plan = plan;
+    plan->enqueuing = run;
+    if (st && !resident) {
+      std::lock_guard<std::mutex> slk(st->mu);
+      run->store = st;
+      st->enqueuing = run;
     }
     *run_out = run;
     return ok();
