@@ -187,10 +187,10 @@ int dlo_host_store_create_ex(const dlo_plan *plan, uint32_t flags, int64_t pinne
 int dlo_host_store_info(const dlo_host_store *store, int32_t *pinned_blocks,
                         int64_t *pinned_bytes, int32_t *staged_blocks);
 
-/* Destroys the store.  Copies that read it must have completed: the caller
- * synchronises the copy stream of every run that used it first.  A
- * DLO_ASYNC_ENQUEUE run still being enqueued from it is joined here first (its
- * copies must then still be synchronised before the call). */
+/* Destroys the store once nothing reads it: a DLO_ASYNC_ENQUEUE run still
+ * being enqueued from it is joined first, then the call waits for the last copy
+ * placed from it (every placement records an event on its copy stream; runs of
+ * one plan are ordered, so that copy is the last of all). */
 void dlo_host_store_destroy(dlo_host_store *store);
 
 /* Packs blocks [b_begin, b_end): blocks[i] describes block b_begin + i and must

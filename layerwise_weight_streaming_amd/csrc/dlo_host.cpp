@@ -251,6 +251,7 @@ struct dlo_host_store {
   char *staging[2] = {nullptr, nullptr};
   std::mutex mu;                        // guards enqueuing
   dlo_run *enqueuing = nullptr;         // DLO_ASYNC_ENQUEUE run still being enqueued
+  hipEvent_t last_copy = nullptr;       // recorded after every placement from the store
   hipEvent_t staging_free[2] = {nullptr, nullptr};    // DMA out of buffer j done
   int64_t staging_bytes = 0;
   int64_t staged_uses = 0;
@@ -815,6 +816,10 @@ void dlo_host_store_destroy(dlo_host_store *store) {
       store->enqueuing = nullptr;
     }
   }
+  if (store->last_copy) {   // the copies that read the store have completed
+    (void)hipEventSynchronize(store->last_copy);
+    (void)hipEventDestroy(store->last_copy);
+  }
   for (int j = 0; j < 2; ++j) {
     if (store->staging_free[j]) {
       (void)hipEventSynchronize(store->staging_free[j]);
@@ -1059,8 +1064,19 @@ const void *from_staging(const dlo_host_store *, const char *staging, int, int, 
 // call would not wait, made the runtime serialise the copy and compute streams
 // of the whole run: measured overlap 0 on the Super stack.)  `begin`
 // (optional) is recorded on s just before the DMAs.  Returns a dlo status.
+int place_copies(const dlo_plan *plan, dlo_host_store *st, int b, char *dst, hipStream_t s, hipEvent_t begin);
+
 int place(const dlo_plan *plan, dlo_host_store *st, int b, char *dst, hipStream_t s,
           hipEvent_t begin = nullptr) {
+  int rc = DLO_OK;
+  if (!st->last_copy)
+    rc = check_hip(hipEventCreateWithFlags(&st->last_copy, hipEventDisableTiming), "hipEventCreate");
+  if (!rc) rc = place_copies(plan, st, b, dst, s, begin);
+  if (!rc) rc = check_hip(hipEventRecord(st->last_copy, s), "hipEventRecord");
+  return rc;
+}
+
+int place_copies(const dlo_plan *plan, dlo_host_store *st, int b, char *dst, hipStream_t s, hipEvent_t begin) {
   if (st->pinned[b]) {
     if (begin) {
       int rc = check_hip(hipEventRecord(begin, s), "hipEventRecord");
