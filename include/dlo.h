@@ -307,10 +307,11 @@ int dlo_plan_schedule_ex(const dlo_plan *plan, int32_t passes, int32_t n_residen
 typedef struct {
   void *slot[2];            /* device, slot_bytes each, distinct (unused if nothing streams) */
   int64_t slot_bytes;       /* capacity of each slot */
-  float *x;                 /* device fp32 [tokens, x_row_stride], updated in place; 16-B
-                               aligned, x_row_stride % 4 == 0 (else DLO_E_ARG) */
+  float *x;                 /* device fp32 [batch x tokens, x_row_stride], updated in place;
+                               16-B aligned, x_row_stride % 4 == 0 (else DLO_E_ARG) */
   int64_t x_row_stride;     /* elements; >= the widest block's d */
-  const float *cond;        /* device fp32 [>= widest d]: conditioning vector */
+  const float *cond;        /* device fp32 [batch, cond_stride]: a conditioning vector per
+                               sample (>= widest d floats each) */
   void *workspace;          /* device, >= dlo_plan_workspace_bytes(plan, tokens) */
   int64_t workspace_bytes;
   void *compute_stream;     /* hipStream_t */
@@ -329,6 +330,16 @@ typedef struct {
   const void *const *resident_blocks; /* device pointer per resident block (entries 0 .. R-1,
                                          or all with DLO_RESIDENT), holding the block's slot
                                          image (see dlo_place_block); NULL entry: DLO_E_ARG */
+  int32_t batch;            /* samples, 0 read as 1 (< 0: DLO_E_ARG).  Sample b is rows
+                               b*tokens .. (b+1)*tokens - 1 of x and row b of cond; every block
+                               runs the samples one after another on its slot (a quantised
+                               block's weights dequantised once), so one copy of a block serves
+                               the whole batch.  The workspace is per sample
+                               (dlo_plan_workspace_bytes of tokens).  With DLO_TRACE_TIMING the
+                               kernel times are the first sample's; t_compute_* span the batch. */
+  int32_t reserved0;        /* 0 */
+  int64_t cond_stride;      /* floats between the samples' conditioning vectors; 0: the widest
+                               block's d; between 1 and the widest d - 1: DLO_E_ARG */
 } dlo_forward_args;
 
 /* Enqueues `passes` passes of the stack.  x is updated on the compute stream;

@@ -72,7 +72,8 @@ class ForwardArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64), ("compute_stream", ctypes.c_void_p),
                 ("copy_stream", ctypes.c_void_p), ("tokens", ctypes.c_int32),
                 ("passes", ctypes.c_int32), ("flags", ctypes.c_uint32), ("n_resident", ctypes.c_int32),
-                ("resident_blocks", ctypes.POINTER(ctypes.c_void_p))]
+                ("resident_blocks", ctypes.POINTER(ctypes.c_void_p)),
+                ("batch", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("cond_stride", ctypes.c_int64)]
 
 
 class SlotEvent(ctypes.Structure):
@@ -488,7 +489,7 @@ class Run:
 
 def forward_stack(plan, store, *, x, x_row_stride, cond, workspace, workspace_bytes,
                   compute_stream, copy_stream, tokens, passes, slots=(0, 0), slot_bytes=0,
-                  flags=0, resident_blocks=None, n_resident=0, want_run=True):
+                  flags=0, resident_blocks=None, n_resident=0, want_run=True, batch=1, cond_stride=0):
     """dlo_forward_stack; device pointers and streams as integers."""
     a = ForwardArgs()
     a.slot[0], a.slot[1] = slots
@@ -498,6 +499,7 @@ def forward_stack(plan, store, *, x, x_row_stride, cond, workspace, workspace_by
     a.compute_stream, a.copy_stream = compute_stream, copy_stream
     a.tokens, a.passes, a.flags = tokens, passes, flags
     a.n_resident = n_resident
+    a.batch, a.cond_stride = batch, cond_stride
     keep = None
     if resident_blocks is not None:
         keep = (ctypes.c_void_p * len(resident_blocks))(*resident_blocks)

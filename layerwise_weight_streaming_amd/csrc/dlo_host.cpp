@@ -1160,7 +1160,8 @@ Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, 
 // row to E4M3, times the weight's codes and per-tensor scale ([Doc] "Request
 // and loading constraints", online FP8 linears).
 hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forward_args *a,
-                         const Workspace &w, hipStream_t s, hipEvent_t *kernel_end) {
+                         const Workspace &w, hipStream_t s, hipEvent_t *kernel_end, float *x,
+                         bool prep) {
   const int d = bp.d, H = bp.heads, dh = d / H, T = a->tokens;
   auto P = [&](int lp) { return base + bp.logical_byte(lp); };
   auto F = [&](int lp) { return reinterpret_cast<const float *>(P(lp)); };
@@ -1180,7 +1181,7 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
       S8[i] = reinterpret_cast<const float *>(base + bp.param_byte(kFp8Scale[i]));
       if (i == 0 || w8a8) continue;
       const int64_t n = kWeightD2[i] * d * d;
-      if ((e = dlo::launch_dequant_fp8(W8[i], n, S8[i], dst, s)) != hipSuccess) return e;
+      if (prep && (e = dlo::launch_dequant_fp8(W8[i], n, S8[i], dst, s)) != hipSuccess) return e;
       Wt[i] = dst;
       dst += n;
     }
@@ -1194,7 +1195,8 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
       W8[i] = reinterpret_cast<const uint8_t *>(P(kWeightP[i]));
       SM[i] = reinterpret_cast<const uint8_t *>(sc);
       if (w8a8 && i > 0) continue;   // W8A8: only the adaLN weight runs in bf16
-      e = bp.kind == KIND_DIT_INT8
+      e = !prep ? hipSuccess
+          : bp.kind == KIND_DIT_INT8
               ? dlo::launch_dequant_int8(reinterpret_cast<const int8_t *>(P(kWeightP[i])), rows, cols,
                                          reinterpret_cast<const float *>(sc), dst, s)
               : dlo::launch_dequant_mxfp8(reinterpret_cast<const uint8_t *>(P(kWeightP[i])), rows, cols,
@@ -1207,7 +1209,6 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
     for (int i = 0; i < 5; ++i) Wt[i] = reinterpret_cast<const uint16_t *>(P(kWeightP[i]));
   }
   if (kernel_end && (e = hipEventRecord(kernel_end[0], s)) != hipSuccess) return e;
-  float *x = a->x;
   const int64_t ldx = a->x_row_stride;
   const float *mod = w.mod;
   // q and k from one GEMM; v from a second one that stores V^T, the layout the
@@ -1289,6 +1290,9 @@ int validate_forward(const dlo_plan *plan, const dlo_host_store *store, const dl
   if (!plan || !a) return fail(DLO_E_ARG, "NULL plan or args");
   if (a->flags & ~(DLO_TRACE_DIGEST | DLO_TRACE_TIMING | DLO_RESIDENT | DLO_FP8_COMPUTE | DLO_ASYNC_ENQUEUE))
     return fail(DLO_E_ARG, "unknown flags 0x%x", a->flags);
+  if (a->batch < 0) return fail(DLO_E_ARG, "batch %d < 0", a->batch);
+  if (a->cond_stride < 0 || (a->cond_stride > 0 && a->cond_stride < plan->max_d))
+    return fail(DLO_E_ARG, "cond_stride %lld below the widest block %d", (long long)a->cond_stride, plan->max_d);
   const int n = (int)plan->blocks.size();
   if (!(a->flags & DLO_RESIDENT) && (a->n_resident < 0 || a->n_resident > n))
     return fail(DLO_E_ARG, "n_resident %d not in [0, %d]", a->n_resident, n);
@@ -1352,8 +1356,10 @@ namespace {
 // fills the staging buffers of pageable blocks.  Returns a dlo status.
 int enqueue_program(const dlo_plan *plan, dlo_host_store *store, const dlo_forward_args *a, dlo_run *run,
                     const std::vector<dlo_sched_op> &prog, bool resident) {
-  constexpr int TEV = 3 + DLO_KERNELS_PER_BLOCK;  // copy begin, copy end, compute begin, kernels
+  constexpr int TEV = 4 + DLO_KERNELS_PER_BLOCK;  // copy begin, copy end, compute begin, kernels, compute end
   hipStream_t cs = (hipStream_t)a->compute_stream, ps = (hipStream_t)a->copy_stream;
+  const int batch = a->batch < 1 ? 1 : a->batch;
+  const int64_t cond_stride = a->cond_stride > 0 ? a->cond_stride : plan->max_d;
   const Workspace w = carve(a->workspace, plan->max_d, a->tokens, plan->max_fp8_d, plan->max_q_d, plan->max_mx_d, plan->max_i8_d);
   hipEvent_t t0 = run->timing ? run->tev.back() : nullptr;
   auto tev = [&](int64_t t, int j) { return run->tev[(size_t)(t * TEV + j)]; };
@@ -1406,8 +1412,16 @@ int enqueue_program(const dlo_plan *plan, dlo_host_store *store, const dlo_forwa
         if (run->digest)
           HIP(dlo::launch_digest(base, offs, lens, bp.n_groups, run->d_digest + 2 * op.step, cs));
         if (run->timing) HIP(hipEventRecord(tev(op.step, 2), cs));
-        if (e == hipSuccess)
-          HIP(block_forward(bp, base, a, w, cs, run->timing ? &run->tev[(size_t)(op.step * TEV + 3)] : nullptr));
+        // the batch's samples one after another on the slot's weights (a quantised
+        // block's dequantised weights made once); each sample's SiLU(c) first
+        for (int b = 0; b < batch && e == hipSuccess; ++b) {
+          if (batch > 1) HIP(dlo::launch_silu(a->cond + b * cond_stride, w.silu_c, plan->max_d, cs));
+          if (e == hipSuccess)
+            HIP(block_forward(bp, base, a, w, cs,
+                              run->timing && b == 0 ? &run->tev[(size_t)(op.step * TEV + 3)] : nullptr,
+                              a->x + b * (int64_t)a->tokens * a->x_row_stride, b == 0));
+        }
+        if (run->timing) HIP(hipEventRecord(tev(op.step, 3 + DLO_KERNELS_PER_BLOCK), cs));
         if (run->digest)
           HIP(dlo::launch_digest(base, offs, lens, bp.n_groups, run->d_digest + 2 * op.step + 1, cs));
         break;
@@ -1448,7 +1462,7 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
   run->timing = a->flags & DLO_TRACE_TIMING;
   run->digest = a->flags & DLO_TRACE_DIGEST;
   const int64_t total = (int64_t)steps.size();
-  constexpr int TEV = 3 + DLO_KERNELS_PER_BLOCK;  // copy begin, copy end, compute begin, kernels
+  constexpr int TEV = 4 + DLO_KERNELS_PER_BLOCK;  // copy begin, copy end, compute begin, kernels, compute end
 
   // --- resources (events, digest buffer): failures here have enqueued nothing
   (void)hipGetDevice(&run->device);
@@ -1554,7 +1568,7 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
       }
     }
     if (run->timing) {
-      constexpr int TEV = 3 + DLO_KERNELS_PER_BLOCK;
+      constexpr int TEV = 4 + DLO_KERNELS_PER_BLOCK;
       hipEvent_t t0 = run->tev.back();
       auto since = [&](hipEvent_t ev) {
         float ms = -1.f;
@@ -1570,7 +1584,7 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
           r.t_copy_end = since(ev(1));
         }
         r.t_compute_begin = since(ev(2));
-        r.t_compute_end = since(ev(3 + DLO_KERNELS_PER_BLOCK - 1));
+        r.t_compute_end = since(ev(3 + DLO_KERNELS_PER_BLOCK));
         float prev = r.t_compute_begin;
         for (int j = 0; j < DLO_KERNELS_PER_BLOCK; ++j) {
           const float tj = since(ev(3 + j));

@@ -17,14 +17,14 @@ class StackRunner:
     blocks: [(d_model, n_heads, [(name, dtype, numel)])] -- the plan's shapes.
     """
 
-    def __init__(self, blocks, k, tokens, D, pinned=True, device=0, store_mode=None, pinned_limit=0):
+    def __init__(self, blocks, k, tokens, D, pinned=True, device=0, store_mode=None, pinned_limit=0, batch=1):
         import torch
 
         self.torch = torch
         self.dev = torch.device("cuda", device)
         self.plan = Plan(blocks, k)
         self.store = HostStore(self.plan, pinned=pinned, mode=store_mode, pinned_limit=pinned_limit)
-        self.tokens, self.D = tokens, D
+        self.tokens, self.D, self.batch = tokens, D, batch
         self.n_blocks = len(blocks)
         sb = self.plan.slot_bytes
         # exactly two slots, each the size of the largest block
@@ -33,8 +33,8 @@ class StackRunner:
         self.slot_alloc_bytes = torch.cuda.memory_allocated(self.dev) - before
         self.ws_bytes = self.plan.workspace_bytes(tokens)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.dev)
-        self.x = torch.zeros((tokens, D), dtype=torch.float32, device=self.dev)
-        self.cond = torch.zeros((D,), dtype=torch.float32, device=self.dev)
+        self.x = torch.zeros((batch * tokens, D), dtype=torch.float32, device=self.dev)
+        self.cond = torch.zeros((batch, D) if batch > 1 else (D,), dtype=torch.float32, device=self.dev)
         self.compute = torch.cuda.Stream(device=self.dev)
         self.copy = torch.cuda.Stream(device=self.dev)
         self.resident = None
@@ -86,7 +86,7 @@ class StackRunner:
             tokens=self.tokens, passes=passes,
             slots=(self.slots[0].data_ptr(), self.slots[1].data_ptr()),
             slot_bytes=self.plan.slot_bytes, flags=flags, resident_blocks=res_ptrs,
-            n_resident=n_resident, want_run=want_run)
+            n_resident=n_resident, want_run=want_run, batch=self.batch, cond_stride=self.D)
 
     def synchronize(self):
         self.compute.synchronize()

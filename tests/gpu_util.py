@@ -83,10 +83,10 @@ def fp8_blocks(w, stack, which=None):
     return out
 
 
-def make_runner_params(w, blocks, k=None, pinned=True):
+def make_runner_params(w, blocks, k=None, pinned=True, batch=1):
     """A runner over explicit per-block parameter lists (any schema form)."""
     from layerwise_weight_streaming_amd.runner import StackRunner
     specs = [(w.width(b), w.heads(b), [(nm, dt, int(a.size)) for nm, dt, a in ps]) for b, ps in enumerate(blocks)]
-    r = StackRunner(specs, w.k if k is None else k, w.tokens, w.D, pinned=pinned)
+    r = StackRunner(specs, w.k if k is None else k, w.tokens, w.D, pinned=pinned, batch=batch)
     r.pack(0, [(w.width(b), w.heads(b), ps) for b, ps in enumerate(blocks)])
     return r

@@ -279,6 +279,46 @@ def test_async_enqueue_staged_store(mode, limit_blocks):
     r.close()
 
 
+@pytest.mark.parametrize("form,flags", [("bf16", 0), ("fp8", 0), ("fp8", dlo.FP8_COMPUTE)],
+                         ids=["bf16", "fp8_w8a16", "fp8_w8a8"])
+def test_batch_is_its_samples_one_by_one(form, flags):
+    """A batch of 3 samples (own x rows, own conditioning) through one streamed run: every
+    block's copy serves the three, and each sample's result is bit-identical to a run of
+    that sample alone; the slot trace and digests are the single-sample ones.  fp8: the
+    dequantised weights (W8A16) are made once per block step and reused by the samples."""
+    require_gpu()
+    w = synth.WORKLOADS["tiny"]
+    B = 3
+    say(f"batch {B}, {form}, flags {flags}")
+    stack = synth.make_stack(w, 31)
+    blocks = fp8_blocks(w, stack) if form == "fp8" else stack.blocks
+    xs = [synth.activations(40 + b, w.tokens, w.D) for b in range(B)]
+    cs = [synth.conditioning(40 + b, w.D) for b in range(B)]
+    r1 = make_runner_params(w, blocks)
+    want, tr1 = [], None
+    for b in range(B):
+        r1.set_inputs(xs[b], cs[b])
+        run = r1.forward(w.passes, flags=flags | dlo.TRACE_DIGEST)
+        tr1 = run.trace()
+        want.append(r1.x_host())
+        run.close()
+    r1.close()
+    rb = make_runner_params(w, blocks, batch=B)
+    rb.set_inputs(np.concatenate(xs, axis=0), np.stack(cs, axis=0))
+    run = rb.forward(w.passes, flags=flags | dlo.TRACE_DIGEST | dlo.TRACE_TIMING)
+    tr = run.trace()
+    kt = run.kernel_times()
+    got = rb.x_host()
+    run.close()
+    rb.close()
+    for b in range(B):
+        assert np.array_equal(got[b * w.tokens:(b + 1) * w.tokens].view(np.uint32), want[b].view(np.uint32)), b
+    strip = lambda t: [{k: v for k, v in e.items() if not k.startswith("t_")} for e in t]
+    assert strip(tr) == strip(tr1)
+    assert all(e["t_compute_end"] >= e["t_compute_begin"] >= 0 for e in tr)
+    assert kt.shape == (len(tr), dlo.KERNELS_PER_BLOCK) and np.all(kt >= 0)
+
+
 @pytest.mark.parametrize("n_resident", [1, 3, 7, 8])
 def test_resident_layers_match_full_streaming(n_resident):
     """Blocks 0 .. R-1 resident, the rest streamed: the slot trace and digests follow

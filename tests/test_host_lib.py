@@ -275,6 +275,8 @@ def test_forward_validation_errors():
     assert _status(F, flags=32) == "DLO_E_ARG"
     # DLO_ASYNC_ENQUEUE hands the run to a thread that dlo_run_enqueued joins: a handle is required
     assert _status(F, flags=dlo.ASYNC_ENQUEUE, want_run=False) == "DLO_E_ARG"
+    assert _status(F, batch=-1) == "DLO_E_ARG"
+    assert _status(F, batch=2, cond_stride=p.block_info(0)["d_model"] - 1) == "DLO_E_ARG"
     assert _status(F, flags=dlo.RESIDENT) == "DLO_E_ARG"        # no resident pointers
     assert _status(F, n_resident=-1) == "DLO_E_ARG"
     assert _status(F, n_resident=4) == "DLO_E_ARG"              # more than the 3 blocks
