@@ -45,18 +45,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 // from Abramowitz & Stegun (1964) formula 7.1.26: erfc(x) = (a1 t + ... + a5 t^5)
 // exp(-x^2), t = 1 / (1 + p x), |error in erf| <= 1.5e-7 -- far below the bf16
 // rounding of the stored activation, at half the VALU work of the library erff.
-// z >= 0: z - 0.5 z erfc(x); z < 0: 0.5 z erfc(x).
+// The constants are folded: g = erfc(x) / 2 = (a1' t + ... + a5' t^5)
+// exp2(-log2(e) z^2 / 2), ai' = ai / 2, t = 1 / (1 + (p / sqrt 2) |z|).  Then
+// z Phi(z) = z - z g for z >= 0 and z g for z < 0, i.e. max(z, 0) - |z g| for
+// both signs: 12 VALU instructions, two of them transcendental.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float x = fabsf(z) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, x, 1.0f));
-  float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
-  poly = __builtin_fmaf(poly, t, 1.421413741f);
-  poly = __builtin_fmaf(poly, t, -0.284496736f);
-  poly = __builtin_fmaf(poly, t, 0.254829592f);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.2316418882663604f, fabsf(z), 1.0f));
+  float poly = __builtin_fmaf(0.5307027145f, t, -0.7265760135f);
+  poly = __builtin_fmaf(poly, t, 0.7107068705f);
+  poly = __builtin_fmaf(poly, t, -0.142248368f);
+  poly = __builtin_fmaf(poly, t, 0.127414796f);
   poly *= t;
-  const float erfc_x = poly * __builtin_amdgcn_exp2f(-1.4426950408889634f * x * x);
-  const float h = 0.5f * z * erfc_x;
-  return z >= 0.f ? z - h : h;
+  const float g = poly * __builtin_amdgcn_exp2f(z * -0.7213475204444817f * z);
+  return fmaxf(z, 0.f) - fabsf(z * g);
 }
 
 // XCD-aware tile order.  Workgroup w is dispatched to XCD w % 8; renumber so
