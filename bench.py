@@ -271,28 +271,67 @@ def mfma_sustained(torch, dev, iters=2000, reps=3):
 
 
 def library_gemm(torch, dev, T, d, reps=5):
-    """hipBLASLt (torch.matmul on bf16) on the block's five GEMM shapes, for context
-    only (the path never calls it): A [T, K] times B^T with B [N, K] row-major, as
-    libdlo's GEMMs take them, no bias or epilogue; median of reps after a warm call."""
+    """hipBLASLt (through torch) on the block's five GEMM shapes, for context only
+    (the path never calls it): A [T, K] times B^T with B [N, K] row-major, as
+    libdlo's GEMMs take them; median of reps after a warm call.
+
+    "ms": the bare product (torch.matmul, bf16 out, no epilogue).
+    "ms_with_epilogue": the product plus the epilogue libdlo fuses, done the
+    cheapest way torch offers: q,k and v: addmm with the bias (hipBLASLt's bias
+    epilogue; v without libdlo's transposed store); fc1: _addmm_activation with
+    GELU (hipBLASLt's bias + GELU epilogue, the tanh form, cheaper than erf);
+    out and fc2: the product in fp32 (mm with out_dtype, else bf16 widened),
+    then y += bias and X += gate * y on the fp32 residual (two elementwise
+    passes)."""
     shapes = {"gemm_qk": (2 * d, d), "gemm_v_t": (d, d), "gemm_out_residual": (d, d),
               "gemm_fc1_gelu": (4 * d, d), "gemm_fc2_residual": (d, 4 * d)}
     g = torch.Generator(device="cpu").manual_seed(11)
-    out = {}
-    for name, (N, K) in shapes.items():
-        A = (torch.randn(T, K, generator=g) * 0.5).to(torch.bfloat16).to(dev)
-        B = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16).to(dev)
-        torch.matmul(A, B.t())
+
+    def med(f):
+        f()
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            C = torch.matmul(A, B.t())
+            f()
             e1.record()
             torch.cuda.synchronize(dev)
             ts.append(e0.elapsed_time(e1))
-            del C
-        ms = float(np.median(ts))
-        out[name] = {"M": T, "N": N, "K": K, "ms": ms, "TFLOPs": 2 * T * N * K / (ms * 1e-3) / 1e12}
+        return float(np.median(ts))
+
+    out = {}
+    for name, (N, K) in shapes.items():
+        A = (torch.randn(T, K, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+        B = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+        bias = (torch.randn(N, generator=g) * 0.1).to(dev)
+        ms = med(lambda: torch.matmul(A, B.t()))
+        rec = {"M": T, "N": N, "K": K, "ms": ms, "TFLOPs": 2 * T * N * K / (ms * 1e-3) / 1e12}
+        if name.endswith("_residual"):
+            X = torch.randn(T, N, generator=g).to(dev)
+            gate = (torch.randn(N, generator=g) * 0.1).to(dev)
+
+            def prod32():
+                try:
+                    return torch.mm(A, B.t(), out_dtype=torch.float32), "mm out_dtype=float32"
+                except Exception:
+                    return torch.matmul(A, B.t()).float(), "bf16 matmul widened to fp32"
+            rec["epilogue"] = prod32()[1] + ", y += bias, X += gate * y"
+
+            def step():
+                y = prod32()[0]
+                y.add_(bias)
+                X.addcmul_(y, gate)
+            rec["ms_with_epilogue"] = med(step)
+            del X
+        elif name == "gemm_fc1_gelu":
+            bb = bias.to(torch.bfloat16)
+            rec["epilogue"] = "_addmm_activation(use_gelu=True)"
+            rec["ms_with_epilogue"] = med(lambda: torch._addmm_activation(bb, A, B.t(), use_gelu=True))
+        else:
+            bb = bias.to(torch.bfloat16)
+            rec["epilogue"] = "addmm (bias)"
+            rec["ms_with_epilogue"] = med(lambda: torch.addmm(bb, A, B.t()))
+        out[name] = rec
         del A, B
     torch.cuda.empty_cache()
     return out
@@ -591,8 +630,8 @@ def main():
 
     if args.library_gemm:
         lib_gemm = library_gemm(torch, dev, T, w.width(0))
-        log("hipBLASLt on the block's GEMM shapes: " +
-            ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in lib_gemm.items()))
+        log("hipBLASLt on the block's GEMM shapes (bare / with the epilogue): " +
+            ", ".join(f"{k} {v['ms']:.3f} / {v['ms_with_epilogue']:.3f} ms" for k, v in lib_gemm.items()))
 
     blocks_done = n * P * args.steps
     result = {
@@ -634,7 +673,8 @@ def main():
         "env": environment(torch, dev),
     }
     if args.library_gemm:
-        result["library_gemm"] = {"note": "hipBLASLt via torch.matmul, bf16, no epilogue; context only",
+        result["library_gemm"] = {"note": "hipBLASLt through torch, bf16; ms: bare product, "
+                                          "ms_with_epilogue: with the epilogue libdlo fuses, by torch; context only",
                                   **lib_gemm}
 
     if not args.no_verify:
