@@ -94,6 +94,14 @@ def test_tiny_stack_ragged_token_counts(tokens):
     _run_and_compare("tiny", passes=3, seed=8, tokens=tokens)
 
 
+@pytest.mark.parametrize("n_blocks,passes", [(1, 1), (1, 3), (2, 3)])
+def test_short_stacks(n_blocks, passes):
+    # one block: a single step prefetches nothing; over several passes the block's
+    # hook prefetches the block itself into the other slot.  Two blocks: the even
+    # ring, where the plain parity and the prefetched slot agree.
+    _run_and_compare("tiny", n_blocks=n_blocks, passes=passes, seed=11)
+
+
 def test_8blk_stack_streamed():
     _run_and_compare("8blk")
 
