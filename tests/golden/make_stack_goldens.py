@@ -17,7 +17,10 @@ Cases (BASELINE-style workloads, seeded):
 * ``irregular``: the irregular stack's first 5 blocks (widths 2048, 3072,
   4096, 2048, 3072 in a residual of width 4096) at its own 8192 tokens, three
   passes (15 steps: an odd block count crosses the pass boundary twice),
-  checkpoints after steps 5, 10 and 15.
+  checkpoints after steps 5, 10 and 15;
+* ``super``: the Super-shaped stack's first 3 blocks (d = 5120, 40 heads,
+  28 800 tokens) over two passes (6 steps: the odd count crosses the pass
+  boundary at full size), checkpoints after steps 3 and 6.
 
 Output: tests/golden/stack_<case>.npz with ``rows`` (25 token indices), ``x0``
 (input rows, float64), ``steps`` (checkpoint step counts) and ``ref`` (the
@@ -25,7 +28,7 @@ oracle's float64 rows stored as float32, [len(steps), len(rows), D]: the
 rounding, 2^-24 relative, is far below the 2e-2 parity bound).
 
 Usage: python tests/golden/make_stack_goldens.py [nano] [irregular]
-(about 10 min for nano and 3 min for irregular on 8 cores).
+(about 10 min for nano, 3 min for irregular and 25 min for super on 8 cores).
 """
 from __future__ import annotations
 
@@ -47,6 +50,7 @@ CASES = {
     # name: (workload, seed, n_blocks, passes, tokens, checkpoint steps, sampled rows)
     "nano": ("nano", 4, 72, 2, None, (24, 72, 144), 48),
     "irregular": ("irregular", 2, 5, 3, None, (5, 10, 15), 48),
+    "super": ("super", 6, 3, 2, None, (3, 6), 48),
 }
 
 

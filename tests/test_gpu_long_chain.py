@@ -14,7 +14,9 @@ are compared with them:
   (one pass) and 144 (two chained passes in one call: the pass boundary);
 * ``irregular``: 5 blocks of widths 2048, 3072, 4096, 2048, 3072 in a residual
   of width 4096 at the workload's own 8192 tokens (k = 4), checkpoints after
-  1, 2 and 3 passes.
+  1, 2 and 3 passes;
+* ``super``: the first 3 Super-shaped blocks (d = 5120, 40 heads, 28 800
+  tokens, k = 2), checkpoints after 1 and 2 passes.
 
 Metrics at each checkpoint, over the sampled rows: max|gpu - ref| / max|ref|
 and the same on the accumulated update x - x0, both <= 2e-2.  The per-step
@@ -125,11 +127,13 @@ def test_nano_full_stack_two_passes():
     say("nano update error along the chain (24, 72, 144 steps): " + ", ".join(f"{e[1]:.3e}" for e in errs))
 
 
-def test_irregular_prefix_full_tokens():
+def _prefix_by_passes(name):
+    """The golden's first n blocks at the workload's own size, one run per pass
+    count; trace and slot digests checked on every run."""
     require_gpu()
-    g = _golden("irregular")
+    g = _golden(name)
     seed, n, passes, T, D = (int(v) for v in g["meta"])
-    w = synth.WORKLOADS["irregular"]
+    w = synth.WORKLOADS[name]
     assert (T, D) == (w.tokens, w.D)
     x0 = synth.activations(seed, T, D)
     c = synth.conditioning(seed, D)
@@ -137,11 +141,21 @@ def test_irregular_prefix_full_tokens():
     r, dig = _runner(w, seed, n, digests=True)
     errs = []
     for p in range(1, passes + 1):
-        say(f"irregular: {n} blocks, T={T}, {p} passes")
+        say(f"{name}: {n} blocks, T={T}, {p} passes")
         r.set_inputs(x0, c)
         run = r.forward(p, flags=dlo.TRACE_DIGEST)
         _check_trace(run.trace(), n, p, dig)
-        errs.append(_compare(f"irregular {p} passes", r.x_host(), g, p - 1))
+        errs.append(_compare(f"{name} {p} passes", r.x_host(), g, p - 1))
         run.close()
     r.close()
-    say("irregular update error along the chain: " + ", ".join(f"{e[1]:.3e}" for e in errs))
+    say(f"{name} update error along the chain: " + ", ".join(f"{e[1]:.3e}" for e in errs))
+
+
+def test_irregular_prefix_full_tokens():
+    _prefix_by_passes("irregular")
+
+
+def test_super_prefix_full_size_two_passes():
+    # three full Super-shaped blocks (d = 5120, 28 800 tokens, 944 MB slots): the
+    # odd count takes the tail -> head correction at the pass boundary
+    _prefix_by_passes("super")
