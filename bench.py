@@ -395,7 +395,7 @@ def cpu_tiny_stack(seed, threads):
             "tokens_per_s": w.tokens * w.passes / dt, "s_per_stack": dt}
 
 
-def cpu_baseline(w, seed, n_blocks, rows=640, full_block=False):
+def cpu_baseline(w, seed, n_blocks, rows=4096, full_block=False):
     """The oracle, untouched, on a bounded sample: sampled output rows of the first block.
 
     dit_block_rows computes LN1 and the k/v projections for every token and the

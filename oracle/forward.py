@@ -13,7 +13,7 @@ The pages never spell out the block (the model code is used unchanged, [Jul]
 "Module Architecture").  The block below is the plainest adaLN-Zero DiT block
 that matches the stated workloads (adaLN 6-way modulation from a conditioning
 vector, LayerNorm, fused QKV, attention, output projection, 4d GELU MLP,
-residual).  Readings, all listed in the design doc:
+residual).  Readings where the pages leave a step open:
 
 * mod = SiLU(c[:d]) @ W_ada^T + b_ada, split into six d-wide chunks in the
   order shift1, scale1, gate1, shift2, scale2, gate2;

@@ -8,7 +8,7 @@ loader first finalises a 1-byte weight and an fp32 scale per tensor, and the
 method then shards and reassembles those tensors by their recorded layouts like
 any other dtype group ([Doc] "Request and loading constraints", the paragraph
 on online FP8, INT8 and MXFP8 linears).  The pages do not fix the FP8 variant or
-the scaling rule; the readings here (listed in the design doc as well):
+the scaling rule; the readings here:
 
 * the code is OCP FP8 E4M3 ("E4M3FN"): 1 sign, 4 exponent (bias 7), 3 mantissa
   bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN; there is
@@ -100,8 +100,8 @@ def dequantize(codes: np.ndarray, scale) -> np.ndarray:
 def quantize_rows(x):
     """Per-row (per-token) dynamic E4M3 of an activation matrix [M, K].
 
-    The reading of an online FP8 linear's input (the pages leave it open; listed
-    in the design doc): row r gets scale_r = amax_r / 448 in float32 (NaN entries
+    The reading of an online FP8 linear's input (the pages leave it open): row r
+    gets scale_r = amax_r / 448 in float32 (NaN entries
     ignored, 1.0 for an all-zero row), and each element the E4M3 code nearest to
     float32(x) / scale_r, the division in float32, ties to the even code,
     saturating at +-448.  Returns (codes uint8 [M, K], scales float32 [M]).

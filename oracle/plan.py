@@ -9,7 +9,7 @@ rank-ordered concatenation of the shards).  Slot sizing follows [Aug] section 3
 and [Jul] "Double-Buffer Memory Bound": two buffers, each sized to the largest
 block.
 
-Readings where the pages are silent (listed in the design doc as well):
+Readings where the pages are silent:
 
 * dtype groups are ordered by first appearance in the parameter list;
 * inside a slot, group g's region starts at the previous region's end rounded

@@ -9,7 +9,7 @@ online MXFP8, an fp8 weight plus an e8m0 block scale; all are plain 1-byte
 dtypes packed in physical order like any other group ([Doc] "Request and
 loading constraints", the paragraph on online FP8, INT8 and MXFP8 linears).
 They fix neither the INT8 scale's granularity nor the MX block rule; the
-readings here (listed in the design doc as well):
+readings here:
 
 * INT8: symmetric, one fp32 scale per output channel (row of the [out, in]
   weight): scale_r = amax_r(|w|) / 127 in float32 (1.0 for an all-zero row,

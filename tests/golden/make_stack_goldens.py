@@ -9,7 +9,7 @@ bf16, then dropped, so a 72-block stack fits in memory), and stores, at a few
 checkpoints along the chain, the residual rows of a fixed random sample of
 tokens together with the input rows.
 
-Cases (BASELINE-style workloads, seeded):
+Cases (seeded, at the workloads' own shapes):
 
 * ``nano``: the Nano-shaped stack in full -- 72 blocks, d = 3072, 24 heads,
   4096 tokens -- two chained passes (144 block steps), checkpoints after block
