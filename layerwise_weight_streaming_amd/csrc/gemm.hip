@@ -488,8 +488,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   const int nk = K / KSTAGE;
   const int frow = lane & 31, fk = lane >> 5;
 
-  // all fragments of one stage: bf16, 2 k-steps x (4 A rows, 2 B columns);
-  // F8, one k-step x (4 A rows, 2 B columns) of two 16-B halves each
+  // all fragments of one stage in 32 x 32 tiles: INT8, 2 k-steps of 32 x (4 A
+  // rows, 2 B columns); F8, one k-step x (4 A rows, 2 B columns) of two 16-B
+  // halves each
   struct FragsB {
     bf16x8 a[2][4], b[2][NJ];
   };
@@ -622,7 +623,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
                                                        ? __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0)
                                                        : __builtin_amdgcn_mfma_i32_32x32x32_i8(bv, av, c, 0, 0, 0));
           }
-    } else if constexpr (M16) {
+    } else {
+      static_assert(M16, "bf16 operands run on 16x16x32 tiles");
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -630,16 +632,6 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
           acc16[i][j] = EPI == EPI_BIAS_T
                             ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc16[i][j], 0, 0, 0)
                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc16[i][j], 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = EPI == EPI_BIAS_T
-                            ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0)
-                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][j], f.a[kk][i], acc[i][j], 0, 0, 0);
     }
   };
   // Barrier opening global phase p.  Before it, this wave's loads of the tile
