@@ -396,7 +396,8 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
  * quantised h and h2 itself (counted in ln1_modulate / ln2_modulate), so
  * quant_h and quant_h2 stay 0, and for MXFP8 the fc1 GEMM's epilogue writes the
  * quantised u (quant_u stays 0); INT8 quantises all four inputs in their own
- * passes. */
+ * passes.  A slot that launches nothing records no event (each timed event
+ * between two kernels costs the stream a few microseconds) and reads exactly 0. */
 #define DLO_KERNELS_PER_BLOCK 14
 int dlo_run_kernel_times(dlo_run *run, float *ms, int64_t cap, int64_t *n_out);
 /* name of kernel j (0 <= j < DLO_KERNELS_PER_BLOCK) of a block forward */

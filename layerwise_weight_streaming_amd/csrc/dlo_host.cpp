@@ -266,8 +266,11 @@ struct dlo_run {
   hipEvent_t final_ev = nullptr;
   bool timing = false, digest = false;
   std::vector<dlo_slot_event> recs;
-  // timing events, per step: copy begin, copy end, compute begin, kernel ends [8]
+  // timing events, per step: copy begin, copy end, compute begin, kernel ends
+  // [DLO_KERNELS_PER_BLOCK], compute end; kmask[t] bit j: kernel slot j of step
+  // t launched work and recorded its end event (an empty slot records none)
   std::vector<hipEvent_t> tev;
+  std::vector<uint32_t> kmask;
   uint64_t *d_digest = nullptr;
   bool finished = false;
   std::vector<float> kernel_ms;
@@ -1160,8 +1163,8 @@ Workspace carve(void *ws, int32_t max_d, int64_t T, int32_t fp8_d, int32_t q_d, 
 // row to E4M3, times the weight's codes and per-tensor scale ([Doc] "Request
 // and loading constraints", online FP8 linears).
 hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forward_args *a,
-                         const Workspace &w, hipStream_t s, hipEvent_t *kernel_end, float *x,
-                         bool prep) {
+                         const Workspace &w, hipStream_t s, hipEvent_t *kernel_end, uint32_t *kmask,
+                         float *x, bool prep) {
   const int d = bp.d, H = bp.heads, dh = d / H, T = a->tokens;
   auto P = [&](int lp) { return base + bp.logical_byte(lp); };
   auto F = [&](int lp) { return reinterpret_cast<const float *>(P(lp)); };
@@ -1208,7 +1211,16 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
   } else {
     for (int i = 0; i < 5; ++i) Wt[i] = reinterpret_cast<const uint16_t *>(P(kWeightP[i]));
   }
-  if (kernel_end && (e = hipEventRecord(kernel_end[0], s)) != hipSuccess) return e;
+  // kernel slot j's end event is recorded only when the slot launched work: an
+  // event record between kernels costs the stream a few microseconds, and an
+  // empty slot's duration is 0
+  auto mark = [&](bool launched, int j) {
+    if (!kernel_end || !launched) return hipSuccess;
+    *kmask |= 1u << j;
+    return hipEventRecord(kernel_end[j], s);
+  };
+  const bool dequant = prep && ((fp8 && !w8a8) || i8 || mx);
+  if ((e = mark(dequant, 0)) != hipSuccess) return e;
   const int64_t ldx = a->x_row_stride;
   const float *mod = w.mod;
   // q and k from one GEMM; v from a second one that stores V^T, the layout the
@@ -1243,9 +1255,10 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
     return mx ? dlo::launch_quant_rows_mx(A, K, T, K, q8, K, mxs, T64, s)
               : dlo::launch_quant_rows_fp8(A, K, T, K, q8, K, qs, s);
   };
-#define DLO_STEP(call, j)                                                   \
+#define DLO_STEP_IF(launched, call, j)                                      \
   if ((e = (call)) != hipSuccess) return e;                                 \
-  if (kernel_end && (e = hipEventRecord(kernel_end[j], s)) != hipSuccess) return e;
+  if ((e = mark((launched), j)) != hipSuccess) return e;
+#define DLO_STEP(call, j) DLO_STEP_IF(true, call, j)
   DLO_STEP(fp8 ? dlo::launch_adaln_gemv_fp8(W8[0], S8[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s)
                : dlo::launch_adaln_gemv(Wt[0], w.silu_c, F(P_ADA_B), w.mod, 6 * d, d, s), 1)
   // W8A8 FP8 / MXFP8: LayerNorm + modulate writes the next linear's codes
@@ -1258,14 +1271,14 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
     return dlo::launch_ln_modulate(x, ldx, T, d, F(pw), F(pb), F(pe), shift_, scale_, w.h, s);
   };
   DLO_STEP(ln(P_N1_W, P_N1_B, P_N1_EPS, mod + 0 * d, mod + 1 * d), 2)
-  DLO_STEP(i8 ? quant(w.h, d) : hipSuccess, 3)
+  DLO_STEP_IF(i8 && w8a8, i8 ? quant(w.h, d) : hipSuccess, 3)
   DLO_STEP(linear(w.h, d, 1, 0, 2 * d, F(P_QKV_B), nullptr, qk, 2 * d, dlo::EPI_BIAS), 4)
   DLO_STEP(linear(w.h, d, 1, 2 * d, d, F(P_QKV_B) + 2 * d, nullptr, vt, ldvt, dlo::EPI_BIAS_T), 5)
   DLO_STEP(dlo::launch_attention(qk, 2 * d, vt, ldvt, T, H, dh, attn, d, s), 6)
-  DLO_STEP(quant(attn, d), 7)
+  DLO_STEP_IF(w8a8, quant(attn, d), 7)
   DLO_STEP(linear(attn, d, 2, 0, d, F(P_OUT_B), mod + 2 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 8)
   DLO_STEP(ln(P_N2_W, P_N2_B, P_N2_EPS, mod + 3 * d, mod + 4 * d), 9)
-  DLO_STEP(i8 ? quant(w.h, d) : hipSuccess, 10)
+  DLO_STEP_IF(i8 && w8a8, i8 ? quant(w.h, d) : hipSuccess, 10)
   if (w8a8 && mx) {
     // MXFP8: the fc1 epilogue quantises u itself (32-column blocks never leave
     // its column tile); u's codes and scales take the place of the bf16 u
@@ -1273,15 +1286,16 @@ hipError_t block_forward(const BlockPlan &bp, const char *base, const dlo_forwar
     uint8_t *us = uq + align_up((int64_t)T * 4 * d, DLO_ALIGN);
     DLO_STEP(dlo::launch_gemm_mxfp8(q8, d, mxs, T64, W8[3], d, SM[3], kWeightRows[3] * d, T, 4 * d, d,
                                     F(P_FC1_B), nullptr, uq, 4 * d, dlo::EPI_GELU_MX, s, us, T64), 11)
-    DLO_STEP(hipSuccess, 12)
+    DLO_STEP_IF(false, hipSuccess, 12)
     DLO_STEP(dlo::launch_gemm_mxfp8(uq, 4 * d, us, T64, W8[4], 4 * d, SM[4], kWeightRows[4] * d, T, d, 4 * d,
                                     F(P_FC2_B), mod + 5 * d, x, ldx, dlo::EPI_GATED_RESIDUAL, s), 13)
   } else {
     DLO_STEP(linear(w.h, d, 3, 0, 4 * d, F(P_FC1_B), nullptr, u, 4 * d, dlo::EPI_BIAS_GELU), 11)
-    DLO_STEP(quant(u, 4 * d), 12)
+    DLO_STEP_IF(w8a8, quant(u, 4 * d), 12)
     DLO_STEP(linear(u, 4 * d, 4, 0, d, F(P_FC2_B), mod + 5 * d, x, ldx, dlo::EPI_GATED_RESIDUAL), 13)
   }
 #undef DLO_STEP
+#undef DLO_STEP_IF
   return hipSuccess;
 }
 
@@ -1419,6 +1433,7 @@ int enqueue_program(const dlo_plan *plan, dlo_host_store *store, const dlo_forwa
           if (e == hipSuccess)
             HIP(block_forward(bp, base, a, w, cs,
                               run->timing && b == 0 ? &run->tev[(size_t)(op.step * TEV + 3)] : nullptr,
+                              run->timing ? &run->kmask[(size_t)op.step] : nullptr,
                               a->x + b * (int64_t)a->tokens * a->x_row_stride, b == 0));
         }
         if (run->timing) HIP(hipEventRecord(tev(op.step, 3 + DLO_KERNELS_PER_BLOCK), cs));
@@ -1473,6 +1488,7 @@ int dlo_forward_stack(const dlo_plan *plan, const dlo_host_store *store,
   if (!rc && !plan->last_done)
     rc = check_hip(hipEventCreateWithFlags(&plan->last_done, hipEventDisableTiming), "hipEventCreate");
   if (!rc && run->timing) {
+    run->kmask.assign((size_t)total, 0u);
     run->tev.assign((size_t)(total * TEV + 1), nullptr);
     for (auto &e : run->tev)
       if (!rc) rc = check_hip(hipEventCreate(&e), "hipEventCreate");
@@ -1587,9 +1603,13 @@ int dlo_slot_trace(dlo_run *run, dlo_slot_event *out, int64_t cap, int64_t *n_ou
         r.t_compute_end = since(ev(3 + DLO_KERNELS_PER_BLOCK));
         float prev = r.t_compute_begin;
         for (int j = 0; j < DLO_KERNELS_PER_BLOCK; ++j) {
-          const float tj = since(ev(3 + j));
-          run->kernel_ms[(size_t)(t * DLO_KERNELS_PER_BLOCK + j)] = tj - prev;
-          prev = tj;
+          float dt = 0.f;   // an empty slot recorded no event
+          if (run->kmask[(size_t)t] >> j & 1u) {
+            const float tj = since(ev(3 + j));
+            dt = tj - prev;
+            prev = tj;
+          }
+          run->kernel_ms[(size_t)(t * DLO_KERNELS_PER_BLOCK + j)] = dt;
         }
       }
     }

@@ -197,6 +197,15 @@ def test_timing_trace_is_ordered():
     tr = run.trace()
     kt = run.kernel_times()
     assert kt.shape == (16, dlo.KERNELS_PER_BLOCK) and np.all(kt >= 0)
+    # a bf16 block launches nothing in the dequantisation and W8A8 quantisation
+    # slots: they read exactly 0; every other slot ran a kernel
+    names = dlo.kernel_names()
+    empty = [j for j, nm in enumerate(names) if nm == "dequant_weights" or nm.startswith("quant_")]
+    assert len(empty) == 5
+    assert np.all(kt[:, empty] == 0)
+    assert np.all(np.delete(kt, empty, axis=1) > 0)
+    for e, row in zip(tr, kt):
+        assert row.sum() <= e["t_compute_end"] - e["t_compute_begin"] + 1e-3
     for e in tr:
         assert 0 <= e["t_copy_begin"] <= e["t_copy_end"] <= e["t_compute_end"]
         assert e["t_copy_end"] <= e["t_compute_begin"] + 1e-3 <= e["t_compute_end"] + 1e-3
