@@ -404,3 +404,30 @@ def test_fp8_weight_groups_streamed(name, n_blocks, tokens, which):
     r.forward(w.passes, resident=True, want_run=False)
     assert np.array_equal(r.x_host().view(np.uint32), x_gpu.view(np.uint32))
     r.close()
+
+
+def test_device_weight_memory_is_two_slots_at_any_depth():
+    """The device holds weights in exactly two slots of the largest block whatever
+    the stack's depth: the runner's slot allocation is two slots (torch rounds an
+    allocation up to 512 B), and a streamed run allocates no device memory of its
+    own (measured as the device's free memory around a second, warm run)."""
+    torch = require_gpu()
+    w = synth.WORKLOADS["8blk"]
+    slot_bytes = None
+    for n in (1, 3, 8):
+        say(f"device weight memory, {n} blocks")
+        stack = synth.make_stack(w, 2, n)
+        r = make_runner(w, stack)
+        sb = r.plan.slot_bytes
+        slot_bytes = sb if slot_bytes is None else slot_bytes
+        assert sb == slot_bytes                      # the slot is the largest block, not the stack
+        assert 0 <= r.slot_alloc_bytes - 2 * sb < 1024
+        r.forward(w.passes, want_run=False)
+        r.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        run = r.forward(w.passes, flags=dlo.TRACE_TIMING)
+        run.trace()
+        free1 = torch.cuda.mem_get_info()[0]
+        assert free0 - free1 < (1 << 20), (n, free0 - free1)
+        run.close()
+        r.close()
