@@ -431,3 +431,27 @@ def test_device_weight_memory_is_two_slots_at_any_depth():
         assert free0 - free1 < (1 << 20), (n, free0 - free1)
         run.close()
         r.close()
+
+
+def test_streamed_run_waits_for_the_previous_run():
+    """A streamed run of a plan is enqueued only once the plan's previous run has
+    completed (copies queued behind a run still executing ran slower): the second of
+    two back-to-back calls returns only after the first run's GPU work is done."""
+    import time
+    require_gpu()
+    w = synth.WORKLOADS["8blk"]
+    stack = synth.make_stack(w, 3)
+    r = make_runner(w, stack)
+    r.forward(2, want_run=False)
+    r.synchronize()
+    t0 = time.perf_counter()
+    run = r.forward(40, flags=dlo.TRACE_TIMING)   # 320 block steps, a few hundred ms of copies
+    r.forward(1, want_run=False)
+    t_second = time.perf_counter() - t0
+    tr = run.trace()
+    gpu_ms = max(e["t_compute_end"] for e in tr)
+    say(f"first run {gpu_ms:.1f} ms on the GPU; the second call returned after {t_second * 1e3:.1f} ms")
+    assert gpu_ms > 50
+    assert t_second * 1e3 >= 0.8 * gpu_ms
+    run.close()
+    r.close()
